@@ -1,0 +1,224 @@
+"""Python binding of the canonical convolution (argument marshalling only).
+
+``conv_bind``, ``conv_out_shape``, ``conv_plan`` and ``conv_run`` wrap the C
+ABI calls of the same names one to one.  ``conv`` chains them for torch
+tensors on the GPU: torch provides the device memory (output, workspace) and
+the current HIP stream; every step of the computation runs in the library's
+kernels.  The ATen-style helpers (``conv1d`` ... ``_convolution``) only
+translate ATen's arguments into the canonical ones (executorch PR #25084,
+"Add triton::convolution and the conv routing framework", description: every
+ATen convolution overload maps onto the one canonical op).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+from . import _abi as A
+
+_TORCH_DT = {torch.float32: A.F32, torch.float16: A.F16, torch.bfloat16: A.BF16}
+
+
+class ConvError(RuntimeError):
+    def __init__(self, status: int, msg: str = ""):
+        self.status = status
+        name = A.lib().conv_status_string(status).decode()
+        super().__init__(f"{name}" + (f": {msg}" if msg else ""))
+
+
+def _check(status: int, msg: str = "") -> None:
+    if status != A.OK:
+        raise ConvError(status, msg)
+
+
+# ---------------------------------------------------------------- descriptors --
+
+def describe(t: Optional[torch.Tensor]) -> Optional[A.ConvTensor]:
+    """Tensor descriptor (sizes, element strides, dtype) of a torch tensor."""
+    if t is None:
+        return None
+    if t.dtype not in _TORCH_DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() > A.MAX_RANK:
+        raise ValueError("at most 5 dims")
+    d = A.ConvTensor()
+    d.rank = t.dim()
+    d.dtype = _TORCH_DT[t.dtype]
+    for i, (s, st) in enumerate(zip(t.shape, t.stride())):
+        d.sizes[i] = s
+        d.strides[i] = st
+    return d
+
+
+def tensor_desc(sizes: Sequence[int], strides: Sequence[int], dtype: torch.dtype) -> A.ConvTensor:
+    d = A.ConvTensor()
+    d.rank = len(sizes)
+    d.dtype = _TORCH_DT[dtype]
+    for i, (s, st) in enumerate(zip(sizes, strides)):
+        d.sizes[i] = s
+        d.strides[i] = st
+    return d
+
+
+def _list(v) -> Tuple[int, ...]:
+    if v is None:
+        return ()
+    if isinstance(v, int):
+        return (v,)
+    return tuple(int(a) for a in v)
+
+
+def make_args(*, transposed: bool = False, groups: int = 1, stride=None, padding_before=None,
+              padding_after=None, dilation=None, output_padding=None,
+              padding_mode: str = "explicit") -> A.ConvArgs:
+    a = A.ConvArgs()
+    a.transposed = int(bool(transposed))
+    a.padding_mode = {"explicit": A.PAD_EXPLICIT, "same": A.PAD_SAME, "valid": A.PAD_VALID}[padding_mode]
+    a.groups = int(groups)
+    pb, pa = _list(padding_before), _list(padding_after)
+    if len(pb) != len(pa):
+        raise ValueError("padding_before and padding_after need the same number of values")
+    for name, vals in (("stride", _list(stride)), ("padding_before", pb), ("padding_after", pa),
+                       ("dilation", _list(dilation)), ("output_padding", _list(output_padding))):
+        if len(vals) > A.MAX_SPATIAL:
+            raise ValueError(f"{name}: at most 3 values")
+        arr = getattr(a, name)
+        for i, v in enumerate(vals):
+            arr[i] = v
+    a.n_stride = len(_list(stride))
+    a.n_padding = len(pb)
+    a.n_dilation = len(_list(dilation))
+    a.n_output_padding = len(_list(output_padding))
+    return a
+
+
+# ------------------------------------------------------------ the four calls --
+
+def conv_bind(x: A.ConvTensor, w: A.ConvTensor, b: Optional[A.ConvTensor],
+              args: A.ConvArgs) -> A.ConvDesc:
+    d = A.ConvDesc()
+    err = ctypes.create_string_buffer(256)
+    st = A.lib().conv_bind(ctypes.byref(x), ctypes.byref(w), ctypes.byref(b) if b is not None else None,
+                           ctypes.byref(args), ctypes.byref(d), err, len(err))
+    _check(st, err.value.decode())
+    return d
+
+
+def conv_out_shape(d: A.ConvDesc) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
+    y = A.ConvTensor()
+    _check(A.lib().conv_out_shape(ctypes.byref(d), ctypes.byref(y)))
+    return tuple(y.sizes[: y.rank]), tuple(y.strides[: y.rank])
+
+
+def conv_plan(d: A.ConvDesc, y: A.ConvTensor, force_kernel: Union[int, str, None] = None) -> A.ConvPlan:
+    if force_kernel is None:
+        force_kernel = os.environ.get("MICONV_FORCE_KERNEL", "auto")
+    if isinstance(force_kernel, str):
+        force_kernel = A.KERNELS[force_kernel]
+    p = A.ConvPlan()
+    _check(A.lib().conv_plan(ctypes.byref(d), ctypes.byref(y), int(force_kernel), ctypes.byref(p)))
+    if os.environ.get("MICONV_LOG"):
+        print(f"[miconv] plan kernel={kernel_name(p.kernel)} variant={p.variant} grid={p.grid[0]} "
+              f"block={p.block} vec_ok={p.vec_ok} ws={p.workspace_bytes}", flush=True)
+    return p
+
+
+def conv_run(p: A.ConvPlan, x_ptr: int, w_ptr: int, b_ptr: Optional[int], y_ptr: int,
+             ws_ptr: Optional[int] = None, ws_bytes: int = 0, stream: Optional[int] = None) -> None:
+    _check(A.lib().conv_run(ctypes.byref(p), x_ptr, w_ptr, b_ptr, y_ptr, ws_ptr, ws_bytes, stream))
+
+
+def kernel_name(k: int) -> str:
+    return A.lib().conv_kernel_name(k).decode()
+
+
+# -------------------------------------------------------------- torch helper --
+
+class Prepared:
+    """bind + out_shape + plan for fixed tensor descriptors (reusable)."""
+
+    def __init__(self, x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], args: A.ConvArgs,
+                 force_kernel=None):
+        self.desc = conv_bind(describe(x), describe(w), describe(b), args)
+        self.sizes, self.strides = conv_out_shape(self.desc)
+        self.dtype = x.dtype
+        self.plan = conv_plan(self.desc, tensor_desc(self.sizes, self.strides, x.dtype), force_kernel)
+
+    def empty_output(self, device) -> torch.Tensor:
+        return torch.empty_strided(self.sizes, self.strides, dtype=self.dtype, device=device)
+
+    def workspace(self, device) -> Optional[torch.Tensor]:
+        n = int(self.plan.workspace_bytes)
+        return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+    def run(self, x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], y: torch.Tensor,
+            ws: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        conv_run(self.plan, x.data_ptr(), w.data_ptr(), b.data_ptr() if b is not None else None,
+                 y.data_ptr(), ws.data_ptr() if ws is not None else None,
+                 ws.numel() if ws is not None else 0, stream)
+        return y
+
+
+def conv(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None, *, stride=1,
+         padding_before=0, padding_after=0, dilation=1, groups: int = 1, transposed: bool = False,
+         output_padding=0, padding_mode: str = "explicit", force_kernel=None) -> torch.Tensor:
+    """The canonical convolution on GPU tensors (x, w, b share one dtype)."""
+    for t in (x, w) + ((b,) if b is not None else ()):
+        if not t.is_cuda:
+            raise ValueError("the canonical convolution runs on the GPU only; move tensors to cuda")
+    if padding_mode != "explicit":
+        padding_before = padding_after = None
+    args = make_args(transposed=transposed, groups=groups, stride=stride,
+                     padding_before=padding_before, padding_after=padding_after,
+                     dilation=dilation, output_padding=output_padding if transposed else None,
+                     padding_mode=padding_mode)
+    prep = Prepared(x, w, b, args, force_kernel)
+    y = prep.empty_output(x.device)
+    return prep.run(x, w, b, y, prep.workspace(x.device))
+
+
+# ------------------------------------------------------- ATen-style overloads --
+
+def _pad_args(padding):
+    if isinstance(padding, str):
+        return dict(padding_mode=padding)
+    p = _list(padding)
+    return dict(padding_before=p, padding_after=p)
+
+
+def conv1d(input, weight, bias=None, stride=1, padding=0, dilation=1, groups=1):
+    return conv(input, weight, bias, stride=stride, dilation=dilation, groups=groups, **_pad_args(padding))
+
+
+conv2d = conv1d
+conv3d = conv1d
+
+
+def conv_transpose1d(input, weight, bias=None, stride=1, padding=0, output_padding=0, groups=1,
+                     dilation=1):
+    p = _list(padding)
+    return conv(input, weight, bias, stride=stride, padding_before=p, padding_after=p, dilation=dilation,
+                groups=groups, transposed=True, output_padding=output_padding)
+
+
+conv_transpose2d = conv_transpose1d
+conv_transpose3d = conv_transpose1d
+
+
+def convolution(input, weight, bias, stride, padding, dilation, transposed, output_padding, groups):
+    """``aten.convolution``: symmetric padding, explicit transposed flag."""
+    p = _list(padding)
+    return conv(input, weight, bias, stride=stride, padding_before=p, padding_after=p, dilation=dilation,
+                groups=groups, transposed=bool(transposed), output_padding=output_padding)
+
+
+def _convolution(input, weight, bias, stride, padding, dilation, transposed, output_padding, groups,
+                 benchmark=False, deterministic=False, cudnn_enabled=True, allow_tf32=True):
+    """``aten._convolution``: the extra flags select nothing here (fp32 inputs
+    are always computed in full fp32, never in a TF32-class mode)."""
+    return convolution(input, weight, bias, stride, padding, dilation, transposed, output_padding, groups)

@@ -1,0 +1,103 @@
+// Device-side helpers shared by the gfx950 kernels: storage types, exact
+// widening to fp32, round-to-nearest-even narrowing, and MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miconv {
+
+// Storage types: the kernels move raw bits and convert explicitly.
+struct bf16_t { uint16_t u; };
+struct f16_t { uint16_t u; };
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+template <typename T> struct Dt;
+template <> struct Dt<float> {
+    static constexpr int size = 4;
+    static constexpr int code = 0;
+};
+template <> struct Dt<f16_t> {
+    static constexpr int size = 2;
+    static constexpr int code = 1;
+};
+template <> struct Dt<bf16_t> {
+    static constexpr int size = 2;
+    static constexpr int code = 2;
+};
+
+// Widen one element to fp32 (exact for every input type).
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v.u << 16); }
+__device__ __forceinline__ float to_f32(f16_t v)
+{
+    _Float16 h;
+    __builtin_memcpy(&h, &v.u, 2);
+    return (float)h;
+}
+
+// Low / high 16-bit halves of a packed word, widened.
+__device__ __forceinline__ float lo_f32(uint32_t w, bf16_t) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w, bf16_t) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float lo_f32(uint32_t w, f16_t) { return to_f32(f16_t{(uint16_t)(w & 0xffffu)}); }
+__device__ __forceinline__ float hi_f32(uint32_t w, f16_t) { return to_f32(f16_t{(uint16_t)(w >> 16)}); }
+
+// Narrow fp32 to the storage type, rounding to nearest even.
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v)
+{
+    __bf16 h = (__bf16)v;
+    bf16_t r;
+    __builtin_memcpy(&r.u, &h, 2);
+    return r;
+}
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float v)
+{
+    _Float16 h = (_Float16)v;
+    f16_t r;
+    __builtin_memcpy(&r.u, &h, 2);
+    return r;
+}
+
+// Narrow two fp32 values into one packed 32-bit word (lo, hi).
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    T a = from_f32<T>(lo), b = from_f32<T>(hi);
+    return (uint32_t)a.u | ((uint32_t)b.u << 16);
+}
+
+template <typename T> __device__ __forceinline__ T load_elem(const T *p) { return *p; }
+
+// 8-element MFMA step: D(16x16) += A(16x32) * B(32x16) for 2-byte types, with
+// the A/B fragments holding 8 consecutive K elements of one row / column.
+__device__ __forceinline__ void mma_16x16x32(const uint4 &a, const uint4 &b, f32x4 &c, bf16_t)
+{
+    bf16x8 av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_16x16x32(const uint4 &a, const uint4 &b, f32x4 &c, f16_t)
+{
+    f16x8 av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
+}
+
+// fp32: eight 16x16x4 steps cover the same 32-wide K slice.  Lane l's j-th
+// element is K index 8*(l/16) + j; step j feeds element j of every lane, so
+// step j sums K = {j, 8+j, 16+j, 24+j}: together the eight steps sum all 32.
+__device__ __forceinline__ void mma_16x16x32_f32(const float (&a)[8], const float (&b)[8], f32x4 &c)
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+}
+
+}  // namespace miconv

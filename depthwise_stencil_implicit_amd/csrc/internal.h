@@ -1,0 +1,44 @@
+// Host-side internals shared by the binding, planner and launcher.
+#pragma once
+
+#include <cstdint>
+
+#include "../../include/miconv.h"
+
+namespace miconv {
+
+// Output length of one spatial dim (< 1 means no valid output).
+int64_t out_len(int transposed, int64_t L, int64_t k, int64_t s, int64_t pb, int64_t pa, int64_t dil,
+                int64_t op);
+
+// Channels-last-like and not also contiguous-like.
+bool channels_last_like(const conv_tensor &t);
+
+// Batched output descriptor of a canonical call.
+void batched_out(const conv_desc &d, conv_tensor &y);
+
+inline int64_t esize(int32_t dtype) { return dtype == CONV_F32 ? 4 : 2; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Implicit GEMM schedule table (kernel CONV_K_IGEMM / CONV_K_IGEMM_T).
+struct IgemmCfg {
+    int bm, bn, bk;     // workgroup tile: rows, columns, K per step
+    int wm, wn;         // waves along rows / columns (block = 64 * wm * wn)
+};
+const IgemmCfg &igemm_cfg(int variant);
+int igemm_num_cfgs();
+
+// Plan-field indices for the implicit GEMM (plan.tile[]).
+enum { IG_CIG_PAD = 0, IG_COG_PAD = 1, IG_PHASES = 2, IG_MTILES = 3, IG_NTILES = 4, IG_ROWS = 5 };
+
+// Launchers (defined in the .hip files).  `vec` selects the 16-byte path.
+int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *ws,
+                 void *stream, bool vec);
+int launch_plane(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream);
+int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream,
+                bool vec);
+int launch_grp(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream);
+int launch_reduce(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream);
+
+}  // namespace miconv

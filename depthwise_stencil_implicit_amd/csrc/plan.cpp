@@ -1,0 +1,334 @@
+// conv_plan: route a canonical call to a kernel and fix its launch.
+//
+// executorch PR #25084 ("Add triton::convolution and the conv routing
+// framework"), description: each template declares what it supports, tests
+// can force one schedule, and the planner refuses calls whose output layout
+// differs from the one the op computes.
+// executorch PR #25085 ("Route 2-D depthwise and few-channel grouped
+// convolutions to a Triton direct-stencil kernel"), description: depthwise and
+// up-to-8-input-channel grouped 2-D convolutions with dilation 1 and kernels up
+// to 9x9 go to the direct stencil; grouped calls with a wide per-group product
+// stay on the GEMM path.
+// executorch PR #25091 ("Run transposed convolutions on the implicit-GEMM
+// template"), description: transposed calls run on the implicit GEMM with the
+// transposed gather.
+//
+// Routing (host only, deterministic):
+//   transposed                                        -> IGEMM_T
+//   r <= 2, dil 1, k <= 9, groups > 1, Cig <= 8:
+//       few outputs (<= 4 positions, >= 32 taps each) -> REDUCE
+//       depthwise, multiplier 1, channel-contiguous,
+//       compiled (k, s) schedule                       -> DW_CL
+//       grouped (Cig even), fp16/bf16                  -> GRP
+//       otherwise                                      -> PLANE
+//   everything else                                   -> IGEMM
+#include <cstring>
+#include <initializer_list>
+
+#include "internal.h"
+
+namespace miconv {
+bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw);
+int dwcl_strip(int64_t s);
+bool grp_supported(const conv_desc &d);
+void grp_geometry(const conv_desc &d, conv_plan_t &p);
+void reduce_geometry(const conv_desc &d, conv_plan_t &p);
+}  // namespace miconv
+
+namespace {
+
+using namespace miconv;
+
+constexpr int64_t kLdsBudget = 64 * 1024;
+constexpr int64_t kI32 = 0x7fffffffLL;
+
+int64_t numel(const conv_tensor &t)
+{
+    int64_t n = 1;
+    for (int i = 0; i < t.rank; ++i) n *= t.sizes[i];
+    return n;
+}
+
+int64_t cig(const conv_desc &d) { return d.C_in / d.groups; }
+int64_t cog(const conv_desc &d) { return d.C_out / d.groups; }
+
+bool all_dil1(const conv_desc &d)
+{
+    for (int i = 0; i < d.spatial; ++i)
+        if (d.dilation[i] != 1) return false;
+    return true;
+}
+
+bool k_le(const conv_desc &d, int64_t kmax)
+{
+    for (int i = 0; i < d.spatial; ++i)
+        if (d.k[i] > kmax) return false;
+    return true;
+}
+
+bool sizes_fit_i32(const conv_desc &d)
+{
+    for (int i = 0; i < 3; ++i)
+        if (d.in[i] > kI32 / 4 || d.out[i] > kI32 / 4 || d.k[i] > 4096 || d.stride[i] > 65536 ||
+            d.dilation[i] > 65536 || d.padding_before[i] > kI32 / 4 || d.padding_after[i] > kI32 / 4)
+            return false;
+    return d.C_in < kI32 && d.C_out < kI32;
+}
+
+// ---------------------------------------------------------------- supports --
+
+bool stencil_domain(const conv_desc &d)
+{
+    return !d.transposed && (d.spatial == 1 || d.spatial == 2) && cig(d) >= 1 && cig(d) <= 8 && k_le(d, 9);
+}
+
+bool supports_dwcl(const conv_desc &d, const conv_tensor &y)
+{
+    if (!stencil_domain(d) || d.spatial != 2 || !all_dil1(d)) return false;
+    if (cig(d) != 1 || d.groups != d.C_in || d.C_out != d.C_in) return false;
+    if (!dwcl_has_schedule(d.k[0], d.k[1], d.stride[0], d.stride[1])) return false;
+    return d.x.strides[1] == 1 && y.strides[1] == 1;
+}
+
+bool supports_plane(const conv_desc &d) { return stencil_domain(d); }
+
+bool supports_reduce(const conv_desc &d) { return stencil_domain(d); }
+
+bool supports_igemm(const conv_desc &d) { return !d.transposed; }
+bool supports_igemm_t(const conv_desc &d) { return d.transposed != 0; }
+
+bool few_outputs(const conv_desc &d)
+{
+    const int64_t positions = d.out[0] * d.out[1] * d.out[2];
+    const int64_t taps = cig(d) * d.k[0] * d.k[1] * d.k[2];
+    return positions <= 4 && taps >= 32;
+}
+
+int route(const conv_desc &d, const conv_tensor &y)
+{
+    if (d.transposed) return CONV_K_IGEMM_T;
+    if (stencil_domain(d) && all_dil1(d) && d.groups > 1) {
+        if (few_outputs(d)) return CONV_K_REDUCE;
+        if (supports_dwcl(d, y)) return CONV_K_DW_CL;
+        if (cig(d) >= 2 && grp_supported(d)) return CONV_K_GRP;
+        return CONV_K_PLANE;
+    }
+    return CONV_K_IGEMM;
+}
+
+// ---------------------------------------------------------------- geometry --
+
+void geom_dwcl(const conv_desc &d, conv_plan_t &p)
+{
+    const int64_t V = 16 / esize(d.dtype);
+    const int64_t cv = cdiv(d.C_in, V);
+    int64_t cvb = 1;
+    while (cvb * 2 <= cv && cvb * 2 <= 32) cvb *= 2;
+    const int64_t sp = 256 / cvb;
+    const int64_t to = dwcl_strip(d.stride[1]);
+    const int64_t ch_chunks = cdiv(cv, cvb);
+    const int64_t col_chunks = cdiv(d.out[1], sp * to);
+    const int64_t per_row = d.N * col_chunks * ch_chunks;
+    int64_t rh = per_row * d.out[0] / 2048;
+    if (rh < 1) rh = 1;
+    if (rh > d.out[0]) rh = d.out[0];
+    const int64_t row_chunks = cdiv(d.out[0], rh);
+    p.tile[0] = to;
+    p.tile[1] = cvb;
+    p.tile[2] = sp;
+    p.tile[3] = rh;
+    p.tile[4] = ch_chunks;
+    p.tile[5] = col_chunks;
+    p.tile[6] = row_chunks;
+    p.grid[0] = per_row * row_chunks;
+    p.block = 256;
+    p.lds_bytes = (int32_t)(d.k[0] * d.k[1] * cvb * V * 4);
+    const int64_t ev = V;
+    bool vec = d.C_in % ev == 0 && d.x.strides[0] % ev == 0 && d.x.strides[2] % ev == 0 &&
+               d.x.strides[3] % ev == 0 && p.y.strides[0] % ev == 0 && p.y.strides[2] % ev == 0 &&
+               p.y.strides[3] % ev == 0;
+    p.vec_ok = vec ? 1 : 0;
+}
+
+bool geom_plane(const conv_desc &d, conv_plan_t &p)
+{
+    const bool two = d.spatial == 2;
+    const int64_t OH = two ? d.out[0] : 1, OW = two ? d.out[1] : d.out[0];
+    const int64_t KH = two ? d.k[0] : 1, KW = two ? d.k[1] : d.k[0];
+    const int64_t SH = two ? d.stride[0] : 1, SW = two ? d.stride[1] : d.stride[0];
+    const int64_t DH = two ? d.dilation[0] : 1, DW = two ? d.dilation[1] : d.dilation[0];
+    int64_t TW, R, TH;
+    if (!two) {
+        TW = 256;
+        R = 1;
+        TH = 1;
+    } else {
+        TW = OW >= 48 ? 64 : (OW >= 24 ? 32 : 16);
+        R = 2;
+        TH = (256 / TW) * R;
+    }
+    auto lds = [&](int64_t th, int64_t tw) {
+        const int64_t ih = (th - 1) * SH + (KH - 1) * DH + 1;
+        const int64_t iw = (tw - 1) * SW + (KW - 1) * DW + 1;
+        return cig(d) * ih * iw * 4;
+    };
+    while (lds(TH, TW) > kLdsBudget) {
+        if (TH > R)
+            TH /= 2;
+        else if (TW > 1)
+            TW /= 2;
+        else
+            return false;
+    }
+    if (TH % R) R = 1;
+    const int64_t IH = (TH - 1) * SH + (KH - 1) * DH + 1;
+    const int64_t IW = (TW - 1) * SW + (KW - 1) * DW + 1;
+    int64_t mb = 1;
+    while (mb < cog(d) && mb < 16) mb *= 2;
+    p.tile[0] = TH;
+    p.tile[1] = TW;
+    p.tile[2] = R;
+    p.tile[3] = mb;
+    p.tile[4] = IH;
+    p.tile[5] = IW;
+    p.tile[6] = cdiv(OH, TH);
+    p.tile[7] = cdiv(OW, TW);
+    p.grid[0] = d.N * d.groups * p.tile[6] * p.tile[7];
+    p.block = 256;
+    p.lds_bytes = (int32_t)lds(TH, TW);
+    return p.grid[0] <= kI32;
+}
+
+void geom_igemm(const conv_desc &d, conv_plan_t &p)
+{
+    int variant;
+    if (d.dtype == CONV_F32)
+        variant = 3;
+    else if (cog(d) <= 32)
+        variant = 2;
+    else if (cog(d) <= 64)
+        variant = 1;
+    else
+        variant = 0;
+    const IgemmCfg &c = igemm_cfg(variant);
+    const int64_t taps = d.k[0] * d.k[1] * d.k[2];
+    const int64_t cig_pad = round_up(cig(d), c.bk);
+    const int64_t cog_pad = round_up(cog(d) > 0 ? cog(d) : 1, c.bn);
+    int64_t phases = 1, rows = d.N;
+    for (int i = 0; i < 3; ++i) {
+        if (d.transposed) {
+            phases *= d.stride[i];
+            rows *= cdiv(d.out[i], d.stride[i]);
+        } else {
+            rows *= d.out[i];
+        }
+    }
+    p.variant = variant;
+    p.tile[IG_CIG_PAD] = cig_pad;
+    p.tile[IG_COG_PAD] = cog_pad;
+    p.tile[IG_PHASES] = phases;
+    p.tile[IG_MTILES] = cdiv(rows, c.bm);
+    p.tile[IG_NTILES] = cog_pad / c.bn;
+    p.tile[IG_ROWS] = rows;
+    p.grid[0] = d.groups * phases * p.tile[IG_MTILES] * p.tile[IG_NTILES];
+    p.block = 64 * c.wm * c.wn;
+    p.lds_bytes = 0;
+    p.workspace_bytes = round_up(d.groups * cog_pad * taps * cig_pad * esize(d.dtype), 256);
+    const int64_t ev = 16 / esize(d.dtype);
+    bool vec = d.x.strides[1] == 1 && cig(d) % ev == 0 && d.x.strides[0] % ev == 0;
+    for (int i = 0; i < d.spatial; ++i) vec = vec && d.x.strides[2 + i] % ev == 0;
+    p.vec_ok = vec ? 1 : 0;
+}
+
+// Algorithmic FLOPs: 2 per (output element, input channel, tap) term whose
+// input index is an integer -- every tap for forward calls (padding-border
+// taps included, the usual GEMM count), and for transposed calls only the taps
+// whose numerator is divisible by the stride.
+int64_t algorithmic_flops(const conv_desc &d)
+{
+    double terms = (double)d.N * (double)d.C_out * (double)cig(d);
+    for (int i = 0; i < d.spatial; ++i) {
+        if (!d.transposed) {
+            terms *= (double)d.out[i] * (double)d.k[i];
+        } else {
+            int64_t cnt = 0;
+            for (int64_t o = 0; o < d.out[i]; ++o)
+                for (int64_t t = 0; t < d.k[i]; ++t)
+                    if ((o + d.padding_before[i] - t * d.dilation[i]) % d.stride[i] == 0) ++cnt;
+            terms *= (double)cnt;
+        }
+    }
+    return (int64_t)(2.0 * terms);
+}
+
+bool same_layout(const conv_tensor &a, const conv_tensor &b)
+{
+    if (a.rank != b.rank || a.dtype != b.dtype) return false;
+    for (int i = 0; i < a.rank; ++i) {
+        if (a.sizes[i] != b.sizes[i]) return false;
+        if (a.sizes[i] > 1 && a.strides[i] != b.strides[i]) return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force_kernel, conv_plan_t *p)
+{
+    if (!d || !y || !p) return CONV_EINVAL;
+    if (d->spatial < 1 || d->spatial > 3 || d->groups < 1 || d->x.rank != d->spatial + 2) return CONV_EINVAL;
+    conv_tensor expect;
+    if (conv_out_shape(d, &expect) != CONV_OK) return CONV_EINVAL;
+    if (!same_layout(*y, expect)) return CONV_ELAYOUT;
+    if (!sizes_fit_i32(*d)) return CONV_EUNSUPPORTED;
+
+    conv_plan_t plan;
+    std::memset(&plan, 0, sizeof(plan));
+    plan.d = *d;
+    batched_out(*d, plan.y);
+    const conv_tensor &yb = plan.y;
+
+    int k = force_kernel;
+    if (k == CONV_K_AUTO) {
+        k = route(*d, yb);
+    } else {
+        bool ok;
+        switch (k) {
+        case CONV_K_DW_CL: ok = supports_dwcl(*d, yb); break;
+        case CONV_K_PLANE: ok = supports_plane(*d); break;
+        case CONV_K_GRP: ok = stencil_domain(*d) && grp_supported(*d); break;
+        case CONV_K_REDUCE: ok = supports_reduce(*d); break;
+        case CONV_K_IGEMM: ok = supports_igemm(*d); break;
+        case CONV_K_IGEMM_T: ok = supports_igemm_t(*d); break;
+        default: ok = false;
+        }
+        if (!ok) return CONV_EUNSUPPORTED;
+    }
+    plan.kernel = k;
+    switch (k) {
+    case CONV_K_DW_CL: geom_dwcl(*d, plan); break;
+    case CONV_K_PLANE:
+        if (!geom_plane(*d, plan)) {
+            if (force_kernel != CONV_K_AUTO) return CONV_EUNSUPPORTED;
+            plan.kernel = CONV_K_IGEMM;
+            geom_igemm(*d, plan);
+        }
+        break;
+    case CONV_K_GRP: grp_geometry(*d, plan); break;
+    case CONV_K_REDUCE: reduce_geometry(*d, plan); break;
+    default: geom_igemm(*d, plan); break;
+    }
+    if (plan.grid[0] > kI32) return CONV_EUNSUPPORTED;
+
+    int64_t ny = numel(yb);
+    if (ny == 0) plan.grid[0] = 0;
+    int64_t max_off = 0;
+    for (const conv_tensor *t : {&d->x, &d->w, &yb})
+        for (int i = 0; i < t->rank; ++i)
+            if (t->sizes[i] > 0) max_off += (t->sizes[i] - 1) * t->strides[i];
+    plan.index64 = max_off > kI32 ? 1 : 0;
+    plan.flops = algorithmic_flops(*d);
+    plan.bytes = (numel(d->x) + numel(d->w) + (d->has_bias ? d->C_out : 0) + ny) * esize(d->dtype);
+    *p = plan;
+    return CONV_OK;
+}

@@ -1,0 +1,82 @@
+// conv_run: check the call and enqueue the planned kernel(s) on the caller's
+// stream; plus the name/status helpers of the C ABI.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace {
+
+using namespace miconv;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t numel(const conv_tensor &t)
+{
+    int64_t n = 1;
+    for (int i = 0; i < t.rank; ++i) n *= t.sizes[i];
+    return n;
+}
+
+}  // namespace
+
+extern "C" int conv_run(const conv_plan_t *p, const void *x, const void *w, const void *b, void *y,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!p) return CONV_EINVAL;
+    const conv_desc &d = p->d;
+    if (numel(p->y) == 0 || p->grid[0] == 0) return CONV_OK;
+    if (!x || !w || !y) return CONV_EINVAL;
+    if (d.has_bias != (b != nullptr)) return CONV_EINVAL;
+    const uintptr_t es = (uintptr_t)esize(d.dtype);
+    if (!aligned(x, es) || !aligned(w, es) || !aligned(y, es) || (b && !aligned(b, es))) return CONV_EALIGN;
+    if (p->workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < (size_t)p->workspace_bytes) return CONV_EINVAL;
+        if (!aligned(workspace, 16)) return CONV_EALIGN;
+    }
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+        (void)hipGetLastError();
+        return CONV_EDEVICE;
+    }
+    const bool vec = p->vec_ok && aligned(x, 16) && aligned(y, 16);
+    switch (p->kernel) {
+    case CONV_K_DW_CL: return launch_dwcl(*p, x, w, b, y, stream, vec);
+    case CONV_K_PLANE: return launch_plane(*p, x, w, b, y, stream);
+    case CONV_K_GRP: return launch_grp(*p, x, w, b, y, stream);
+    case CONV_K_REDUCE: return launch_reduce(*p, x, w, b, y, stream);
+    case CONV_K_IGEMM:
+    case CONV_K_IGEMM_T: return launch_igemm(*p, x, w, b, y, workspace, stream, vec);
+    default: return CONV_EINVAL;
+    }
+}
+
+extern "C" const char *conv_kernel_name(int32_t kernel)
+{
+    switch (kernel) {
+    case CONV_K_AUTO: return "auto";
+    case CONV_K_DW_CL: return "dw_cl";
+    case CONV_K_PLANE: return "plane";
+    case CONV_K_GRP: return "grp";
+    case CONV_K_REDUCE: return "reduce";
+    case CONV_K_IGEMM: return "igemm";
+    case CONV_K_IGEMM_T: return "igemm_t";
+    default: return "?";
+    }
+}
+
+extern "C" const char *conv_status_string(int32_t status)
+{
+    switch (status) {
+    case CONV_OK: return "ok";
+    case CONV_EINVAL: return "invalid argument";
+    case CONV_EUNSUPPORTED: return "kernel does not support this call";
+    case CONV_ELAYOUT: return "output layout differs from conv_out_shape";
+    case CONV_EALIGN: return "pointer not aligned to its element size";
+    case CONV_EDEVICE: return "no usable GPU or HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int32_t conv_abi_version(void) { return 1; }

@@ -1,0 +1,237 @@
+/*
+ * miconv.h -- C ABI of the MI355X (gfx950) canonical convolution library.
+ *
+ * One canonical convolution op (executorch PR #25084, "Add triton::convolution
+ * and the conv routing framework", description): explicit padding_before and
+ * padding_after per spatial dim, stride, dilation, groups, and separately
+ * defined forward and transposed semantics.
+ *
+ *   forward     y[n, g*Cog+j, o] = b[g*Cog+j]
+ *                 + sum_{c<Cig} sum_t x[n, g*Cig+c, o*s - pb + t*dil] * w[g*Cog+j, c, t]
+ *   transposed  y[n, g*Cog+j, o] = b[g*Cog+j]
+ *                 + sum_{c<Cig} sum_t x[n, g*Cig+c, (o + pb - t*dil)/s] * w[g*Cig+c, j, t]
+ *               where a term exists only when the quotient is an exact integer
+ *               inside the input (executorch PR #25091, "Run transposed
+ *               convolutions on the implicit-GEMM template", description: the
+ *               transposed gather, with the [C_in, C_out/groups, k...] weight
+ *               read with its first two axes swapped).
+ *   Terms whose input index falls outside [0, L) are zero padding (the masked
+ *   loads of the LOOP_BODY_2D template in torch/_inductor/kernel/conv.py).
+ *
+ * Four calls make up the path (the binding, the shared output layout, the
+ * planner and the launch that the PR #25084 description lists):
+ *   conv_bind      tensor descriptors + user arguments -> canonical conv_desc
+ *   conv_out_shape conv_desc -> output sizes and strides
+ *   conv_plan      conv_desc + output descriptor -> kernel choice and launch
+ *   conv_run       plan + device pointers + stream -> asynchronous launch
+ *
+ * Conventions
+ *   - Strides are in elements, not bytes.  Sizes are logical: x is
+ *     [N, C_in, L_1..L_r] whatever its memory order; r = 1..3.  An unbatched x
+ *     ([C_in, L...]) is accepted and gives an unbatched y.
+ *   - x, w, b and y share one dtype.  Accumulation is fp32; the bias is
+ *     added in fp32 and the result rounded once (nearest even) to the dtype.
+ *   - The library keeps no mutable global state and never allocates device
+ *     memory: the caller owns every buffer, the workspace and the stream.
+ *     conv_desc and conv_plan_t are plain caller-owned structs (no destroy
+ *     call); a plan may be reused for any call with the same descriptors.
+ *   - Every function is reentrant.  conv_run does not synchronise.
+ */
+#ifndef MICONV_H
+#define MICONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MICONV_API __attribute__((visibility("default")))
+#else
+#define MICONV_API
+#endif
+
+#define CONV_MAX_RANK 5
+#define CONV_MAX_SPATIAL 3
+
+typedef enum conv_dtype { CONV_F32 = 0, CONV_F16 = 1, CONV_BF16 = 2 } conv_dtype;
+
+typedef enum conv_status {
+    CONV_OK = 0,
+    CONV_EINVAL = 1,       /* arguments violate the op's rules */
+    CONV_EUNSUPPORTED = 2, /* forced kernel outside its supported domain */
+    CONV_ELAYOUT = 3,      /* y's sizes/strides differ from conv_out_shape */
+    CONV_EALIGN = 4,       /* a pointer is not aligned to its element size */
+    CONV_EDEVICE = 5       /* no usable GPU, or a HIP launch/runtime error */
+} conv_status;
+
+typedef enum conv_padding_mode {
+    CONV_PAD_EXPLICIT = 0, /* padding_before / padding_after as given */
+    CONV_PAD_SAME = 1,     /* stride 1 only: total dil*(k-1), before = total/2 */
+    CONV_PAD_VALID = 2     /* no padding */
+} conv_padding_mode;
+
+/* Kernels the planner can choose (also the values accepted by force_kernel). */
+typedef enum conv_kernel {
+    CONV_K_AUTO = -1,
+    CONV_K_DW_CL = 1,   /* depthwise, channel-contiguous input: per-lane register sliding window */
+    CONV_K_PLANE = 2,   /* depthwise / few-channel grouped, any layout: LDS halo tile, fan-out */
+    CONV_K_GRP = 3,     /* few-channel grouped, half types: packed dot2 over input-channel pairs */
+    CONV_K_REDUCE = 4,  /* depthwise / few-channel grouped, few outputs: wavefront reduction over taps */
+    CONV_K_IGEMM = 5,   /* implicit GEMM, forward: on-the-fly im2col tile in LDS, MFMA */
+    CONV_K_IGEMM_T = 6  /* implicit GEMM with the transposed gather, phase-split by stride */
+} conv_kernel;
+
+/* A tensor descriptor: no data pointer, only shape, strides and dtype. */
+typedef struct conv_tensor {
+    int32_t rank;                     /* number of dims (0 = absent) */
+    int32_t dtype;                    /* conv_dtype */
+    int64_t sizes[CONV_MAX_RANK];
+    int64_t strides[CONV_MAX_RANK];   /* elements; entries >= rank are ignored */
+} conv_tensor;
+
+/* User-level arguments, ATen style.  Each per-dimension list has a count:
+ * 0 = use the default (stride 1, padding 0, dilation 1, output_padding 0),
+ * 1 = broadcast the single value to every spatial dim, r = one per dim. */
+typedef struct conv_args {
+    int32_t transposed;               /* 0 forward, 1 transposed */
+    int32_t padding_mode;             /* conv_padding_mode */
+    int64_t groups;                   /* 0 = default 1 */
+    int32_t n_stride, n_padding, n_dilation, n_output_padding;
+    int64_t stride[CONV_MAX_SPATIAL];
+    int64_t padding_before[CONV_MAX_SPATIAL];
+    int64_t padding_after[CONV_MAX_SPATIAL];   /* shares n_padding */
+    int64_t dilation[CONV_MAX_SPATIAL];
+    int64_t output_padding[CONV_MAX_SPATIAL];
+} conv_args;
+
+/* The canonical call.  Spatial arrays hold r entries; the rest are 1 (sizes,
+ * stride, dilation) or 0 (paddings).  x is the batched view of the caller's x
+ * (a leading size-1 dim is added when unbatched); b has rank 0 when absent. */
+typedef struct conv_desc {
+    int32_t spatial;                  /* r = 1..3 */
+    int32_t transposed;
+    int32_t unbatched;
+    int32_t dtype;
+    int32_t has_bias;
+    int32_t reserved0;
+    int64_t N, C_in, C_out, groups;
+    int64_t in[CONV_MAX_SPATIAL];
+    int64_t k[CONV_MAX_SPATIAL];
+    int64_t out[CONV_MAX_SPATIAL];
+    int64_t stride[CONV_MAX_SPATIAL];
+    int64_t padding_before[CONV_MAX_SPATIAL];
+    int64_t padding_after[CONV_MAX_SPATIAL];
+    int64_t dilation[CONV_MAX_SPATIAL];
+    int64_t output_padding[CONV_MAX_SPATIAL];
+    conv_tensor x, w, b;
+} conv_desc;
+
+/* A launch plan.  Produced by conv_plan on the host without any device call. */
+typedef struct conv_plan_t {
+    conv_desc d;
+    conv_tensor y;                    /* batched view of y */
+    int32_t kernel;                   /* conv_kernel */
+    int32_t variant;                  /* kernel-specific schedule id */
+    int32_t vec_ok;                   /* strides allow 16-byte vector access */
+    int32_t index64;                  /* some element offset needs 64 bits */
+    int64_t workspace_bytes;          /* device scratch conv_run needs (0 = none) */
+    int64_t tile[8];                  /* kernel-specific tile parameters */
+    int64_t grid[3];
+    int32_t block;
+    int32_t lds_bytes;
+    int64_t flops;                    /* algorithmic FLOPs of the call */
+    int64_t bytes;                    /* algorithmic bytes: x + w + b read once, y written once */
+} conv_plan_t;
+
+/*
+ * conv_bind -- map tensor descriptors and ATen-style arguments onto the
+ * canonical op, filling defaults and validating (executorch PR #25084,
+ * description: the binding maps every convolution overload onto the
+ * canonical op, filling defaults and validating the arguments).
+ *
+ *   x  [N, C_in, L...] or unbatched [C_in, L...]; r = rank - 2 (or - 1).
+ *   w  forward [C_out, C_in/groups, k...]; transposed [C_in, C_out/groups, k...].
+ *   b  [C_out] or NULL.
+ *   a  user arguments (see conv_args).  'same' needs stride 1 and splits the
+ *      total dil*(k-1) as before = total/2, after = total - before.
+ *   out  receives the canonical call.
+ *   err, err_len  optional buffer for a message on failure (may be NULL).
+ *
+ * Returns CONV_OK or CONV_EINVAL (rank outside 3..5 / 2..4, dtype mismatch,
+ * channel or group mismatch, non-positive stride/dilation/groups, negative
+ * padding, output_padding >= max(stride, dilation) or nonzero on a forward
+ * call, an output length < 1, a negative size or stride).
+ */
+MICONV_API int conv_bind(const conv_tensor *x, const conv_tensor *w, const conv_tensor *b,
+              const conv_args *a, conv_desc *out, char *err, size_t err_len);
+
+/*
+ * conv_out_shape -- the output layout, shared by the op and its planner so
+ * the output is allocated once and kernels only write into it (executorch
+ * PR #25084, description: the output layout ATen's convolution returns).
+ *
+ *   Sizes: forward O = floor((L + pb + pa - dil*(k-1) - 1)/s) + 1,
+ *          transposed O = (L-1)*s - pb - pa + dil*(k-1) + op + 1.
+ *   Strides: dense; channels-last (C fastest, then the last spatial dim, ...,
+ *   then N) when x or w is channels-last-like and not also contiguous-like,
+ *   contiguous otherwise.  Unbatched calls give an unbatched y.
+ *
+ * Returns CONV_OK, or CONV_EINVAL for a NULL or inconsistent descriptor.
+ */
+MICONV_API int conv_out_shape(const conv_desc *d, conv_tensor *y);
+
+/*
+ * conv_plan -- route the call and fix the launch (executorch PR #25084,
+ * description: templates declare what they support and the planner routes
+ * every overload; PR #25085, description: depthwise and up-to-8-channel
+ * grouped 2-D convolutions with dilation 1 and kernels up to 9x9 go to the
+ * direct stencil; PR #25091, description: transposed calls run on the
+ * implicit GEMM with the transposed gather).  Host only, deterministic.
+ *
+ *   d            canonical call from conv_bind.
+ *   y            output descriptor; must equal conv_out_shape(d) exactly.
+ *   force_kernel CONV_K_AUTO, or a conv_kernel to run (tests pin schedules).
+ *   p            receives the plan.
+ *
+ * Returns CONV_OK, CONV_ELAYOUT (y differs from conv_out_shape),
+ * CONV_EUNSUPPORTED (forced kernel outside its domain) or CONV_EINVAL.
+ */
+MICONV_API int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force_kernel, conv_plan_t *p);
+
+/*
+ * conv_run -- launch the planned kernels on the caller's HIP stream.
+ *
+ *   x, w, y      device pointers laid out as the plan's descriptors say.
+ *   b            device pointer or NULL (must be non-NULL iff d.has_bias).
+ *   workspace    device scratch of at least p->workspace_bytes bytes, 256-byte
+ *                aligned, or NULL when p->workspace_bytes == 0.  Its content
+ *                is overwritten; calls sharing one workspace must not overlap.
+ *   stream       hipStream_t (NULL = the default stream).
+ *
+ * Asynchronous: returns after enqueueing.  A call with an empty output is a
+ * no-op returning CONV_OK.  Returns CONV_EINVAL (NULL pointer, missing
+ * workspace), CONV_EALIGN (a pointer not aligned to its element size) or
+ * CONV_EDEVICE (no GPU, or a launch error).  16-byte vector paths are used
+ * only when the pointers allow them; otherwise the scalar path of the same
+ * kernel runs.
+ */
+MICONV_API int conv_run(const conv_plan_t *p, const void *x, const void *w, const void *b, void *y,
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Name of a conv_kernel value ("dw_cl", "plane", ...), or "?" . */
+MICONV_API const char *conv_kernel_name(int32_t kernel);
+
+/* Message for a conv_status value. */
+MICONV_API const char *conv_status_string(int32_t status);
+
+/* Library ABI version (sizes of the structs above are part of it). */
+MICONV_API int32_t conv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MICONV_H */

@@ -1,0 +1,288 @@
+"""Host logic of the boundary, on the CPU: binding rules and error contract,
+output shapes and strides (against the reference's own, independently written
+rule and torch), routing, forced kernels, and conv_run's checks."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from depthwise_stencil_implicit_amd import _abi as A
+from depthwise_stencil_implicit_amd import api, synth
+
+
+def T(shape, dtype=torch.bfloat16, cl=False):
+    t = torch.empty(shape, dtype=dtype)
+    return synth.channels_last_copy(t) if cl else t
+
+
+def bind(x, w, b=None, **kw):
+    return api.conv_bind(api.describe(x), api.describe(w), api.describe(b), api.make_args(**kw))
+
+
+def bind_status(x, w, b=None, **kw):
+    try:
+        bind(x, w, b, **kw)
+        return A.OK
+    except api.ConvError as e:
+        return e.status
+
+
+def prep(x, w, b=None, force=None, **kw):
+    return api.Prepared(x, w, b, api.make_args(**kw), force_kernel=force)
+
+
+def wl_tensors(wl):
+    x = T(wl.x_shape, synth.DTYPES[wl.dtype], wl.channels_last)
+    w = T(wl.w_shape, synth.DTYPES[wl.dtype])
+    c_out = wl.w_shape[1] * wl.groups if wl.transposed else wl.w_shape[0]
+    b = T((c_out,), synth.DTYPES[wl.dtype]) if wl.has_bias else None
+    return x, w, b
+
+
+def wl_args(wl):
+    r = len(wl.x_shape) - 2
+    ex = lambda v: tuple(v) * r if len(v) == 1 else tuple(v)
+    return dict(transposed=wl.transposed, groups=wl.groups, stride=ex(wl.stride),
+                padding_before=ex(wl.padding_before), padding_after=ex(wl.padding_after),
+                dilation=ex(wl.dilation), output_padding=ex(wl.output_padding) if wl.transposed else None)
+
+
+# ------------------------------------------------------------------ binding --
+
+def test_defaults_are_filled_and_broadcast():
+    d = bind(T((2, 4, 9, 7)), T((6, 2, 3, 3)), groups=2, stride=2, padding_before=(1, 1), padding_after=(0, 2))
+    assert d.spatial == 2 and d.N == 2 and d.C_in == 4 and d.C_out == 6 and d.groups == 2
+    assert tuple(d.stride[:2]) == (2, 2) and tuple(d.dilation[:2]) == (1, 1)
+    assert tuple(d.padding_before[:2]) == (1, 1) and tuple(d.padding_after[:2]) == (0, 2)
+    assert tuple(d.out[:3]) == ((9 + 1 + 0 - 3) // 2 + 1, (7 + 1 + 2 - 3) // 2 + 1, 1)
+    assert tuple(d.k[:3]) == (3, 3, 1) and d.has_bias == 0
+
+
+def test_unbatched_input_gets_a_batch_dim():
+    d = bind(T((4, 12)), T((8, 4, 3)), padding_before=1, padding_after=1)
+    assert d.unbatched == 1 and d.N == 1 and d.x.rank == 3 and d.spatial == 1
+    sizes, strides = api.conv_out_shape(d)
+    assert sizes == (8, 12) and strides == (12, 1)
+
+
+@pytest.mark.parametrize("k,dil,pb,pa", [(3, 1, 1, 1), (4, 1, 1, 2), (4, 2, 3, 3), (5, 3, 6, 6), (2, 1, 0, 1)])
+def test_same_padding_split(k, dil, pb, pa):
+    d = bind(T((1, 2, 11)), T((3, 2, k)), dilation=dil, padding_mode="same")
+    assert (d.padding_before[0], d.padding_after[0], d.out[0]) == (pb, pa, 11)
+
+
+def test_valid_padding():
+    d = bind(T((1, 2, 11, 8)), T((3, 2, 3, 2)), padding_mode="valid")
+    assert tuple(d.padding_before[:2]) == (0, 0) and tuple(d.out[:2]) == (9, 7)
+
+
+@pytest.mark.parametrize("case", [
+    dict(x=((1, 4, 8, 8), torch.float16), w=((4, 1, 3, 3), torch.bfloat16), kw=dict(groups=4)),  # dtype mismatch
+    dict(x=((1, 4, 8, 8),), w=((4, 2, 3, 3),), kw=dict(groups=4)),            # Cig mismatch
+    dict(x=((1, 6, 8, 8),), w=((4, 3, 3, 3),), kw=dict(groups=4)),            # C_in % groups
+    dict(x=((1, 4, 8, 8),), w=((6, 1, 3, 3),), kw=dict(groups=4)),            # C_out % groups
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), kw=dict(padding_before=-1, padding_after=0)),
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), kw=dict(stride=0)),
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), kw=dict(dilation=0)),
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), kw=dict(groups=-1)),
+    dict(x=((1, 4, 2, 2),), w=((4, 4, 3, 3),), kw=dict()),                    # output length < 1
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), kw=dict(stride=2, padding_mode="same")),
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), kw=dict(transposed=True, padding_mode="same")),
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), kw=dict(transposed=True, stride=2, output_padding=2)),
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), kw=dict(stride=2, output_padding=1)),  # forward op
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3),), kw=dict()),                        # rank mismatch
+    dict(x=((1, 4, 8, 8),), w=((4, 4),), kw=dict()),                           # weight rank < 3
+    dict(x=((1, 4, 0, 8),), w=((4, 4, 3, 3),), kw=dict()),                     # empty spatial dim
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), kw=dict(stride=(1, 2, 3))),     # too many values
+    dict(x=((1, 4, 8, 8),), w=((4, 4, 3, 3),), b=(5,), kw=dict()),            # bias size
+])
+def test_invalid_calls_are_rejected(case):
+    x = T(*case["x"]) if len(case["x"]) == 2 else T(case["x"][0])
+    w = T(*case["w"]) if len(case["w"]) == 2 else T(case["w"][0])
+    b = T(case["b"]) if "b" in case else None
+    assert bind_status(x, w, b, **case["kw"]) == A.EINVAL
+
+
+def test_error_message_is_written():
+    with pytest.raises(api.ConvError, match="divisible by groups"):
+        bind(T((1, 6, 8, 8)), T((4, 3, 3, 3)), groups=4)
+
+
+def test_aten_overload_mapping():
+    """conv_transpose's symmetric padding p is a crop of p at each end; a
+    'same' string maps to the padding mode; _convolution's flags are inert."""
+    x, w = T((2, 4, 10)), T((4, 3, 3))
+    d = bind(x, w, transposed=True, stride=2, padding_before=1, padding_after=1, output_padding=1)
+    assert d.out[0] == (10 - 1) * 2 - 2 + 2 + 1 + 1 and d.C_out == 3
+    d2 = bind(T((1, 3, 9, 9)), T((6, 3, 4, 4)), padding_mode="same")
+    assert tuple(d2.padding_before[:2]) == (1, 1) and tuple(d2.padding_after[:2]) == (2, 2)
+
+
+# ------------------------------------------------------------ shape/strides --
+
+def _layout_cases():
+    rng = np.random.default_rng(21)
+    cases = []
+    for i in range(60):
+        r = int(rng.integers(1, 4))
+        transposed = bool(rng.integers(0, 2))
+        groups = int(rng.choice([1, 2, 4]))
+        cig, cog = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        L = [int(rng.integers(1, 9)) for _ in range(r)]
+        k = [int(rng.integers(1, 4)) for _ in range(r)]
+        s = [int(rng.integers(1, 4)) for _ in range(r)]
+        d = [int(rng.integers(1, 3)) for _ in range(r)]
+        pb = [int(rng.integers(0, 3)) for _ in range(r)]
+        pa = [int(rng.integers(0, 3)) for _ in range(r)]
+        op = [int(rng.integers(0, max(a, b))) if transposed else 0 for a, b in zip(s, d)]
+        N = int(rng.choice([0, 1, 3]))
+        cl = bool(rng.integers(0, 2))
+        wcl = bool(rng.integers(0, 4) == 0)
+        cases.append((r, transposed, groups, cig, cog, L, k, s, d, pb, pa, op, N, cl, wcl))
+    return cases
+
+
+@pytest.mark.parametrize("case", _layout_cases())
+def test_out_shape_and_strides_match_reference_rule(case):
+    r, transposed, groups, cig, cog, L, k, s, d, pb, pa, op, N, cl, wcl = case
+    x = T((N, groups * cig) + tuple(L), cl=cl)
+    w = T(((groups * cig, cog) if transposed else (groups * cog, cig)) + tuple(k), cl=wcl)
+    kw = dict(transposed=transposed, groups=groups, stride=s, padding_before=pb, padding_after=pa, dilation=d,
+              output_padding=op if transposed else None)
+    ref_shape = oracle.out_shape(tuple(x.shape), tuple(w.shape), stride=s, padding_before=pb,
+                                 padding_after=pa, dilation=d, groups=groups, transposed=transposed,
+                                 output_padding=op)
+    if any(o < 1 for o in ref_shape[2:]):
+        assert bind_status(x, w, **kw) == A.EINVAL
+        return
+    dd = bind(x, w, **kw)
+    sizes, strides = api.conv_out_shape(dd)
+    assert sizes == ref_shape
+    assert strides == oracle.out_strides(ref_shape, tuple(x.shape), tuple(x.stride()), tuple(w.shape),
+                                         tuple(w.stride()))
+
+
+EXPECTED = {  # (sizes, strides, kernel) of the five workloads
+    "dw_f32_nchw_1x32x32x32_k3": ((1, 32, 32, 32), (32768, 1024, 32, 1), "plane"),
+    "dw_bf16_nhwc_32x256x56x56_k3s1": ((32, 256, 56, 56), (802816, 1, 14336, 256), "dw_cl"),
+    "dw_bf16_nhwc_32x256x56x56_k5s1": ((32, 256, 56, 56), (802816, 1, 14336, 256), "dw_cl"),
+    "dw_bf16_nhwc_32x256x56x56_k7s1": ((32, 256, 56, 56), (802816, 1, 14336, 256), "dw_cl"),
+    "dw_bf16_nhwc_32x256x56x56_k3s2": ((32, 256, 28, 28), (200704, 1, 7168, 256), "dw_cl"),
+    "dw_bf16_nhwc_32x256x56x56_k5s2": ((32, 256, 28, 28), (200704, 1, 7168, 256), "dw_cl"),
+    "dw_bf16_nhwc_32x256x56x56_k7s2": ((32, 256, 28, 28), (200704, 1, 7168, 256), "dw_cl"),
+    "grp_f16_nchw_32x256x28x28_g64_m2": ((32, 512, 28, 28), (401408, 784, 28, 1), ("grp", "plane")),
+    "dense_bf16_nhwc_64x256x56x56_k3": ((64, 256, 56, 56), (802816, 1, 14336, 256), "igemm"),
+    "convT1d_bf16_nlc_16x512x8192_k4s2": ((16, 512, 16383), (8388096, 1, 512), "igemm_t"),
+}
+
+
+@pytest.mark.parametrize("wl", synth.all_workloads(), ids=lambda w: w.name)
+def test_workload_layouts_and_routes(wl):
+    x, w, b = wl_tensors(wl)
+    p = prep(x, w, b, **wl_args(wl))
+    sizes, strides, kern = EXPECTED[wl.name]
+    assert p.sizes == sizes and p.strides == strides
+    kern = kern if isinstance(kern, tuple) else (kern,)
+    assert api.kernel_name(p.plan.kernel) in kern
+
+
+def test_workload_algorithmic_counts():
+    got = {}
+    for wl in synth.all_workloads():
+        x, w, b = wl_tensors(wl)
+        p = prep(x, w, b, **wl_args(wl))
+        got[wl.name] = (p.plan.flops, p.plan.bytes)
+    assert got["dense_bf16_nhwc_64x256x56x56_k3"] == (2 * 200704 * 256 * 2304, 206701056)
+    # transposed: 2 taps of parity per output, 16383 outputs per (n, co, ci)
+    assert got["convT1d_bf16_nlc_16x512x8192_k4s2"] == (2 * 16 * 512 * 512 * 32766, 404733952)
+    assert got["grp_f16_nchw_32x256x28x28_g64_m2"] == (2 * 32 * 512 * 784 * 36, 38572032)
+    assert got["dw_bf16_nhwc_32x256x56x56_k7s1"] == (2 * 32 * 256 * 3136 * 49, 102786048)
+    assert got["dw_f32_nchw_1x32x32x32_k3"] == (589824, 263424)
+
+
+# -------------------------------------------------- plan / failure contract --
+
+def test_forced_kernel_outside_its_domain_is_refused():
+    x, w = T((2, 8, 12, 12)), T((8, 1, 3, 3))
+    kw = dict(groups=8, padding_before=1, padding_after=1)
+    with pytest.raises(api.ConvError) as e:
+        prep(x, w, force="dw_cl", **kw)          # NCHW input: no channel-contiguous schedule
+    assert e.value.status == A.EUNSUPPORTED
+    with pytest.raises(api.ConvError) as e:
+        prep(x, w, force="igemm_t", **kw)        # forward call on the transposed kernel
+    assert e.value.status == A.EUNSUPPORTED
+    with pytest.raises(api.ConvError) as e:
+        prep(T((1, 18, 8, 8)), T((4, 9, 3, 3)), force="plane", groups=2)   # 9 channels per group
+    assert e.value.status == A.EUNSUPPORTED
+    for k in ("plane", "reduce", "igemm"):
+        prep(x, w, force=k, **kw)                # inside their domains
+
+
+def test_output_layout_mismatch_is_refused():
+    x, w = T((2, 8, 12, 12)), T((8, 1, 3, 3))
+    d = bind(x, w, groups=8, padding_before=1, padding_after=1)
+    sizes, strides = api.conv_out_shape(d)
+    good = api.tensor_desc(sizes, strides, torch.bfloat16)
+    api.conv_plan(d, good)
+    for bad_sizes, bad_strides in [(sizes, (strides[0], 1, strides[2] * 8, 8)),
+                                   ((2, 8, 12, 11), strides)]:
+        with pytest.raises(api.ConvError) as e:
+            api.conv_plan(d, api.tensor_desc(bad_sizes, bad_strides, torch.bfloat16))
+        assert e.value.status == A.ELAYOUT
+    with pytest.raises(api.ConvError) as e:
+        api.conv_plan(d, api.tensor_desc(sizes, strides, torch.float16))
+    assert e.value.status == A.ELAYOUT
+
+
+def test_routing_rules():
+    name = lambda p: api.kernel_name(p.plan.kernel)
+    # depthwise channels-last with a compiled schedule -> dw_cl; same call NCHW -> plane
+    assert name(prep(T((1, 16, 9, 9), cl=True), T((16, 1, 3, 3)), groups=16)) == "dw_cl"
+    assert name(prep(T((1, 16, 9, 9)), T((16, 1, 3, 3)), groups=16)) == "plane"
+    # dilation, 3-D, wide groups, dense -> igemm
+    assert name(prep(T((1, 16, 9, 9)), T((16, 1, 3, 3)), groups=16, dilation=2)) == "igemm"
+    assert name(prep(T((1, 16, 5, 5, 5)), T((16, 1, 3, 3, 3)), groups=16)) == "igemm"
+    assert name(prep(T((1, 32, 9, 9)), T((32, 16, 3, 3)), groups=2)) == "igemm"
+    assert name(prep(T((1, 8, 9, 9)), T((8, 8, 3, 3)))) == "igemm"
+    # a large kernel over a tiny input -> reduce
+    assert name(prep(T((1, 16, 7, 7)), T((16, 1, 7, 7)), groups=16)) == "reduce"
+    # 1-D depthwise runs on the stencil with H = 1
+    assert name(prep(T((2, 16, 40)), T((16, 1, 5)), groups=16)) == "plane"
+    # every transposed call -> igemm_t
+    assert name(prep(T((1, 8, 9)), T((8, 4, 3)), transposed=True, groups=2)) == "igemm_t"
+
+
+def test_plans_are_deterministic():
+    x, w, b = T((4, 64, 20, 20), cl=True), T((64, 64, 3, 3)), T((64,))
+    p1 = prep(x, w, b, padding_before=1, padding_after=1).plan
+    p2 = prep(x, w, b, padding_before=1, padding_after=1).plan
+    assert bytes(p1) == bytes(p2)
+
+
+def test_run_checks_before_touching_the_device():
+    x, w = T((2, 8, 12, 12), cl=True), T((8, 8, 3, 3))
+    p = prep(x, w, None, padding_before=1, padding_after=1)
+    assert p.plan.workspace_bytes > 0
+    L = A.lib()
+    run = lambda *a: L.conv_run(ctypes.byref(p.plan), *a)
+    assert run(0x1001, 0x2000, None, 0x3000, 0x4000, p.plan.workspace_bytes, None) == A.EALIGN
+    assert run(None, 0x2000, None, 0x3000, 0x4000, p.plan.workspace_bytes, None) == A.EINVAL
+    assert run(0x1000, 0x2000, 0x5000, 0x3000, 0x4000, p.plan.workspace_bytes, None) == A.EINVAL  # bias
+    assert run(0x1000, 0x2000, None, 0x3000, None, 0, None) == A.EINVAL                            # workspace
+    assert run(0x1000, 0x2000, None, 0x3000, 0x4000, p.plan.workspace_bytes - 1, None) == A.EINVAL
+    if not torch.cuda.is_available():
+        assert run(0x1000, 0x2000, None, 0x3000, 0x4000, p.plan.workspace_bytes, None) == A.EDEVICE
+
+
+def test_empty_output_runs_as_a_noop_without_a_device():
+    x, w = T((0, 8, 12, 12)), T((8, 1, 3, 3))
+    p = prep(x, w, groups=8)
+    assert p.plan.grid[0] == 0
+    assert A.lib().conv_run(ctypes.byref(p.plan), None, None, None, None, None, 0, None) == A.OK
+
+
+def test_cpu_tensors_are_refused_by_the_product_path():
+    with pytest.raises(ValueError, match="GPU only"):
+        api.conv(torch.zeros((1, 2, 5)), torch.zeros((2, 2, 3)))

@@ -1,0 +1,263 @@
+"""GPU parity: the library's kernels against the double-precision reference.
+
+Every comparison is element by element, |y_gpu - y| <= eps * A with
+A = sum|x*w| + |b| (eps = 1e-6 fp32, 2^-11 fp16, 2^-8 bf16); integer-valued
+and all-ones inputs must match exactly.  Output shapes and strides must equal
+the reference's layout rule exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from depthwise_stencil_implicit_amd import _abi, api, synth
+
+from gpu_util import EPS, assert_close, check_full, check_points, expand_kw, ref_inputs, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------ the workloads --
+
+FULL = [synth.depthwise_f32_small()] + synth.depthwise_bf16_cl_all() + [synth.grouped_f16()]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
+def test_workload_full_output(wl):
+    _flush(f"workload {wl.name}")
+    y = check_full(wl)
+    exp = oracle.out_strides(tuple(y.shape), wl.x_shape,
+                             synth.channels_last_copy(torch.empty(wl.x_shape, dtype=torch.int8)).stride()
+                             if wl.channels_last else torch.empty(wl.x_shape, dtype=torch.int8).stride(),
+                             wl.w_shape, torch.empty(wl.w_shape, dtype=torch.int8).stride())
+    assert tuple(y.stride()) == exp
+
+
+@pytest.mark.parametrize("wl", [synth.dense_bf16_cl(), synth.transposed_bf16_nlc()], ids=lambda w: w.name)
+def test_workload_sampled_outputs(wl):
+    _flush(f"workload {wl.name} (sampled)")
+    y = check_points(wl, n=6000, seed=1)
+    exp = oracle.out_strides(tuple(y.shape), wl.x_shape,
+                             synth.channels_last_copy(torch.empty(wl.x_shape, dtype=torch.int8)).stride(),
+                             wl.w_shape, torch.empty(wl.w_shape, dtype=torch.int8).stride())
+    assert tuple(y.stride()) == exp
+
+
+@pytest.mark.parametrize("wl", [synth.dense_bf16_cl().with_batch(2), synth.transposed_bf16_nlc().with_batch(1)],
+                         ids=lambda w: w.name)
+def test_workload_reduced_batch_full_output(wl):
+    """The same calls at a batch the reference finishes in seconds, whole output."""
+    _flush(f"workload {wl.name}")
+    check_full(wl)
+
+
+# ----------------------------------------------------------------- sweeps --
+
+def _geom_cases(kind, n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    tries = 0
+    while len(out) < n and tries < 10000:
+        tries += 1
+        dtype = ["f32", "f16", "bf16"][len(out) % 3]
+        cl = bool(rng.integers(0, 2))
+        bias = bool(rng.integers(0, 2))
+        if kind in ("igemm", "igemm_t"):
+            r = int(rng.integers(1, 4))
+            groups = int(rng.choice([1, 1, 2, 3]))
+            cig = int(rng.choice([1, 3, 8, 16, 40]))
+            cog = int(rng.choice([1, 5, 16, 33, 70]))
+            L = [int(rng.integers(3, 12 if r < 3 else 6)) for _ in range(r)]
+            k = [int(rng.integers(1, 4)) for _ in range(r)]
+            s = [int(rng.integers(1, 4)) for _ in range(r)]
+            d = [int(rng.integers(1, 3)) for _ in range(r)]
+            N = int(rng.integers(1, 4))
+        else:
+            r = int(rng.integers(1, 3))
+            cig = int(rng.integers(1, 9)) if kind != "dw_cl" else 1
+            mult = int(rng.choice([1, 2, 3, 16, 17])) if kind != "dw_cl" else 1
+            groups = int(rng.integers(2, 6)) if kind != "dw_cl" else int(rng.choice([8, 12, 20, 40, 64]))
+            cog = mult
+            N = int(rng.integers(1, 3))
+            if kind == "dw_cl":
+                r = 2
+                kk = int(rng.choice([3, 5, 7]))
+                ss = int(rng.integers(1, 3))
+                k, s, d = [kk, kk], [ss, ss], [1, 1]
+                L = [int(rng.integers(kk, 20)), int(rng.integers(kk, 40))]
+                cl = True
+            elif kind == "reduce":
+                k = [int(rng.integers(3, 10)) for _ in range(r)]
+                s = [int(rng.integers(1, 3)) for _ in range(r)]
+                d = [1] * r
+                L = [int(rng.integers(kk, kk + 2)) for kk in k]
+            else:
+                k = [int(rng.integers(1, 10)) for _ in range(r)]
+                s = [int(rng.integers(1, 4)) for _ in range(r)]
+                d = [int(rng.integers(1, 3)) for _ in range(r)]
+                L = [int(rng.integers(max(3, k[i]), 40)) for i in range(r)]
+        pb = [int(rng.integers(0, 3)) for _ in range(r)]
+        pa = [int(rng.integers(0, 3)) for _ in range(r)]
+        transposed = kind == "igemm_t"
+        op = [int(rng.integers(0, max(si, di))) if transposed else 0 for si, di in zip(s, d)]
+        if transposed:
+            ok = all((Li - 1) * si + di * (ki - 1) + 1 + opi - pbi - pai >= 1
+                     for Li, si, di, ki, pbi, pai, opi in zip(L, s, d, k, pb, pa, op))
+        else:
+            ok = all(Li + pbi + pai - di * (ki - 1) - 1 >= 0 for Li, pbi, pai, di, ki in zip(L, pb, pa, d, k))
+        if not ok:
+            continue
+        wl = synth.random_case(1000 + len(out) + 100 * seed, rank=r, transposed=transposed, dtype=dtype,
+                               channels_last=cl, N=N, C_in=groups * cig, C_out=groups * cog, groups=groups,
+                               L=L, k=k, stride=s, padding_before=pb, padding_after=pa, dilation=d,
+                               output_padding=op, has_bias=bias)
+        out.append(wl)
+    return out
+
+
+SWEEP = {kind: _geom_cases(kind, n, seed) for kind, n, seed in
+         [("igemm", 24, 1), ("igemm_t", 24, 2), ("plane", 24, 3), ("dw_cl", 18, 4), ("reduce", 9, 5)]}
+
+
+def _desc(wl):
+    kw = expand_kw(wl)
+    return (f"{wl.name} {wl.dtype} x{wl.x_shape} w{wl.w_shape} cl={wl.channels_last} g={wl.groups} "
+            f"s={kw['stride']} pb={kw['padding_before']} pa={kw['padding_after']} d={kw['dilation']} "
+            f"op={kw['output_padding']} bias={wl.has_bias}")
+
+
+@pytest.mark.parametrize("kind,wl", [(k, w) for k, ws in SWEEP.items() for w in ws],
+                         ids=lambda v: v if isinstance(v, str) else v.name)
+def test_forced_kernel_sweep(kind, wl):
+    _flush(f"sweep {kind}: {_desc(wl)}")
+    check_full(wl, force=kind)
+
+
+# ------------------------------------------------------------- exactness --
+
+EXACT_CASES = [
+    ("dw_cl", synth.random_case(7, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=32,
+                                C_out=32, groups=32, L=[13, 21], k=[5, 5], stride=[1, 1],
+                                padding_before=[2, 1], padding_after=[1, 2], dilation=[1, 1],
+                                output_padding=[0, 0], has_bias=True)),
+    ("plane", synth.random_case(8, rank=2, transposed=False, dtype="f16", channels_last=False, N=2, C_in=12,
+                                C_out=24, groups=3, L=[17, 19], k=[3, 4], stride=[2, 1],
+                                padding_before=[1, 2], padding_after=[0, 1], dilation=[1, 1],
+                                output_padding=[0, 0], has_bias=True)),
+    ("igemm", synth.random_case(9, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=64,
+                                C_out=48, groups=1, L=[9, 10], k=[3, 3], stride=[1, 2],
+                                padding_before=[1, 0], padding_after=[2, 1], dilation=[1, 1],
+                                output_padding=[0, 0], has_bias=True)),
+    ("igemm_t", synth.random_case(10, rank=1, transposed=True, dtype="bf16", channels_last=True, N=2,
+                                  C_in=32, C_out=32, groups=1, L=[40], k=[4], stride=[2], padding_before=[1],
+                                  padding_after=[2], dilation=[1], output_padding=[0], has_bias=False)),
+    ("igemm", synth.random_case(11, rank=3, transposed=False, dtype="f32", channels_last=False, N=1, C_in=6,
+                                C_out=10, groups=2, L=[5, 6, 7], k=[2, 3, 2], stride=[1, 2, 1],
+                                padding_before=[1, 0, 1], padding_after=[0, 1, 1], dilation=[2, 1, 1],
+                                output_padding=[0, 0, 0], has_bias=True)),
+]
+
+
+@pytest.mark.parametrize("kind,wl", EXACT_CASES, ids=lambda v: v if isinstance(v, str) else v.name)
+@pytest.mark.parametrize("values", ["ones", "ints"])
+def test_exact_results(kind, wl, values):
+    """All-ones and small-integer inputs have exact fp32 sums in any order, and
+    results small enough to be exact in the output dtype."""
+    import dataclasses
+    if values == "ones":
+        wl = dataclasses.replace(wl, x_dist=("ones",), w_dist=("ones",), b_dist=("ones",))
+    else:
+        wl = dataclasses.replace(wl, x_dist=("ints", -3, 3), w_dist=("ints", -2, 2), b_dist=("ints", -4, 4))
+    _flush(f"exact {values} {kind}: {_desc(wl)}")
+    check_full(wl, force=kind, exact=True)
+
+
+# ------------------------------------------------------------ memory safety --
+
+@pytest.mark.parametrize("kind,wl", [(k, ws[i]) for k, ws in SWEEP.items() for i in (0, 1)],
+                         ids=lambda v: v if isinstance(v, str) else v.name)
+def test_writes_stay_inside_output(kind, wl):
+    """y sits inside a canary-filled buffer and starts as NaN: afterwards the
+    canary is intact and no element of y is left NaN."""
+    _flush(f"guard {kind}: {_desc(wl)}")
+    x, w, b = synth.make_inputs(wl, device="cuda")
+    kw = expand_kw(wl)
+    args = api.make_args(transposed=kw["transposed"], groups=kw["groups"], stride=kw["stride"],
+                         padding_before=kw["padding_before"], padding_after=kw["padding_after"],
+                         dilation=kw["dilation"], output_padding=kw["output_padding"] if kw["transposed"] else None)
+    prep = api.Prepared(x, w, b, args, force_kernel=kind)
+    numel = int(np.prod(prep.sizes))
+    span = 1 + sum((s - 1) * st for s, st in zip(prep.sizes, prep.strides))
+    guard = 4096
+    buf = torch.full((span + 2 * guard,), 7.0, dtype=x.dtype, device="cuda")
+    y = torch.as_strided(buf, prep.sizes, prep.strides, guard)
+    y.fill_(float("nan"))
+    prep.run(x, w, b, y, prep.workspace(x.device))
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    assert (buf[:guard] == 7.0).all() and (buf[guard + span:] == 7.0).all()
+    xr, wr, br = ref_inputs(x, w, b)
+    yr, A = oracle.conv(xr, wr, br, **kw)
+    assert_close(y, yr, A, EPS[wl.dtype], wl.name)
+    assert numel == y.numel()
+
+
+# ------------------------------------------------------------- edge cases --
+
+def test_empty_batch_is_a_noop():
+    x = torch.empty((0, 8, 5, 5), dtype=torch.bfloat16, device="cuda")
+    w = torch.randn((8, 1, 3, 3), device="cuda").to(torch.bfloat16)
+    y = api.conv(x, w, None, groups=8, padding_before=1, padding_after=1)
+    assert tuple(y.shape) == (0, 8, 5, 5)
+
+
+def test_unbatched_and_same_padding():
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn((6, 11, 9), generator=g).to(torch.float16)
+    w = (0.3 * torch.randn((12, 2, 3, 4), generator=g)).to(torch.float16)
+    b = torch.randn((12,), generator=g).to(torch.float16)
+    y = api.conv2d(x.cuda(), w.cuda(), b.cuda(), padding="same", groups=3)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (12, 11, 9)
+    yr, A = oracle.conv(x.double()[None].numpy(), w.double().numpy(), b.double().numpy(),
+                        padding_before=(1, 1), padding_after=(1, 2), groups=3)
+    assert_close(y[None], yr, A, EPS["f16"], "unbatched same")
+
+
+def test_misaligned_output_uses_scalar_path():
+    """A y view at an odd element offset defeats 16-byte stores; the run must
+    still be correct (the launcher falls back to the element-wise path)."""
+    wl = synth.depthwise_bf16_cl(3, 1).with_batch(2)
+    x, w, b = synth.make_inputs(wl, device="cuda")
+    kw = expand_kw(wl)
+    args = api.make_args(groups=wl.groups, stride=kw["stride"], padding_before=kw["padding_before"],
+                         padding_after=kw["padding_after"])
+    prep = api.Prepared(x, w, b, args)
+    span = 1 + sum((s - 1) * st for s, st in zip(prep.sizes, prep.strides))
+    buf = torch.zeros(span + 1, dtype=x.dtype, device="cuda")
+    y = torch.as_strided(buf, prep.sizes, prep.strides, 1)
+    prep.run(x, w, b, y)
+    torch.cuda.synchronize()
+    xr, wr, br = ref_inputs(x, w, b)
+    yr, A = oracle.conv(xr, wr, br, **kw)
+    assert_close(y, yr, A, EPS["bf16"], "misaligned y")
+
+
+def test_aten_style_overloads_match_reference():
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn((2, 4, 10), generator=g).to(torch.bfloat16)
+    w = (0.3 * torch.randn((4, 3, 3), generator=g)).to(torch.bfloat16)
+    y = api.conv_transpose1d(x.cuda(), w.cuda(), None, stride=2, padding=1, output_padding=1)
+    torch.cuda.synchronize()
+    yr, A = oracle.conv(x.double().numpy(), w.double().numpy(), None, stride=2, padding_before=1,
+                        padding_after=1, transposed=True, output_padding=1)
+    assert_close(y, yr, A, EPS["bf16"], "conv_transpose1d")
+    y2 = api.convolution(x.cuda(), w.permute(1, 0, 2).contiguous().cuda(), None, [1], [2], [1], False, [0], 1)
+    torch.cuda.synchronize()
+    yr2, A2 = oracle.conv(x.double().numpy(), w.permute(1, 0, 2).double().numpy(), None, padding_before=2,
+                          padding_after=2)
+    assert_close(y2, yr2, A2, EPS["bf16"], "convolution")
