@@ -4,19 +4,23 @@
 // executorch PR #25085 ("Route 2-D depthwise and few-channel grouped
 // convolutions to a Triton direct-stencil kernel"), description: a direct
 // stencil for depthwise convolutions with dilation 1 and kernels up to 9x9,
-// with a register sliding window schedule for channel-contiguous inputs.
+// with a register sliding-window schedule for channel-contiguous inputs.
 //
 // Layout on gfx950: x is [N][H][W][C] in memory (C fastest).  A lane owns one
-// 16-byte vector of V consecutive channels and a strip of TO consecutive output
-// columns of one output row at a time.  For each kernel row it walks the
-// (TO-1)*S + KW input columns of the strip once, left to right: each 16-byte
-// load (V channels of one pixel) is widened to fp32 once and feeds every output
-// of the strip whose window covers that column, so the loaded row segment is
-// the register sliding window.  Lanes of a wave hold consecutive channel
-// vectors of the same pixels, so every load and store of the wave is one
-// contiguous run of C elements.  Weights of the workgroup's channels are staged
-// once in LDS as fp32 [KH][KW][channels].  Accumulation is fp32 FMA; the bias
-// is added first and the result rounded once to the output dtype.
+// 32-bit word of channels (two 16-bit channels, or one fp32 channel) and a
+// strip of TO consecutive output columns; it walks RPT output rows.  For each
+// output row and kernel row it loads the (TO-1)*S + K input words of its strip
+// left to right; each load is widened to fp32 once and feeds every output of
+// the strip whose window covers that column -- the loaded row segment is the
+// register sliding window.  Consecutive lanes hold consecutive channel words of
+// the same pixel, so every wave load and store is one contiguous run.  All
+// K*K weights of the lane's channels live in registers as fp32 for the whole
+// kernel: no LDS and no barrier.
+//
+// Loads are raw buffer loads whose out-of-range offsets return zero, so the
+// zero padding costs no branch and all loads of a row can be in flight at once.
+// Accumulation is fp32 FMA, the bias is the initial value, and each result is
+// rounded once to the output dtype.
 #include "dev_common.h"
 #include "internal.h"
 
@@ -25,62 +29,15 @@ namespace miconv {
 struct DwArgs {
     const void *x, *w, *b;
     void *y;
-    int64_t xs_n, xs_h, xs_w;  // channel stride is 1
-    int64_t ys_n, ys_h, ys_w;  // channel stride is 1
-    int64_t ws0, ws2, ws3;     // weight strides (output channel, kh, kw)
+    int64_t ys_n, ys_h, ys_w;         // element strides of y (channel stride 1)
+    int32_t xs_n, xs_h, xs_w;         // element strides of x (channel stride 1), 32-bit
+    int32_t x_bytes;                  // bytes addressable from x (buffer range)
+    int64_t ws0, ws2, ws3;            // weight strides (output channel, kh, kw)
     int32_t N, H, W, C, OH, OW, pb_h, pb_w;
-    int32_t cvb, sp, rh;       // channel vectors / strips / rows per workgroup
-    int32_t ch_chunks, col_chunks, row_chunks, total;
+    int32_t cpb, spb, rpt;            // lane words / strips per workgroup, rows per thread
+    int32_t ch_chunks, strip_chunks, row_chunks, nstrips, total;
     int32_t has_bias;
 };
-
-template <typename T, int V, bool VEC>
-__device__ __forceinline__ void load_vec(const T *p, int c, int C, bool inb, float (&out)[V])
-{
-    if (VEC) {
-        if (inb) {
-            if constexpr (Dt<T>::size == 2) {
-                const uint4 u = *reinterpret_cast<const uint4 *>(p);
-                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    out[2 * i] = lo_f32(w4[i], T{});
-                    out[2 * i + 1] = hi_f32(w4[i], T{});
-                }
-            } else {
-                const float4 f = *reinterpret_cast<const float4 *>(p);
-                out[0] = f.x; out[1] = f.y; out[2] = f.z; out[3] = f.w;
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < V; ++v) out[v] = 0.f;
-        }
-    } else {
-#pragma unroll
-        for (int v = 0; v < V; ++v) out[v] = (inb && c + v < C) ? to_f32(p[v]) : 0.f;
-    }
-}
-
-template <typename T, int V, bool VEC>
-__device__ __forceinline__ void store_vec(T *p, int c, int C, const float (&v)[V])
-{
-    if (VEC) {
-        if constexpr (Dt<T>::size == 2) {
-            uint4 u;
-            u.x = pack2<T>(v[0], v[1]);
-            u.y = pack2<T>(v[2], v[3]);
-            u.z = pack2<T>(v[4], v[5]);
-            u.w = pack2<T>(v[6], v[7]);
-            *reinterpret_cast<uint4 *>(p) = u;
-        } else {
-            *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i)
-            if (c + i < C) p[i] = from_f32<T>(v[i]);
-    }
-}
 
 __device__ __forceinline__ int xcd_block(int b, int total)
 {
@@ -89,124 +46,133 @@ __device__ __forceinline__ int xcd_block(int b, int total)
     return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
 }
 
-template <typename T, int KH, int KW, int S, int TO, bool VEC>
+template <typename T> struct Word;
+template <> struct Word<bf16_t> {
+    static constexpr int V = 2;
+    __device__ static void widen(uint32_t u, float (&f)[2]) { f[0] = lo_f32(u, bf16_t{}); f[1] = hi_f32(u, bf16_t{}); }
+    __device__ static uint32_t narrow(const float (&f)[2]) { return pack2<bf16_t>(f[0], f[1]); }
+};
+template <> struct Word<f16_t> {
+    static constexpr int V = 2;
+    __device__ static void widen(uint32_t u, float (&f)[2]) { f[0] = lo_f32(u, f16_t{}); f[1] = hi_f32(u, f16_t{}); }
+    __device__ static uint32_t narrow(const float (&f)[2]) { return pack2<f16_t>(f[0], f[1]); }
+};
+template <> struct Word<float> {
+    static constexpr int V = 1;
+    __device__ static void widen(uint32_t u, float (&f)[1]) { f[0] = __uint_as_float(u); }
+    __device__ static uint32_t narrow(const float (&f)[1]) { return __float_as_uint(f[0]); }
+};
+
+template <typename T, int K, int S, int TO>
 __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
 {
-    constexpr int V = 16 / Dt<T>::size;
-    constexpr int NCOL = (TO - 1) * S + KW;
-    extern __shared__ __attribute__((aligned(16))) float sw[];  // [KH][KW][cvb*V]
+    constexpr int V = Word<T>::V;
+    constexpr int ES = Dt<T>::size;
+    constexpr int NCOL = (TO - 1) * S + K;
 
     const int tid = threadIdx.x;
     int blk = xcd_block(blockIdx.x, a.total);
     const int chc = blk % a.ch_chunks;
     blk /= a.ch_chunks;
-    const int colc = blk % a.col_chunks;
-    blk /= a.col_chunks;
+    const int stc = blk % a.strip_chunks;
+    blk /= a.strip_chunks;
     const int rowc = blk % a.row_chunks;
     const int n = blk / a.row_chunks;
 
-    const int CW = a.cvb * V;  // channels per workgroup
-    const int c_base = chc * CW;
-    const T *__restrict__ Wt = static_cast<const T *>(a.w);
-    for (int i = tid; i < KH * KW * CW; i += blockDim.x) {
-        const int cl = i % CW;
-        const int kk = i / CW;
-        const int kw = kk % KW, kh = kk / KW;
-        const int c = c_base + cl;
-        sw[i] = c < a.C ? to_f32(Wt[c * a.ws0 + kh * a.ws2 + kw * a.ws3]) : 0.f;
-    }
-    __syncthreads();
+    const int word = chc * a.cpb + tid % a.cpb;     // channel word index
+    const int c0 = word * V;
+    const int strip = stc * a.spb + tid / a.cpb;
+    if (c0 >= a.C || strip >= a.nstrips) return;
+    const int ow0 = strip * TO;
 
-    const int cvl = tid % a.cvb;
-    const int sp = tid / a.cvb;
-    if (sp >= a.sp) return;
-    const int c0 = c_base + cvl * V;
-    if (c0 >= a.C) return;
-    const int ow0 = (colc * a.sp + sp) * TO;
-    if (ow0 >= a.OW) return;
-
+    // Weights of this lane's channels, fp32, in registers.
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.w), (short)0,
+                                                                        0x7fffffff, 0x00020000);
+    const T *Wt = static_cast<const T *>(a.w);
+    float wv[K][K][V];
+#pragma unroll
+    for (int kh = 0; kh < K; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < K; ++kw)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int c = min(c0 + v, a.C - 1);
+                wv[kh][kw][v] = to_f32(Wt[(int64_t)c * a.ws0 + kh * a.ws2 + kw * a.ws3]);
+            }
+    (void)wr;
     float bias[V];
     {
         const T *Bp = static_cast<const T *>(a.b);
 #pragma unroll
-        for (int v = 0; v < V; ++v) bias[v] = (a.has_bias && c0 + v < a.C) ? to_f32(Bp[c0 + v]) : 0.f;
+        for (int v = 0; v < V; ++v) bias[v] = a.has_bias ? to_f32(Bp[min(c0 + v, a.C - 1)]) : 0.f;
     }
 
-    const T *__restrict__ X = static_cast<const T *>(a.x) + (int64_t)n * a.xs_n + c0;
-    T *__restrict__ Y = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + c0;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
+    const int xbase = n * a.xs_n + c0;              // element offset of (n, 0, 0, c0)
     const int iw0 = ow0 * S - a.pb_w;
-    const float *swl = sw + cvl * V;
+    T *__restrict__ Y = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + c0;
 
-    const int oh_end = min(a.OH, (rowc + 1) * a.rh);
-    for (int oh = rowc * a.rh; oh < oh_end; ++oh) {
+    const int oh_beg = rowc * a.rpt;
+    const int oh_end = min(a.OH, oh_beg + a.rpt);
+    for (int oh = oh_beg; oh < oh_end; ++oh) {
         float acc[TO][V];
 #pragma unroll
         for (int t = 0; t < TO; ++t)
 #pragma unroll
             for (int v = 0; v < V; ++v) acc[t][v] = bias[v];
-
 #pragma unroll
-        for (int kh = 0; kh < KH; ++kh) {
+        for (int kh = 0; kh < K; ++kh) {
             const int ih = oh * S - a.pb_h + kh;
-            if ((unsigned)ih >= (unsigned)a.H) continue;
-            float wv[KW][V];
-#pragma unroll
-            for (int kw = 0; kw < KW; ++kw) {
-                const float *q = swl + (kh * KW + kw) * CW;
-#pragma unroll
-                for (int v = 0; v < V; v += 4) {
-                    const float4 f = *reinterpret_cast<const float4 *>(q + v);
-                    wv[kw][v] = f.x; wv[kw][v + 1] = f.y; wv[kw][v + 2] = f.z; wv[kw][v + 3] = f.w;
-                }
-            }
-            const T *row = X + (int64_t)ih * a.xs_h;
+            const bool row_ok = (unsigned)ih < (unsigned)a.H;
+            const int rbase = xbase + ih * a.xs_h;
 #pragma unroll
             for (int col = 0; col < NCOL; ++col) {
                 const int iw = iw0 + col;
+                const bool ok = row_ok && (unsigned)iw < (unsigned)a.W;
+                const int off = ok ? (rbase + iw * a.xs_w) * ES : 0x7fffffff;
+                const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
                 float xv[V];
-                load_vec<T, V, VEC>(row + (int64_t)iw * a.xs_w, c0, a.C, (unsigned)iw < (unsigned)a.W, xv);
+                Word<T>::widen(u, xv);
 #pragma unroll
                 for (int t = 0; t < TO; ++t) {
                     const int kw = col - t * S;
-                    if (kw >= 0 && kw < KW) {
+                    if (kw >= 0 && kw < K) {
 #pragma unroll
-                        for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xv[v], wv[kw][v], acc[t][v]);
+                        for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xv[v], wv[kh][kw][v], acc[t][v]);
                     }
                 }
             }
         }
         T *yrow = Y + (int64_t)oh * a.ys_h;
 #pragma unroll
-        for (int t = 0; t < TO; ++t)
-            if (ow0 + t < a.OW) store_vec<T, V, VEC>(yrow + (int64_t)(ow0 + t) * a.ys_w, c0, a.C, acc[t]);
+        for (int t = 0; t < TO; ++t) {
+            if (ow0 + t < a.OW) {
+                const uint32_t u = Word<T>::narrow(acc[t]);
+                *reinterpret_cast<uint32_t *>(yrow + (int64_t)(ow0 + t) * a.ys_w) = u;
+            }
+        }
     }
 }
 
 namespace {
 
-template <typename T, int KH, int KW, int S, int TO>
-hipError_t go(const DwArgs &a, bool vec, size_t lds, hipStream_t s)
+template <typename T, int K, int S, int TO>
+hipError_t go(const DwArgs &a, hipStream_t s)
 {
-    if (vec)
-        hipLaunchKernelGGL((dwcl_kernel<T, KH, KW, S, TO, true>), dim3(a.total), dim3(256), lds, s, a);
-    else
-        hipLaunchKernelGGL((dwcl_kernel<T, KH, KW, S, TO, false>), dim3(a.total), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((dwcl_kernel<T, K, S, TO>), dim3(a.total), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch(const DwArgs &a, int k, int s, bool vec, size_t lds, hipStream_t st)
+hipError_t dispatch(const DwArgs &a, int k, int s, int to, hipStream_t st)
 {
-    // Strip width: 8 output columns at stride 1, 4 at stride 2.
-    if (s == 1) {
-        if (k == 3) return go<T, 3, 3, 1, 8>(a, vec, lds, st);
-        if (k == 5) return go<T, 5, 5, 1, 8>(a, vec, lds, st);
-        if (k == 7) return go<T, 7, 7, 1, 8>(a, vec, lds, st);
-    } else if (s == 2) {
-        if (k == 3) return go<T, 3, 3, 2, 4>(a, vec, lds, st);
-        if (k == 5) return go<T, 5, 5, 2, 4>(a, vec, lds, st);
-        if (k == 7) return go<T, 7, 7, 2, 4>(a, vec, lds, st);
-    }
+#define MICONV_DW(KK, SS, TT) \
+    if (k == KK && s == SS && to == TT) return go<T, KK, SS, TT>(a, st);
+    MICONV_DW(3, 1, 14) MICONV_DW(3, 1, 8) MICONV_DW(5, 1, 14) MICONV_DW(5, 1, 8) MICONV_DW(7, 1, 14)
+    MICONV_DW(7, 1, 8) MICONV_DW(3, 2, 7) MICONV_DW(3, 2, 4) MICONV_DW(5, 2, 7) MICONV_DW(5, 2, 4)
+    MICONV_DW(7, 2, 7) MICONV_DW(7, 2, 4)
+#undef MICONV_DW
     return hipErrorInvalidValue;
 }
 
@@ -218,19 +184,28 @@ bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw)
     return kh == kw && sh == sw && (kh == 3 || kh == 5 || kh == 7) && (sh == 1 || sh == 2);
 }
 
-int dwcl_strip(int64_t s) { return s == 1 ? 8 : 4; }
+// Strip width (outputs per lane along W): the candidate that wastes the fewest
+// lanes on the last, partial strip of a row.
+int dwcl_strip(int64_t s, int64_t ow)
+{
+    const int a = s == 1 ? 14 : 7, b = s == 1 ? 8 : 4;
+    const int64_t wa = cdiv(ow, a) * a - ow, wb = cdiv(ow, b) * b - ow;
+    return wa <= wb ? a : b;
+}
 
 int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream, bool vec)
 {
+    (void)vec;
     const conv_desc &d = p.d;
     DwArgs a;
     a.x = x;
     a.w = w;
     a.b = b;
     a.y = y;
-    a.xs_n = d.x.strides[0];
-    a.xs_h = d.x.strides[2];
-    a.xs_w = d.x.strides[3];
+    a.xs_n = (int32_t)d.x.strides[0];
+    a.xs_h = (int32_t)d.x.strides[2];
+    a.xs_w = (int32_t)d.x.strides[3];
+    a.x_bytes = (int32_t)p.tile[7];
     a.ys_n = p.y.strides[0];
     a.ys_h = p.y.strides[2];
     a.ys_w = p.y.strides[3];
@@ -245,22 +220,22 @@ int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *
     a.OW = (int32_t)d.out[1];
     a.pb_h = (int32_t)d.padding_before[0];
     a.pb_w = (int32_t)d.padding_before[1];
-    a.cvb = (int32_t)p.tile[1];
-    a.sp = (int32_t)p.tile[2];
-    a.rh = (int32_t)p.tile[3];
+    a.cpb = (int32_t)p.tile[1];
+    a.spb = (int32_t)p.tile[2];
+    a.rpt = (int32_t)p.tile[3];
     a.ch_chunks = (int32_t)p.tile[4];
-    a.col_chunks = (int32_t)p.tile[5];
+    a.strip_chunks = (int32_t)p.tile[5];
     a.row_chunks = (int32_t)p.tile[6];
+    a.nstrips = (int32_t)cdiv(d.out[1], p.tile[0]);
     a.total = (int32_t)p.grid[0];
     a.has_bias = d.has_bias;
-    const size_t lds = (size_t)p.lds_bytes;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    const int k = (int)d.k[0], st = (int)d.stride[0];
+    const int k = (int)d.k[0], st = (int)d.stride[0], to = (int)p.tile[0];
     switch (d.dtype) {
-    case CONV_F32: e = dispatch<float>(a, k, st, vec, lds, s); break;
-    case CONV_F16: e = dispatch<f16_t>(a, k, st, vec, lds, s); break;
-    default: e = dispatch<bf16_t>(a, k, st, vec, lds, s); break;
+    case CONV_F32: e = dispatch<float>(a, k, st, to, s); break;
+    case CONV_F16: e = dispatch<f16_t>(a, k, st, to, s); break;
+    default: e = dispatch<bf16_t>(a, k, st, to, s); break;
     }
     return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
 }

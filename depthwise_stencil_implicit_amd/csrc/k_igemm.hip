@@ -25,10 +25,23 @@
 // over that phase's taps only, and is a plain stride-1 gather over j: the
 // structurally-zero taps the literal gather would multiply are never visited.
 //
-// Weights are first repacked (into the caller's workspace) to
-// [G][Cog_pad][taps][Cig_pad], zero-padded, so every B load is a 16-byte vector.
-// MFMA: v_mfma_f32_16x16x32_{bf16,f16}; fp32 inputs use eight
-// v_mfma_f32_16x16x4_f32 steps per 32-wide K slice.  fp32 accumulation.
+// gfx950 mapping
+//   * Weights are first repacked (into the caller's workspace) to
+//     [G][Cog_pad][taps][Cig_pad], zero padded, so B tiles are 16-byte loads.
+//   * A rows are gathered with raw buffer loads: an absent input position gets
+//     an out-of-range offset and the hardware returns zeros, so padding costs
+//     no branch and a thread's loads of one K step are all in flight together.
+//   * LDS tiles hold rows of 8 sixteen-byte chunks; chunk c of row r is stored
+//     at position c ^ (r & 7), so the 8 lanes that share a read cycle hit 8
+//     different bank groups.  Two stages: the next step's global loads are in
+//     flight while the MFMAs consume the current stage.
+//   * MFMA v_mfma_f32_16x16x32_{bf16,f16} (fp32: eight v_mfma_f32_16x16x4_f32
+//     per 32-wide K slice) with operands swapped -- weights as the MFMA A
+//     operand -- so each lane ends holding 4 consecutive output channels of one
+//     output position: one 8-byte store per lane into channel-contiguous y.
+//   * Workgroups are dealt to the 8 XCDs round-robin; the block index is
+//     remapped so each XCD gets one contiguous range of tiles (shared halo
+//     rows and weight slices stay in that XCD's L2).
 #include "dev_common.h"
 #include "internal.h"
 
@@ -38,21 +51,20 @@ namespace miconv {
 
 struct IgArgs {
     const void *x;
-    const void *w;  // repacked
+    const void *w;  // repacked weights
     const void *b;
     void *y;
-    int64_t xs_n, xs_c, xs_l[3];
     int64_t ys_n, ys_c, ys_l[3];
-    int64_t rows;  // rows per phase: N * J0 * J1 * J2
+    int32_t xs_n, xs_c, xs_l[3];  // element strides of x (32-bit: the planner keeps the span < 2 GB)
+    int32_t x_bytes;
+    int32_t rows;                 // rows per phase: N * J0 * J1 * J2
     int32_t Cig, Cog, cig_pad, cog_pad, taps;
     int32_t L[3], K[3], O[3], S[3], PB[3], D[3], J[3];
     int32_t G, phases, m_tiles, n_tiles, transposed, has_bias;
-    int32_t total_tiles;
+    int32_t total_tiles, y_vec4;
+    int32_t w_bytes;              // bytes of the repacked weights (buffer range)
 };
 
-// Block index -> tile index, so that each XCD (blocks are dealt to the 8 XCDs
-// round-robin) receives one contiguous range of tiles: neighbouring tiles share
-// halo rows and weight slices in that XCD's L2.
 __device__ __forceinline__ int xcd_tile(int b, int total)
 {
     const int q = total >> 3, r = total & 7;
@@ -61,24 +73,26 @@ __device__ __forceinline__ int xcd_tile(int b, int total)
     return off + local;
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool VEC>
+// Byte offset of 16-byte chunk `c` of LDS row `r` (rows of 8 chunks).
+__device__ __forceinline__ int swz(int r, int c) { return (r * 8 + (c ^ (r & 7))) * 16; }
+
+template <typename T, int BM, int BN, int WM, int WN, bool VEC>
 __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgArgs a)
 {
     constexpr int NT = 64 * WM * WN;
     constexpr int ES = Dt<T>::size;
-    constexpr int EV = 16 / ES;           // elements per 16-byte chunk
-    constexpr int CH = BK / EV;           // chunks per tile row
-    constexpr int LDK = BK + EV;          // LDS row pitch (elements), one chunk of skew
-    constexpr int A_IT = (BM * CH + NT - 1) / NT;
-    constexpr int B_IT = (BN * CH + NT - 1) / NT;
-    constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+    constexpr int EV = 16 / ES;            // elements per chunk
+    constexpr int BK = 8 * EV;             // K elements per step (8 chunks per row)
+    constexpr int A_IT = BM * 8 / NT;      // A chunks per thread per step
+    constexpr int B_IT = BN * 8 / NT;      // B chunks per thread per step
+    constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
-    static_assert(NT % CH == 0, "chunk column must be fixed per thread");
-    static_assert(BK % 32 == 0 && TM % 16 == 0 && TN % 16 == 0, "tile shape");
+    static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0 && NT % 8 == 0, "chunks per thread");
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * (BM + BN) * LDK * ES];
-    T *sA = reinterpret_cast<T *>(smem);
-    T *sB = sA + 2 * BM * LDK;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned char *sA = smem;                        // [2][BM][8 chunks]
+    unsigned char *sB = smem + 2 * BM * 128;         // [2][BN][8 chunks]
 
     const int tid = threadIdx.x;
     const int tile = xcd_tile(blockIdx.x, a.total_tiles);
@@ -89,131 +103,129 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgArgs a)
     const int phase = rest % a.phases;
     const int g = rest / a.phases;
 
-    // Phase residues (transposed); zero for forward calls.
-    int rho[3];
-    {
+    int rho0 = 0, rho1 = 0, rho2 = 0;
+    if (a.transposed) {
         int p = phase;
-        rho[2] = p % a.S[2]; p /= a.S[2];
-        rho[1] = p % a.S[1]; p /= a.S[1];
-        rho[0] = p;
-        if (!a.transposed) rho[0] = rho[1] = rho[2] = 0;
+        rho2 = p % a.S[2];
+        p /= a.S[2];
+        rho1 = p % a.S[1];
+        rho0 = p / a.S[1];
     }
+    const int JJ = a.J[0] * a.J[1] * a.J[2];
+    const int J12 = a.J[1] * a.J[2];
 
-    const T *__restrict__ X = static_cast<const T *>(a.x);
-    const T *__restrict__ W = static_cast<const T *>(a.w);
-
-    // ---- per-thread A rows (fixed for the whole K loop) ----
-    const int kc = tid % CH;
-    int64_t a_nb[A_IT];
-    int a_base[A_IT][3];
+    // ---- A rows of this thread (fixed over the K loop) ----
+    const int kc = tid & 7;
+    int a_nb[A_IT], a_b0[A_IT], a_b1[A_IT], a_b2[A_IT];
     bool a_ok[A_IT];
-    const int64_t JJ = (int64_t)a.J[0] * a.J[1] * a.J[2];
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
-        const int row = (tid + i * NT) / CH;
-        const int64_t m = (int64_t)m_tile * BM + row;
-        bool ok = row < BM && m < a.rows;
-        int64_t n = 0;
-        int j[3] = {0, 0, 0};
-        if (ok) {
-            n = m / JJ;
-            int64_t r = m - n * JJ;
-            j[2] = (int)(r % a.J[2]);
-            r /= a.J[2];
-            j[1] = (int)(r % a.J[1]);
-            j[0] = (int)(r / a.J[1]);
-        }
-#pragma unroll
-        for (int d = 0; d < 3; ++d) {
-            if (a.transposed) {
-                ok = ok && (a.S[d] * j[d] + rho[d] < a.O[d]);
-                a_base[i][d] = j[d];
-            } else {
-                a_base[i][d] = j[d] * a.S[d] - a.PB[d];
-            }
+        const int row = (tid >> 3) + i * (NT / 8);
+        const int m = m_tile * BM + row;
+        bool ok = m < a.rows;
+        const int mm = ok ? m : 0;
+        const int n = mm / JJ;
+        const int r = mm - n * JJ;
+        const int j0 = r / J12, r2 = r - j0 * J12;
+        const int j1 = r2 / a.J[2], j2 = r2 - j1 * a.J[2];
+        if (a.transposed) {
+            ok = ok && a.S[0] * j0 + rho0 < a.O[0] && a.S[1] * j1 + rho1 < a.O[1] && a.S[2] * j2 + rho2 < a.O[2];
+            a_b0[i] = j0;
+            a_b1[i] = j1;
+            a_b2[i] = j2;
+        } else {
+            a_b0[i] = j0 * a.S[0] - a.PB[0];
+            a_b1[i] = j1 * a.S[1] - a.PB[1];
+            a_b2[i] = j2 * a.S[2] - a.PB[2];
         }
         a_ok[i] = ok;
-        a_nb[i] = n * a.xs_n + (int64_t)g * a.Cig * a.xs_c;
+        a_nb[i] = n * a.xs_n + g * a.Cig * a.xs_c;
     }
 
-    // Tap validity for this phase (uniform across the workgroup).
-    auto tap_off = [&](int t, int off[3]) -> bool {
-        int tt[3];
-        tt[2] = t % a.K[2];
-        tt[1] = (t / a.K[2]) % a.K[1];
-        tt[0] = t / (a.K[2] * a.K[1]);
-        bool ok = true;
-#pragma unroll
-        for (int d = 0; d < 3; ++d) {
-            if (a.transposed) {
-                const int num = rho[d] + a.PB[d] - tt[d] * a.D[d];
-                const int md = num % a.S[d];
-                ok = ok && (md == 0);
-                off[d] = num / a.S[d];
-            } else {
-                off[d] = tt[d] * a.D[d];
-            }
+    // Tap t -> input offsets for this phase; false when the tap is absent.
+    auto tap_offsets = [&](int t, int &o0, int &o1, int &o2) -> bool {
+        const int t2 = t % a.K[2];
+        const int t01 = t / a.K[2];
+        const int t1 = t01 % a.K[1];
+        const int t0 = t01 / a.K[1];
+        if (!a.transposed) {
+            o0 = t0 * a.D[0];
+            o1 = t1 * a.D[1];
+            o2 = t2 * a.D[2];
+            return true;
         }
-        return ok;
-    };
-    auto next_tap = [&](int t, int off[3]) -> int {
-        while (t < a.taps && !tap_off(t, off)) ++t;
-        return t;
+        const int n0 = rho0 + a.PB[0] - t0 * a.D[0];
+        const int n1 = rho1 + a.PB[1] - t1 * a.D[1];
+        const int n2 = rho2 + a.PB[2] - t2 * a.D[2];
+        o0 = n0 / a.S[0];
+        o1 = n1 / a.S[1];
+        o2 = n2 / a.S[2];
+        return n0 % a.S[0] == 0 && n1 % a.S[1] == 0 && n2 % a.S[2] == 0;
     };
 
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.w), (short)0, a.w_bytes, 0x00020000);
+    const T *__restrict__ X = static_cast<const T *>(a.x);
     const int ncb = a.cig_pad / BK;
+    // B chunk offsets: per-thread constant part; the step adds a uniform part.
+    const int wtile0 = (g * a.cog_pad + n_tile * BN) * a.taps * a.cig_pad * ES;
+    int b_off[B_IT];
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+        const int col = (tid >> 3) + i * (NT / 8);
+        b_off[i] = (col * a.taps * a.cig_pad + kc * EV) * ES;
+    }
 
     uint4 ra[A_IT], rb[B_IT];
-    auto gload = [&](int t, const int off[3], int cb) {
+    auto gload = [&](int t, int o0, int o1, int o2, int cb) {
         const int c = cb * BK + kc * EV;
 #pragma unroll
         for (int i = 0; i < A_IT; ++i) {
-            const int i0 = a_base[i][0] + off[0], i1 = a_base[i][1] + off[1], i2 = a_base[i][2] + off[2];
+            const int i0 = a_b0[i] + o0, i1 = a_b1[i] + o1, i2 = a_b2[i] + o2;
             const bool inb = a_ok[i] && (unsigned)i0 < (unsigned)a.L[0] && (unsigned)i1 < (unsigned)a.L[1] &&
                              (unsigned)i2 < (unsigned)a.L[2];
-            const int64_t pix = a_nb[i] + i0 * a.xs_l[0] + i1 * a.xs_l[1] + i2 * a.xs_l[2];
-            if (VEC) {
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (inb && c < a.Cig) v = *reinterpret_cast<const uint4 *>(X + pix + c);
-                ra[i] = v;
+            const int pix = a_nb[i] + i0 * a.xs_l[0] + i1 * a.xs_l[1] + i2 * a.xs_l[2];
+            if constexpr (VEC) {
+                const int off = (inb && c < a.Cig) ? (pix + c) * ES : 0x7fffffff;
+                ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
             } else {
                 T tmp[EV];
 #pragma unroll
                 for (int e = 0; e < EV; ++e) {
-                    T z;
-                    __builtin_memset(&z, 0, sizeof(T));
-                    tmp[e] = (inb && c + e < a.Cig) ? X[pix + (int64_t)(c + e) * a.xs_c] : z;
+                    const bool ok = inb && c + e < a.Cig;
+                    const int idx = ok ? pix + (c + e) * a.xs_c : 0;
+                    T v = X[idx];
+                    if (!ok) __builtin_memset(&v, 0, sizeof(T));
+                    tmp[e] = v;
                 }
                 __builtin_memcpy(&ra[i], tmp, 16);
             }
         }
-        const int64_t wrow0 = ((int64_t)g * a.cog_pad + (int64_t)n_tile * BN) * a.taps;
+        const int step_off = wtile0 + (t * a.cig_pad + cb * BK) * ES;
 #pragma unroll
-        for (int i = 0; i < B_IT; ++i) {
-            const int col = (tid + i * NT) / CH;
-            if (col < BN) {
-                const int64_t off_w = ((wrow0 + (int64_t)col * a.taps + t) * a.cig_pad) + cb * BK + kc * EV;
-                rb[i] = *reinterpret_cast<const uint4 *>(W + off_w);
-            }
-        }
+        for (int i = 0; i < B_IT; ++i)
+            rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, b_off[i], step_off, 0));
     };
     auto sstore = [&](int stage) {
-        T *A = sA + stage * BM * LDK;
-        T *B = sB + stage * BN * LDK;
+        unsigned char *A = sA + stage * BM * 128;
+        unsigned char *B = sB + stage * BN * 128;
 #pragma unroll
         for (int i = 0; i < A_IT; ++i) {
-            const int row = (tid + i * NT) / CH;
-            if (row < BM) *reinterpret_cast<uint4 *>(A + row * LDK + kc * EV) = ra[i];
+            const int row = (tid >> 3) + i * (NT / 8);
+            *reinterpret_cast<uint4 *>(A + swz(row, kc)) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < B_IT; ++i) {
-            const int col = (tid + i * NT) / CH;
-            if (col < BN) *reinterpret_cast<uint4 *>(B + col * LDK + kc * EV) = rb[i];
+            const int col = (tid >> 3) + i * (NT / 8);
+            *reinterpret_cast<uint4 *>(B + swz(col, kc)) = rb[i];
         }
     };
 
     const int wave = tid >> 6, lane = tid & 63;
     const int wr = wave / WN, wc = wave % WN;
+    const int lr = lane & 15, lg = lane >> 4;
     f32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -221,113 +233,134 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgArgs a)
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int stage) {
-        const T *A = sA + stage * BM * LDK;
-        const T *B = sB + stage * BN * LDK;
+        const unsigned char *A = sA + stage * BM * 128;
+        const unsigned char *B = sB + stage * BN * 128;
+        if constexpr (ES == 2) {
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            const int koff = kk * 32 + (lane >> 4) * 8;
-            if constexpr (ES == 2) {
-                uint4 af[FM], bfr[FN];
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    af[i] = *reinterpret_cast<const uint4 *>(A + (wr * TM + i * 16 + (lane & 15)) * LDK + koff);
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    bfr[j] = *reinterpret_cast<const uint4 *>(B + (wc * TN + j * 16 + (lane & 15)) * LDK + koff);
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) mma_16x16x32(af[i], bfr[j], acc[i][j], T{});
-            } else {
-                float af[FM][8], bfr[FN][8];
+            for (int kk = 0; kk < 2; ++kk) {
+                uint4 af[FM], bf[FN];
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
-                    const float *p = reinterpret_cast<const float *>(A) + (wr * TM + i * 16 + (lane & 15)) * LDK + koff;
-                    const float4 v0 = *reinterpret_cast<const float4 *>(p);
-                    const float4 v1 = *reinterpret_cast<const float4 *>(p + 4);
-                    af[i][0] = v0.x; af[i][1] = v0.y; af[i][2] = v0.z; af[i][3] = v0.w;
-                    af[i][4] = v1.x; af[i][5] = v1.y; af[i][6] = v1.z; af[i][7] = v1.w;
+                    const int r = wr * TM + i * 16 + lr;
+                    af[i] = *reinterpret_cast<const uint4 *>(A + swz(r, kk * 4 + lg));
                 }
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const float *p = reinterpret_cast<const float *>(B) + (wc * TN + j * 16 + (lane & 15)) * LDK + koff;
-                    const float4 v0 = *reinterpret_cast<const float4 *>(p);
-                    const float4 v1 = *reinterpret_cast<const float4 *>(p + 4);
-                    bfr[j][0] = v0.x; bfr[j][1] = v0.y; bfr[j][2] = v0.z; bfr[j][3] = v0.w;
-                    bfr[j][4] = v1.x; bfr[j][5] = v1.y; bfr[j][6] = v1.z; bfr[j][7] = v1.w;
+                    const int r = wc * TN + j * 16 + lr;
+                    bf[j] = *reinterpret_cast<const uint4 *>(B + swz(r, kk * 4 + lg));
                 }
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) mma_16x16x32_f32(af[i], bfr[j], acc[i][j]);
+                    for (int j = 0; j < FN; ++j) mma_16x16x32(bf[j], af[i], acc[i][j], T{});
             }
+        } else {
+            float af[FM][8], bf[FN][8];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = wr * TM + i * 16 + lr;
+                const float4 v0 = *reinterpret_cast<const float4 *>(A + swz(r, 2 * lg));
+                const float4 v1 = *reinterpret_cast<const float4 *>(A + swz(r, 2 * lg + 1));
+                af[i][0] = v0.x; af[i][1] = v0.y; af[i][2] = v0.z; af[i][3] = v0.w;
+                af[i][4] = v1.x; af[i][5] = v1.y; af[i][6] = v1.z; af[i][7] = v1.w;
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int r = wc * TN + j * 16 + lr;
+                const float4 v0 = *reinterpret_cast<const float4 *>(B + swz(r, 2 * lg));
+                const float4 v1 = *reinterpret_cast<const float4 *>(B + swz(r, 2 * lg + 1));
+                bf[j][0] = v0.x; bf[j][1] = v0.y; bf[j][2] = v0.z; bf[j][3] = v0.w;
+                bf[j][4] = v1.x; bf[j][5] = v1.y; bf[j][6] = v1.z; bf[j][7] = v1.w;
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) mma_16x16x32_f32(bf[j], af[i], acc[i][j]);
         }
     };
 
-    // ---- K loop: (valid tap, channel block) steps, double-buffered LDS ----
-    int off[3];
-    int t = next_tap(0, off);
-    int cb = 0;
+    // ---- K loop over (valid tap, channel block), double-buffered ----
+    int t = 0, o0 = 0, o1 = 0, o2 = 0;
+    while (t < a.taps && !tap_offsets(t, o0, o1, o2)) ++t;
     if (t < a.taps && ncb > 0) {
-        gload(t, off, cb);
+        int cb = 0;
+        gload(t, o0, o1, o2, cb);
         sstore(0);
         __syncthreads();
         int stage = 0;
         while (true) {
-            int nt = t, ncb_i = cb + 1;
-            int noff[3] = {off[0], off[1], off[2]};
-            if (ncb_i == ncb) {
-                ncb_i = 0;
-                nt = next_tap(t + 1, noff);
+            int nt = t, ncbi = cb + 1, p0 = o0, p1 = o1, p2 = o2;
+            if (ncbi == ncb) {
+                ncbi = 0;
+                ++nt;
+                while (nt < a.taps && !tap_offsets(nt, p0, p1, p2)) ++nt;
             }
             const bool more = nt < a.taps;
-            if (more) gload(nt, noff, ncb_i);
+            if (more) gload(nt, p0, p1, p2, ncbi);
             compute(stage);
             if (more) sstore(stage ^ 1);
             __syncthreads();
             if (!more) break;
             stage ^= 1;
             t = nt;
-            cb = ncb_i;
-            off[0] = noff[0]; off[1] = noff[1]; off[2] = noff[2];
+            cb = ncbi;
+            o0 = p0;
+            o1 = p1;
+            o2 = p2;
         }
     }
 
-    // ---- epilogue: bias in fp32, one rounding, store at y's strides ----
+    // ---- epilogue: lane holds 4 consecutive channels of one output position ----
     T *__restrict__ Y = static_cast<T *>(a.y);
     const T *__restrict__ Bias = static_cast<const T *>(a.b);
+    float bias[FN][4];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int co = n_tile * BN + wc * TN + j * 16 + (lane & 15);
-        if (co >= a.Cog) continue;
-        const int cog = g * a.Cog + co;
-        const float bias = a.has_bias ? to_f32(Bias[cog]) : 0.f;
+        const int co = n_tile * BN + wc * TN + j * 16 + lg * 4;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for (int e = 0; e < 4; ++e)
+            bias[j][e] = (a.has_bias && co + e < a.Cog) ? to_f32(Bias[g * a.Cog + co + e]) : 0.f;
+    }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = wr * TM + i * 16 + (lane >> 4) * 4 + e;
-                const int64_t m = (int64_t)m_tile * BM + row;
-                if (m >= a.rows) continue;
-                const int64_t n = m / JJ;
-                int64_t r = m - n * JJ;
-                int o[3];
-                o[2] = (int)(r % a.J[2]);
-                r /= a.J[2];
-                o[1] = (int)(r % a.J[1]);
-                o[0] = (int)(r / a.J[1]);
-                bool ok = true;
-                if (a.transposed) {
+    for (int i = 0; i < FM; ++i) {
+        const int m = m_tile * BM + wr * TM + i * 16 + lr;
+        if (m >= a.rows) continue;
+        const int n = m / JJ;
+        const int r = m - n * JJ;
+        int q0 = r / J12;
+        const int r2 = r - q0 * J12;
+        int q1 = r2 / a.J[2], q2 = r2 - q1 * a.J[2];
+        if (a.transposed) {
+            q0 = a.S[0] * q0 + rho0;
+            q1 = a.S[1] * q1 + rho1;
+            q2 = a.S[2] * q2 + rho2;
+            if (q0 >= a.O[0] || q1 >= a.O[1] || q2 >= a.O[2]) continue;
+        }
+        const int64_t yrow = (int64_t)n * a.ys_n + q0 * a.ys_l[0] + q1 * a.ys_l[1] + q2 * a.ys_l[2];
 #pragma unroll
-                    for (int d = 0; d < 3; ++d) {
-                        o[d] = a.S[d] * o[d] + rho[d];
-                        ok = ok && o[d] < a.O[d];
+        for (int j = 0; j < FN; ++j) {
+            const int co = n_tile * BN + wc * TN + j * 16 + lg * 4;
+            const int cg = g * a.Cog + co;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] + bias[j][e];
+            T *dst = Y + yrow + (int64_t)cg * a.ys_c;
+            if (a.y_vec4) {
+                // Cog % 4 == 0 here, so a group of 4 is either all in or all out.
+                if (co < a.Cog) {
+                    if constexpr (ES == 2) {
+                        uint2 u;
+                        u.x = pack2<T>(v[0], v[1]);
+                        u.y = pack2<T>(v[2], v[3]);
+                        *reinterpret_cast<uint2 *>(dst) = u;
+                    } else {
+                        *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
                     }
                 }
-                if (!ok) continue;
-                const int64_t yo = n * a.ys_n + (int64_t)cog * a.ys_c + o[0] * a.ys_l[0] + o[1] * a.ys_l[1] +
-                                   o[2] * a.ys_l[2];
-                Y[yo] = from_f32<T>(acc[i][j][e] + bias);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (co + e < a.Cog) dst[(int64_t)e * a.ys_c] = from_f32<T>(v[e]);
             }
         }
     }
@@ -364,18 +397,26 @@ __global__ void igemm_repack(const T *__restrict__ w, T *__restrict__ wr, int64_
 namespace {
 
 constexpr IgemmCfg kCfgs[] = {
-    {128, 128, 32, 2, 2},  // 0: 2-byte types, wide N
-    {128, 64, 32, 2, 2},   // 1: 2-byte types, N <= 64
-    {256, 32, 32, 4, 1},   // 2: 2-byte types, N <= 32
-    {64, 64, 32, 2, 2},    // 3: fp32
+    {256, 256, 64, 2, 4},  // 0: 2-byte types, wide N, 8 waves (wave tile 128 x 64)
+    {160, 256, 64, 2, 2},  // 1: 2-byte types, wide N, finer M (wave tile 80 x 128)
+    {128, 128, 64, 2, 2},  // 2: 2-byte types, N <= 128
+    {256, 64, 64, 4, 1},   // 3: 2-byte types, N <= 64
+    {256, 32, 64, 4, 1},   // 4: 2-byte types, N <= 32
+    {128, 64, 32, 2, 2},   // 5: fp32
 };
 
 template <typename T, int V, bool VEC>
 hipError_t launch_cfg(const IgArgs &a, hipStream_t s)
 {
     constexpr IgemmCfg c = kCfgs[V];
-    hipLaunchKernelGGL((igemm_kernel<T, c.bm, c.bn, c.bk, c.wm, c.wn, VEC>), dim3(a.total_tiles),
-                       dim3(64 * c.wm * c.wn), 0, s, a);
+    const size_t lds = (size_t)2 * (c.bm + c.bn) * 128;
+    auto kern = igemm_kernel<T, c.bm, c.bn, c.wm, c.wn, VEC>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(a.total_tiles), dim3(64 * c.wm * c.wn), lds, s, a);
     return hipGetLastError();
 }
 
@@ -383,12 +424,14 @@ template <typename T>
 hipError_t launch_typed(const IgArgs &a, int variant, bool vec, hipStream_t s)
 {
     if constexpr (Dt<T>::size == 4) {
-        return vec ? launch_cfg<T, 3, true>(a, s) : launch_cfg<T, 3, false>(a, s);
+        return vec ? launch_cfg<T, 5, true>(a, s) : launch_cfg<T, 5, false>(a, s);
     } else {
         switch (variant) {
         case 0: return vec ? launch_cfg<T, 0, true>(a, s) : launch_cfg<T, 0, false>(a, s);
         case 1: return vec ? launch_cfg<T, 1, true>(a, s) : launch_cfg<T, 1, false>(a, s);
         case 2: return vec ? launch_cfg<T, 2, true>(a, s) : launch_cfg<T, 2, false>(a, s);
+        case 3: return vec ? launch_cfg<T, 3, true>(a, s) : launch_cfg<T, 3, false>(a, s);
+        case 4: return vec ? launch_cfg<T, 4, true>(a, s) : launch_cfg<T, 4, false>(a, s);
         default: return hipErrorInvalidValue;
         }
     }
@@ -428,13 +471,13 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
     a.b = b;
     a.y = y;
     const int r = d.spatial;
-    a.xs_n = d.x.strides[0];
-    a.xs_c = d.x.strides[1];
+    a.xs_n = (int32_t)d.x.strides[0];
+    a.xs_c = (int32_t)d.x.strides[1];
     a.ys_n = p.y.strides[0];
     a.ys_c = p.y.strides[1];
     for (int i = 0; i < 3; ++i) {
         const bool on = i < r;
-        a.xs_l[i] = on ? d.x.strides[2 + i] : 0;
+        a.xs_l[i] = on ? (int32_t)d.x.strides[2 + i] : 0;
         a.ys_l[i] = on ? p.y.strides[2 + i] : 0;
         a.L[i] = (int32_t)d.in[i];
         a.K[i] = (int32_t)d.k[i];
@@ -444,6 +487,7 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
         a.D[i] = (int32_t)d.dilation[i];
         a.J[i] = (int32_t)(d.transposed ? cdiv(d.out[i], d.stride[i]) : d.out[i]);
     }
+    a.x_bytes = (int32_t)p.tile[IG_XBYTES];
     a.Cig = (int32_t)(d.C_in / d.groups);
     a.Cog = (int32_t)(d.C_out / d.groups);
     a.cig_pad = (int32_t)p.tile[IG_CIG_PAD];
@@ -453,10 +497,18 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
     a.phases = (int32_t)p.tile[IG_PHASES];
     a.m_tiles = (int32_t)p.tile[IG_MTILES];
     a.n_tiles = (int32_t)p.tile[IG_NTILES];
-    a.rows = p.tile[IG_ROWS];
+    a.rows = (int32_t)p.tile[IG_ROWS];
     a.transposed = d.transposed;
     a.has_bias = d.has_bias;
     a.total_tiles = (int32_t)p.grid[0];
+    a.w_bytes = (int32_t)p.workspace_bytes;
+    // 4 consecutive output channels form one aligned vector in y.
+    a.y_vec4 = (p.y.strides[1] == 1 && (reinterpret_cast<uintptr_t>(y) & (4 * esize(d.dtype) - 1)) == 0 &&
+                p.y.strides[0] % 4 == 0 && (r < 1 || p.y.strides[2] % 4 == 0) &&
+                (r < 2 || p.y.strides[3] % 4 == 0) && (r < 3 || p.y.strides[4] % 4 == 0) &&
+                (d.C_out / d.groups) % 4 == 0)
+                   ? 1
+                   : 0;
 
     hipError_t e;
     switch (d.dtype) {

@@ -29,7 +29,7 @@
 
 namespace miconv {
 bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw);
-int dwcl_strip(int64_t s);
+int dwcl_strip(int64_t s, int64_t ow);
 bool grp_supported(const conv_desc &d);
 void grp_geometry(const conv_desc &d, conv_plan_t &p);
 void reduce_geometry(const conv_desc &d, conv_plan_t &p);
@@ -82,12 +82,28 @@ bool stencil_domain(const conv_desc &d)
     return !d.transposed && (d.spatial == 1 || d.spatial == 2) && cig(d) >= 1 && cig(d) <= 8 && k_le(d, 9);
 }
 
+// Byte span of a tensor (largest element offset + 1) times the element size.
+int64_t span_bytes(const conv_tensor &t, int64_t es)
+{
+    int64_t off = 0;
+    for (int i = 0; i < t.rank; ++i)
+        if (t.sizes[i] > 0) off += (t.sizes[i] - 1) * t.strides[i];
+    return (off + 1) * es;
+}
+
 bool supports_dwcl(const conv_desc &d, const conv_tensor &y)
 {
     if (!stencil_domain(d) || d.spatial != 2 || !all_dil1(d)) return false;
     if (cig(d) != 1 || d.groups != d.C_in || d.C_out != d.C_in) return false;
     if (!dwcl_has_schedule(d.k[0], d.k[1], d.stride[0], d.stride[1])) return false;
-    return d.x.strides[1] == 1 && y.strides[1] == 1;
+    if (d.x.strides[1] != 1 || y.strides[1] != 1) return false;
+    // One lane word holds 4 bytes of channels: word-aligned channel runs.
+    const int64_t v = 4 / esize(d.dtype);
+    if (d.C_in % v) return false;
+    for (int i : {0, 2, 3})
+        if (d.x.strides[i] % v || y.strides[i] % v) return false;
+    // 32-bit buffer offsets.
+    return span_bytes(d.x, esize(d.dtype)) <= kI32 - 4096;
 }
 
 bool supports_plane(const conv_desc &d) { return stencil_domain(d); }
@@ -120,34 +136,30 @@ int route(const conv_desc &d, const conv_tensor &y)
 
 void geom_dwcl(const conv_desc &d, conv_plan_t &p)
 {
-    const int64_t V = 16 / esize(d.dtype);
-    const int64_t cv = cdiv(d.C_in, V);
-    int64_t cvb = 1;
-    while (cvb * 2 <= cv && cvb * 2 <= 32) cvb *= 2;
-    const int64_t sp = 256 / cvb;
-    const int64_t to = dwcl_strip(d.stride[1]);
-    const int64_t ch_chunks = cdiv(cv, cvb);
-    const int64_t col_chunks = cdiv(d.out[1], sp * to);
-    const int64_t per_row = d.N * col_chunks * ch_chunks;
-    int64_t rh = per_row * d.out[0] / 2048;
-    if (rh < 1) rh = 1;
-    if (rh > d.out[0]) rh = d.out[0];
-    const int64_t row_chunks = cdiv(d.out[0], rh);
+    const int64_t words = d.C_in * esize(d.dtype) / 4;
+    const int64_t cpb = words < 256 ? words : 256;
+    const int64_t spb = 256 / cpb;
+    const int64_t to = dwcl_strip(d.stride[1], d.out[1]);
+    const int64_t nstrips = cdiv(d.out[1], to);
+    const int64_t strip_chunks = cdiv(nstrips, spb);
+    const int64_t ch_chunks = cdiv(words, cpb);
+    const int64_t per_row = d.N * strip_chunks * ch_chunks;
+    int64_t rpt = per_row * d.out[0] / 1024;
+    if (rpt < 1) rpt = 1;
+    if (rpt > d.out[0]) rpt = d.out[0];
+    const int64_t row_chunks = cdiv(d.out[0], rpt);
     p.tile[0] = to;
-    p.tile[1] = cvb;
-    p.tile[2] = sp;
-    p.tile[3] = rh;
+    p.tile[1] = cpb;
+    p.tile[2] = spb;
+    p.tile[3] = rpt;
     p.tile[4] = ch_chunks;
-    p.tile[5] = col_chunks;
+    p.tile[5] = strip_chunks;
     p.tile[6] = row_chunks;
+    p.tile[7] = span_bytes(d.x, esize(d.dtype));
     p.grid[0] = per_row * row_chunks;
     p.block = 256;
-    p.lds_bytes = (int32_t)(d.k[0] * d.k[1] * cvb * V * 4);
-    const int64_t ev = V;
-    bool vec = d.C_in % ev == 0 && d.x.strides[0] % ev == 0 && d.x.strides[2] % ev == 0 &&
-               d.x.strides[3] % ev == 0 && p.y.strides[0] % ev == 0 && p.y.strides[2] % ev == 0 &&
-               p.y.strides[3] % ev == 0;
-    p.vec_ok = vec ? 1 : 0;
+    p.lds_bytes = 0;
+    p.vec_ok = 1;
 }
 
 bool geom_plane(const conv_desc &d, conv_plan_t &p)
@@ -199,21 +211,10 @@ bool geom_plane(const conv_desc &d, conv_plan_t &p)
     return p.grid[0] <= kI32;
 }
 
-void geom_igemm(const conv_desc &d, conv_plan_t &p)
+// Implicit GEMM: choose the tile shape with the least estimated CU time,
+// rounds of workgroups over the 256 CUs times the tile area each runs.
+bool geom_igemm(const conv_desc &d, conv_plan_t &p)
 {
-    int variant;
-    if (d.dtype == CONV_F32)
-        variant = 3;
-    else if (cog(d) <= 32)
-        variant = 2;
-    else if (cog(d) <= 64)
-        variant = 1;
-    else
-        variant = 0;
-    const IgemmCfg &c = igemm_cfg(variant);
-    const int64_t taps = d.k[0] * d.k[1] * d.k[2];
-    const int64_t cig_pad = round_up(cig(d), c.bk);
-    const int64_t cog_pad = round_up(cog(d) > 0 ? cog(d) : 1, c.bn);
     int64_t phases = 1, rows = d.N;
     for (int i = 0; i < 3; ++i) {
         if (d.transposed) {
@@ -223,21 +224,50 @@ void geom_igemm(const conv_desc &d, conv_plan_t &p)
             rows *= d.out[i];
         }
     }
-    p.variant = variant;
+    const int64_t es = esize(d.dtype);
+    const int64_t xspan = span_bytes(d.x, es);
+    // Element offsets into x are 32-bit in the kernel.
+    if (xspan / es >= kI32 || rows >= kI32) return false;
+    int best = -1;
+    double best_cost = 0;
+    const int lo = d.dtype == CONV_F32 ? 5 : 0, hi = d.dtype == CONV_F32 ? 5 : 4;
+    for (int v = lo; v <= hi; ++v) {
+        const IgemmCfg &c = igemm_cfg(v);
+        const int64_t lds = 2 * (int64_t)(c.bm + c.bn) * 128;
+        const int64_t occ = lds > 80 * 1024 ? 1 : 2;
+        const int64_t tiles = d.groups * phases * cdiv(rows, c.bm) * cdiv(cog(d) > 0 ? cog(d) : 1, c.bn);
+        const double rounds = (double)cdiv(tiles, 256 * occ);
+        // Smaller tiles re-read more A and B per MAC; weigh them by tile perimeter.
+        const double eff = 1.0 + 0.25 * (256.0 / c.bm + 256.0 / c.bn - 2.0) / 2.0;
+        const double cost = rounds * occ * c.bm * c.bn * eff;
+        if (best < 0 || cost < best_cost) {
+            best = v;
+            best_cost = cost;
+        }
+    }
+    const IgemmCfg &c = igemm_cfg(best);
+    const int64_t taps = d.k[0] * d.k[1] * d.k[2];
+    const int64_t cig_pad = round_up(cig(d), c.bk);
+    const int64_t cog_pad = round_up(cog(d) > 0 ? cog(d) : 1, c.bn);
+    p.variant = best;
     p.tile[IG_CIG_PAD] = cig_pad;
     p.tile[IG_COG_PAD] = cog_pad;
     p.tile[IG_PHASES] = phases;
     p.tile[IG_MTILES] = cdiv(rows, c.bm);
     p.tile[IG_NTILES] = cog_pad / c.bn;
     p.tile[IG_ROWS] = rows;
+    p.tile[IG_XBYTES] = xspan < kI32 - 4096 ? xspan : 0;
     p.grid[0] = d.groups * phases * p.tile[IG_MTILES] * p.tile[IG_NTILES];
     p.block = 64 * c.wm * c.wn;
-    p.lds_bytes = 0;
-    p.workspace_bytes = round_up(d.groups * cog_pad * taps * cig_pad * esize(d.dtype), 256);
-    const int64_t ev = 16 / esize(d.dtype);
-    bool vec = d.x.strides[1] == 1 && cig(d) % ev == 0 && d.x.strides[0] % ev == 0;
+    p.lds_bytes = (int32_t)(2 * (c.bm + c.bn) * 128);
+    p.workspace_bytes = round_up(d.groups * cog_pad * taps * cig_pad * es, 256);
+    if (p.workspace_bytes >= kI32) return false;   // 32-bit buffer offsets into the weights
+    // 16-byte buffer-load path: contiguous, chunk-aligned channels, span < 2 GB.
+    const int64_t ev = 16 / es;
+    bool vec = d.x.strides[1] == 1 && cig(d) % ev == 0 && d.x.strides[0] % ev == 0 && p.tile[IG_XBYTES] > 0;
     for (int i = 0; i < d.spatial; ++i) vec = vec && d.x.strides[2 + i] % ev == 0;
     p.vec_ok = vec ? 1 : 0;
+    return true;
 }
 
 // Algorithmic FLOPs: 2 per (output element, input channel, tap) term whose
@@ -311,12 +341,14 @@ extern "C" int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force
         if (!geom_plane(*d, plan)) {
             if (force_kernel != CONV_K_AUTO) return CONV_EUNSUPPORTED;
             plan.kernel = CONV_K_IGEMM;
-            geom_igemm(*d, plan);
+            if (!geom_igemm(*d, plan)) return CONV_EUNSUPPORTED;
         }
         break;
     case CONV_K_GRP: grp_geometry(*d, plan); break;
     case CONV_K_REDUCE: reduce_geometry(*d, plan); break;
-    default: geom_igemm(*d, plan); break;
+    default:
+        if (!geom_igemm(*d, plan)) return CONV_EUNSUPPORTED;
+        break;
     }
     if (plan.grid[0] > kI32) return CONV_EUNSUPPORTED;
 

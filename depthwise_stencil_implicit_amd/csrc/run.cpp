@@ -42,7 +42,24 @@ extern "C" int conv_run(const conv_plan_t *p, const void *x, const void *w, cons
     }
     const bool vec = p->vec_ok && aligned(x, 16) && aligned(y, 16);
     switch (p->kernel) {
-    case CONV_K_DW_CL: return launch_dwcl(*p, x, w, b, y, stream, vec);
+    case CONV_K_DW_CL:
+        // Lanes move 4-byte channel words; a view that is not word-aligned
+        // runs on the layout-generic plane stencil instead.
+        if (!aligned(x, 4) || !aligned(y, 4)) {
+            conv_tensor yc = p->y;
+            if (d.unbatched) {
+                for (int i = 1; i < yc.rank; ++i) {
+                    yc.sizes[i - 1] = yc.sizes[i];
+                    yc.strides[i - 1] = yc.strides[i];
+                }
+                yc.rank -= 1;
+            }
+            conv_plan_t q;
+            const int st = conv_plan(&d, &yc, CONV_K_PLANE, &q);
+            if (st != CONV_OK) return st;
+            return launch_plane(q, x, w, b, y, stream);
+        }
+        return launch_dwcl(*p, x, w, b, y, stream, vec);
     case CONV_K_PLANE: return launch_plane(*p, x, w, b, y, stream);
     case CONV_K_GRP: return launch_grp(*p, x, w, b, y, stream);
     case CONV_K_REDUCE: return launch_reduce(*p, x, w, b, y, stream);
