@@ -13,16 +13,24 @@
 // left to right; each load is widened to fp32 once and feeds every output of
 // the strip whose window covers that column -- the loaded row segment is the
 // register sliding window.  Consecutive lanes hold consecutive channel words of
-// the same pixel, so every wave load and store is one contiguous run.  All
-// K*K weights of the lane's channels live in registers as fp32 for the whole
-// kernel: no LDS and no barrier.
+// the same pixel, so every wave load and store is one contiguous run.
+// Workgroups are persistent -- one resident round over all CUs -- and each
+// keeps one (strip chunk, channel chunk), so its weights are staged in LDS
+// (fp32 [tap][channel]) once; each kernel row reads back only its K weights
+// per channel.
 //
-// Loads are raw buffer loads whose out-of-range offsets return zero, so the
-// zero padding costs no branch and all loads of a row can be in flight at once.
+// Loads are raw buffer loads: a lane's column offsets are computed once, the
+// row offset (uniform across the wave) rides in the scalar offset, and absent
+// rows or columns get an out-of-range offset so the hardware returns zeros --
+// no branch for the padding.  The (output row, kernel row) steps form one
+// rolled loop with a one-step prefetch, which keeps the register footprint
+// near 120 VGPRs (four waves per SIMD) while a row segment is in flight.
 // Accumulation is fp32 FMA, the bias is the initial value, and each result is
 // rounded once to the output dtype.
 #include "dev_common.h"
 #include "internal.h"
+
+#include <algorithm>
 
 namespace miconv {
 
@@ -69,98 +77,154 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     constexpr int V = Word<T>::V;
     constexpr int ES = Dt<T>::size;
     constexpr int NCOL = (TO - 1) * S + K;
+    constexpr int INVALID = 0x7fffff00;
+    extern __shared__ __attribute__((aligned(16))) float sw[];  // [K*K taps][CW + 2] fp32
 
+    // Persistent workgroups: a workgroup keeps one (strip chunk, channel
+    // chunk) for its whole life and walks one contiguous block of output rows
+    // (n, oh).  Workgroup numbers are remapped so each XCD owns a contiguous
+    // band of row blocks: neighbouring rows share K-1 input rows in its L2.
     const int tid = threadIdx.x;
-    int blk = xcd_block(blockIdx.x, a.total);
-    const int chc = blk % a.ch_chunks;
-    blk /= a.ch_chunks;
-    const int stc = blk % a.strip_chunks;
-    blk /= a.strip_chunks;
-    const int rowc = blk % a.row_chunks;
-    const int n = blk / a.row_chunks;
+    const int SC = a.strip_chunks * a.ch_chunks;
+    const int vb = xcd_block(blockIdx.x, gridDim.x);
+    const int sc = vb % SC;
+    const int chc = sc % a.ch_chunks;
+    const int stc = sc / a.ch_chunks;
+    const int q = vb / SC;
+    const int nwg = gridDim.x / SC;
+    const int rows_total = a.N * a.OH;
+    const int first = (int)((int64_t)q * rows_total / nwg);
+    const int last = (int)((int64_t)(q + 1) * rows_total / nwg);
 
-    const int word = chc * a.cpb + tid % a.cpb;     // channel word index
-    const int c0 = word * V;
+    // Stage this workgroup's weights once: consecutive threads read
+    // consecutive taps of one channel (contiguous for a dense weight).
+    const int CW = a.cpb * V;
+    const int pitch = CW + 2;
+    const int c_base = chc * CW;
+    {
+        const T *Wt = static_cast<const T *>(a.w);
+        for (int i = tid; i < K * K * CW; i += 256) {
+            const int cl = i / (K * K);
+            const int tap = i - cl * (K * K);
+            const int c = min(c_base + cl, a.C - 1);
+            const int kh = tap / K, kw = tap - kh * K;
+            sw[tap * pitch + cl] = to_f32(Wt[(int64_t)c * a.ws0 + kh * a.ws2 + kw * a.ws3]);
+        }
+    }
+    __syncthreads();
+
+    const int cl0 = (tid % a.cpb) * V;
+    const int c0 = c_base + cl0;
     const int strip = stc * a.spb + tid / a.cpb;
-    if (c0 >= a.C || strip >= a.nstrips) return;
+    if (c0 >= a.C || strip >= a.nstrips || tid >= a.cpb * a.spb || first >= last) return;
     const int ow0 = strip * TO;
 
-    // Weights of this lane's channels, fp32, in registers.
-    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.w), (short)0,
-                                                                        0x7fffffff, 0x00020000);
-    const T *Wt = static_cast<const T *>(a.w);
-    float wv[K][K][V];
-#pragma unroll
-    for (int kh = 0; kh < K; ++kh)
-#pragma unroll
-        for (int kw = 0; kw < K; ++kw)
-#pragma unroll
-            for (int v = 0; v < V; ++v) {
-                const int c = min(c0 + v, a.C - 1);
-                wv[kh][kw][v] = to_f32(Wt[(int64_t)c * a.ws0 + kh * a.ws2 + kw * a.ws3]);
-            }
-    (void)wr;
     float bias[V];
     {
         const T *Bp = static_cast<const T *>(a.b);
 #pragma unroll
-        for (int v = 0; v < V; ++v) bias[v] = a.has_bias ? to_f32(Bp[min(c0 + v, a.C - 1)]) : 0.f;
+        for (int v = 0; v < V; ++v) bias[v] = a.has_bias ? to_f32(Bp[c0 + v]) : 0.f;
     }
 
+    // Column byte offsets of this lane's strip; absent columns are out of range.
+    int vcol[NCOL];
+    const int iw0 = ow0 * S - a.pb_w;
+#pragma unroll
+    for (int col = 0; col < NCOL; ++col) {
+        const int iw = iw0 + col;
+        vcol[col] = (unsigned)iw < (unsigned)a.W ? (iw * a.xs_w + c0) * ES : INVALID;
+    }
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
-    const int xbase = n * a.xs_n + c0;              // element offset of (n, 0, 0, c0)
-    const int iw0 = ow0 * S - a.pb_w;
-    T *__restrict__ Y = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + c0;
+    T *__restrict__ Y = static_cast<T *>(a.y) + c0;
 
-    const int oh_beg = rowc * a.rpt;
-    const int oh_end = min(a.OH, oh_beg + a.rpt);
-    for (int oh = oh_beg; oh < oh_end; ++oh) {
-        float acc[TO][V];
+    // Output rows first .. last-1, K steps (kernel rows) each, in one loop
+    // with a one-step prefetch that also crosses output rows.
+    const int steps = (last - first) * K;
+
+    auto fetch = [&](int step, uint32_t (&buf)[NCOL]) {
+        const int r = step / K;
+        const int kh = step - r * K;
+        const int row = first + r;
+        const int n = row / a.OH;
+        const int oh = row - n * a.OH;
+        const int ih = oh * S - a.pb_h + kh;
+        const bool ok = (unsigned)ih < (unsigned)a.H;
+        const int soff = ok ? (n * a.xs_n + ih * a.xs_h) * ES : 0;
+        const int vbad = ok ? 0 : INVALID;
 #pragma unroll
-        for (int t = 0; t < TO; ++t)
+        for (int col = 0; col < NCOL; ++col)
+            buf[col] = __builtin_amdgcn_raw_buffer_load_b32(xr, vcol[col] + vbad, soff, 0);
+    };
+
+    uint32_t cur[NCOL], nxt[NCOL];
+    float acc[TO][V];
+    fetch(0, cur);
+    for (int step = 0; step < steps; ++step) {
+        const int r = step / K;
+        const int kh = step - r * K;
+        if (step + 1 < steps) fetch(step + 1, nxt);
+        if (kh == 0) {
 #pragma unroll
-            for (int v = 0; v < V; ++v) acc[t][v] = bias[v];
+            for (int t = 0; t < TO; ++t)
 #pragma unroll
-        for (int kh = 0; kh < K; ++kh) {
-            const int ih = oh * S - a.pb_h + kh;
-            const bool row_ok = (unsigned)ih < (unsigned)a.H;
-            const int rbase = xbase + ih * a.xs_h;
+                for (int v = 0; v < V; ++v) acc[t][v] = bias[v];
+        }
+        float wk[K][V];
 #pragma unroll
-            for (int col = 0; col < NCOL; ++col) {
-                const int iw = iw0 + col;
-                const bool ok = row_ok && (unsigned)iw < (unsigned)a.W;
-                const int off = ok ? (rbase + iw * a.xs_w) * ES : 0x7fffffff;
-                const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
-                float xv[V];
-                Word<T>::widen(u, xv);
+        for (int kw = 0; kw < K; ++kw)
 #pragma unroll
-                for (int t = 0; t < TO; ++t) {
-                    const int kw = col - t * S;
-                    if (kw >= 0 && kw < K) {
+            for (int v = 0; v < V; ++v) wk[kw][v] = sw[(kh * K + kw) * pitch + cl0 + v];
 #pragma unroll
-                        for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xv[v], wv[kh][kw][v], acc[t][v]);
-                    }
+        for (int col = 0; col < NCOL; ++col) {
+            float xv[V];
+            Word<T>::widen(cur[col], xv);
+#pragma unroll
+            for (int t = 0; t < TO; ++t) {
+                const int kw = col - t * S;
+                if (kw >= 0 && kw < K) {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xv[v], wk[kw][v], acc[t][v]);
                 }
             }
         }
-        T *yrow = Y + (int64_t)oh * a.ys_h;
+        if (kh == K - 1) {
+            const int row = first + r;
+            const int n = row / a.OH;
+            const int oh = row - n * a.OH;
+            T *yrow = Y + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h;
 #pragma unroll
-        for (int t = 0; t < TO; ++t) {
-            if (ow0 + t < a.OW) {
-                const uint32_t u = Word<T>::narrow(acc[t]);
-                *reinterpret_cast<uint32_t *>(yrow + (int64_t)(ow0 + t) * a.ys_w) = u;
+            for (int t = 0; t < TO; ++t) {
+                if (ow0 + t < a.OW)
+                    *reinterpret_cast<uint32_t *>(yrow + (int64_t)(ow0 + t) * a.ys_w) = Word<T>::narrow(acc[t]);
             }
         }
+#pragma unroll
+        for (int col = 0; col < NCOL; ++col) cur[col] = nxt[col];
     }
 }
 
 namespace {
 
 template <typename T, int K, int S, int TO>
-hipError_t go(const DwArgs &a, hipStream_t s)
+hipError_t go(DwArgs a, hipStream_t s)
 {
-    hipLaunchKernelGGL((dwcl_kernel<T, K, S, TO>), dim3(a.total), dim3(256), 0, s, a);
+    auto kern = dwcl_kernel<T, K, S, TO>;
+    const size_t lds = (size_t)K * K * (a.cpb * Word<T>::V + 2) * sizeof(float);
+    // One resident round of persistent workgroups, a multiple of the number
+    // of (strip, channel) chunks, and no more than there are rows to share.
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), 256, lds);
+    if (e != hipSuccess) return e;
+    const int64_t SC = (int64_t)a.strip_chunks * a.ch_chunks;
+    int64_t slots = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
+    const int64_t rows = (int64_t)a.N * a.OH;
+    int64_t per_sc = std::max<int64_t>(1, std::min<int64_t>(slots / SC, rows));
+    const int64_t grid = per_sc * SC;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 

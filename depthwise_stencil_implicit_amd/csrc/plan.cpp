@@ -143,11 +143,11 @@ void geom_dwcl(const conv_desc &d, conv_plan_t &p)
     const int64_t nstrips = cdiv(d.out[1], to);
     const int64_t strip_chunks = cdiv(nstrips, spb);
     const int64_t ch_chunks = cdiv(words, cpb);
+    // Persistent workgroups: the launcher sizes the grid to one resident
+    // round; grid[0] here is the upper bound (one row per workgroup).
+    const int64_t rpt = 1;
+    const int64_t row_chunks = d.out[0];
     const int64_t per_row = d.N * strip_chunks * ch_chunks;
-    int64_t rpt = per_row * d.out[0] / 1024;
-    if (rpt < 1) rpt = 1;
-    if (rpt > d.out[0]) rpt = d.out[0];
-    const int64_t row_chunks = cdiv(d.out[0], rpt);
     p.tile[0] = to;
     p.tile[1] = cpb;
     p.tile[2] = spb;
