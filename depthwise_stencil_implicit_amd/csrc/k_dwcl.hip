@@ -78,6 +78,8 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     constexpr int ES = Dt<T>::size;
     constexpr int NCOL = (TO - 1) * S + K;
     constexpr int INVALID = 0x7fffff00;
+    constexpr int M = (K + S - 1) / S;   // output rows open at once (accumulator slots)
+    constexpr int U = M * S;             // input rows per unrolled block: slot pattern repeats
     extern __shared__ __attribute__((aligned(16))) float sw[];  // [K*K taps][CW + 2] fp32
 
     // Persistent workgroups: a workgroup keeps one (strip chunk, channel
@@ -137,70 +139,95 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
     T *__restrict__ Y = static_cast<T *>(a.y) + c0;
+    const float *swl = sw + cl0;
 
-    // Output rows first .. last-1, K steps (kernel rows) each, in one loop
-    // with a one-step prefetch that also crosses output rows.
-    const int steps = (last - first) * K;
+    // The block of output rows splits into per-image segments.  In a segment
+    // with output rows oh0 + j (j < nj), input row ih0 + i (ih0 = oh0*S - pb)
+    // feeds output j at kernel row kh = i - j*S.  Input rows are streamed once;
+    // output j lives in accumulator slot j mod M from its first input row to
+    // its last (kh = K-1), where it is stored and its slot reset to the bias.
+    // Unrolling the stream by U = M*S input rows makes every (slot, kh) pair a
+    // compile-time constant.  Slots of rows outside the segment (j < 0 or
+    // j >= nj) collect harmless partial sums that are never stored.
+    for (int row0 = first; row0 < last;) {
+        const int n = row0 / a.OH;
+        const int oh0 = row0 - n * a.OH;
+        const int nj = min(last - row0, a.OH - oh0);
+        row0 += nj;
+        const int ih0 = oh0 * S - a.pb_h;
+        const int ni = (nj - 1) * S + K;   // input rows of the segment
+        const int xbase = n * a.xs_n;
+        T *Yn = Y + (int64_t)n * a.ys_n;
 
-    auto fetch = [&](int step, uint32_t (&buf)[NCOL]) {
-        const int r = step / K;
-        const int kh = step - r * K;
-        const int row = first + r;
-        const int n = row / a.OH;
-        const int oh = row - n * a.OH;
-        const int ih = oh * S - a.pb_h + kh;
-        const bool ok = (unsigned)ih < (unsigned)a.H;
-        const int soff = ok ? (n * a.xs_n + ih * a.xs_h) * ES : 0;
-        const int vbad = ok ? 0 : INVALID;
+        float acc[M][TO][V];
 #pragma unroll
-        for (int col = 0; col < NCOL; ++col)
-            buf[col] = __builtin_amdgcn_raw_buffer_load_b32(xr, vcol[col] + vbad, soff, 0);
-    };
-
-    uint32_t cur[NCOL], nxt[NCOL];
-    float acc[TO][V];
-    fetch(0, cur);
-    for (int step = 0; step < steps; ++step) {
-        const int r = step / K;
-        const int kh = step - r * K;
-        if (step + 1 < steps) fetch(step + 1, nxt);
-        if (kh == 0) {
+        for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int t = 0; t < TO; ++t)
 #pragma unroll
-                for (int v = 0; v < V; ++v) acc[t][v] = bias[v];
-        }
-        float wk[K][V];
+                for (int v = 0; v < V; ++v) acc[m][t][v] = bias[v];
+
+        auto fetch = [&](int i, uint32_t (&buf)[NCOL]) {
+            const int ih = ih0 + i;
+            const bool ok = (unsigned)ih < (unsigned)a.H && i < ni;
+            const int soff = ok ? (xbase + ih * a.xs_h) * ES : 0;
+            const int vbad = ok ? 0 : INVALID;
 #pragma unroll
-        for (int kw = 0; kw < K; ++kw)
+            for (int col = 0; col < NCOL; ++col)
+                buf[col] = __builtin_amdgcn_raw_buffer_load_b32(xr, vcol[col] + vbad, soff, 0);
+        };
+
+        uint32_t cur[NCOL], nxt[NCOL];
+        fetch(0, cur);
+        for (int ib = 0; ib < ni; ib += U) {
 #pragma unroll
-            for (int v = 0; v < V; ++v) wk[kw][v] = sw[(kh * K + kw) * pitch + cl0 + v];
+            for (int u = 0; u < U; ++u) {
+                const int i = ib + u;
+                if (i < ni) {
+                    fetch(i + 1, nxt);
+                    float xv[NCOL][V];
 #pragma unroll
-        for (int col = 0; col < NCOL; ++col) {
-            float xv[V];
-            Word<T>::widen(cur[col], xv);
+                    for (int col = 0; col < NCOL; ++col) Word<T>::widen(cur[col], xv[col]);
+                    // Open outputs j = J*M + jp with kh = u - jp*S in [0, K).
 #pragma unroll
-            for (int t = 0; t < TO; ++t) {
-                const int kw = col - t * S;
-                if (kw >= 0 && kw < K) {
+                    for (int jp = -M; jp <= M; ++jp) {
+                        const int kh = u - jp * S;
+                        if (kh < 0 || kh >= K) continue;
+                        const int slot = ((jp % M) + M) % M;
+                        float wk[K][V];
 #pragma unroll
-                    for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xv[v], wk[kw][v], acc[t][v]);
+                        for (int kw = 0; kw < K; ++kw)
+#pragma unroll
+                            for (int v = 0; v < V; ++v) wk[kw][v] = swl[(kh * K + kw) * pitch + v];
+#pragma unroll
+                        for (int t = 0; t < TO; ++t)
+#pragma unroll
+                            for (int kw = 0; kw < K; ++kw)
+#pragma unroll
+                                for (int v = 0; v < V; ++v)
+                                    acc[slot][t][v] = __builtin_fmaf(xv[t * S + kw][v], wk[kw][v], acc[slot][t][v]);
+                        if (kh == K - 1) {
+                            // Output j = (ib / S) + jp (ib is a multiple of U = M*S) is complete.
+                            const int j = ib / S + jp;
+                            if (j >= 0 && j < nj) {
+                                T *yrow = Yn + (int64_t)(oh0 + j) * a.ys_h;
+#pragma unroll
+                                for (int t = 0; t < TO; ++t)
+                                    if (ow0 + t < a.OW)
+                                        *reinterpret_cast<uint32_t *>(yrow + (int64_t)(ow0 + t) * a.ys_w) =
+                                            Word<T>::narrow(acc[slot][t]);
+                            }
+#pragma unroll
+                            for (int t = 0; t < TO; ++t)
+#pragma unroll
+                                for (int v = 0; v < V; ++v) acc[slot][t][v] = bias[v];
+                        }
+                    }
+#pragma unroll
+                    for (int col = 0; col < NCOL; ++col) cur[col] = nxt[col];
                 }
             }
         }
-        if (kh == K - 1) {
-            const int row = first + r;
-            const int n = row / a.OH;
-            const int oh = row - n * a.OH;
-            T *yrow = Y + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h;
-#pragma unroll
-            for (int t = 0; t < TO; ++t) {
-                if (ow0 + t < a.OW)
-                    *reinterpret_cast<uint32_t *>(yrow + (int64_t)(ow0 + t) * a.ys_w) = Word<T>::narrow(acc[t]);
-            }
-        }
-#pragma unroll
-        for (int col = 0; col < NCOL; ++col) cur[col] = nxt[col];
     }
 }
 
@@ -233,9 +260,8 @@ hipError_t dispatch(const DwArgs &a, int k, int s, int to, hipStream_t st)
 {
 #define MICONV_DW(KK, SS, TT) \
     if (k == KK && s == SS && to == TT) return go<T, KK, SS, TT>(a, st);
-    MICONV_DW(3, 1, 14) MICONV_DW(3, 1, 8) MICONV_DW(5, 1, 14) MICONV_DW(5, 1, 8) MICONV_DW(7, 1, 14)
-    MICONV_DW(7, 1, 8) MICONV_DW(3, 2, 7) MICONV_DW(3, 2, 4) MICONV_DW(5, 2, 7) MICONV_DW(5, 2, 4)
-    MICONV_DW(7, 2, 7) MICONV_DW(7, 2, 4)
+    MICONV_DW(3, 1, 8) MICONV_DW(3, 1, 14) MICONV_DW(5, 1, 8) MICONV_DW(7, 1, 4) MICONV_DW(3, 2, 7)
+    MICONV_DW(5, 2, 7) MICONV_DW(7, 2, 4)
 #undef MICONV_DW
     return hipErrorInvalidValue;
 }
@@ -248,13 +274,27 @@ bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw)
     return kh == kw && sh == sw && (kh == 3 || kh == 5 || kh == 7) && (sh == 1 || sh == 2);
 }
 
-// Strip width (outputs per lane along W): the candidate that wastes the fewest
-// lanes on the last, partial strip of a row.
-int dwcl_strip(int64_t s, int64_t ow)
+// Strip width (outputs per lane along W).  The rolling window holds
+// ceil(K/S) * TO accumulators per channel, so wide kernels get narrow strips;
+// among a kernel's compiled widths, the one wasting the fewest lanes on the
+// last, partial strip of a row wins (ties: the first listed).
+int dwcl_strip(int64_t k, int64_t s, int64_t ow)
 {
-    const int a = s == 1 ? 14 : 7, b = s == 1 ? 8 : 4;
-    const int64_t wa = cdiv(ow, a) * a - ow, wb = cdiv(ow, b) * b - ow;
-    return wa <= wb ? a : b;
+    int cand[2] = {0, 0};
+    if (s == 1) {
+        if (k == 3) { cand[0] = 8; cand[1] = 14; }
+        else if (k == 5) cand[0] = 8;
+        else cand[0] = 4;
+    } else {
+        cand[0] = k == 7 ? 4 : 7;
+    }
+    int best = cand[0];
+    int64_t waste = cdiv(ow, best) * best - ow;
+    if (cand[1]) {
+        const int64_t w2 = cdiv(ow, cand[1]) * cand[1] - ow;
+        if (w2 < waste) best = cand[1];
+    }
+    return best;
 }
 
 int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream, bool vec)

@@ -96,12 +96,14 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgArgs a)
 
     const int tid = threadIdx.x;
     const int tile = xcd_tile(blockIdx.x, a.total_tiles);
+    // Tile order (fastest first): column tile, phase, row tile, group -- the
+    // tiles that gather the same input rows run side by side on one XCD.
     const int n_tile = tile % a.n_tiles;
     int rest = tile / a.n_tiles;
-    const int m_tile = rest % a.m_tiles;
-    rest /= a.m_tiles;
     const int phase = rest % a.phases;
-    const int g = rest / a.phases;
+    rest /= a.phases;
+    const int m_tile = rest % a.m_tiles;
+    const int g = rest / a.m_tiles;
 
     int rho0 = 0, rho1 = 0, rho2 = 0;
     if (a.transposed) {

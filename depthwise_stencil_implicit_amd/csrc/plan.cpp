@@ -29,7 +29,7 @@
 
 namespace miconv {
 bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw);
-int dwcl_strip(int64_t s, int64_t ow);
+int dwcl_strip(int64_t k, int64_t s, int64_t ow);
 bool grp_supported(const conv_desc &d);
 void grp_geometry(const conv_desc &d, conv_plan_t &p);
 void reduce_geometry(const conv_desc &d, conv_plan_t &p);
@@ -139,7 +139,7 @@ void geom_dwcl(const conv_desc &d, conv_plan_t &p)
     const int64_t words = d.C_in * esize(d.dtype) / 4;
     const int64_t cpb = words < 256 ? words : 256;
     const int64_t spb = 256 / cpb;
-    const int64_t to = dwcl_strip(d.stride[1], d.out[1]);
+    const int64_t to = dwcl_strip(d.k[1], d.stride[1], d.out[1]);
     const int64_t nstrips = cdiv(d.out[1], to);
     const int64_t strip_chunks = cdiv(nstrips, spb);
     const int64_t ch_chunks = cdiv(words, cpb);
