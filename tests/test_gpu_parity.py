@@ -63,7 +63,7 @@ def _geom_cases(kind, n, seed):
     tries = 0
     while len(out) < n and tries < 10000:
         tries += 1
-        dtype = ["f32", "f16", "bf16"][len(out) % 3]
+        dtype = ["f32", "f16", "bf16"][len(out) % 3] if kind != "grp" else ["f16", "bf16"][len(out) % 2]
         cl = bool(rng.integers(0, 2))
         bias = bool(rng.integers(0, 2))
         if kind in ("igemm", "igemm_t"):
@@ -120,7 +120,8 @@ def _geom_cases(kind, n, seed):
 
 
 SWEEP = {kind: _geom_cases(kind, n, seed) for kind, n, seed in
-         [("igemm", 24, 1), ("igemm_t", 24, 2), ("plane", 24, 3), ("dw_cl", 18, 4), ("reduce", 9, 5)]}
+         [("igemm", 24, 1), ("igemm_t", 24, 2), ("plane", 24, 3), ("dw_cl", 18, 4), ("reduce", 9, 5),
+          ("grp", 24, 6)]}
 
 
 def _desc(wl):
@@ -148,6 +149,13 @@ EXACT_CASES = [
                                 C_out=24, groups=3, L=[17, 19], k=[3, 4], stride=[2, 1],
                                 padding_before=[1, 2], padding_after=[0, 1], dilation=[1, 1],
                                 output_padding=[0, 0], has_bias=True)),
+    ("grp", synth.random_case(12, rank=2, transposed=False, dtype="bf16", channels_last=False, N=2, C_in=20,
+                              C_out=40, groups=4, L=[15, 17], k=[3, 3], stride=[1, 2],
+                              padding_before=[1, 1], padding_after=[1, 0], dilation=[1, 1],
+                              output_padding=[0, 0], has_bias=True)),
+    ("grp", synth.random_case(13, rank=1, transposed=False, dtype="f16", channels_last=True, N=3, C_in=14,
+                              C_out=21, groups=7, L=[33], k=[5], stride=[1], padding_before=[2],
+                              padding_after=[1], dilation=[2], output_padding=[0], has_bias=False)),
     ("igemm", synth.random_case(9, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=64,
                                 C_out=48, groups=1, L=[9, 10], k=[3, 3], stride=[1, 2],
                                 padding_before=[1, 0], padding_after=[2, 1], dilation=[1, 1],
