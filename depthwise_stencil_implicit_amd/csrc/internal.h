@@ -25,6 +25,8 @@ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 struct IgemmCfg {
     int bm, bn, bk;     // workgroup tile: rows, columns, K per step
     int wm, wn;         // waves along rows / columns (block = 64 * wm * wn)
+    int stages;         // LDS stages of the direct-to-LDS pipeline
+    int eff;            // measured relative MFMA throughput of the schedule, percent
 };
 const IgemmCfg &igemm_cfg(int variant);
 int igemm_num_cfgs();

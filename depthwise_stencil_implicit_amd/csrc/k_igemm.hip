@@ -46,6 +46,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace miconv {
 
@@ -368,6 +369,293 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgArgs a)
     }
 }
 
+// Vector path with direct-to-LDS loads.  Each buffer_load ... lds deposits one
+// wave's 64 sixteen-byte chunks contiguously at a wave-uniform LDS address, so
+// lane L of a wave covering rows r0..r0+7 fills slot (r0 + L/8, L%8) and
+// fetches the logical chunk that the XOR swizzle puts there, (L%8) ^ (L/8).
+// No registers hold tiles in flight, which leaves room for STAGES LDS stages:
+// the loads of step s + STAGES - 1 are issued while step s is multiplied.
+// An out-of-range offset deposits zeros, which is the padding.
+//
+// Each stage is its own LDS array and the step loop is unrolled by STAGES, so
+// every stage is a compile-time choice: the compiler then only waits, before
+// reading a stage, for the loads that target that stage.  The workgroup
+// barrier is a bare s_barrier (a compiler-only memory clobber keeps LDS
+// accesses on their side of it); before it each wave waits for its own loads of
+// the stage about to be read, so after it every wave's loads have landed.  A
+// fenced __syncthreads() would instead drain every load in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
+{
+    // The body uses LDS address-space pointers that only the device pass can
+    // instantiate; the host pass needs nothing but the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int NW = WM * WN;
+    constexpr int ES = Dt<T>::size;
+    constexpr int EV = 16 / ES;
+    constexpr int BK = 8 * EV;
+    constexpr int A_IT = BM / (NW * 8);   // DMA instructions per wave per step, A tile
+    constexpr int B_IT = BN / (NW * 8);
+    constexpr int LPS = A_IT + B_IT;      // loads per wave per step
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int STAGE_BYTES = (BM + BN) * 128;
+    static_assert(BM % (NW * 8) == 0 && BN % (NW * 8) == 0, "rows per DMA round");
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
+    static_assert(STAGES >= 2 && STAGES <= 4 && (STAGES - 2) * LPS < 64, "stages / vmcnt range");
+
+    __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st2[STAGES > 2 ? STAGE_BYTES : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char st3[STAGES > 3 ? STAGE_BYTES : 16];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int tile = xcd_tile(blockIdx.x, a.total_tiles);
+    // Tile order (fastest first): column tile, phase, row tile, group.
+    const int n_tile = tile % a.n_tiles;
+    int rest = tile / a.n_tiles;
+    const int phase = rest % a.phases;
+    rest /= a.phases;
+    const int m_tile = rest % a.m_tiles;
+    const int g = rest / a.m_tiles;
+
+    int rho0 = 0, rho1 = 0, rho2 = 0;
+    if (a.transposed) {
+        int p = phase;
+        rho2 = p % a.S[2];
+        p /= a.S[2];
+        rho1 = p % a.S[1];
+        rho0 = p / a.S[1];
+    }
+    const int JJ = a.J[0] * a.J[1] * a.J[2];
+    const int J12 = a.J[1] * a.J[2];
+
+    // Rows this lane fetches: r = i*NW*8 + wave*8 + lane/8; chunk kc.
+    const int kc = (lane & 7) ^ (lane >> 3);
+    int a_nb[A_IT], a_b0[A_IT], a_b1[A_IT], a_b2[A_IT];
+    bool a_ok[A_IT];
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) {
+        const int row = i * NW * 8 + wave * 8 + (lane >> 3);
+        const int m = m_tile * BM + row;
+        bool ok = m < a.rows;
+        const int mm = ok ? m : 0;
+        const int n = mm / JJ;
+        const int r = mm - n * JJ;
+        const int j0 = r / J12, r2 = r - j0 * J12;
+        const int j1 = r2 / a.J[2], j2 = r2 - j1 * a.J[2];
+        if (a.transposed) {
+            ok = ok && a.S[0] * j0 + rho0 < a.O[0] && a.S[1] * j1 + rho1 < a.O[1] && a.S[2] * j2 + rho2 < a.O[2];
+            a_b0[i] = j0;
+            a_b1[i] = j1;
+            a_b2[i] = j2;
+        } else {
+            a_b0[i] = j0 * a.S[0] - a.PB[0];
+            a_b1[i] = j1 * a.S[1] - a.PB[1];
+            a_b2[i] = j2 * a.S[2] - a.PB[2];
+        }
+        a_ok[i] = ok;
+        a_nb[i] = n * a.xs_n + g * a.Cig * a.xs_c;
+    }
+    const int wtile0 = (g * a.cog_pad + n_tile * BN) * a.taps * a.cig_pad * ES;
+    int b_off[B_IT];
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+        const int col = i * NW * 8 + wave * 8 + (lane >> 3);
+        b_off[i] = (col * a.taps * a.cig_pad + kc * EV) * ES;
+    }
+
+    auto tap_offsets = [&](int t, int &o0, int &o1, int &o2) -> bool {
+        const int t2 = t % a.K[2];
+        const int t01 = t / a.K[2];
+        const int t1 = t01 % a.K[1];
+        const int t0 = t01 / a.K[1];
+        if (!a.transposed) {
+            o0 = t0 * a.D[0];
+            o1 = t1 * a.D[1];
+            o2 = t2 * a.D[2];
+            return true;
+        }
+        const int n0 = rho0 + a.PB[0] - t0 * a.D[0];
+        const int n1 = rho1 + a.PB[1] - t1 * a.D[1];
+        const int n2 = rho2 + a.PB[2] - t2 * a.D[2];
+        o0 = n0 / a.S[0];
+        o1 = n1 / a.S[1];
+        o2 = n2 / a.S[2];
+        return n0 % a.S[0] == 0 && n1 % a.S[1] == 0 && n2 % a.S[2] == 0;
+    };
+
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.w), (short)0, a.w_bytes, 0x00020000);
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+
+    // Step cursor: (tap, channel block) over the phase's taps.
+    const int ncb = a.cig_pad / BK;
+    int it_t = 0, it_cb = 0, it_o0 = 0, it_o1 = 0, it_o2 = 0;
+    while (it_t < a.taps && !tap_offsets(it_t, it_o0, it_o1, it_o2)) ++it_t;
+    // Number of steps: valid taps x channel blocks (uniform).
+    int nsteps = 0;
+    if (ncb > 0) {
+        int dummy0, dummy1, dummy2;
+        for (int t = 0; t < a.taps; ++t) nsteps += tap_offsets(t, dummy0, dummy1, dummy2) ? ncb : 0;
+    }
+
+    auto issue = [&](unsigned char *A) {
+        unsigned char *B = A + BM * 128;
+        const int c = it_cb * BK + kc * EV;
+#pragma unroll
+        for (int i = 0; i < A_IT; ++i) {
+            const int i0 = a_b0[i] + it_o0, i1 = a_b1[i] + it_o1, i2 = a_b2[i] + it_o2;
+            const bool inb = a_ok[i] && (unsigned)i0 < (unsigned)a.L[0] && (unsigned)i1 < (unsigned)a.L[1] &&
+                             (unsigned)i2 < (unsigned)a.L[2] && c < a.Cig;
+            const int pix = a_nb[i] + i0 * a.xs_l[0] + i1 * a.xs_l[1] + i2 * a.xs_l[2];
+            const int off = inb ? (pix + c) * ES : 0x7fffff00;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(A + (i * NW * 8 + wave * 8) * 128), 16, off, 0,
+                                                     0, 0);
+        }
+        const int step_off = wtile0 + (it_t * a.cig_pad + it_cb * BK) * ES;
+#pragma unroll
+        for (int i = 0; i < B_IT; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(B + (i * NW * 8 + wave * 8) * 128), 16, b_off[i],
+                                                     step_off, 0, 0);
+        // advance the cursor
+        if (++it_cb == ncb) {
+            it_cb = 0;
+            ++it_t;
+            while (it_t < a.taps && !tap_offsets(it_t, it_o0, it_o1, it_o2)) ++it_t;
+        }
+    };
+
+    const int wr = wave / WN, wc = wave % WN;
+    const int lr = lane & 15, lg = lane >> 4;
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const unsigned char *A) {
+        const unsigned char *B = A + BM * 128;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            uint4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const uint4 *>(A + swz(wr * TM + i * 16 + lr, kk * 4 + lg));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const uint4 *>(B + swz(wc * TN + j * 16 + lr, kk * 4 + lg));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) mma_16x16x32(bf[j], af[i], acc[i][j], T{});
+        }
+    };
+    // One step: wait for this wave's loads of the stage, barrier, refill the
+    // stage read one step ago, multiply.  Stages are named arrays, so after
+    // inlining each access targets one known LDS object.
+    auto wait_own = [&](int s) {
+        if (s + STAGES - 2 < nsteps) {
+            constexpr int N = (STAGES - 2) * LPS;
+            __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+        } else {
+            __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+        }
+    };
+#define MICONV_DMA_STEP(CUR, NEXT, S)                 \
+    if ((S) < nsteps) {                               \
+        wait_own(S);                                  \
+        lds_barrier();                                \
+        if ((S) + STAGES - 1 < nsteps) issue(NEXT);   \
+        compute(CUR);                                 \
+    }
+
+    // Prologue: steps 0 .. STAGES-2 into stages 0 .. STAGES-2.
+    if (0 < nsteps) issue(st0);
+    if constexpr (STAGES > 2)
+        if (1 < nsteps) issue(st1);
+    if constexpr (STAGES > 3)
+        if (2 < nsteps) issue(st2);
+
+    for (int s = 0; s < nsteps; s += STAGES) {
+        if constexpr (STAGES == 2) {
+            MICONV_DMA_STEP(st0, st1, s)
+            MICONV_DMA_STEP(st1, st0, s + 1)
+        } else if constexpr (STAGES == 3) {
+            MICONV_DMA_STEP(st0, st2, s)
+            MICONV_DMA_STEP(st1, st0, s + 1)
+            MICONV_DMA_STEP(st2, st1, s + 2)
+        } else {
+            MICONV_DMA_STEP(st0, st3, s)
+            MICONV_DMA_STEP(st1, st0, s + 1)
+            MICONV_DMA_STEP(st2, st1, s + 2)
+            MICONV_DMA_STEP(st3, st2, s + 3)
+        }
+    }
+#undef MICONV_DMA_STEP
+
+    // ---- epilogue: lane holds 4 consecutive channels of one output position ----
+    T *__restrict__ Y = static_cast<T *>(a.y);
+    const T *__restrict__ Bias = static_cast<const T *>(a.b);
+    float bias[FN][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int co = n_tile * BN + wc * TN + j * 16 + lg * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            bias[j][e] = (a.has_bias && co + e < a.Cog) ? to_f32(Bias[g * a.Cog + co + e]) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m_tile * BM + wr * TM + i * 16 + lr;
+        if (m >= a.rows) continue;
+        const int n = m / JJ;
+        const int r = m - n * JJ;
+        int q0 = r / J12;
+        const int r2 = r - q0 * J12;
+        int q1 = r2 / a.J[2], q2 = r2 - q1 * a.J[2];
+        if (a.transposed) {
+            q0 = a.S[0] * q0 + rho0;
+            q1 = a.S[1] * q1 + rho1;
+            q2 = a.S[2] * q2 + rho2;
+            if (q0 >= a.O[0] || q1 >= a.O[1] || q2 >= a.O[2]) continue;
+        }
+        const int64_t yrow = (int64_t)n * a.ys_n + q0 * a.ys_l[0] + q1 * a.ys_l[1] + q2 * a.ys_l[2];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int co = n_tile * BN + wc * TN + j * 16 + lg * 4;
+            const int cg = g * a.Cog + co;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] + bias[j][e];
+            T *dst = Y + yrow + (int64_t)cg * a.ys_c;
+            if (a.y_vec4) {
+                if (co < a.Cog) {
+                    uint2 u;
+                    u.x = pack2<T>(v[0], v[1]);
+                    u.y = pack2<T>(v[2], v[3]);
+                    *reinterpret_cast<uint2 *>(dst) = u;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (co + e < a.Cog) dst[(int64_t)e * a.ys_c] = from_f32<T>(v[e]);
+            }
+        }
+    }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 // Weight repack: w (any strides) -> [G][Cog_pad][taps][Cig_pad], zero padded.
 template <typename T>
 __global__ void igemm_repack(const T *__restrict__ w, T *__restrict__ wr, int64_t total, int32_t Cig, int32_t Cog,
@@ -398,27 +686,39 @@ __global__ void igemm_repack(const T *__restrict__ w, T *__restrict__ wr, int64_
 
 namespace {
 
+// eff: per-tile throughput relative to config 0 (measured throughput times the
+// launch's rounds of workgroups over its exact rounds of work, dense 3x3 and
+// transposed 1-D bf16 workloads on MI355X); the planner's cost estimate.
 constexpr IgemmCfg kCfgs[] = {
-    {256, 256, 64, 2, 4},  // 0: 2-byte types, wide N, 8 waves (wave tile 128 x 64)
-    {160, 256, 64, 2, 2},  // 1: 2-byte types, wide N, finer M (wave tile 80 x 128)
-    {128, 128, 64, 2, 2},  // 2: 2-byte types, N <= 128
-    {256, 64, 64, 4, 1},   // 3: 2-byte types, N <= 64
-    {256, 32, 64, 4, 1},   // 4: 2-byte types, N <= 32
-    {128, 64, 32, 2, 2},   // 5: fp32
+    {256, 256, 64, 2, 4, 2, 100},  // 0: 8 waves, wave tile 128 x 64
+    {160, 256, 64, 2, 2, 3, 72},   // 1: 4 waves, wave tile 80 x 128
+    {128, 128, 64, 2, 2, 4, 53},   // 2: 4 waves, wave tile 64 x 64
+    {256, 64, 64, 4, 1, 3, 50},    // 3: 4 waves, N <= 64
+    {256, 32, 64, 4, 1, 3, 45},    // 4: 4 waves, N <= 32
+    {128, 64, 32, 2, 2, 2, 100},   // 5: fp32 (register-staged path only)
+    {128, 256, 64, 2, 2, 3, 70},   // 6: 4 waves, wave tile 64 x 128
+    {256, 128, 64, 2, 2, 3, 60},   // 7: 4 waves, wave tile 128 x 64
+    {128, 256, 64, 2, 4, 3, 70},   // 8: 8 waves, wave tile 64 x 64
 };
 
 template <typename T, int V, bool VEC>
 hipError_t launch_cfg(const IgArgs &a, hipStream_t s)
 {
     constexpr IgemmCfg c = kCfgs[V];
-    const size_t lds = (size_t)2 * (c.bm + c.bn) * 128;
-    auto kern = igemm_kernel<T, c.bm, c.bn, c.wm, c.wn, VEC>;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
+    if constexpr (VEC && Dt<T>::size == 2) {
+        // Static LDS only (stages are separate arrays).
+        hipLaunchKernelGGL((igemm_dma_kernel<T, c.bm, c.bn, c.wm, c.wn, c.stages>), dim3(a.total_tiles),
+                           dim3(64 * c.wm * c.wn), 0, s, a);
+    } else {
+        const size_t lds = (size_t)2 * (c.bm + c.bn) * 128;
+        auto kern = igemm_kernel<T, c.bm, c.bn, c.wm, c.wn, VEC>;
+        if (lds > 65536) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(kern, dim3(a.total_tiles), dim3(64 * c.wm * c.wn), lds, s, a);
     }
-    hipLaunchKernelGGL(kern, dim3(a.total_tiles), dim3(64 * c.wm * c.wn), lds, s, a);
     return hipGetLastError();
 }
 
@@ -434,6 +734,9 @@ hipError_t launch_typed(const IgArgs &a, int variant, bool vec, hipStream_t s)
         case 2: return vec ? launch_cfg<T, 2, true>(a, s) : launch_cfg<T, 2, false>(a, s);
         case 3: return vec ? launch_cfg<T, 3, true>(a, s) : launch_cfg<T, 3, false>(a, s);
         case 4: return vec ? launch_cfg<T, 4, true>(a, s) : launch_cfg<T, 4, false>(a, s);
+        case 6: return vec ? launch_cfg<T, 6, true>(a, s) : launch_cfg<T, 6, false>(a, s);
+        case 7: return vec ? launch_cfg<T, 7, true>(a, s) : launch_cfg<T, 7, false>(a, s);
+        case 8: return vec ? launch_cfg<T, 8, true>(a, s) : launch_cfg<T, 8, false>(a, s);
         default: return hipErrorInvalidValue;
         }
     }

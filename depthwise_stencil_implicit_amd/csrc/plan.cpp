@@ -23,6 +23,7 @@
 //       otherwise                                      -> PLANE
 //   everything else                                   -> IGEMM
 #include <cstring>
+#include <cstdlib>
 #include <initializer_list>
 
 #include "internal.h"
@@ -230,20 +231,26 @@ bool geom_igemm(const conv_desc &d, conv_plan_t &p)
     if (xspan / es >= kI32 || rows >= kI32) return false;
     int best = -1;
     double best_cost = 0;
-    const int lo = d.dtype == CONV_F32 ? 5 : 0, hi = d.dtype == CONV_F32 ? 5 : 4;
+    const int lo = d.dtype == CONV_F32 ? 5 : 0, hi = d.dtype == CONV_F32 ? 5 : igemm_num_cfgs() - 1;
     for (int v = lo; v <= hi; ++v) {
+        if ((v == 5) != (d.dtype == CONV_F32)) continue;
         const IgemmCfg &c = igemm_cfg(v);
-        const int64_t lds = 2 * (int64_t)(c.bm + c.bn) * 128;
+        const int64_t lds = (int64_t)c.stages * (c.bm + c.bn) * 128;
         const int64_t occ = lds > 80 * 1024 ? 1 : 2;
         const int64_t tiles = d.groups * phases * cdiv(rows, c.bm) * cdiv(cog(d) > 0 ? cog(d) : 1, c.bn);
         const double rounds = (double)cdiv(tiles, 256 * occ);
-        // Smaller tiles re-read more A and B per MAC; weigh them by tile perimeter.
-        const double eff = 1.0 + 0.25 * (256.0 / c.bm + 256.0 / c.bn - 2.0) / 2.0;
-        const double cost = rounds * occ * c.bm * c.bn * eff;
+        // CU time of one resident round, over the schedule's measured efficiency.
+        const double cost = rounds * occ * c.bm * c.bn / (double)c.eff;
         if (best < 0 || cost < best_cost) {
             best = v;
             best_cost = cost;
         }
+    }
+    // Tuning knob: MICONV_IGEMM_CFG=<index> forces a tile configuration of the
+    // same dtype class (used to sweep schedules; the default is the estimate).
+    if (const char *env = std::getenv("MICONV_IGEMM_CFG")) {
+        const int v = std::atoi(env);
+        if (v >= lo && v < igemm_num_cfgs() && (v == 5) == (d.dtype == CONV_F32)) best = v;
     }
     const IgemmCfg &c = igemm_cfg(best);
     const int64_t taps = d.k[0] * d.k[1] * d.k[2];
@@ -259,7 +266,7 @@ bool geom_igemm(const conv_desc &d, conv_plan_t &p)
     p.tile[IG_XBYTES] = xspan < kI32 - 4096 ? xspan : 0;
     p.grid[0] = d.groups * phases * p.tile[IG_MTILES] * p.tile[IG_NTILES];
     p.block = 64 * c.wm * c.wn;
-    p.lds_bytes = (int32_t)(2 * (c.bm + c.bn) * 128);
+    p.lds_bytes = (int32_t)(c.stages * (c.bm + c.bn) * 128);
     p.workspace_bytes = round_up(d.groups * cog_pad * taps * cig_pad * es, 256);
     if (p.workspace_bytes >= kI32) return false;   // 32-bit buffer offsets into the weights
     // 16-byte buffer-load path: contiguous, chunk-aligned channels, span < 2 GB.
