@@ -391,7 +391,17 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int STAGES>
+// Byte offset of 16-byte chunk c of LDS row r with KC chunks per row.  KC = 8:
+// c ^ (r & 7); KC = 4: c ^ ((r >> 1) & 3).  Either way the 8 lanes of one
+// ds_read_b128 cycle (8 consecutive rows, one logical chunk) land on 8
+// different 16-byte bank groups.
+template <int KC> __device__ __forceinline__ int swz_k(int r, int c)
+{
+    if constexpr (KC == 8) return (r * 8 + (c ^ (r & 7))) * 16;
+    else return (r * 4 + (c ^ ((r >> 1) & 3))) * 16;
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int STAGES, int KC>
 __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
 {
     // The body uses LDS address-space pointers that only the device pass can
@@ -400,14 +410,17 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     constexpr int NW = WM * WN;
     constexpr int ES = Dt<T>::size;
     constexpr int EV = 16 / ES;
-    constexpr int BK = 8 * EV;
-    constexpr int A_IT = BM / (NW * 8);   // DMA instructions per wave per step, A tile
-    constexpr int B_IT = BN / (NW * 8);
+    constexpr int BK = KC * EV;           // K elements per step
+    constexpr int RPI = 64 / KC;          // rows one wave DMA instruction fills
+    constexpr int RB = KC * 16;           // bytes per LDS row
+    constexpr int A_IT = BM / (NW * RPI); // DMA instructions per wave per step, A tile
+    constexpr int B_IT = BN / (NW * RPI);
     constexpr int LPS = A_IT + B_IT;      // loads per wave per step
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
-    constexpr int STAGE_BYTES = (BM + BN) * 128;
-    static_assert(BM % (NW * 8) == 0 && BN % (NW * 8) == 0, "rows per DMA round");
+    constexpr int STAGE_BYTES = (BM + BN) * RB;
+    static_assert(KC == 4 || KC == 8, "chunks per row");
+    static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "rows per DMA round");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
     static_assert(STAGES >= 2 && STAGES <= 4 && (STAGES - 2) * LPS < 64, "stages / vmcnt range");
 
@@ -438,13 +451,14 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     const int JJ = a.J[0] * a.J[1] * a.J[2];
     const int J12 = a.J[1] * a.J[2];
 
-    // Rows this lane fetches: r = i*NW*8 + wave*8 + lane/8; chunk kc.
-    const int kc = (lane & 7) ^ (lane >> 3);
+    // Rows this lane fetches: r = i*NW*RPI + wave*RPI + lane/KC, all with the
+    // same row bits the swizzle uses, so the logical chunk kc is fixed.
+    const int kc = KC == 8 ? ((lane & 7) ^ (lane >> 3)) : ((lane & 3) ^ ((lane >> 3) & 3));
     int a_nb[A_IT], a_b0[A_IT], a_b1[A_IT], a_b2[A_IT];
     bool a_ok[A_IT];
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
-        const int row = i * NW * 8 + wave * 8 + (lane >> 3);
+        const int row = i * NW * RPI + wave * RPI + lane / KC;
         const int m = m_tile * BM + row;
         bool ok = m < a.rows;
         const int mm = ok ? m : 0;
@@ -469,7 +483,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     int b_off[B_IT];
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
-        const int col = i * NW * 8 + wave * 8 + (lane >> 3);
+        const int col = i * NW * RPI + wave * RPI + lane / KC;
         b_off[i] = (col * a.taps * a.cig_pad + kc * EV) * ES;
     }
 
@@ -511,7 +525,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     }
 
     auto issue = [&](unsigned char *A) {
-        unsigned char *B = A + BM * 128;
+        unsigned char *B = A + BM * RB;
         const int c = it_cb * BK + kc * EV;
 #pragma unroll
         for (int i = 0; i < A_IT; ++i) {
@@ -520,14 +534,14 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
                              (unsigned)i2 < (unsigned)a.L[2] && c < a.Cig;
             const int pix = a_nb[i] + i0 * a.xs_l[0] + i1 * a.xs_l[1] + i2 * a.xs_l[2];
             const int off = inb ? (pix + c) * ES : 0x7fffff00;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(A + (i * NW * 8 + wave * 8) * 128), 16, off, 0,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(A + (i * NW * RPI + wave * RPI) * RB), 16, off,
+                                                     0, 0, 0);
         }
         const int step_off = wtile0 + (it_t * a.cig_pad + it_cb * BK) * ES;
 #pragma unroll
         for (int i = 0; i < B_IT; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(B + (i * NW * 8 + wave * 8) * 128), 16, b_off[i],
-                                                     step_off, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(B + (i * NW * RPI + wave * RPI) * RB), 16,
+                                                     b_off[i], step_off, 0, 0);
         // advance the cursor
         if (++it_cb == ncb) {
             it_cb = 0;
@@ -545,16 +559,16 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const unsigned char *A) {
-        const unsigned char *B = A + BM * 128;
+        const unsigned char *B = A + BM * RB;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < KC / 4; ++kk) {
             uint4 af[FM], bf[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const uint4 *>(A + swz(wr * TM + i * 16 + lr, kk * 4 + lg));
+                af[i] = *reinterpret_cast<const uint4 *>(A + swz_k<KC>(wr * TM + i * 16 + lr, kk * 4 + lg));
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bf[j] = *reinterpret_cast<const uint4 *>(B + swz(wc * TN + j * 16 + lr, kk * 4 + lg));
+                bf[j] = *reinterpret_cast<const uint4 *>(B + swz_k<KC>(wc * TN + j * 16 + lr, kk * 4 + lg));
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -699,6 +713,8 @@ constexpr IgemmCfg kCfgs[] = {
     {128, 256, 64, 2, 2, 3, 70},   // 6: 4 waves, wave tile 64 x 128
     {256, 128, 64, 2, 2, 3, 60},   // 7: 4 waves, wave tile 128 x 64
     {128, 256, 64, 2, 4, 3, 70},   // 8: 8 waves, wave tile 64 x 64
+    {256, 256, 32, 2, 4, 4, 93},   // 9: 8 waves, K step 32, 4 stages (deeper prefetch)
+    {256, 256, 32, 2, 4, 3, 88},   // 10: 8 waves, K step 32, 3 stages
 };
 
 template <typename T, int V, bool VEC>
@@ -707,7 +723,7 @@ hipError_t launch_cfg(const IgArgs &a, hipStream_t s)
     constexpr IgemmCfg c = kCfgs[V];
     if constexpr (VEC && Dt<T>::size == 2) {
         // Static LDS only (stages are separate arrays).
-        hipLaunchKernelGGL((igemm_dma_kernel<T, c.bm, c.bn, c.wm, c.wn, c.stages>), dim3(a.total_tiles),
+        hipLaunchKernelGGL((igemm_dma_kernel<T, c.bm, c.bn, c.wm, c.wn, c.stages, c.bk / 8>), dim3(a.total_tiles),
                            dim3(64 * c.wm * c.wn), 0, s, a);
     } else {
         const size_t lds = (size_t)2 * (c.bm + c.bn) * 128;
@@ -737,6 +753,8 @@ hipError_t launch_typed(const IgArgs &a, int variant, bool vec, hipStream_t s)
         case 6: return vec ? launch_cfg<T, 6, true>(a, s) : launch_cfg<T, 6, false>(a, s);
         case 7: return vec ? launch_cfg<T, 7, true>(a, s) : launch_cfg<T, 7, false>(a, s);
         case 8: return vec ? launch_cfg<T, 8, true>(a, s) : launch_cfg<T, 8, false>(a, s);
+        case 9: return vec ? launch_cfg<T, 9, true>(a, s) : launch_cfg<T, 9, false>(a, s);
+        case 10: return vec ? launch_cfg<T, 10, true>(a, s) : launch_cfg<T, 10, false>(a, s);
         default: return hipErrorInvalidValue;
         }
     }

@@ -254,7 +254,9 @@ bool geom_igemm(const conv_desc &d, conv_plan_t &p)
     }
     const IgemmCfg &c = igemm_cfg(best);
     const int64_t taps = d.k[0] * d.k[1] * d.k[2];
-    const int64_t cig_pad = round_up(cig(d), c.bk);
+    // Channel padding: a multiple of every K step either kernel path may use
+    // (the register-staged fallback steps 64 channels of 16-bit types, 32 of fp32).
+    const int64_t cig_pad = round_up(cig(d), d.dtype == CONV_F32 ? 32 : 64);
     const int64_t cog_pad = round_up(cog(d) > 0 ? cog(d) : 1, c.bn);
     p.variant = best;
     p.tile[IG_CIG_PAD] = cig_pad;
