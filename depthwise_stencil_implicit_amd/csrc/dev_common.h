@@ -47,6 +47,18 @@ __device__ __forceinline__ float hi_f32(uint32_t w, bf16_t) { return __uint_as_f
 __device__ __forceinline__ float lo_f32(uint32_t w, f16_t) { return to_f32(f16_t{(uint16_t)(w & 0xffffu)}); }
 __device__ __forceinline__ float hi_f32(uint32_t w, f16_t) { return to_f32(f16_t{(uint16_t)(w >> 16)}); }
 
+// Two products of a packed 16-bit pair added to an fp32 accumulator:
+// c + a.lo*b.lo + a.hi*b.hi (v_dot2_f32_f16 / v_dot2_f32_bf16).
+template <typename T> __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c);
+template <> __device__ __forceinline__ float dot2<f16_t>(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+template <> __device__ __forceinline__ float dot2<bf16_t>(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 // Narrow fp32 to the storage type, rounding to nearest even.
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }

@@ -71,6 +71,14 @@ template <> struct Word<float> {
     __device__ static uint32_t narrow(const float (&f)[1]) { return __float_as_uint(f[0]); }
 };
 
+// Weight words per kernel row: 16-bit types keep K/2 packed column pairs
+// (kw = 2p, 2p+1) and the last, odd column as fp32; fp32 keeps K fp32 taps.
+template <typename T, int K> struct DwTaps {
+    static constexpr bool DOT = Word<T>::V == 2;
+    static constexpr int KP = DOT ? K / 2 : 0;
+    static constexpr int WPR = DOT ? KP + 1 : K;
+};
+
 template <typename T, int K, int S, int TO>
 __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
 {
@@ -80,7 +88,11 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     constexpr int INVALID = 0x7fffff00;
     constexpr int M = (K + S - 1) / S;   // output rows open at once (accumulator slots)
     constexpr int U = M * S;             // input rows per unrolled block: slot pattern repeats
-    extern __shared__ __attribute__((aligned(16))) float sw[];  // [K*K taps][CW + 2] fp32
+    constexpr bool DOT = DwTaps<T, K>::DOT;
+    constexpr int KP = DwTaps<T, K>::KP;
+    constexpr int WPR = DwTaps<T, K>::WPR;
+    static_assert(!DOT || (K & 1), "pairs leave one odd column");
+    extern __shared__ __attribute__((aligned(16))) uint32_t sw[];  // [K*WPR][CW + 2] words
 
     // Persistent workgroups: a workgroup keeps one (strip chunk, channel
     // chunk) for its whole life and walks one contiguous block of output rows
@@ -98,19 +110,28 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     const int first = (int)((int64_t)q * rows_total / nwg);
     const int last = (int)((int64_t)(q + 1) * rows_total / nwg);
 
-    // Stage this workgroup's weights once: consecutive threads read
-    // consecutive taps of one channel (contiguous for a dense weight).
+    // Stage this workgroup's weights once, entry (kh, j) of channel cl at
+    // sw[(kh*WPR + j)*pitch + cl]: a packed pair of the stored 16-bit values
+    // (j < KP) or one fp32 tap.
     const int CW = a.cpb * V;
     const int pitch = CW + 2;
     const int c_base = chc * CW;
     {
         const T *Wt = static_cast<const T *>(a.w);
-        for (int i = tid; i < K * K * CW; i += 256) {
-            const int cl = i / (K * K);
-            const int tap = i - cl * (K * K);
+        for (int i = tid; i < K * WPR * CW; i += 256) {
+            const int cl = i / (K * WPR);
+            const int e = i - cl * (K * WPR);
+            const int kh = e / WPR, j = e - kh * WPR;
             const int c = min(c_base + cl, a.C - 1);
-            const int kh = tap / K, kw = tap - kh * K;
-            sw[tap * pitch + cl] = to_f32(Wt[(int64_t)c * a.ws0 + kh * a.ws2 + kw * a.ws3]);
+            const T *wr = Wt + (int64_t)c * a.ws0 + kh * a.ws2;
+            uint32_t v;
+            if constexpr (DOT) {
+                if (j < KP) v = (uint32_t)wr[(2 * j) * a.ws3].u | ((uint32_t)wr[(2 * j + 1) * a.ws3].u << 16);
+                else v = __float_as_uint(to_f32(wr[(K - 1) * a.ws3]));
+            } else {
+                v = __float_as_uint(to_f32(wr[j * a.ws3]));
+            }
+            sw[e * pitch + cl] = v;
         }
     }
     __syncthreads();
@@ -139,7 +160,7 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
     T *__restrict__ Y = static_cast<T *>(a.y) + c0;
-    const float *swl = sw + cl0;
+    const uint32_t *swl = sw + cl0;
 
     // The block of output rows splits into per-image segments.  In a segment
     // with output rows oh0 + j (j < nj), input row ih0 + i (ih0 = oh0*S - pb)
@@ -185,38 +206,73 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
                 const int i = ib + u;
                 if (i < ni) {
                     fetch(i + 1, nxt);
+                    // Row operands.  16-bit: the pair of columns (q, q+1) of each
+                    // channel packed into one word, and the odd last column widened;
+                    // fp32: every column as is.  Unused entries fold away.
+                    uint32_t plo[NCOL], phi[NCOL];
                     float xv[NCOL][V];
 #pragma unroll
-                    for (int col = 0; col < NCOL; ++col) Word<T>::widen(cur[col], xv[col]);
+                    for (int col = 0; col < NCOL; ++col) {
+                        if constexpr (DOT) {
+                            if (col + 1 < NCOL) {
+                                plo[col] = (cur[col] & 0xffffu) | (cur[col + 1] << 16);
+                                phi[col] = (cur[col] >> 16) | (cur[col + 1] & 0xffff0000u);
+                            }
+                        }
+                        Word<T>::widen(cur[col], xv[col]);
+                    }
                     // Open outputs j = J*M + jp with kh = u - jp*S in [0, K).
 #pragma unroll
                     for (int jp = -M; jp <= M; ++jp) {
                         const int kh = u - jp * S;
                         if (kh < 0 || kh >= K) continue;
+                        // Output j = ib/S + jp (ib is a multiple of U = M*S).  Rows
+                        // outside the segment are skipped (a uniform branch), so the
+                        // halo rows of a short segment cost loads but no arithmetic;
+                        // a skipped slot still holds the bias when its next output
+                        // (j + M, whose first input row follows j's last) opens it.
+                        const int j = ib / S + jp;
+                        if (j < 0 || j >= nj) continue;
                         const int slot = ((jp % M) + M) % M;
-                        float wk[K][V];
+                        if constexpr (DOT) {
+                            uint2 wp[KP];
 #pragma unroll
-                        for (int kw = 0; kw < K; ++kw)
+                            for (int pp = 0; pp < KP; ++pp)
+                                wp[pp] = *reinterpret_cast<const uint2 *>(swl + (kh * WPR + pp) * pitch);
+                            const uint2 ws = *reinterpret_cast<const uint2 *>(swl + (kh * WPR + KP) * pitch);
 #pragma unroll
-                            for (int v = 0; v < V; ++v) wk[kw][v] = swl[(kh * K + kw) * pitch + v];
+                            for (int t = 0; t < TO; ++t) {
 #pragma unroll
-                        for (int t = 0; t < TO; ++t)
+                                for (int pp = 0; pp < KP; ++pp) {
+                                    acc[slot][t][0] = dot2<T>(plo[t * S + 2 * pp], wp[pp].x, acc[slot][t][0]);
+                                    acc[slot][t][1] = dot2<T>(phi[t * S + 2 * pp], wp[pp].y, acc[slot][t][1]);
+                                }
+                                acc[slot][t][0] = __builtin_fmaf(xv[t * S + K - 1][0], __uint_as_float(ws.x), acc[slot][t][0]);
+                                acc[slot][t][V - 1] =
+                                    __builtin_fmaf(xv[t * S + K - 1][V - 1], __uint_as_float(ws.y), acc[slot][t][V - 1]);
+                            }
+                        } else {
+                            float wk[K][V];
 #pragma unroll
                             for (int kw = 0; kw < K; ++kw)
 #pragma unroll
-                                for (int v = 0; v < V; ++v)
-                                    acc[slot][t][v] = __builtin_fmaf(xv[t * S + kw][v], wk[kw][v], acc[slot][t][v]);
-                        if (kh == K - 1) {
-                            // Output j = (ib / S) + jp (ib is a multiple of U = M*S) is complete.
-                            const int j = ib / S + jp;
-                            if (j >= 0 && j < nj) {
-                                T *yrow = Yn + (int64_t)(oh0 + j) * a.ys_h;
+                                for (int v = 0; v < V; ++v) wk[kw][v] = __uint_as_float(swl[(kh * K + kw) * pitch + v]);
 #pragma unroll
-                                for (int t = 0; t < TO; ++t)
-                                    if (ow0 + t < a.OW)
-                                        *reinterpret_cast<uint32_t *>(yrow + (int64_t)(ow0 + t) * a.ys_w) =
-                                            Word<T>::narrow(acc[slot][t]);
-                            }
+                            for (int t = 0; t < TO; ++t)
+#pragma unroll
+                                for (int kw = 0; kw < K; ++kw)
+#pragma unroll
+                                    for (int v = 0; v < V; ++v)
+                                        acc[slot][t][v] = __builtin_fmaf(xv[t * S + kw][v], wk[kw][v], acc[slot][t][v]);
+                        }
+                        if (kh == K - 1) {
+                            // Output j is complete.
+                            T *yrow = Yn + (int64_t)(oh0 + j) * a.ys_h;
+#pragma unroll
+                            for (int t = 0; t < TO; ++t)
+                                if (ow0 + t < a.OW)
+                                    *reinterpret_cast<uint32_t *>(yrow + (int64_t)(ow0 + t) * a.ys_w) =
+                                        Word<T>::narrow(acc[slot][t]);
 #pragma unroll
                             for (int t = 0; t < TO; ++t)
 #pragma unroll
@@ -237,7 +293,7 @@ template <typename T, int K, int S, int TO>
 hipError_t go(DwArgs a, hipStream_t s)
 {
     auto kern = dwcl_kernel<T, K, S, TO>;
-    const size_t lds = (size_t)K * K * (a.cpb * Word<T>::V + 2) * sizeof(float);
+    const size_t lds = (size_t)K * DwTaps<T, K>::WPR * (a.cpb * Word<T>::V + 2) * sizeof(uint32_t);
     // One resident round of persistent workgroups, a multiple of the number
     // of (strip, channel) chunks, and no more than there are rows to share.
     int dev = 0, cus = 0, per_cu = 0;

@@ -35,16 +35,6 @@ struct GpArgs {
     int32_t TH, TW, IH, IW, tpr, tiles_h, tiles_w, total, has_bias, npairs, cog_pad;
 };
 
-template <typename T> __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c);
-template <> __device__ __forceinline__ float dot2<f16_t>(uint32_t a, uint32_t b, float c)
-{
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
-}
-template <> __device__ __forceinline__ float dot2<bf16_t>(uint32_t a, uint32_t b, float c)
-{
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
 template <typename T, int P, int JB>
 __global__ __launch_bounds__(256) void grp_kernel(GpArgs a)
 {
