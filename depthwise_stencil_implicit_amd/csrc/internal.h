@@ -34,6 +34,23 @@ int igemm_num_cfgs();
 // Plan-field indices for the implicit GEMM (plan.tile[]).
 enum { IG_CIG_PAD = 0, IG_COG_PAD = 1, IG_PHASES = 2, IG_MTILES = 3, IG_NTILES = 4, IG_ROWS = 5, IG_XBYTES = 6 };
 
+// Depthwise channels-last stencil (kernel CONV_K_DW_CL): a lane's strip of TO
+// outputs reads NCOL input columns per row.  Each wave streams input rows
+// through a ring of D rows in LDS (direct-to-LDS loads); before it reads a
+// ring row it waits until at most the VMEM instructions issued after that
+// row's loads are pending: D-1 rows of loads plus the stores of D-1 steps (TO
+// per step that completes an output row, every S-th step).  D is the deepest
+// ring whose worst case fits the 6-bit vmcnt field.
+constexpr int dwcl_ncol(int K, int S, int TO) { return (TO - 1) * S + K; }
+constexpr int dwcl_pending(int K, int S, int TO, int D)
+{
+    return (D - 1) * dwcl_ncol(K, S, TO) + ((D - 1 + S - 1) / S) * TO;
+}
+constexpr int dwcl_ring_depth(int K, int S, int TO)
+{
+    return dwcl_pending(K, S, TO, 4) <= 63 ? 4 : dwcl_pending(K, S, TO, 3) <= 63 ? 3 : 2;
+}
+
 // Launchers (defined in the .hip files).  `vec` selects the 16-byte path.
 int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *ws,
                  void *stream, bool vec);

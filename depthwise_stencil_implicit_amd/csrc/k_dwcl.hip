@@ -8,41 +8,47 @@
 //
 // Layout on gfx950: x is [N][H][W][C] in memory (C fastest).  A lane owns one
 // 32-bit word of channels (two 16-bit channels, or one fp32 channel) and a
-// strip of TO consecutive output columns; it walks RPT output rows.  For each
-// output row and kernel row it loads the (TO-1)*S + K input words of its strip
-// left to right; each load is widened to fp32 once and feeds every output of
-// the strip whose window covers that column -- the loaded row segment is the
-// register sliding window.  Consecutive lanes hold consecutive channel words of
-// the same pixel, so every wave load and store is one contiguous run.
-// Workgroups are persistent -- one resident round over all CUs -- and each
-// keeps one (strip chunk, channel chunk), so its weights are staged in LDS
-// (fp32 [tap][channel]) once; each kernel row reads back only its K weights
-// per channel.
+// strip of TO consecutive output columns.  Consecutive lanes hold consecutive
+// channel words of the same pixel, so every wave load and store is one
+// contiguous run.  Workgroups are persistent -- one resident round over all
+// CUs -- and each keeps one (strip chunk, channel chunk), so its weights are
+// staged in LDS once; each workgroup walks a contiguous block of output rows.
 //
-// Loads are raw buffer loads: a lane's column offsets are computed once, the
-// row offset (uniform across the wave) rides in the scalar offset, and absent
-// rows or columns get an out-of-range offset so the hardware returns zeros --
-// no branch for the padding.  The (output row, kernel row) steps form one
-// rolled loop with a one-step prefetch, which keeps the register footprint
-// near 120 VGPRs (four waves per SIMD) while a row segment is in flight.
-// Accumulation is fp32 FMA, the bias is the initial value, and each result is
-// rounded once to the output dtype.
+// Rows are streamed once: input row i of a segment feeds the ceil(K/S) output
+// rows whose windows cover it, each held in a rolling accumulator slot until
+// its last kernel row, where it is stored (rounded once) and the slot reset
+// to the bias.  fp16/bf16 take a kernel row as K/2 packed column pairs
+// (v_dot2_f32_{f16,bf16}: two products per instruction, fp32 accumulation)
+// plus the odd last column as an fp32 FMA; fp32 uses one FMA per tap.
+//
+// Each wave streams its rows through its own ring of D rows in LDS, filled by
+// direct-to-LDS buffer loads (buffer_load_dword ... lds) D-1 rows ahead, so
+// D-1 rows of loads are in flight without holding registers.  Loads are raw
+// buffer loads: column offsets are computed once, the row offset rides in the
+// scalar offset, and absent rows or columns get an out-of-range offset that
+// the hardware answers with zeros -- no branch for the padding.  Stores are
+// raw buffer stores issued by every step that completes an output row (to an
+// out-of-range offset, which the hardware drops, when the row or column is
+// absent), so the number of VMEM instructions issued after each ring row is a
+// compile-time constant and the wait before reading it is exact.
 #include "dev_common.h"
 #include "internal.h"
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 namespace miconv {
 
 struct DwArgs {
     const void *x, *w, *b;
     void *y;
-    int64_t ys_n, ys_h, ys_w;         // element strides of y (channel stride 1)
+    int32_t ys_n, ys_h, ys_w;         // element strides of y (channel stride 1), 32-bit
     int32_t xs_n, xs_h, xs_w;         // element strides of x (channel stride 1), 32-bit
-    int32_t x_bytes;                  // bytes addressable from x (buffer range)
+    int32_t x_bytes, y_bytes;         // bytes addressable from x and y (buffer ranges)
     int64_t ws0, ws2, ws3;            // weight strides (output channel, kh, kw)
     int32_t N, H, W, C, OH, OW, pb_h, pb_w;
-    int32_t cpb, spb, rpt;            // lane words / strips per workgroup, rows per thread
+    int32_t cpb, spb;                 // lane words / strips per workgroup
     int32_t ch_chunks, strip_chunks, row_chunks, nstrips, total;
     int32_t has_bias;
 };
@@ -71,6 +77,39 @@ template <> struct Word<float> {
     __device__ static uint32_t narrow(const float (&f)[1]) { return __float_as_uint(f[0]); }
 };
 
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1 in order (a loop whose
+// index is a compile-time constant in the body).
+template <int... I, class F> __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F &&f)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(std::make_integer_sequence<int, N>{}, static_cast<F &&>(f));
+}
+
+// Stores issued by stream step v (TO when its row completes an output row).
+template <int K, int S, int TO> __device__ constexpr int dw_stores_at(int v)
+{
+    return (((v - (K - 1)) % S) + S) % S == 0 ? TO : 0;
+}
+// VMEM instructions that may still be pending when step u (position in the
+// unrolled block) reads its ring row: the loads of the D-1 rows after it and
+// the stores of the D-1 steps before it -- of this segment only when the
+// block is the segment's first (earlier rows came from the prologue).
+template <int K, int S, int TO, int D> __device__ constexpr int dw_pending_at(int u, bool first)
+{
+    int n = (D - 1) * dwcl_ncol(K, S, TO);
+    for (int d = 1; d < D; ++d)
+        if (!first || u - d >= 0) n += dw_stores_at<K, S, TO>(u - d);
+    return n;
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Weight words per kernel row: 16-bit types keep K/2 packed column pairs
 // (kw = 2p, 2p+1) and the last, odd column as fp32; fp32 keeps K fp32 taps.
 template <typename T, int K> struct DwTaps {
@@ -82,17 +121,24 @@ template <typename T, int K> struct DwTaps {
 template <typename T, int K, int S, int TO>
 __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
 {
+    // The body takes LDS address-space pointers, which only the device pass
+    // instantiates; the host pass needs nothing but the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
     constexpr int V = Word<T>::V;
     constexpr int ES = Dt<T>::size;
-    constexpr int NCOL = (TO - 1) * S + K;
+    constexpr int NCOL = dwcl_ncol(K, S, TO);
     constexpr int INVALID = 0x7fffff00;
     constexpr int M = (K + S - 1) / S;   // output rows open at once (accumulator slots)
     constexpr int U = M * S;             // input rows per unrolled block: slot pattern repeats
+    constexpr int D = dwcl_ring_depth(K, S, TO);
+    constexpr int RING = D * NCOL * 64;  // ring words per wave
     constexpr bool DOT = DwTaps<T, K>::DOT;
     constexpr int KP = DwTaps<T, K>::KP;
     constexpr int WPR = DwTaps<T, K>::WPR;
     static_assert(!DOT || (K & 1), "pairs leave one odd column");
-    extern __shared__ __attribute__((aligned(16))) uint32_t sw[];  // [K*WPR][CW + 2] words
+    static_assert(dwcl_pending(K, S, TO, D) <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) uint32_t ring[4 * RING];
+    typedef __attribute__((address_space(3))) void *lds_ptr;
 
     // Persistent workgroups: a workgroup keeps one (strip chunk, channel
     // chunk) for its whole life and walks one contiguous block of output rows
@@ -110,37 +156,17 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     const int first = (int)((int64_t)q * rows_total / nwg);
     const int last = (int)((int64_t)(q + 1) * rows_total / nwg);
 
-    // Stage this workgroup's weights once, entry (kh, j) of channel cl at
-    // sw[(kh*WPR + j)*pitch + cl]: a packed pair of the stored 16-bit values
-    // (j < KP) or one fp32 tap.
-    const int CW = a.cpb * V;
-    const int pitch = CW + 2;
-    const int c_base = chc * CW;
-    {
-        const T *Wt = static_cast<const T *>(a.w);
-        for (int i = tid; i < K * WPR * CW; i += 256) {
-            const int cl = i / (K * WPR);
-            const int e = i - cl * (K * WPR);
-            const int kh = e / WPR, j = e - kh * WPR;
-            const int c = min(c_base + cl, a.C - 1);
-            const T *wr = Wt + (int64_t)c * a.ws0 + kh * a.ws2;
-            uint32_t v;
-            if constexpr (DOT) {
-                if (j < KP) v = (uint32_t)wr[(2 * j) * a.ws3].u | ((uint32_t)wr[(2 * j + 1) * a.ws3].u << 16);
-                else v = __float_as_uint(to_f32(wr[(K - 1) * a.ws3]));
-            } else {
-                v = __float_as_uint(to_f32(wr[j * a.ws3]));
-            }
-            sw[e * pitch + cl] = v;
-        }
-    }
-    __syncthreads();
+    const int c_base = chc * a.cpb * V;
 
+    // Every wave runs on its own: no barriers.
     const int cl0 = (tid % a.cpb) * V;
     const int c0 = c_base + cl0;
     const int strip = stc * a.spb + tid / a.cpb;
     if (c0 >= a.C || strip >= a.nstrips || tid >= a.cpb * a.spb || first >= last) return;
     const int ow0 = strip * TO;
+    const int wave = tid >> 6, lane = tid & 63;
+    uint32_t *ringw = ring + wave * RING;        // this wave's ring: [D][NCOL][64 lanes]
+    const uint32_t *ringl = ringw + lane;
 
     float bias[V];
     {
@@ -149,27 +175,55 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
         for (int v = 0; v < V; ++v) bias[v] = a.has_bias ? to_f32(Bp[c0 + v]) : 0.f;
     }
 
-    // Column byte offsets of this lane's strip; absent columns are out of range.
-    int vcol[NCOL];
+    // This lane's weights, held in registers for the whole walk.  16-bit: per
+    // kernel row KP packed column pairs of the stored values per channel
+    // (wpl / wph for the low / high channel of the word) and the odd last
+    // column as fp32 (wsl / wsh); fp32: every tap (wf).
+    uint32_t wpl[K][KP > 0 ? KP : 1], wph[K][KP > 0 ? KP : 1];
+    float wsl[K], wsh[K], wf[K][DOT ? 1 : K];
+    {
+        const T *Wt = static_cast<const T *>(a.w);
+        const T *w0 = Wt + (int64_t)c0 * a.ws0;
+        const T *w1 = Wt + (int64_t)(V == 2 ? c0 + 1 : c0) * a.ws0;
+#pragma unroll
+        for (int kh = 0; kh < K; ++kh) {
+            if constexpr (DOT) {
+#pragma unroll
+                for (int pp = 0; pp < KP; ++pp) {
+                    const int64_t o0 = kh * a.ws2 + (2 * pp) * a.ws3, o1 = o0 + a.ws3;
+                    wpl[kh][pp] = (uint32_t)w0[o0].u | ((uint32_t)w0[o1].u << 16);
+                    wph[kh][pp] = (uint32_t)w1[o0].u | ((uint32_t)w1[o1].u << 16);
+                }
+                wsl[kh] = to_f32(w0[kh * a.ws2 + (K - 1) * a.ws3]);
+                wsh[kh] = to_f32(w1[kh * a.ws2 + (K - 1) * a.ws3]);
+            } else {
+#pragma unroll
+                for (int kw = 0; kw < K; ++kw) wf[kh][kw] = to_f32(w0[kh * a.ws2 + kw * a.ws3]);
+            }
+        }
+    }
+
+    // Column byte offsets of this lane's strip (input and output); absent
+    // columns are out of range.
+    int vcol[NCOL], ycol[TO];
     const int iw0 = ow0 * S - a.pb_w;
 #pragma unroll
     for (int col = 0; col < NCOL; ++col) {
         const int iw = iw0 + col;
         vcol[col] = (unsigned)iw < (unsigned)a.W ? (iw * a.xs_w + c0) * ES : INVALID;
     }
+#pragma unroll
+    for (int t = 0; t < TO; ++t) ycol[t] = ow0 + t < a.OW ? ((ow0 + t) * a.ys_w + c0) * ES : INVALID;
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
-    T *__restrict__ Y = static_cast<T *>(a.y) + c0;
-    const uint32_t *swl = sw + cl0;
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, a.y_bytes, 0x00020000);
 
     // The block of output rows splits into per-image segments.  In a segment
     // with output rows oh0 + j (j < nj), input row ih0 + i (ih0 = oh0*S - pb)
-    // feeds output j at kernel row kh = i - j*S.  Input rows are streamed once;
-    // output j lives in accumulator slot j mod M from its first input row to
-    // its last (kh = K-1), where it is stored and its slot reset to the bias.
-    // Unrolling the stream by U = M*S input rows makes every (slot, kh) pair a
-    // compile-time constant.  Slots of rows outside the segment (j < 0 or
-    // j >= nj) collect harmless partial sums that are never stored.
+    // feeds output j at kernel row kh = i - j*S.  Output j lives in
+    // accumulator slot j mod M from its first input row to its last; unrolling
+    // the stream by U = M*S rows makes every (slot, kh) pair a compile-time
+    // constant.
     for (int row0 = first; row0 < last;) {
         const int n = row0 / a.OH;
         const int oh0 = row0 - n * a.OH;
@@ -178,7 +232,7 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
         const int ih0 = oh0 * S - a.pb_h;
         const int ni = (nj - 1) * S + K;   // input rows of the segment
         const int xbase = n * a.xs_n;
-        T *Yn = Y + (int64_t)n * a.ys_n;
+        const int ybase = n * a.ys_n;
 
         float acc[M][TO][V];
 #pragma unroll
@@ -188,24 +242,37 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
 #pragma unroll
                 for (int v = 0; v < V; ++v) acc[m][t][v] = bias[v];
 
-        auto fetch = [&](int i, uint32_t (&buf)[NCOL]) {
+        // Load input row i into ring slot i mod D (rows past the segment or
+        // the image read zeros; they are issued anyway to keep counts fixed).
+        auto issue = [&](int i) {
             const int ih = ih0 + i;
             const bool ok = (unsigned)ih < (unsigned)a.H && i < ni;
             const int soff = ok ? (xbase + ih * a.xs_h) * ES : 0;
             const int vbad = ok ? 0 : INVALID;
+            uint32_t *dst = ringw + (i % D) * (NCOL * 64);
 #pragma unroll
             for (int col = 0; col < NCOL; ++col)
-                buf[col] = __builtin_amdgcn_raw_buffer_load_b32(xr, vcol[col] + vbad, soff, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(dst + col * 64), 4, vcol[col] + vbad, soff, 0,
+                                                         0);
         };
-
-        uint32_t cur[NCOL], nxt[NCOL];
-        fetch(0, cur);
-        for (int ib = 0; ib < ni; ib += U) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+        for (int i = 0; i < D - 1; ++i) issue(i);
+
+        for (int ib = 0; ib < ni; ib += U) {
+            static_for<U>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
                 const int i = ib + u;
                 if (i < ni) {
-                    fetch(i + 1, nxt);
+                    issue(i + D - 1);
+                    // Wait until row i has landed in the ring.
+                    if (ib == 0) wait_vmcnt<dw_pending_at<K, S, TO, D>(u, true)>();
+                    else wait_vmcnt<dw_pending_at<K, S, TO, D>(u, false)>();
+                    asm volatile("" ::: "memory");
+                    uint32_t cur[NCOL];
+                    const uint32_t *src = ringl + (i % D) * (NCOL * 64);
+#pragma unroll
+                    for (int col = 0; col < NCOL; ++col) cur[col] = src[col * 64];
+
                     // Row operands.  16-bit: the pair of columns (q, q+1) of each
                     // channel packed into one word, and the odd last column widened;
                     // fp32: every column as is.  Unused entries fold away.
@@ -221,70 +288,60 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
                         }
                         Word<T>::widen(cur[col], xv[col]);
                     }
-                    // Open outputs j = J*M + jp with kh = u - jp*S in [0, K).
+                    // Open outputs j = ib/S + jp (ib is a multiple of U = M*S) with
+                    // kh = u - jp*S in [0, K).
 #pragma unroll
                     for (int jp = -M; jp <= M; ++jp) {
                         const int kh = u - jp * S;
                         if (kh < 0 || kh >= K) continue;
-                        // Output j = ib/S + jp (ib is a multiple of U = M*S).  Rows
-                        // outside the segment are skipped (a uniform branch), so the
-                        // halo rows of a short segment cost loads but no arithmetic;
-                        // a skipped slot still holds the bias when its next output
-                        // (j + M, whose first input row follows j's last) opens it.
                         const int j = ib / S + jp;
-                        if (j < 0 || j >= nj) continue;
                         const int slot = ((jp % M) + M) % M;
-                        if constexpr (DOT) {
-                            uint2 wp[KP];
+                        // Rows outside the segment cost no arithmetic (a uniform
+                        // branch); a skipped slot still holds the bias when its
+                        // next output (j + M, whose first input row follows j's
+                        // last) opens it.
+                        if (j >= 0 && j < nj) {
+                            if constexpr (DOT) {
 #pragma unroll
-                            for (int pp = 0; pp < KP; ++pp)
-                                wp[pp] = *reinterpret_cast<const uint2 *>(swl + (kh * WPR + pp) * pitch);
-                            const uint2 ws = *reinterpret_cast<const uint2 *>(swl + (kh * WPR + KP) * pitch);
+                                for (int t = 0; t < TO; ++t) {
 #pragma unroll
-                            for (int t = 0; t < TO; ++t) {
-#pragma unroll
-                                for (int pp = 0; pp < KP; ++pp) {
-                                    acc[slot][t][0] = dot2<T>(plo[t * S + 2 * pp], wp[pp].x, acc[slot][t][0]);
-                                    acc[slot][t][1] = dot2<T>(phi[t * S + 2 * pp], wp[pp].y, acc[slot][t][1]);
+                                    for (int pp = 0; pp < KP; ++pp) {
+                                        acc[slot][t][0] = dot2<T>(plo[t * S + 2 * pp], wpl[kh][pp], acc[slot][t][0]);
+                                        acc[slot][t][1] = dot2<T>(phi[t * S + 2 * pp], wph[kh][pp], acc[slot][t][1]);
+                                    }
+                                    acc[slot][t][0] = __builtin_fmaf(xv[t * S + K - 1][0], wsl[kh], acc[slot][t][0]);
+                                    acc[slot][t][V - 1] =
+                                        __builtin_fmaf(xv[t * S + K - 1][V - 1], wsh[kh], acc[slot][t][V - 1]);
                                 }
-                                acc[slot][t][0] = __builtin_fmaf(xv[t * S + K - 1][0], __uint_as_float(ws.x), acc[slot][t][0]);
-                                acc[slot][t][V - 1] =
-                                    __builtin_fmaf(xv[t * S + K - 1][V - 1], __uint_as_float(ws.y), acc[slot][t][V - 1]);
+                            } else {
+#pragma unroll
+                                for (int t = 0; t < TO; ++t)
+#pragma unroll
+                                    for (int kw = 0; kw < K; ++kw)
+                                        acc[slot][t][0] = __builtin_fmaf(xv[t * S + kw][0], wf[kh][kw], acc[slot][t][0]);
                             }
-                        } else {
-                            float wk[K][V];
-#pragma unroll
-                            for (int kw = 0; kw < K; ++kw)
-#pragma unroll
-                                for (int v = 0; v < V; ++v) wk[kw][v] = __uint_as_float(swl[(kh * K + kw) * pitch + v]);
-#pragma unroll
-                            for (int t = 0; t < TO; ++t)
-#pragma unroll
-                                for (int kw = 0; kw < K; ++kw)
-#pragma unroll
-                                    for (int v = 0; v < V; ++v)
-                                        acc[slot][t][v] = __builtin_fmaf(xv[t * S + kw][v], wk[kw][v], acc[slot][t][v]);
                         }
                         if (kh == K - 1) {
-                            // Output j is complete.
-                            T *yrow = Yn + (int64_t)(oh0 + j) * a.ys_h;
+                            // Output j is complete: TO stores, always issued (dropped
+                            // out of range for an absent row or column).
+                            const bool ok = j >= 0 && j < nj;
+                            const int soff = ok ? (ybase + (oh0 + j) * a.ys_h) * ES : 0;
+                            const int vbad = ok ? 0 : INVALID;
 #pragma unroll
                             for (int t = 0; t < TO; ++t)
-                                if (ow0 + t < a.OW)
-                                    *reinterpret_cast<uint32_t *>(yrow + (int64_t)(ow0 + t) * a.ys_w) =
-                                        Word<T>::narrow(acc[slot][t]);
+                                __builtin_amdgcn_raw_buffer_store_b32(Word<T>::narrow(acc[slot][t]), yr,
+                                                                      ycol[t] + vbad, soff, 0);
 #pragma unroll
                             for (int t = 0; t < TO; ++t)
 #pragma unroll
                                 for (int v = 0; v < V; ++v) acc[slot][t][v] = bias[v];
                         }
                     }
-#pragma unroll
-                    for (int col = 0; col < NCOL; ++col) cur[col] = nxt[col];
                 }
-            }
+            });
         }
     }
+#endif
 }
 
 namespace {
@@ -293,7 +350,7 @@ template <typename T, int K, int S, int TO>
 hipError_t go(DwArgs a, hipStream_t s)
 {
     auto kern = dwcl_kernel<T, K, S, TO>;
-    const size_t lds = (size_t)K * DwTaps<T, K>::WPR * (a.cpb * Word<T>::V + 2) * sizeof(uint32_t);
+    const size_t lds = 0;  // the input-row rings are static LDS
     // One resident round of persistent workgroups, a multiple of the number
     // of (strip, channel) chunks, and no more than there are rows to share.
     int dev = 0, cus = 0, per_cu = 0;
@@ -366,9 +423,10 @@ int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *
     a.xs_h = (int32_t)d.x.strides[2];
     a.xs_w = (int32_t)d.x.strides[3];
     a.x_bytes = (int32_t)p.tile[7];
-    a.ys_n = p.y.strides[0];
-    a.ys_h = p.y.strides[2];
-    a.ys_w = p.y.strides[3];
+    a.y_bytes = (int32_t)p.tile[3];
+    a.ys_n = (int32_t)p.y.strides[0];
+    a.ys_h = (int32_t)p.y.strides[2];
+    a.ys_w = (int32_t)p.y.strides[3];
     a.ws0 = d.w.strides[0];
     a.ws2 = d.w.strides[2];
     a.ws3 = d.w.strides[3];
@@ -382,7 +440,6 @@ int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *
     a.pb_w = (int32_t)d.padding_before[1];
     a.cpb = (int32_t)p.tile[1];
     a.spb = (int32_t)p.tile[2];
-    a.rpt = (int32_t)p.tile[3];
     a.ch_chunks = (int32_t)p.tile[4];
     a.strip_chunks = (int32_t)p.tile[5];
     a.row_chunks = (int32_t)p.tile[6];

@@ -103,8 +103,8 @@ bool supports_dwcl(const conv_desc &d, const conv_tensor &y)
     if (d.C_in % v) return false;
     for (int i : {0, 2, 3})
         if (d.x.strides[i] % v || y.strides[i] % v) return false;
-    // 32-bit buffer offsets.
-    return span_bytes(d.x, esize(d.dtype)) <= kI32 - 4096;
+    // 32-bit buffer offsets for loads and stores.
+    return span_bytes(d.x, esize(d.dtype)) <= kI32 - 4096 && span_bytes(y, esize(d.dtype)) <= kI32 - 4096;
 }
 
 bool supports_plane(const conv_desc &d) { return stencil_domain(d); }
@@ -146,20 +146,23 @@ void geom_dwcl(const conv_desc &d, conv_plan_t &p)
     const int64_t ch_chunks = cdiv(words, cpb);
     // Persistent workgroups: the launcher sizes the grid to one resident
     // round; grid[0] here is the upper bound (one row per workgroup).
-    const int64_t rpt = 1;
     const int64_t row_chunks = d.out[0];
     const int64_t per_row = d.N * strip_chunks * ch_chunks;
     p.tile[0] = to;
     p.tile[1] = cpb;
     p.tile[2] = spb;
-    p.tile[3] = rpt;
+    p.tile[3] = span_bytes(p.y, esize(d.dtype));
     p.tile[4] = ch_chunks;
     p.tile[5] = strip_chunks;
     p.tile[6] = row_chunks;
     p.tile[7] = span_bytes(d.x, esize(d.dtype));
     p.grid[0] = per_row * row_chunks;
     p.block = 256;
-    p.lds_bytes = 0;
+    // Weights (dynamic) plus four waves' input-row rings (static).
+    const int k = (int)d.k[1], s = (int)d.stride[1];
+    const int64_t wpr = d.dtype == CONV_F32 ? k : k / 2 + 1;
+    const int64_t ring = 4LL * dwcl_ring_depth(k, s, (int)to) * dwcl_ncol(k, s, (int)to) * 256;
+    p.lds_bytes = (int32_t)(k * wpr * (cpb * (4 / esize(d.dtype)) + 2) * 4 + ring);
     p.vec_ok = 1;
 }
 
