@@ -38,17 +38,26 @@ enum { IG_CIG_PAD = 0, IG_COG_PAD = 1, IG_PHASES = 2, IG_MTILES = 3, IG_NTILES =
 // outputs reads NCOL input columns per row.  Each wave streams input rows
 // through a ring of D rows in LDS (direct-to-LDS loads); before it reads a
 // ring row it waits until at most the VMEM instructions issued after that
-// row's loads are pending: D-1 rows of loads plus the stores of D-1 steps (TO
-// per step that completes an output row, every S-th step).  D is the deepest
-// ring whose worst case fits the 6-bit vmcnt field.
+// row's loads are pending: D-1 rows of loads plus the stores of D-1 steps
+// (every S-th step completes an output row).  With q (the wave's 64 lanes are
+// 64 consecutive channel words of one strip) a row takes ceil(NCOL/4)
+// 16-byte loads and an output row ceil(TO/4) 16-byte stores; otherwise NCOL
+// and TO 4-byte ones.  D is the deepest ring (up to 4) whose worst case fits
+// the 6-bit vmcnt field.
 constexpr int dwcl_ncol(int K, int S, int TO) { return (TO - 1) * S + K; }
-constexpr int dwcl_pending(int K, int S, int TO, int D)
+constexpr int dwcl_loads_per_row(int K, int S, int TO, bool q)
 {
-    return (D - 1) * dwcl_ncol(K, S, TO) + ((D - 1 + S - 1) / S) * TO;
+    return q ? (dwcl_ncol(K, S, TO) + 3) / 4 : dwcl_ncol(K, S, TO);
 }
-constexpr int dwcl_ring_depth(int K, int S, int TO)
+constexpr int dwcl_stores_per_row(int TO, bool q) { return q ? (TO + 3) / 4 : TO; }
+constexpr int dwcl_ring_cols(int K, int S, int TO, bool q) { return q ? 4 * dwcl_loads_per_row(K, S, TO, q) : dwcl_ncol(K, S, TO); }
+constexpr int dwcl_pending(int K, int S, int TO, int D, bool q)
 {
-    return dwcl_pending(K, S, TO, 4) <= 63 ? 4 : dwcl_pending(K, S, TO, 3) <= 63 ? 3 : 2;
+    return (D - 1) * dwcl_loads_per_row(K, S, TO, q) + ((D - 1 + S - 1) / S) * dwcl_stores_per_row(TO, q);
+}
+constexpr int dwcl_ring_depth(int K, int S, int TO, bool q)
+{
+    return dwcl_pending(K, S, TO, 4, q) <= 63 ? 4 : dwcl_pending(K, S, TO, 3, q) <= 63 ? 3 : 2;
 }
 
 // Launchers (defined in the .hip files).  `vec` selects the 16-byte path.

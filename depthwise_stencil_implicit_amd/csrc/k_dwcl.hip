@@ -88,20 +88,20 @@ template <int N, class F> __device__ __forceinline__ void static_for(F &&f)
     static_for_impl(std::make_integer_sequence<int, N>{}, static_cast<F &&>(f));
 }
 
-// Stores issued by stream step v (TO when its row completes an output row).
-template <int K, int S, int TO> __device__ constexpr int dw_stores_at(int v)
+// Stores issued by stream step v: NS when its row completes an output row.
+template <int K, int S, int NS> __device__ constexpr int dw_stores_at(int v)
 {
-    return (((v - (K - 1)) % S) + S) % S == 0 ? TO : 0;
+    return (((v - (K - 1)) % S) + S) % S == 0 ? NS : 0;
 }
 // VMEM instructions that may still be pending when step u (position in the
-// unrolled block) reads its ring row: the loads of the D-1 rows after it and
-// the stores of the D-1 steps before it -- of this segment only when the
-// block is the segment's first (earlier rows came from the prologue).
-template <int K, int S, int TO, int D> __device__ constexpr int dw_pending_at(int u, bool first)
+// unrolled block) reads its ring row: the loads (LPR per row) of the D-1 rows
+// after it and the stores of the D-1 steps before it -- of this segment only
+// when the block is the segment's first (earlier rows came from the prologue).
+template <int K, int S, int LPR, int NS, int D> __device__ constexpr int dw_pending_at(int u, bool first)
 {
-    int n = (D - 1) * dwcl_ncol(K, S, TO);
+    int n = (D - 1) * LPR;
     for (int d = 1; d < D; ++d)
-        if (!first || u - d >= 0) n += dw_stores_at<K, S, TO>(u - d);
+        if (!first || u - d >= 0) n += dw_stores_at<K, S, NS>(u - d);
     return n;
 }
 template <int N> __device__ __forceinline__ void wait_vmcnt()
@@ -118,7 +118,7 @@ template <typename T, int K> struct DwTaps {
     static constexpr int WPR = DOT ? KP + 1 : K;
 };
 
-template <typename T, int K, int S, int TO>
+template <typename T, int K, int S, int TO, bool Q>
 __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
 {
     // The body takes LDS address-space pointers, which only the device pass
@@ -130,14 +130,21 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     constexpr int INVALID = 0x7fffff00;
     constexpr int M = (K + S - 1) / S;   // output rows open at once (accumulator slots)
     constexpr int U = M * S;             // input rows per unrolled block: slot pattern repeats
-    constexpr int D = dwcl_ring_depth(K, S, TO);
-    constexpr int RING = D * NCOL * 64;  // ring words per wave
+    constexpr int D = dwcl_ring_depth(K, S, TO, Q);
+    constexpr int LPR = dwcl_loads_per_row(K, S, TO, Q);  // load instructions per input row
+    constexpr int NS = dwcl_stores_per_row(TO, Q);        // store instructions per output row
+    constexpr int RCOL = dwcl_ring_cols(K, S, TO, Q);     // ring columns per row (>= NCOL)
+    constexpr int RING = D * RCOL * 64;  // ring words per wave
     constexpr bool DOT = DwTaps<T, K>::DOT;
     constexpr int KP = DwTaps<T, K>::KP;
     constexpr int WPR = DwTaps<T, K>::WPR;
     static_assert(!DOT || (K & 1), "pairs leave one odd column");
-    static_assert(dwcl_pending(K, S, TO, D) <= 63, "vmcnt range");
-    __shared__ __attribute__((aligned(16))) uint32_t ring[4 * RING];
+    static_assert(dwcl_pending(K, S, TO, D, Q) <= 63, "vmcnt range");
+    // One LDS object: four waves' input-row rings, then (16-byte path) their
+    // TO x 64-word output staging tiles.  A single object keeps the compiler's
+    // direct-to-LDS tracking from draining the ring around unrelated LDS use.
+    __shared__ __attribute__((aligned(16))) uint32_t ring[4 * RING + (Q ? 4 * TO * 64 : 0)];
+    uint32_t *stg = ring + 4 * RING;
     typedef __attribute__((address_space(3))) void *lds_ptr;
 
     // Persistent workgroups: a workgroup keeps one (strip chunk, channel
@@ -165,7 +172,11 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     if (c0 >= a.C || strip >= a.nstrips || tid >= a.cpb * a.spb || first >= last) return;
     const int ow0 = strip * TO;
     const int wave = tid >> 6, lane = tid & 63;
-    uint32_t *ringw = ring + wave * RING;        // this wave's ring: [D][NCOL][64 lanes]
+    uint32_t *ringw = ring + wave * RING;        // this wave's ring: [D][RCOL][64 lanes]
+    uint32_t *stgw = stg + (Q ? wave * TO * 64 : 0);
+    // LDS byte addresses of the staging tile: this lane's word column, and the tile base.
+    const uint32_t sa_r = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)stgw;
+    const uint32_t sa_w = sa_r + 4 * lane;
     const uint32_t *ringl = ringw + lane;
 
     float bias[V];
@@ -204,16 +215,31 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     }
 
     // Column byte offsets of this lane's strip (input and output); absent
-    // columns are out of range.
-    int vcol[NCOL], ycol[TO];
+    // columns are out of range.  16-byte path: load m of a row brings columns
+    // 4m .. 4m+3 of the wave's 64-word run, lane l fetching the 16 bytes of
+    // column 4m + l/16, words 4*(l%16) .. +3 -- exactly the [column][lane]
+    // order the ring keeps; store s writes chunk 64s + l of the wave's
+    // [TO][16 chunks] output tile.
     const int iw0 = ow0 * S - a.pb_w;
+    const int cw = c0 - (Q ? lane * V : 0);      // first channel of the wave's run (16-byte path)
+    int vcol[LPR], ycol[Q ? 1 : TO];
+    if constexpr (Q) {
 #pragma unroll
-    for (int col = 0; col < NCOL; ++col) {
-        const int iw = iw0 + col;
-        vcol[col] = (unsigned)iw < (unsigned)a.W ? (iw * a.xs_w + c0) * ES : INVALID;
+        for (int m = 0; m < LPR; ++m) {
+            const int col = 4 * m + (lane >> 4);
+            const int iw = iw0 + col;
+            vcol[m] = col < NCOL && (unsigned)iw < (unsigned)a.W ? (iw * a.xs_w + cw + 4 * V * (lane & 15)) * ES
+                                                                 : INVALID;
+        }
+    } else {
+#pragma unroll
+        for (int col = 0; col < NCOL; ++col) {
+            const int iw = iw0 + col;
+            vcol[col] = (unsigned)iw < (unsigned)a.W ? (iw * a.xs_w + c0) * ES : INVALID;
+        }
+#pragma unroll
+        for (int t = 0; t < TO; ++t) ycol[t] = ow0 + t < a.OW ? ((ow0 + t) * a.ys_w + c0) * ES : INVALID;
     }
-#pragma unroll
-    for (int t = 0; t < TO; ++t) ycol[t] = ow0 + t < a.OW ? ((ow0 + t) * a.ys_w + c0) * ES : INVALID;
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, a.y_bytes, 0x00020000);
@@ -249,11 +275,11 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
             const bool ok = (unsigned)ih < (unsigned)a.H && i < ni;
             const int soff = ok ? (xbase + ih * a.xs_h) * ES : 0;
             const int vbad = ok ? 0 : INVALID;
-            uint32_t *dst = ringw + (i % D) * (NCOL * 64);
+            uint32_t *dst = ringw + (i % D) * (RCOL * 64);
 #pragma unroll
-            for (int col = 0; col < NCOL; ++col)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(dst + col * 64), 4, vcol[col] + vbad, soff, 0,
-                                                         0);
+            for (int m = 0; m < LPR; ++m)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(dst + m * (Q ? 256 : 64)), Q ? 16 : 4,
+                                                         vcol[m] + vbad, soff, 0, 0);
         };
 #pragma unroll
         for (int i = 0; i < D - 1; ++i) issue(i);
@@ -265,11 +291,11 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
                 if (i < ni) {
                     issue(i + D - 1);
                     // Wait until row i has landed in the ring.
-                    if (ib == 0) wait_vmcnt<dw_pending_at<K, S, TO, D>(u, true)>();
-                    else wait_vmcnt<dw_pending_at<K, S, TO, D>(u, false)>();
+                    if (ib == 0) wait_vmcnt<dw_pending_at<K, S, LPR, NS, D>(u, true)>();
+                    else wait_vmcnt<dw_pending_at<K, S, LPR, NS, D>(u, false)>();
                     asm volatile("" ::: "memory");
                     uint32_t cur[NCOL];
-                    const uint32_t *src = ringl + (i % D) * (NCOL * 64);
+                    const uint32_t *src = ringl + (i % D) * (RCOL * 64);
 #pragma unroll
                     for (int col = 0; col < NCOL; ++col) cur[col] = src[col * 64];
 
@@ -322,15 +348,39 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
                             }
                         }
                         if (kh == K - 1) {
-                            // Output j is complete: TO stores, always issued (dropped
+                            // Output j is complete: NS stores, always issued (dropped
                             // out of range for an absent row or column).
                             const bool ok = j >= 0 && j < nj;
                             const int soff = ok ? (ybase + (oh0 + j) * a.ys_h) * ES : 0;
                             const int vbad = ok ? 0 : INVALID;
+                            if constexpr (Q) {
+                                // Transpose through the wave's staging tile: word t of
+                                // lane l goes to [t][l]; 16-byte chunk k (= 16 t + qd)
+                                // then holds words 4 qd .. 4 qd + 3 of column t.  The
+                                // staging accesses are LDS instructions with their own
+                                // wait, invisible to the compiler's direct-to-LDS wait
+                                // logic.
 #pragma unroll
-                            for (int t = 0; t < TO; ++t)
-                                __builtin_amdgcn_raw_buffer_store_b32(Word<T>::narrow(acc[slot][t]), yr,
-                                                                      ycol[t] + vbad, soff, 0);
+                                for (int t = 0; t < TO; ++t) {
+                                    const uint32_t wv = Word<T>::narrow(acc[slot][t]);
+                                    asm volatile("ds_write_b32 %0, %1" ::"v"(sa_w + t * 256), "v"(wv) : "memory");
+                                }
+#pragma unroll
+                                for (int st = 0; st < NS; ++st) {
+                                    const int k = st * 64 + lane, t = k >> 4, qd = k & 15;
+                                    const bool in = t < TO && ow0 + t < a.OW;
+                                    const uint32_t ra = sa_r + 16 * min(k, 16 * TO - 1);
+                                    u32x4 v;
+                                    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(ra) : "memory");
+                                    const int voff = in ? ((ow0 + t) * a.ys_w + cw + 4 * V * qd) * ES : INVALID;
+                                    __builtin_amdgcn_raw_buffer_store_b128(v, yr, voff + vbad, soff, 0);
+                                }
+                            } else {
+#pragma unroll
+                                for (int t = 0; t < TO; ++t)
+                                    __builtin_amdgcn_raw_buffer_store_b32(Word<T>::narrow(acc[slot][t]), yr,
+                                                                          ycol[t] + vbad, soff, 0);
+                            }
 #pragma unroll
                             for (int t = 0; t < TO; ++t)
 #pragma unroll
@@ -346,10 +396,10 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
 
 namespace {
 
-template <typename T, int K, int S, int TO>
+template <typename T, int K, int S, int TO, bool Q>
 hipError_t go(DwArgs a, hipStream_t s)
 {
-    auto kern = dwcl_kernel<T, K, S, TO>;
+    auto kern = dwcl_kernel<T, K, S, TO, Q>;
     const size_t lds = 0;  // the input-row rings are static LDS
     // One resident round of persistent workgroups, a multiple of the number
     // of (strip, channel) chunks, and no more than there are rows to share.
@@ -369,10 +419,10 @@ hipError_t go(DwArgs a, hipStream_t s)
 }
 
 template <typename T>
-hipError_t dispatch(const DwArgs &a, int k, int s, int to, hipStream_t st)
+hipError_t dispatch(const DwArgs &a, int k, int s, int to, bool q, hipStream_t st)
 {
 #define MICONV_DW(KK, SS, TT) \
-    if (k == KK && s == SS && to == TT) return go<T, KK, SS, TT>(a, st);
+    if (k == KK && s == SS && to == TT) return q ? go<T, KK, SS, TT, true>(a, st) : go<T, KK, SS, TT, false>(a, st);
     MICONV_DW(3, 1, 8) MICONV_DW(3, 1, 14) MICONV_DW(5, 1, 8) MICONV_DW(7, 1, 4) MICONV_DW(3, 2, 7)
     MICONV_DW(5, 2, 7) MICONV_DW(7, 2, 4)
 #undef MICONV_DW
@@ -449,10 +499,11 @@ int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     const int k = (int)d.k[0], st = (int)d.stride[0], to = (int)p.tile[0];
+    const bool q = p.variant == 1;
     switch (d.dtype) {
-    case CONV_F32: e = dispatch<float>(a, k, st, to, s); break;
-    case CONV_F16: e = dispatch<f16_t>(a, k, st, to, s); break;
-    default: e = dispatch<bf16_t>(a, k, st, to, s); break;
+    case CONV_F32: e = dispatch<float>(a, k, st, to, q, s); break;
+    case CONV_F16: e = dispatch<f16_t>(a, k, st, to, q, s); break;
+    default: e = dispatch<bf16_t>(a, k, st, to, q, s); break;
     }
     return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
 }

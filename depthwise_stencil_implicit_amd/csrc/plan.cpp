@@ -158,11 +158,14 @@ void geom_dwcl(const conv_desc &d, conv_plan_t &p)
     p.tile[7] = span_bytes(d.x, esize(d.dtype));
     p.grid[0] = per_row * row_chunks;
     p.block = 256;
-    // Weights (dynamic) plus four waves' input-row rings (static).
-    const int k = (int)d.k[1], s = (int)d.stride[1];
-    const int64_t wpr = d.dtype == CONV_F32 ? k : k / 2 + 1;
-    const int64_t ring = 4LL * dwcl_ring_depth(k, s, (int)to) * dwcl_ncol(k, s, (int)to) * 256;
-    p.lds_bytes = (int32_t)(k * wpr * (cpb * (4 / esize(d.dtype)) + 2) * 4 + ring);
+    // variant 1: every wave is 64 consecutive channel words of one strip, so
+    // rows move as 16-byte loads and stores.  LDS: four waves' input-row
+    // rings, plus their output staging for the 16-byte stores.
+    const bool q = cpb % 64 == 0;
+    const int k = (int)d.k[1], s = (int)d.stride[1], t = (int)to;
+    p.variant = q ? 1 : 0;
+    const int64_t ring = 4LL * dwcl_ring_depth(k, s, t, q) * dwcl_ring_cols(k, s, t, q) * 256;
+    p.lds_bytes = (int32_t)(ring + (q ? 4LL * t * 256 : 0));
     p.vec_ok = 1;
 }
 

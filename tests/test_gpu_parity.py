@@ -80,7 +80,7 @@ def _geom_cases(kind, n, seed):
             r = int(rng.integers(1, 3))
             cig = int(rng.integers(1, 9)) if kind != "dw_cl" else 1
             mult = int(rng.choice([1, 2, 3, 16, 17])) if kind != "dw_cl" else 1
-            groups = int(rng.integers(2, 6)) if kind != "dw_cl" else int(rng.choice([8, 12, 20, 40, 64]))
+            groups = int(rng.integers(2, 6)) if kind != "dw_cl" else int(rng.choice([8, 12, 20, 40, 64, 128, 256]))
             cog = mult
             N = int(rng.integers(1, 3))
             if kind == "dw_cl":
@@ -120,7 +120,7 @@ def _geom_cases(kind, n, seed):
 
 
 SWEEP = {kind: _geom_cases(kind, n, seed) for kind, n, seed in
-         [("igemm", 24, 1), ("igemm_t", 24, 2), ("plane", 24, 3), ("dw_cl", 18, 4), ("reduce", 9, 5),
+         [("igemm", 24, 1), ("igemm_t", 24, 2), ("plane", 24, 3), ("dw_cl", 24, 4), ("reduce", 9, 5),
           ("grp", 24, 6)]}
 
 
