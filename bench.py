@@ -37,6 +37,7 @@ METRIC = "HBM GB/s (stencil) and TFLOP/s (implicit GEMM), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6        # dense bf16/fp16 MFMA, 256 CUs x 2048 FMA/clk x 2.4 GHz x 2
 VALU_FP32_PEAK_TFLOPS = 78.6          # 256 CUs x 64 lanes x 2 FLOP/FMA x 2.4 GHz (no packed fp32)
+VALU_DOT2_PEAK_TFLOPS = 157.3         # the same lanes issuing v_dot2_f32_{bf16,f16}: two FMAs each
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -164,6 +165,10 @@ def cpu_baseline(calls, unit, target_s):
             "sample": f"double-precision reference over {samples}, {rounds} pass(es), {total_t:.1f} s wall"}
 
 
+def wl0_dtype(calls):
+    return calls[0].dtype
+
+
 def call_work(wl, unit):
     """Algorithmic bytes or FLOPs of one call, from the library's plan."""
     import torch
@@ -288,10 +293,14 @@ def main():
     # ---- roofline of the dominant kernel ----
     dom = max(per_call, key=lambda c: c["avg_us"])
     ai = dom["flops"] / dom["bytes"]
+    # The 16-bit stencils (dw_cl, grp) multiply through packed dot2, two FMAs
+    # per lane and instruction; every other vector path issues one FMA.
+    valu_peak = VALU_DOT2_PEAK_TFLOPS if (dom["kernel"] in ("dw_cl", "grp") and wl0_dtype(calls) != "f32") \
+        else VALU_FP32_PEAK_TFLOPS
     if dom["kernel"] in ("igemm", "igemm_t"):
         roof = dict(bound="mfma", achieved=dom["TFLOPs"], peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s")
-    elif ai > VALU_FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof = dict(bound="alu", achieved=dom["TFLOPs"], peak=VALU_FP32_PEAK_TFLOPS, unit="TFLOP/s")
+    elif ai > valu_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = dict(bound="alu", achieved=dom["TFLOPs"], peak=valu_peak, unit="TFLOP/s")
     else:
         roof = dict(bound="hbm", achieved=dom["GBps"], peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
