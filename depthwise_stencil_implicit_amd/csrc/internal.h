@@ -34,31 +34,49 @@ int igemm_num_cfgs();
 // Plan-field indices for the implicit GEMM (plan.tile[]).
 enum { IG_CIG_PAD = 0, IG_COG_PAD = 1, IG_PHASES = 2, IG_MTILES = 3, IG_NTILES = 4, IG_ROWS = 5, IG_XBYTES = 6 };
 
-// Depthwise channels-last stencil (kernel CONV_K_DW_CL): a lane's strip of TO
-// outputs reads NCOL input columns per row.  Each wave streams input rows
-// through a ring of D rows in LDS (direct-to-LDS loads); before it reads a
-// ring row it waits until at most the VMEM instructions issued after that
-// row's loads are pending: D-1 rows of loads plus the stores of D-1 steps
-// (every S-th step completes an output row).  With q (the wave's 64 lanes are
-// 64 consecutive channel words of one strip) a row takes ceil(NCOL/4)
-// 16-byte loads and an output row ceil(TO/4) 16-byte stores; otherwise NCOL
-// and TO 4-byte ones.  D is the deepest ring (up to 4) whose worst case fits
-// the 6-bit vmcnt field.
-constexpr int dwcl_ncol(int K, int S, int TO) { return (TO - 1) * S + K; }
-constexpr int dwcl_loads_per_row(int K, int S, int TO, bool q)
+// Depthwise channels-last stencil (kernel CONV_K_DW_CL).  A workgroup of 256
+// threads owns CW consecutive 32-bit channel words, OCOLS consecutive output
+// columns and one block of output rows of one image; thread t is channel word
+// t % CW of the strip of DW_TO output columns t / CW.  Input rows are shared
+// by the workgroup through a ring of D rows in LDS, filled by direct-to-LDS
+// loads of CB bytes per lane (LPW instructions per wave per row).  Finished
+// output rows are staged in LDS (two buffers) and written with CB-byte stores,
+// DW_NS per wave per row, in the step after the one that finished them.
+// Before reading a ring row a wave waits until at most the VMEM instructions
+// issued after that row's loads are pending: the loads of the D-2 rows after
+// it and the stores of the D-1 steps before it.
+constexpr int DW_TO = 7;
+constexpr int dw_cw(int S) { return S == 1 ? 32 : 64; }
+constexpr int dw_ocols(int S) { return 256 / dw_cw(S) * DW_TO; }
+constexpr int dw_icols(int K, int S) { return (dw_ocols(S) - 1) * S + K; }
+constexpr int dw_lpw(int K, int S, int CB) { return (dw_icols(K, S) * (dw_cw(S) * 4 / CB) + 255) / 256; }
+constexpr int dw_ns(int S, int CB) { return (dw_ocols(S) * (dw_cw(S) * 4 / CB) + 255) / 256; }
+constexpr int dw_row_bytes(int K, int S, int CB) { return dw_lpw(K, S, CB) * 256 * CB; }
+constexpr int dw_stage_bytes(int S) { return dw_ocols(S) * dw_cw(S) * 4; }
+// LDS after the ring: the two staging buffers, which first hold the
+// workgroup's weights (CW words x K*K taps of 4 bytes per word).
+constexpr int dw_tail_bytes(int K, int S)
 {
-    return q ? (dwcl_ncol(K, S, TO) + 3) / 4 : dwcl_ncol(K, S, TO);
+    return 2 * dw_stage_bytes(S) > dw_cw(S) * 4 * K * K ? 2 * dw_stage_bytes(S) : dw_cw(S) * 4 * K * K;
 }
-constexpr int dwcl_stores_per_row(int TO, bool q) { return q ? (TO + 3) / 4 : TO; }
-constexpr int dwcl_ring_cols(int K, int S, int TO, bool q) { return q ? 4 * dwcl_loads_per_row(K, S, TO, q) : dwcl_ncol(K, S, TO); }
-constexpr int dwcl_pending(int K, int S, int TO, int D, bool q)
+constexpr int dw_pending(int K, int S, int CB, int D)
 {
-    return (D - 1) * dwcl_loads_per_row(K, S, TO, q) + ((D - 1 + S - 1) / S) * dwcl_stores_per_row(TO, q);
+    return (D - 2) * dw_lpw(K, S, CB) + ((D - 1 + S - 1) / S) * dw_ns(S, CB);
 }
-constexpr int dwcl_ring_depth(int K, int S, int TO, bool q)
+constexpr int dw_depth(int K, int S, int CB)
 {
-    return dwcl_pending(K, S, TO, 4, q) <= 63 ? 4 : dwcl_pending(K, S, TO, 3, q) <= 63 ? 3 : 2;
+    int d = 6;
+    while (d > 3 && (dw_pending(K, S, CB, d) > 63 || d * dw_row_bytes(K, S, CB) + dw_tail_bytes(K, S) > 80 * 1024))
+        --d;
+    return d;
 }
+constexpr int dw_lds_bytes(int K, int S, int CB)
+{
+    return dw_depth(K, S, CB) * dw_row_bytes(K, S, CB) + dw_tail_bytes(K, S);
+}
+// Plan-field indices for the depthwise stencil (plan.tile[]).
+enum { DW_CW = 0, DW_OCOLS = 1, DW_CHCHUNKS = 2, DW_COLCHUNKS = 3, DW_XBYTES = 4, DW_YBYTES = 5, DW_RBLOCKS = 6,
+       DW_RPB = 7 };
 
 // Launchers (defined in the .hip files).  `vec` selects the 16-byte path.
 int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *ws,

@@ -6,31 +6,39 @@
 // stencil for depthwise convolutions with dilation 1 and kernels up to 9x9,
 // with a register sliding-window schedule for channel-contiguous inputs.
 //
-// Layout on gfx950: x is [N][H][W][C] in memory (C fastest).  A lane owns one
-// 32-bit word of channels (two 16-bit channels, or one fp32 channel) and a
-// strip of TO consecutive output columns.  Consecutive lanes hold consecutive
-// channel words of the same pixel, so every wave load and store is one
-// contiguous run.  Workgroups are persistent -- one resident round over all
-// CUs -- and each keeps one (strip chunk, channel chunk), so its weights are
-// staged in LDS once; each workgroup walks a contiguous block of output rows.
+// Layout on gfx950: x is [N][H][W][C] in memory (C fastest).  A workgroup of
+// 256 threads owns CW consecutive 32-bit channel words (two 16-bit channels or
+// one fp32 channel each), OCOLS consecutive output columns and one block of
+// output rows of one image; thread t computes channel word t % CW for the
+// strip of TO output columns t / CW.
 //
-// Rows are streamed once: input row i of a segment feeds the ceil(K/S) output
+// Input rows are shared by the workgroup: row i of the block's stream lands
+// in slot i mod D of an LDS ring that holds the row's full input span (halo
+// columns included) for the workgroup's channel words.  The ring is filled by
+// direct-to-LDS buffer loads (buffer_load ... lds) D-1 rows ahead, without
+// holding registers; the row offset rides in the scalar offset, and absent
+// rows or columns get an out-of-range offset that the hardware answers with
+// zeros -- no branch for the padding.  One barrier per row: each wave first
+// waits for its own loads of the row, so after the barrier the whole row has
+// landed and every wave is done with the previous row, whose slot is then
+// refilled.
+//
+// Rows are streamed once: input row i of a block feeds the ceil(K/S) output
 // rows whose windows cover it, each held in a rolling accumulator slot until
-// its last kernel row, where it is stored (rounded once) and the slot reset
-// to the bias.  fp16/bf16 take a kernel row as K/2 packed column pairs
-// (v_dot2_f32_{f16,bf16}: two products per instruction, fp32 accumulation)
-// plus the odd last column as an fp32 FMA; fp32 uses one FMA per tap.
-//
-// Each wave streams its rows through its own ring of D rows in LDS, filled by
-// direct-to-LDS buffer loads (buffer_load_dword ... lds) D-1 rows ahead, so
-// D-1 rows of loads are in flight without holding registers.  Loads are raw
-// buffer loads: column offsets are computed once, the row offset rides in the
-// scalar offset, and absent rows or columns get an out-of-range offset that
-// the hardware answers with zeros -- no branch for the padding.  Stores are
-// raw buffer stores issued by every step that completes an output row (to an
-// out-of-range offset, which the hardware drops, when the row or column is
-// absent), so the number of VMEM instructions issued after each ring row is a
+// its last kernel row, where it is rounded once, written to an LDS staging
+// tile and the slot reset to the bias.  The next step (after its barrier)
+// writes the staged row to y with CB-byte stores.  fp16/bf16 multiply packed
+// column pairs of one channel with v_dot2_f32_{f16,bf16} (two products per
+// instruction, fp32 accumulation); an odd kernel's last column pairs with a
+// zero half.  fp32 uses one FMA per tap.  Stores are issued by every step that
+// follows a finished output row (dropped out of range for an absent row or
+// column), so the number of VMEM instructions issued after each ring row is a
 // compile-time constant and the wait before reading it is exact.
+//
+// Row blocks of one image alternate direction: odd blocks stream their rows
+// bottom to top (the same recurrence with the kernel flipped vertically), so
+// two neighbouring blocks, which run side by side on one XCD, read the K-1
+// input rows they share at the same time and the second read hits L2.
 #include "dev_common.h"
 #include "internal.h"
 
@@ -48,8 +56,8 @@ struct DwArgs {
     int32_t x_bytes, y_bytes;         // bytes addressable from x and y (buffer ranges)
     int64_t ws0, ws2, ws3;            // weight strides (output channel, kh, kw)
     int32_t N, H, W, C, OH, OW, pb_h, pb_w;
-    int32_t cpb, spb;                 // lane words / strips per workgroup
-    int32_t ch_chunks, strip_chunks, row_chunks, nstrips, total;
+    int32_t ch_chunks, col_chunks;    // workgroup chunks along channel words / output columns
+    int32_t rblocks, rpb;             // row blocks per image, output rows per block
     int32_t has_bias;
 };
 
@@ -63,17 +71,14 @@ __device__ __forceinline__ int xcd_block(int b, int total)
 template <typename T> struct Word;
 template <> struct Word<bf16_t> {
     static constexpr int V = 2;
-    __device__ static void widen(uint32_t u, float (&f)[2]) { f[0] = lo_f32(u, bf16_t{}); f[1] = hi_f32(u, bf16_t{}); }
     __device__ static uint32_t narrow(const float (&f)[2]) { return pack2<bf16_t>(f[0], f[1]); }
 };
 template <> struct Word<f16_t> {
     static constexpr int V = 2;
-    __device__ static void widen(uint32_t u, float (&f)[2]) { f[0] = lo_f32(u, f16_t{}); f[1] = hi_f32(u, f16_t{}); }
     __device__ static uint32_t narrow(const float (&f)[2]) { return pack2<f16_t>(f[0], f[1]); }
 };
 template <> struct Word<float> {
     static constexpr int V = 1;
-    __device__ static void widen(uint32_t u, float (&f)[1]) { f[0] = __uint_as_float(u); }
     __device__ static uint32_t narrow(const float (&f)[1]) { return __float_as_uint(f[0]); }
 };
 
@@ -88,20 +93,26 @@ template <int N, class F> __device__ __forceinline__ void static_for(F &&f)
     static_for_impl(std::make_integer_sequence<int, N>{}, static_cast<F &&>(f));
 }
 
-// Stores issued by stream step v: NS when its row completes an output row.
-template <int K, int S, int NS> __device__ constexpr int dw_stores_at(int v)
+// Stream step v finishes an output row when its row is the last kernel row of
+// some output: v = j*S + K - 1.  The step after it stores that row.
+template <int K, int S> __device__ constexpr bool dw_finishes(int v)
 {
-    return (((v - (K - 1)) % S) + S) % S == 0 ? NS : 0;
+    return (((v - (K - 1)) % S) + S) % S == 0;
+}
+template <int K, int S> __device__ constexpr bool dw_stores(int v, bool first)
+{
+    return (!first || v >= 1) && dw_finishes<K, S>(v - 1);
 }
 // VMEM instructions that may still be pending when step u (position in the
-// unrolled block) reads its ring row: the loads (LPR per row) of the D-1 rows
-// after it and the stores of the D-1 steps before it -- of this segment only
-// when the block is the segment's first (earlier rows came from the prologue).
-template <int K, int S, int LPR, int NS, int D> __device__ constexpr int dw_pending_at(int u, bool first)
+// unrolled block) waits for its ring row: the loads (LPW per row) of the D-2
+// rows issued after it and the stores (NS each) of the D-1 steps before it --
+// of this block's stream only when the unrolled block is the first (earlier
+// rows came from the prologue, which stores nothing).
+template <int K, int S, int LPW, int NS, int D> __device__ constexpr int dw_pending_at(int u, bool first)
 {
-    int n = (D - 1) * LPR;
+    int n = (D - 2) * LPW;
     for (int d = 1; d < D; ++d)
-        if (!first || u - d >= 0) n += dw_stores_at<K, S, NS>(u - d);
+        if ((!first || u - d >= 0) && dw_stores<K, S>(u - d, first)) n += NS;
     return n;
 }
 template <int N> __device__ __forceinline__ void wait_vmcnt()
@@ -109,16 +120,45 @@ template <int N> __device__ __forceinline__ void wait_vmcnt()
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+// Workgroup barrier for LDS: the wave's own LDS writes complete
+// (lgkmcnt(0)) before it arrives, so after the barrier every wave sees every
+// wave's writes; unlike __syncthreads() it leaves the ring loads in flight
+// (the direct-to-LDS rows are covered by the vmcnt wait before it).
+__device__ __forceinline__ void wg_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
-// Weight words per kernel row: 16-bit types keep K/2 packed column pairs
-// (kw = 2p, 2p+1) and the last, odd column as fp32; fp32 keeps K fp32 taps.
-template <typename T, int K> struct DwTaps {
-    static constexpr bool DOT = Word<T>::V == 2;
-    static constexpr int KP = DOT ? K / 2 : 0;
-    static constexpr int WPR = DOT ? KP + 1 : K;
-};
+// Raw buffer descriptor (the same fields __builtin_amdgcn_make_buffer_rsrc
+// fills: base, stride 0, byte range, the flags word) as an SGPR quad for
+// inline assembly.
+__device__ __forceinline__ u32x4 raw_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// 16-byte raw buffer store followed by two wait states.  The hardware may
+// still be reading the data registers of a store wider than 8 bytes when the
+// next instruction issues, and a VALU write to them in that cycle changes
+// what is stored (seen on gfx950: the next store's address landed in the
+// first word of the previous one's data, and the compiler did not pad the
+// pair).  In one asm block nothing can be scheduled between the two.
+__device__ __forceinline__ void store_b128(u32x4 v, u32x4 rsrc, int voff, int soff)
+{
+    asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 1" ::"v"(v), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
 
-template <typename T, int K, int S, int TO, bool Q>
+// Packed 16-bit column pairs of one channel, built with one byte permute:
+// lo(a, b) = (a.lo, b.lo) and hi(a, b) = (a.hi, b.hi) for channel words a, b
+// of two neighbouring columns.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+template <typename T, int K, int S, int CB>
 __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
 {
     // The body takes LDS address-space pointers, which only the device pass
@@ -126,305 +166,314 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int V = Word<T>::V;
     constexpr int ES = Dt<T>::size;
-    constexpr int NCOL = dwcl_ncol(K, S, TO);
+    constexpr int TO = DW_TO;
+    constexpr int CW = dw_cw(S);
+    constexpr int OCOLS = dw_ocols(S);
+    constexpr int ICOLS = dw_icols(K, S);
+    constexpr int WPC = CW * 4 / CB;                 // lanes per column, loads and stores
+    constexpr int LPW = dw_lpw(K, S, CB);            // load instructions per wave per row
+    constexpr int NS = dw_ns(S, CB);                 // store instructions per thread per output row
+    constexpr int ROWB = dw_row_bytes(K, S, CB);     // bytes per ring slot
+    constexpr int STGB = dw_stage_bytes(S);          // bytes per staging buffer
+    constexpr int D = dw_depth(K, S, CB);
+    constexpr int NCOL = (TO - 1) * S + K;           // input columns a lane reads per row
+    constexpr int M = (K + S - 1) / S;               // output rows open at once (accumulator slots)
+    constexpr int U = M * S;                         // input rows per unrolled block: slot pattern repeats
+    constexpr bool DOT = V == 2;
+    constexpr int KP = DOT ? (K + 1) / 2 : 1;        // column pairs per kernel row (16-bit)
+    constexpr int KK = K * K;
     constexpr int INVALID = 0x7fffff00;
-    constexpr int M = (K + S - 1) / S;   // output rows open at once (accumulator slots)
-    constexpr int U = M * S;             // input rows per unrolled block: slot pattern repeats
-    constexpr int D = dwcl_ring_depth(K, S, TO, Q);
-    constexpr int LPR = dwcl_loads_per_row(K, S, TO, Q);  // load instructions per input row
-    constexpr int NS = dwcl_stores_per_row(TO, Q);        // store instructions per output row
-    constexpr int RCOL = dwcl_ring_cols(K, S, TO, Q);     // ring columns per row (>= NCOL)
-    constexpr int RING = D * RCOL * 64;  // ring words per wave
-    constexpr bool DOT = DwTaps<T, K>::DOT;
-    constexpr int KP = DwTaps<T, K>::KP;
-    constexpr int WPR = DwTaps<T, K>::WPR;
-    static_assert(!DOT || (K & 1), "pairs leave one odd column");
-    static_assert(dwcl_pending(K, S, TO, D, Q) <= 63, "vmcnt range");
-    // One LDS object: four waves' input-row rings, then (16-byte path) their
-    // TO x 64-word output staging tiles.  A single object keeps the compiler's
-    // direct-to-LDS tracking from draining the ring around unrelated LDS use.
-    __shared__ __attribute__((aligned(16))) uint32_t ring[4 * RING + (Q ? 4 * TO * 64 : 0)];
-    uint32_t *stg = ring + 4 * RING;
+    static_assert(dw_pending(K, S, CB, D) <= 63, "vmcnt range");
+    static_assert(CB == 4 || CB == 16, "access width");
+    static_assert(CW * V * KK * ES <= dw_tail_bytes(K, S), "weights fit after the ring");
+    // One LDS object: the ring, then the two staging buffers (which first
+    // hold the workgroup's weights).
+    __shared__ __attribute__((aligned(16))) unsigned char lds[D * ROWB + dw_tail_bytes(K, S)];
+    unsigned char *stg = lds + D * ROWB;
     typedef __attribute__((address_space(3))) void *lds_ptr;
 
-    // Persistent workgroups: a workgroup keeps one (strip chunk, channel
-    // chunk) for its whole life and walks one contiguous block of output rows
-    // (n, oh).  Workgroup numbers are remapped so each XCD owns a contiguous
-    // band of row blocks: neighbouring rows share K-1 input rows in its L2.
+    // Task: (image, channel/column chunk, row block), row block fastest, so
+    // the blocks of one image run side by side on one XCD.
     const int tid = threadIdx.x;
-    const int SC = a.strip_chunks * a.ch_chunks;
-    const int vb = xcd_block(blockIdx.x, gridDim.x);
-    const int sc = vb % SC;
-    const int chc = sc % a.ch_chunks;
-    const int stc = sc / a.ch_chunks;
-    const int q = vb / SC;
-    const int nwg = gridDim.x / SC;
-    const int rows_total = a.N * a.OH;
-    const int first = (int)((int64_t)q * rows_total / nwg);
-    const int last = (int)((int64_t)(q + 1) * rows_total / nwg);
-
-    const int c_base = chc * a.cpb * V;
-
-    // Every wave runs on its own: no barriers.
-    const int cl0 = (tid % a.cpb) * V;
-    const int c0 = c_base + cl0;
-    const int strip = stc * a.spb + tid / a.cpb;
-    if (c0 >= a.C || strip >= a.nstrips || tid >= a.cpb * a.spb || first >= last) return;
-    const int ow0 = strip * TO;
     const int wave = tid >> 6, lane = tid & 63;
-    uint32_t *ringw = ring + wave * RING;        // this wave's ring: [D][RCOL][64 lanes]
-    uint32_t *stgw = stg + (Q ? wave * TO * 64 : 0);
-    // LDS byte addresses of the staging tile: this lane's word column, and the tile base.
-    const uint32_t sa_r = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)stgw;
-    const uint32_t sa_w = sa_r + 4 * lane;
-    const uint32_t *ringl = ringw + lane;
+    const int SC = a.col_chunks * a.ch_chunks;
+    const int task = xcd_block(blockIdx.x, gridDim.x);
+    const int rb = task % a.rblocks;
+    const int sc = (task / a.rblocks) % SC;
+    const int n = task / (a.rblocks * SC);
+    const int chc = sc % a.ch_chunks;
+    const int colc = sc / a.ch_chunks;
+    const int ohA = rb * a.rpb;
+    const int nj = min(a.rpb, a.OH - ohA);
+    if (n >= a.N || nj <= 0) return;   // uniform over the workgroup
+    const bool rev = rb & 1;           // odd blocks stream bottom to top
+    const int ni = (nj - 1) * S + K;   // input rows of the block
+
+    // This thread's channel word and output strip.
+    const int wd = tid % CW, st = tid / CW;
+    const int c0 = (chc * CW + wd) * V;              // first channel of the word
+    const bool cok = c0 < a.C;
+    const int ow0 = colc * OCOLS + st * TO;          // first output column of the strip
+    const int lcol = st * TO * S;                    // its first ring column
+
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, a.y_bytes, 0x00020000);
+    const u32x4 yq = raw_rsrc(a.y, (uint32_t)a.y_bytes);
+
+    // Load lanes: instruction m of wave w fills bytes [(4m + w) * 64 * CB, +64 * CB)
+    // of a ring slot; lane l brings chunk (4m + w) * 64 + l, i.e. CB bytes of
+    // ring column chunk / WPC at channel-word offset (chunk % WPC) * CB / 4.
+    // Columns outside the image, past the span or past the channels read zeros.
+    const int col_base = colc * OCOLS * S - a.pb_w;
+    const int chw = chc * CW * V;                    // first channel of the workgroup
+    int voff[LPW];
+#pragma unroll
+    for (int m = 0; m < LPW; ++m) {
+        const int qd = (m * 4 + wave) * 64 + lane;
+        const int col = qd / WPC, w4 = qd % WPC;
+        const int iw = col_base + col;
+        const int ch = chw + w4 * (CB / ES);
+        const bool ok = col < ICOLS && (unsigned)iw < (unsigned)a.W && ch < a.C;
+        voff[m] = ok ? (iw * a.xs_w + ch) * ES : INVALID;
+    }
+    // Store lanes: store r of thread t writes chunk q = r * 256 + t of a staged
+    // row, CB bytes of output column q / WPC at channel-word offset
+    // (q % WPC) * CB / 4.
+    int yoff[NS], soff_l[NS];
+#pragma unroll
+    for (int r = 0; r < NS; ++r) {
+        const int q = r * 256 + tid;
+        const int col = q / WPC, w4 = q % WPC;
+        const int ow = colc * OCOLS + col;
+        const int ch = chw + w4 * (CB / ES);
+        const bool ok = col < OCOLS && ow < a.OW && ch < a.C;
+        yoff[r] = ok ? (ow * a.ys_w + ch) * ES : INVALID;
+        soff_l[r] = min(q, OCOLS * WPC - 1) * CB;
+    }
+
+    // Input row of stream step i, and output row of block-local output j.
+    const int ih_first = ohA * S - a.pb_h;
+    auto in_row = [&](int i) { return rev ? ih_first + ni - 1 - i : ih_first + i; };
+    auto out_row = [&](int j) { return rev ? ohA + nj - 1 - j : ohA + j; };
+    const int xbase = n * a.xs_n;
+    const int ybase = n * a.ys_n;
+
+    // Load input row i into ring slot i mod D (rows past the block or the
+    // image read zeros; they are issued anyway to keep counts fixed).
+    auto issue = [&](int i) {
+        const int ih = in_row(i);
+        const bool ok = (unsigned)ih < (unsigned)a.H && i < ni;
+        const int soff = ok ? (xbase + ih * a.xs_h) * ES : 0;
+        const int vbad = ok ? 0 : INVALID;
+        unsigned char *dst = lds + (i % D) * ROWB + wave * 64 * CB;
+#pragma unroll
+        for (int m = 0; m < LPW; ++m)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(dst + m * 256 * CB), CB, voff[m] + vbad, soff, 0, 0);
+    };
+    // Store staged output row j (block-local) from staging buffer j & 1.
+    auto store = [&](int j) {
+        const bool ok = j >= 0 && j < nj;
+        const int soff = ok ? (ybase + out_row(j) * a.ys_h) * ES : 0;
+        const int vbad = ok ? 0 : INVALID;
+        const unsigned char *src = stg + (j & 1) * STGB;
+#pragma unroll
+        for (int r = 0; r < NS; ++r) {
+            if constexpr (CB == 16) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(src + soff_l[r]);
+                store_b128(v, yq, yoff[r] + vbad, soff);
+            } else {
+                const uint32_t v = *reinterpret_cast<const uint32_t *>(src + soff_l[r]);
+                __builtin_amdgcn_raw_buffer_store_b32(v, yr, yoff[r] + vbad, soff, 0);
+            }
+        }
+    };
+
+    // Weights: the workgroup's CW*V channels x K*K taps, loaded cooperatively
+    // (coalesced when the weight is contiguous) into the staging buffers as
+    // stored values, in the order (channel, kh, kw).
+    {
+        const T *Wt = static_cast<const T *>(a.w);
+        constexpr int E = CW * V * KK;
+        constexpr int PER = (E + 255) / 256;
+        T wv[PER];
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int e = r * 256 + tid;
+            const int c = e / KK, t = e % KK;
+            const int ch = chw + c;
+            const bool ok = e < E && ch < a.C;
+            const int64_t off = ok ? (int64_t)ch * a.ws0 + (t / K) * a.ws2 + (t % K) * a.ws3 : 0;
+            wv[r] = Wt[off];
+            if (!ok) __builtin_memset(&wv[r], 0, sizeof(T));
+        }
+#pragma unroll
+        for (int i = 0; i < D - 1; ++i) issue(i);
+        T *ws = reinterpret_cast<T *>(stg);
+#pragma unroll
+        for (int r = 0; r < PER; ++r)
+            if (r * 256 + tid < E) ws[r * 256 + tid] = wv[r];
+    }
+    wg_barrier();
 
     float bias[V];
     {
         const T *Bp = static_cast<const T *>(a.b);
+        const int cc = cok ? c0 : 0;
 #pragma unroll
-        for (int v = 0; v < V; ++v) bias[v] = a.has_bias ? to_f32(Bp[c0 + v]) : 0.f;
+        for (int v = 0; v < V; ++v) bias[v] = a.has_bias ? to_f32(Bp[cc + v]) : 0.f;
     }
-
-    // This lane's weights, held in registers for the whole walk.  16-bit: per
-    // kernel row KP packed column pairs of the stored values per channel
-    // (wpl / wph for the low / high channel of the word) and the odd last
-    // column as fp32 (wsl / wsh); fp32: every tap (wf).
-    uint32_t wpl[K][KP > 0 ? KP : 1], wph[K][KP > 0 ? KP : 1];
-    float wsl[K], wsh[K], wf[K][DOT ? 1 : K];
+    // This thread's weights, in registers for the whole block.  Kernel row kh
+    // of the stream is stored row kh (K-1-kh when streaming bottom to top).
+    // 16-bit: per kernel row KP packed column pairs (kw = 2p, 2p+1) of the
+    // stored values per channel, an odd kernel's last pair completed with zero
+    // (wpl / wph for the low / high channel of the word); fp32: every tap (wf).
+    uint32_t wpl[K][KP], wph[K][KP];
+    float wf[K][DOT ? 1 : K];
     {
-        const T *Wt = static_cast<const T *>(a.w);
-        const T *w0 = Wt + (int64_t)c0 * a.ws0;
-        const T *w1 = Wt + (int64_t)(V == 2 ? c0 + 1 : c0) * a.ws0;
+        const uint16_t *w16 = reinterpret_cast<const uint16_t *>(stg);
+        const float *w32 = reinterpret_cast<const float *>(stg);
+        const int cl = wd * V;   // local channel
 #pragma unroll
         for (int kh = 0; kh < K; ++kh) {
+            const int sr = rev ? K - 1 - kh : kh;
             if constexpr (DOT) {
 #pragma unroll
                 for (int pp = 0; pp < KP; ++pp) {
-                    const int64_t o0 = kh * a.ws2 + (2 * pp) * a.ws3, o1 = o0 + a.ws3;
-                    wpl[kh][pp] = (uint32_t)w0[o0].u | ((uint32_t)w0[o1].u << 16);
-                    wph[kh][pp] = (uint32_t)w1[o0].u | ((uint32_t)w1[o1].u << 16);
+                    const int t0 = sr * K + 2 * pp;
+                    const bool two = 2 * pp + 1 < K;
+                    wpl[kh][pp] = (uint32_t)w16[cl * KK + t0] | (two ? (uint32_t)w16[cl * KK + t0 + 1] << 16 : 0u);
+                    wph[kh][pp] =
+                        (uint32_t)w16[(cl + 1) * KK + t0] | (two ? (uint32_t)w16[(cl + 1) * KK + t0 + 1] << 16 : 0u);
                 }
-                wsl[kh] = to_f32(w0[kh * a.ws2 + (K - 1) * a.ws3]);
-                wsh[kh] = to_f32(w1[kh * a.ws2 + (K - 1) * a.ws3]);
             } else {
 #pragma unroll
-                for (int kw = 0; kw < K; ++kw) wf[kh][kw] = to_f32(w0[kh * a.ws2 + kw * a.ws3]);
+                for (int kw = 0; kw < K; ++kw) wf[kh][kw] = w32[cl * KK + sr * K + kw];
             }
         }
     }
 
-    // Column byte offsets of this lane's strip (input and output); absent
-    // columns are out of range.  16-byte path: load m of a row brings columns
-    // 4m .. 4m+3 of the wave's 64-word run, lane l fetching the 16 bytes of
-    // column 4m + l/16, words 4*(l%16) .. +3 -- exactly the [column][lane]
-    // order the ring keeps; store s writes chunk 64s + l of the wave's
-    // [TO][16 chunks] output tile.
-    const int iw0 = ow0 * S - a.pb_w;
-    const int cw = c0 - (Q ? lane * V : 0);      // first channel of the wave's run (16-byte path)
-    int vcol[LPR], ycol[Q ? 1 : TO];
-    if constexpr (Q) {
+    float acc[M][TO][V];
 #pragma unroll
-        for (int m = 0; m < LPR; ++m) {
-            const int col = 4 * m + (lane >> 4);
-            const int iw = iw0 + col;
-            vcol[m] = col < NCOL && (unsigned)iw < (unsigned)a.W ? (iw * a.xs_w + cw + 4 * V * (lane & 15)) * ES
-                                                                 : INVALID;
-        }
-    } else {
+    for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int col = 0; col < NCOL; ++col) {
-            const int iw = iw0 + col;
-            vcol[col] = (unsigned)iw < (unsigned)a.W ? (iw * a.xs_w + c0) * ES : INVALID;
-        }
+        for (int t = 0; t < TO; ++t)
 #pragma unroll
-        for (int t = 0; t < TO; ++t) ycol[t] = ow0 + t < a.OW ? ((ow0 + t) * a.ys_w + c0) * ES : INVALID;
-    }
-    const __amdgpu_buffer_rsrc_t xr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, a.x_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, a.y_bytes, 0x00020000);
+            for (int v = 0; v < V; ++v) acc[m][t][v] = bias[v];
+    const uint32_t *ringw = reinterpret_cast<const uint32_t *>(lds) + lcol * CW + wd;
+    uint32_t *stgw = reinterpret_cast<uint32_t *>(stg) + st * TO * CW + wd;
 
-    // The block of output rows splits into per-image segments.  In a segment
-    // with output rows oh0 + j (j < nj), input row ih0 + i (ih0 = oh0*S - pb)
-    // feeds output j at kernel row kh = i - j*S.  Output j lives in
-    // accumulator slot j mod M from its first input row to its last; unrolling
-    // the stream by U = M*S rows makes every (slot, kh) pair a compile-time
-    // constant.
-    for (int row0 = first; row0 < last;) {
-        const int n = row0 / a.OH;
-        const int oh0 = row0 - n * a.OH;
-        const int nj = min(last - row0, a.OH - oh0);
-        row0 += nj;
-        const int ih0 = oh0 * S - a.pb_h;
-        const int ni = (nj - 1) * S + K;   // input rows of the segment
-        const int xbase = n * a.xs_n;
-        const int ybase = n * a.ys_n;
+    // Stream step i (row in_row(i)) feeds block-local output j at kernel row
+    // kh = i - j*S.  Output j lives in accumulator slot j mod M from its first
+    // input row to its last; unrolling the stream by U = M*S rows makes every
+    // (slot, kh) pair a compile-time constant.
+    for (int ib = 0; ib < ni; ib += U) {
+        static_for<U>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            const int i = ib + u;
+            if (i < ni) {
+                // Own loads of row i landed; after the barrier every wave's
+                // have, every wave is done with row i-1 (whose slot the next
+                // issue refills), and the row finished in step i-1 is staged.
+                if (ib == 0) wait_vmcnt<dw_pending_at<K, S, LPW, NS, D>(u, true)>();
+                else wait_vmcnt<dw_pending_at<K, S, LPW, NS, D>(u, false)>();
+                wg_barrier();
+                issue(i + D - 1);
+                if (ib == 0) {
+                    if constexpr (dw_stores<K, S>(u, true)) store((i - 1 - (K - 1)) / S);
+                } else {
+                    if constexpr (dw_stores<K, S>(u, false)) store((i - 1 - (K - 1)) / S);
+                }
+                uint32_t cur[NCOL];
+                const uint32_t *src = ringw + (i % D) * (ROWB / 4);
+#pragma unroll
+                for (int col = 0; col < NCOL; ++col) cur[col] = src[col * CW];
 
-        float acc[M][TO][V];
+                // Row operands.  16-bit: column pairs (c, c+1) of each channel,
+                // and an odd kernel's last column with a zero partner; fp32: the
+                // columns as they are.  Entries no tap uses fold away.
+                uint32_t plo[NCOL], phi[NCOL], zlo[NCOL], zhi[NCOL];
 #pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int t = 0; t < TO; ++t)
-#pragma unroll
-                for (int v = 0; v < V; ++v) acc[m][t][v] = bias[v];
-
-        // Load input row i into ring slot i mod D (rows past the segment or
-        // the image read zeros; they are issued anyway to keep counts fixed).
-        auto issue = [&](int i) {
-            const int ih = ih0 + i;
-            const bool ok = (unsigned)ih < (unsigned)a.H && i < ni;
-            const int soff = ok ? (xbase + ih * a.xs_h) * ES : 0;
-            const int vbad = ok ? 0 : INVALID;
-            uint32_t *dst = ringw + (i % D) * (RCOL * 64);
-#pragma unroll
-            for (int m = 0; m < LPR; ++m)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(dst + m * (Q ? 256 : 64)), Q ? 16 : 4,
-                                                         vcol[m] + vbad, soff, 0, 0);
-        };
-#pragma unroll
-        for (int i = 0; i < D - 1; ++i) issue(i);
-
-        for (int ib = 0; ib < ni; ib += U) {
-            static_for<U>([&](auto uc) {
-                constexpr int u = decltype(uc)::value;
-                const int i = ib + u;
-                if (i < ni) {
-                    issue(i + D - 1);
-                    // Wait until row i has landed in the ring.
-                    if (ib == 0) wait_vmcnt<dw_pending_at<K, S, LPR, NS, D>(u, true)>();
-                    else wait_vmcnt<dw_pending_at<K, S, LPR, NS, D>(u, false)>();
-                    asm volatile("" ::: "memory");
-                    uint32_t cur[NCOL];
-                    const uint32_t *src = ringl + (i % D) * (RCOL * 64);
-#pragma unroll
-                    for (int col = 0; col < NCOL; ++col) cur[col] = src[col * 64];
-
-                    // Row operands.  16-bit: the pair of columns (q, q+1) of each
-                    // channel packed into one word, and the odd last column widened;
-                    // fp32: every column as is.  Unused entries fold away.
-                    uint32_t plo[NCOL], phi[NCOL];
-                    float xv[NCOL][V];
-#pragma unroll
-                    for (int col = 0; col < NCOL; ++col) {
-                        if constexpr (DOT) {
-                            if (col + 1 < NCOL) {
-                                plo[col] = (cur[col] & 0xffffu) | (cur[col + 1] << 16);
-                                phi[col] = (cur[col] >> 16) | (cur[col + 1] & 0xffff0000u);
-                            }
+                for (int col = 0; col < NCOL; ++col) {
+                    if constexpr (DOT) {
+                        if (col + 1 < NCOL) {
+                            plo[col] = pair_lo(cur[col], cur[col + 1]);
+                            phi[col] = pair_hi(cur[col], cur[col + 1]);
                         }
-                        Word<T>::widen(cur[col], xv[col]);
+                        zlo[col] = cur[col] & 0xffffu;
+                        zhi[col] = cur[col] >> 16;
                     }
-                    // Open outputs j = ib/S + jp (ib is a multiple of U = M*S) with
-                    // kh = u - jp*S in [0, K).
+                }
+                // Open outputs j = ib/S + jp (ib is a multiple of U = M*S) with
+                // kh = u - jp*S in [0, K).
 #pragma unroll
-                    for (int jp = -M; jp <= M; ++jp) {
-                        const int kh = u - jp * S;
-                        if (kh < 0 || kh >= K) continue;
-                        const int j = ib / S + jp;
-                        const int slot = ((jp % M) + M) % M;
-                        // Rows outside the segment cost no arithmetic (a uniform
-                        // branch); a skipped slot still holds the bias when its
-                        // next output (j + M, whose first input row follows j's
-                        // last) opens it.
-                        if (j >= 0 && j < nj) {
-                            if constexpr (DOT) {
-#pragma unroll
-                                for (int t = 0; t < TO; ++t) {
-#pragma unroll
-                                    for (int pp = 0; pp < KP; ++pp) {
-                                        acc[slot][t][0] = dot2<T>(plo[t * S + 2 * pp], wpl[kh][pp], acc[slot][t][0]);
-                                        acc[slot][t][1] = dot2<T>(phi[t * S + 2 * pp], wph[kh][pp], acc[slot][t][1]);
-                                    }
-                                    acc[slot][t][0] = __builtin_fmaf(xv[t * S + K - 1][0], wsl[kh], acc[slot][t][0]);
-                                    acc[slot][t][V - 1] =
-                                        __builtin_fmaf(xv[t * S + K - 1][V - 1], wsh[kh], acc[slot][t][V - 1]);
-                                }
-                            } else {
-#pragma unroll
-                                for (int t = 0; t < TO; ++t)
-#pragma unroll
-                                    for (int kw = 0; kw < K; ++kw)
-                                        acc[slot][t][0] = __builtin_fmaf(xv[t * S + kw][0], wf[kh][kw], acc[slot][t][0]);
-                            }
-                        }
-                        if (kh == K - 1) {
-                            // Output j is complete: NS stores, always issued (dropped
-                            // out of range for an absent row or column).
-                            const bool ok = j >= 0 && j < nj;
-                            const int soff = ok ? (ybase + (oh0 + j) * a.ys_h) * ES : 0;
-                            const int vbad = ok ? 0 : INVALID;
-                            if constexpr (Q) {
-                                // Transpose through the wave's staging tile: word t of
-                                // lane l goes to [t][l]; 16-byte chunk k (= 16 t + qd)
-                                // then holds words 4 qd .. 4 qd + 3 of column t.  The
-                                // staging accesses are LDS instructions with their own
-                                // wait, invisible to the compiler's direct-to-LDS wait
-                                // logic.
-#pragma unroll
-                                for (int t = 0; t < TO; ++t) {
-                                    const uint32_t wv = Word<T>::narrow(acc[slot][t]);
-                                    asm volatile("ds_write_b32 %0, %1" ::"v"(sa_w + t * 256), "v"(wv) : "memory");
-                                }
-#pragma unroll
-                                for (int st = 0; st < NS; ++st) {
-                                    const int k = st * 64 + lane, t = k >> 4, qd = k & 15;
-                                    const bool in = t < TO && ow0 + t < a.OW;
-                                    const uint32_t ra = sa_r + 16 * min(k, 16 * TO - 1);
-                                    u32x4 v;
-                                    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(ra) : "memory");
-                                    const int voff = in ? ((ow0 + t) * a.ys_w + cw + 4 * V * qd) * ES : INVALID;
-                                    __builtin_amdgcn_raw_buffer_store_b128(v, yr, voff + vbad, soff, 0);
-                                }
-                            } else {
-#pragma unroll
-                                for (int t = 0; t < TO; ++t)
-                                    __builtin_amdgcn_raw_buffer_store_b32(Word<T>::narrow(acc[slot][t]), yr,
-                                                                          ycol[t] + vbad, soff, 0);
-                            }
+                for (int jp = -M; jp <= M; ++jp) {
+                    const int kh = u - jp * S;
+                    if (kh < 0 || kh >= K) continue;
+                    const int j = ib / S + jp;
+                    const int slot = ((jp % M) + M) % M;
+                    // Rows outside the block cost no arithmetic (a uniform
+                    // branch); a skipped slot still holds the bias when its next
+                    // output (j + M, whose first input row follows j's last)
+                    // opens it.
+                    if (j >= 0 && j < nj) {
+                        if constexpr (DOT) {
 #pragma unroll
                             for (int t = 0; t < TO; ++t)
 #pragma unroll
-                                for (int v = 0; v < V; ++v) acc[slot][t][v] = bias[v];
+                                for (int pp = 0; pp < KP; ++pp) {
+                                    const int col = t * S + 2 * pp;
+                                    const bool two = 2 * pp + 1 < K;
+                                    acc[slot][t][0] = dot2<T>(two ? plo[col] : zlo[col], wpl[kh][pp], acc[slot][t][0]);
+                                    acc[slot][t][V - 1] =
+                                        dot2<T>(two ? phi[col] : zhi[col], wph[kh][pp], acc[slot][t][V - 1]);
+                                }
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < TO; ++t)
+#pragma unroll
+                                for (int kw = 0; kw < K; ++kw)
+                                    acc[slot][t][0] =
+                                        __builtin_fmaf(__uint_as_float(cur[t * S + kw]), wf[kh][kw], acc[slot][t][0]);
+                        }
+                    }
+                    if (kh == K - 1) {
+                        // Output j is complete: round once into staging buffer
+                        // j & 1 (the next step stores it) and reset the slot.
+                        uint32_t *dst = stgw + (j & 1) * (STGB / 4);
+#pragma unroll
+                        for (int t = 0; t < TO; ++t) {
+                            dst[t * CW] = Word<T>::narrow(acc[slot][t]);
+#pragma unroll
+                            for (int v = 0; v < V; ++v) acc[slot][t][v] = bias[v];
                         }
                     }
                 }
-            });
-        }
+            }
+        });
     }
+    // The last output row was staged by the last step: store it once every
+    // wave has written its part.
+    wg_barrier();
+    store(nj - 1);
 #endif
 }
 
 namespace {
 
-template <typename T, int K, int S, int TO, bool Q>
-hipError_t go(DwArgs a, hipStream_t s)
+template <typename T, int K, int S, int CB>
+hipError_t go(DwArgs a, int64_t grid, hipStream_t s)
 {
-    auto kern = dwcl_kernel<T, K, S, TO, Q>;
-    const size_t lds = 0;  // the input-row rings are static LDS
-    // One resident round of persistent workgroups, a multiple of the number
-    // of (strip, channel) chunks, and no more than there are rows to share.
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), 256, lds);
-    if (e != hipSuccess) return e;
-    const int64_t SC = (int64_t)a.strip_chunks * a.ch_chunks;
-    int64_t slots = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
-    const int64_t rows = (int64_t)a.N * a.OH;
-    int64_t per_sc = std::max<int64_t>(1, std::min<int64_t>(slots / SC, rows));
-    const int64_t grid = per_sc * SC;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((dwcl_kernel<T, K, S, CB>), dim3((unsigned)grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t dispatch(const DwArgs &a, int k, int s, int to, bool q, hipStream_t st)
+template <typename T, int CB>
+hipError_t dispatch(const DwArgs &a, int64_t grid, int k, int s, hipStream_t st)
 {
-#define MICONV_DW(KK, SS, TT) \
-    if (k == KK && s == SS && to == TT) return q ? go<T, KK, SS, TT, true>(a, st) : go<T, KK, SS, TT, false>(a, st);
-    MICONV_DW(3, 1, 8) MICONV_DW(3, 1, 14) MICONV_DW(5, 1, 8) MICONV_DW(7, 1, 4) MICONV_DW(3, 2, 7)
-    MICONV_DW(5, 2, 7) MICONV_DW(7, 2, 4)
+#define MICONV_DW(KK, SS) \
+    if (k == KK && s == SS) return go<T, KK, SS, CB>(a, grid, st);
+    MICONV_DW(3, 1) MICONV_DW(5, 1) MICONV_DW(7, 1) MICONV_DW(3, 2) MICONV_DW(5, 2) MICONV_DW(7, 2)
 #undef MICONV_DW
     return hipErrorInvalidValue;
 }
@@ -437,32 +486,8 @@ bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw)
     return kh == kw && sh == sw && (kh == 3 || kh == 5 || kh == 7) && (sh == 1 || sh == 2);
 }
 
-// Strip width (outputs per lane along W).  The rolling window holds
-// ceil(K/S) * TO accumulators per channel, so wide kernels get narrow strips;
-// among a kernel's compiled widths, the one wasting the fewest lanes on the
-// last, partial strip of a row wins (ties: the first listed).
-int dwcl_strip(int64_t k, int64_t s, int64_t ow)
-{
-    int cand[2] = {0, 0};
-    if (s == 1) {
-        if (k == 3) { cand[0] = 8; cand[1] = 14; }
-        else if (k == 5) cand[0] = 8;
-        else cand[0] = 4;
-    } else {
-        cand[0] = k == 7 ? 4 : 7;
-    }
-    int best = cand[0];
-    int64_t waste = cdiv(ow, best) * best - ow;
-    if (cand[1]) {
-        const int64_t w2 = cdiv(ow, cand[1]) * cand[1] - ow;
-        if (w2 < waste) best = cand[1];
-    }
-    return best;
-}
-
 int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream, bool vec)
 {
-    (void)vec;
     const conv_desc &d = p.d;
     DwArgs a;
     a.x = x;
@@ -472,8 +497,8 @@ int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *
     a.xs_n = (int32_t)d.x.strides[0];
     a.xs_h = (int32_t)d.x.strides[2];
     a.xs_w = (int32_t)d.x.strides[3];
-    a.x_bytes = (int32_t)p.tile[7];
-    a.y_bytes = (int32_t)p.tile[3];
+    a.x_bytes = (int32_t)p.tile[DW_XBYTES];
+    a.y_bytes = (int32_t)p.tile[DW_YBYTES];
     a.ys_n = (int32_t)p.y.strides[0];
     a.ys_h = (int32_t)p.y.strides[2];
     a.ys_w = (int32_t)p.y.strides[3];
@@ -488,22 +513,22 @@ int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *
     a.OW = (int32_t)d.out[1];
     a.pb_h = (int32_t)d.padding_before[0];
     a.pb_w = (int32_t)d.padding_before[1];
-    a.cpb = (int32_t)p.tile[1];
-    a.spb = (int32_t)p.tile[2];
-    a.ch_chunks = (int32_t)p.tile[4];
-    a.strip_chunks = (int32_t)p.tile[5];
-    a.row_chunks = (int32_t)p.tile[6];
-    a.nstrips = (int32_t)cdiv(d.out[1], p.tile[0]);
-    a.total = (int32_t)p.grid[0];
+    a.ch_chunks = (int32_t)p.tile[DW_CHCHUNKS];
+    a.col_chunks = (int32_t)p.tile[DW_COLCHUNKS];
+    a.rblocks = (int32_t)p.tile[DW_RBLOCKS];
+    a.rpb = (int32_t)p.tile[DW_RPB];
     a.has_bias = d.has_bias;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    const int k = (int)d.k[0], st = (int)d.stride[0], to = (int)p.tile[0];
-    const bool q = p.variant == 1;
+    const int k = (int)d.k[0], st = (int)d.stride[0];
+    const int64_t grid = p.grid[0];
+    // 16-byte loads and stores need 16-byte aligned channel runs (the plan's
+    // variant 1) and 16-byte aligned x and y.
+    const bool q = p.variant == 1 && vec;
     switch (d.dtype) {
-    case CONV_F32: e = dispatch<float>(a, k, st, to, q, s); break;
-    case CONV_F16: e = dispatch<f16_t>(a, k, st, to, q, s); break;
-    default: e = dispatch<bf16_t>(a, k, st, to, q, s); break;
+    case CONV_F32: e = q ? dispatch<float, 16>(a, grid, k, st, s) : dispatch<float, 4>(a, grid, k, st, s); break;
+    case CONV_F16: e = q ? dispatch<f16_t, 16>(a, grid, k, st, s) : dispatch<f16_t, 4>(a, grid, k, st, s); break;
+    default: e = q ? dispatch<bf16_t, 16>(a, grid, k, st, s) : dispatch<bf16_t, 4>(a, grid, k, st, s); break;
     }
     return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
 }

@@ -24,13 +24,13 @@
 //   everything else                                   -> IGEMM
 #include <cstring>
 #include <cstdlib>
+#include <algorithm>
 #include <initializer_list>
 
 #include "internal.h"
 
 namespace miconv {
 bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw);
-int dwcl_strip(int64_t k, int64_t s, int64_t ow);
 bool grp_supported(const conv_desc &d);
 void grp_geometry(const conv_desc &d, conv_plan_t &p);
 void reduce_geometry(const conv_desc &d, conv_plan_t &p);
@@ -137,35 +137,34 @@ int route(const conv_desc &d, const conv_tensor &y)
 
 void geom_dwcl(const conv_desc &d, conv_plan_t &p)
 {
-    const int64_t words = d.C_in * esize(d.dtype) / 4;
-    const int64_t cpb = words < 256 ? words : 256;
-    const int64_t spb = 256 / cpb;
-    const int64_t to = dwcl_strip(d.k[1], d.stride[1], d.out[1]);
-    const int64_t nstrips = cdiv(d.out[1], to);
-    const int64_t strip_chunks = cdiv(nstrips, spb);
-    const int64_t ch_chunks = cdiv(words, cpb);
-    // Persistent workgroups: the launcher sizes the grid to one resident
-    // round; grid[0] here is the upper bound (one row per workgroup).
-    const int64_t row_chunks = d.out[0];
-    const int64_t per_row = d.N * strip_chunks * ch_chunks;
-    p.tile[0] = to;
-    p.tile[1] = cpb;
-    p.tile[2] = spb;
-    p.tile[3] = span_bytes(p.y, esize(d.dtype));
-    p.tile[4] = ch_chunks;
-    p.tile[5] = strip_chunks;
-    p.tile[6] = row_chunks;
-    p.tile[7] = span_bytes(d.x, esize(d.dtype));
-    p.grid[0] = per_row * row_chunks;
+    const int k = (int)d.k[1], s = (int)d.stride[1];
+    const int64_t es = esize(d.dtype);
+    const int64_t words = d.C_in * es / 4;
+    const int64_t cw = dw_cw(s);
+    p.tile[DW_CW] = cw;
+    p.tile[DW_OCOLS] = dw_ocols(s);
+    p.tile[DW_CHCHUNKS] = cdiv(words, cw);
+    p.tile[DW_COLCHUNKS] = cdiv(d.out[1], dw_ocols(s));
+    p.tile[DW_XBYTES] = span_bytes(d.x, es);
+    p.tile[DW_YBYTES] = span_bytes(p.y, es);
+    // Row blocks: enough workgroups for two per CU, each one block of output
+    // rows of one image (no block crosses an image).
+    const int64_t tasks = d.N * p.tile[DW_CHCHUNKS] * p.tile[DW_COLCHUNKS];
+    int64_t rb = std::max<int64_t>(1, std::min<int64_t>(d.out[0], cdiv(512, std::max<int64_t>(tasks, 1))));
+    const int64_t rpb = cdiv(d.out[0], rb);
+    rb = cdiv(d.out[0], rpb);
+    p.tile[DW_RBLOCKS] = rb;
+    p.tile[DW_RPB] = rpb;
+    p.grid[0] = tasks * rb;
     p.block = 256;
-    // variant 1: every wave is 64 consecutive channel words of one strip, so
-    // rows move as 16-byte loads and stores.  LDS: four waves' input-row
-    // rings, plus their output staging for the 16-byte stores.
-    const bool q = cpb % 64 == 0;
-    const int k = (int)d.k[1], s = (int)d.stride[1], t = (int)to;
+    // variant 1: 16-byte direct-to-LDS loads and 16-byte stores, which need
+    // 16-byte aligned channel runs (x and y must also be 16-byte aligned at run
+    // time; y is dense with x's channel count); variant 0 moves 4-byte channel
+    // words.
+    bool q = (d.C_in * es) % 16 == 0;
+    for (int i : {0, 2, 3}) q = q && (d.x.strides[i] * es) % 16 == 0;
     p.variant = q ? 1 : 0;
-    const int64_t ring = 4LL * dwcl_ring_depth(k, s, t, q) * dwcl_ring_cols(k, s, t, q) * 256;
-    p.lds_bytes = (int32_t)(ring + (q ? 4LL * t * 256 : 0));
+    p.lds_bytes = dw_lds_bytes(k, s, q ? 16 : 4);
     p.vec_ok = 1;
 }
 
