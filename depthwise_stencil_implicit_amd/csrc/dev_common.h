@@ -78,11 +78,18 @@ template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float v)
     return r;
 }
 
-// Narrow two fp32 values into one packed 32-bit word (lo, hi).
-template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi)
+// Narrow two fp32 values into one packed 32-bit word (lo, hi), each rounded
+// to nearest even: one vector conversion (a single v_cvt_pk_bf16_f32 for
+// bf16).
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi)
 {
-    T a = from_f32<T>(lo), b = from_f32<T>(hi);
-    return (uint32_t)a.u | ((uint32_t)b.u << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
 }
 
 template <typename T> __device__ __forceinline__ T load_elem(const T *p) { return *p; }

@@ -308,7 +308,7 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
             if (!ok) __builtin_memset(&wv[r], 0, sizeof(T));
         }
 #pragma unroll
-        for (int i = 0; i < D - 1; ++i) issue(i);
+        for (int i = 0; i < D; ++i) issue(i);
         T *ws = reinterpret_cast<T *>(stg);
 #pragma unroll
         for (int r = 0; r < PER; ++r)
@@ -354,40 +354,44 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
     }
 
     float acc[M][TO][V];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int t = 0; t < TO; ++t)
-#pragma unroll
-            for (int v = 0; v < V; ++v) acc[m][t][v] = bias[v];
     const uint32_t *ringw = reinterpret_cast<const uint32_t *>(lds) + lcol * CW + wd;
     uint32_t *stgw = reinterpret_cast<uint32_t *>(stg) + st * TO * CW + wd;
+    auto read_row = [&](int i, uint32_t (&dst)[NCOL]) {
+        const uint32_t *src = ringw + (i % D) * (ROWB / 4);
+#pragma unroll
+        for (int col = 0; col < NCOL; ++col) dst[col] = src[col * CW];
+    };
+    // Row 0 in registers; from then on step i reads row i+1 while it
+    // multiplies row i.
+    uint32_t cur[NCOL];
+    wait_vmcnt<(D - 1) * LPW>();
+    wg_barrier();
+    read_row(0, cur);
 
     // Stream step i (row in_row(i)) feeds block-local output j at kernel row
     // kh = i - j*S.  Output j lives in accumulator slot j mod M from its first
-    // input row to its last; unrolling the stream by U = M*S rows makes every
-    // (slot, kh) pair a compile-time constant.
+    // input row (kh = 0, which starts from the bias) to its last; unrolling the
+    // stream by U = M*S rows makes every (slot, kh) pair a compile-time
+    // constant.
     for (int ib = 0; ib < ni; ib += U) {
         static_for<U>([&](auto uc) {
             constexpr int u = decltype(uc)::value;
             const int i = ib + u;
             if (i < ni) {
-                // Own loads of row i landed; after the barrier every wave's
-                // have, every wave is done with row i-1 (whose slot the next
-                // issue refills), and the row finished in step i-1 is staged.
+                // Own loads of row i+1 landed; after the barrier every wave's
+                // have, every wave holds row i in registers (its slot is
+                // refilled next), and the row finished in step i-1 is staged.
                 if (ib == 0) wait_vmcnt<dw_pending_at<K, S, LPW, NS, D>(u, true)>();
                 else wait_vmcnt<dw_pending_at<K, S, LPW, NS, D>(u, false)>();
                 wg_barrier();
-                issue(i + D - 1);
+                issue(i + D);
                 if (ib == 0) {
                     if constexpr (dw_stores<K, S>(u, true)) store((i - 1 - (K - 1)) / S);
                 } else {
                     if constexpr (dw_stores<K, S>(u, false)) store((i - 1 - (K - 1)) / S);
                 }
-                uint32_t cur[NCOL];
-                const uint32_t *src = ringw + (i % D) * (ROWB / 4);
-#pragma unroll
-                for (int col = 0; col < NCOL; ++col) cur[col] = src[col * CW];
+                uint32_t nxt[NCOL];
+                read_row(i + 1, nxt);
 
                 // Row operands.  16-bit: column pairs (c, c+1) of each channel,
                 // and an odd kernel's last column with a zero partner; fp32: the
@@ -413,42 +417,41 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
                     const int j = ib / S + jp;
                     const int slot = ((jp % M) + M) % M;
                     // Rows outside the block cost no arithmetic (a uniform
-                    // branch); a skipped slot still holds the bias when its next
-                    // output (j + M, whose first input row follows j's last)
-                    // opens it.
+                    // branch); an output's first kernel row starts from the bias.
                     if (j >= 0 && j < nj) {
-                        if constexpr (DOT) {
 #pragma unroll
-                            for (int t = 0; t < TO; ++t)
+                        for (int t = 0; t < TO; ++t) {
+                            if constexpr (DOT) {
+                                float a0 = kh == 0 ? bias[0] : acc[slot][t][0];
+                                float a1 = kh == 0 ? bias[1] : acc[slot][t][1];
 #pragma unroll
                                 for (int pp = 0; pp < KP; ++pp) {
                                     const int col = t * S + 2 * pp;
                                     const bool two = 2 * pp + 1 < K;
-                                    acc[slot][t][0] = dot2<T>(two ? plo[col] : zlo[col], wpl[kh][pp], acc[slot][t][0]);
-                                    acc[slot][t][V - 1] =
-                                        dot2<T>(two ? phi[col] : zhi[col], wph[kh][pp], acc[slot][t][V - 1]);
+                                    a0 = dot2<T>(two ? plo[col] : zlo[col], wpl[kh][pp], a0);
+                                    a1 = dot2<T>(two ? phi[col] : zhi[col], wph[kh][pp], a1);
                                 }
-                        } else {
-#pragma unroll
-                            for (int t = 0; t < TO; ++t)
+                                acc[slot][t][0] = a0;
+                                acc[slot][t][1] = a1;
+                            } else {
+                                float a0 = kh == 0 ? bias[0] : acc[slot][t][0];
 #pragma unroll
                                 for (int kw = 0; kw < K; ++kw)
-                                    acc[slot][t][0] =
-                                        __builtin_fmaf(__uint_as_float(cur[t * S + kw]), wf[kh][kw], acc[slot][t][0]);
+                                    a0 = __builtin_fmaf(__uint_as_float(cur[t * S + kw]), wf[kh][kw], a0);
+                                acc[slot][t][0] = a0;
+                            }
                         }
                     }
                     if (kh == K - 1) {
                         // Output j is complete: round once into staging buffer
-                        // j & 1 (the next step stores it) and reset the slot.
+                        // j & 1 (the next step stores it).
                         uint32_t *dst = stgw + (j & 1) * (STGB / 4);
 #pragma unroll
-                        for (int t = 0; t < TO; ++t) {
-                            dst[t * CW] = Word<T>::narrow(acc[slot][t]);
-#pragma unroll
-                            for (int v = 0; v < V; ++v) acc[slot][t][v] = bias[v];
-                        }
+                        for (int t = 0; t < TO; ++t) dst[t * CW] = Word<T>::narrow(acc[slot][t]);
                     }
                 }
+#pragma unroll
+                for (int col = 0; col < NCOL; ++col) cur[col] = nxt[col];
             }
         });
     }
