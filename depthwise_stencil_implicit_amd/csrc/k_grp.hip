@@ -13,15 +13,19 @@
 // the window leaves the input and for the missing partner of an odd channel
 // count, so the padding and the odd channel contribute exact zeros.  The
 // weights are staged as the matching pairs, [pair][tap][output channel].
-// A thread owns P consecutive output positions of one row and JB output
-// channels in registers: for every (pair, tap) it reads P input words and JB
-// weight words (uniform addresses: LDS broadcast) and issues P*JB
+// A thread owns P output positions of one row, interleaved with its
+// neighbours' (thread tx of a row takes columns tx, tx + tpr, ...: consecutive
+// lanes read consecutive LDS words and store consecutive elements), and JB
+// output channels in registers: for every (pair, tap) it reads P input words
+// and JB weight words (uniform addresses: LDS broadcast) and issues P*JB
 // v_dot2_f32_{f16,bf16}, each doing both channels of the pair with fp32
 // accumulation -- half the VALU instructions of one FMA per product, with no
 // widening.  Any input strides (row-contiguous NCHW loads coalesce); the
 // output tile is stored at y's strides, the bias added before one rounding.
 #include "dev_common.h"
 #include "internal.h"
+
+#include <algorithm>
 
 namespace miconv {
 
@@ -95,13 +99,13 @@ __global__ __launch_bounds__(256) void grp_kernel(GpArgs a)
     const int ty = tid / a.tpr;
     const int tx = tid - ty * a.tpr;
     const int oh = th * a.TH + ty;
-    const int ow0 = tw * a.TW + tx * P;
-    if (ty >= a.TH || oh >= a.OH || ow0 >= a.OW || tx * P >= a.TW) return;
+    const int ow0 = tw * a.TW + tx;
+    if (ty >= a.TH || oh >= a.OH || ow0 >= a.OW) return;
 
     const T *__restrict__ Bp = static_cast<const T *>(a.b);
     T *__restrict__ Y = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h;
     const int lrow = ty * a.SH;
-    const int lcol = tx * P * a.SW;
+    const int lcol = tx * a.SW;
 
     for (int j0 = 0; j0 < a.Cog; j0 += JB) {
         float acc[P][JB];
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(256) void grp_kernel(GpArgs a)
                 for (int kw = 0; kw < a.KW; ++kw) {
                     uint32_t xv[P];
 #pragma unroll
-                    for (int p = 0; p < P; ++p) xv[p] = srow[p * a.SW + kw * a.DW];
+                    for (int p = 0; p < P; ++p) xv[p] = srow[p * a.tpr * a.SW + kw * a.DW];
                     const uint32_t *wrow = sw + (pr * taps + kh * a.KW + kw) * a.cog_pad + j0;
                     uint32_t wv[JB];
 #pragma unroll
@@ -142,7 +146,173 @@ __global__ __launch_bounds__(256) void grp_kernel(GpArgs a)
             T *yc = Y + (int64_t)(g * a.Cog + j0 + jj) * a.ys_c;
 #pragma unroll
             for (int p = 0; p < P; ++p)
-                if (ow0 + p < a.OW && tx * P + p < a.TW) yc[(int64_t)(ow0 + p) * a.ys_w] = from_f32<T>(acc[p][jj]);
+                if (ow0 + p * a.tpr < a.OW) yc[(int64_t)(ow0 + p * a.tpr) * a.ys_w] = from_f32<T>(acc[p][jj]);
+        }
+    }
+}
+
+// Persistent schedule for kernels with a compile-time extent (KH x KW, KH in
+// {1, KW}, KW in {3, 5, 7}), dilation 1, 32-bit element offsets and a tile
+// of at most 8 words of channel pairs per thread.  Workgroup w serves group
+// w mod G for every tile (image, tile row, tile column) j = w / G,
+// w / G + wpg, ...: the group's weights are staged once, and while the tile
+// in LDS is multiplied, the next tile's inputs are already in flight into
+// registers (two 16-bit loads per pair word), so memory latency overlaps the
+// arithmetic of the previous tile.  Compute is the tiled schedule above with
+// every tap unrolled (ds_read immediate column offsets).
+struct GpPers {
+    int32_t xs_n, xs_c, xs_h, xs_w, ys_n, ys_c, ys_h, ys_w;
+    int32_t x_bytes;   // buffer range of x
+    int32_t wpg;       // workgroups per group
+};
+
+template <typename T, int KH, int KW, int P, int JB>
+__global__ __launch_bounds__(256) void grp_pers_kernel(GpArgs a, GpPers f)
+{
+    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+    constexpr int KK = KH * KW;
+    constexpr int ES = Dt<T>::size;
+    constexpr int SPT = 8;   // staged words per thread
+    constexpr int INVALID = 0x7fffff00;
+    uint32_t *sw = smem;                                   // [npairs][KK][cog_pad]
+    uint32_t *sx = smem + a.npairs * KK * a.cog_pad;       // [npairs][IH][IW]
+    const int tid = threadIdx.x;
+    const int g = blockIdx.x % a.G;
+    const int tiles = a.N * a.tiles_h * a.tiles_w;
+    const int plane = a.IH * a.IW;
+    const int words = a.npairs * plane;
+
+    // The group's weights as channel pairs (pad channels zero), once.
+    {
+        const T *__restrict__ Wt = static_cast<const T *>(a.w);
+        for (int i = tid; i < a.npairs * KK * a.cog_pad; i += 256) {
+            const int j = i % a.cog_pad;
+            const int rest = i / a.cog_pad;
+            const int tap = rest % KK;
+            const int p = rest / KK;
+            uint32_t word = 0;
+            if (j < a.Cog) {
+                const int64_t base = (int64_t)(g * a.Cog + j) * a.ws0 + (int64_t)(tap / KW) * a.ws2 +
+                                     (int64_t)(tap % KW) * a.ws3;
+                const uint16_t lo = Wt[base + (int64_t)(2 * p) * a.ws1].u;
+                const uint16_t hi = (2 * p + 1 < a.Cig) ? Wt[base + (int64_t)(2 * p + 1) * a.ws1].u : (uint16_t)0;
+                word = (uint32_t)lo | ((uint32_t)hi << 16);
+            }
+            sw[i] = word;
+        }
+    }
+
+    // This thread's staging slots: word e = tid + 256 k of the tile, i.e.
+    // pair e / plane at tile row r, column q; its input offset relative to the
+    // tile origin, (r, q), and whether the pair has a second channel.
+    int soff[SPT], srq[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+        const int e = tid + 256 * k;
+        const int p = e / plane, i = e - p * plane;
+        const int r = i / a.IW, q = i - r * a.IW;
+        soff[k] = r * f.xs_h + q * f.xs_w + 2 * p * f.xs_c;
+        // bit 31: slot unused; bit 30: no partner channel; then r << 15 | q.
+        srq[k] = (e >= words ? (1 << 31) : 0) | (2 * p + 1 >= a.Cig ? (1 << 30) : 0) | (r << 15) | q;
+    }
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, f.x_bytes, 0x00020000);
+    uint32_t lo[SPT], hi[SPT];
+    auto fetch = [&](int j) {
+        int t = j;
+        const int tw = t % a.tiles_w;
+        t /= a.tiles_w;
+        const int th = t % a.tiles_h;
+        const int n = t / a.tiles_h;
+        const int ih0 = th * a.TH * a.SH - a.PH;
+        const int iw0 = tw * a.TW * a.SW - a.PW;
+        const int base = n * f.xs_n + g * a.Cig * f.xs_c + ih0 * f.xs_h + iw0 * f.xs_w;
+        const bool tok = j < tiles;
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const int rq = srq[k];
+            const int r = (rq >> 15) & 0x7fff, q = rq & 0x7fff;
+            const bool ok = tok && rq >= 0 && (unsigned)(ih0 + r) < (unsigned)a.H && (unsigned)(iw0 + q) < (unsigned)a.W;
+            const int off = ok ? (base + soff[k]) * ES : INVALID;
+            const int off2 = ok && !(rq & (1 << 30)) ? off + f.xs_c * ES : INVALID;
+            lo[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, off, 0, 0);
+            hi[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, off2, 0, 0);
+        }
+    };
+
+    const int ty = tid / a.tpr;
+    const int tx = tid - ty * a.tpr;
+    const bool active = ty < a.TH;
+    const T *__restrict__ Bp = static_cast<const T *>(a.b);
+    T *__restrict__ Y = static_cast<T *>(a.y);
+    int xa[KH][P];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int p = 0; p < P; ++p) xa[kh][p] = (ty * a.SH + kh) * a.IW + (tx + p * a.tpr) * a.SW;
+
+    int j = blockIdx.x / a.G;
+    fetch(j);
+    for (; j < tiles; j += f.wpg) {
+        // Stage the fetched tile, then start fetching the next one.
+        __syncthreads();   // every thread is done reading the previous tile
+#pragma unroll
+        for (int k = 0; k < SPT; ++k)
+            if (srq[k] >= 0) sx[tid + 256 * k] = (lo[k] & 0xffffu) | (hi[k] << 16);
+        __syncthreads();
+        int t = j;
+        const int tw = t % a.tiles_w;
+        t /= a.tiles_w;
+        const int th = t % a.tiles_h;
+        const int n = t / a.tiles_h;
+        fetch(j + f.wpg);
+
+        const int oh = th * a.TH + ty;
+        const int ow0 = tw * a.TW + tx;
+        if (!active || oh >= a.OH || ow0 >= a.OW) continue;
+        const int ybase = n * f.ys_n + oh * f.ys_h + ow0 * f.ys_w;
+        for (int j0 = 0; j0 < a.Cog; j0 += JB) {
+            float acc[P][JB];
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj) {
+                const float bv = (a.has_bias && j0 + jj < a.Cog) ? to_f32(Bp[g * a.Cog + j0 + jj]) : 0.f;
+#pragma unroll
+                for (int p = 0; p < P; ++p) acc[p][jj] = bv;
+            }
+            for (int pr = 0; pr < a.npairs; ++pr) {
+                const uint32_t *sxp = sx + pr * plane;
+                const uint32_t *swp = sw + pr * KK * a.cog_pad + j0;
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+                    for (int kw = 0; kw < KW; ++kw) {
+                        uint32_t xv[P];
+#pragma unroll
+                        for (int p = 0; p < P; ++p) xv[p] = sxp[xa[kh][p] + kw];
+                        const uint32_t *wrow = swp + (kh * KW + kw) * a.cog_pad;
+                        uint32_t wv[JB];
+#pragma unroll
+                        for (int jj = 0; jj < JB; jj += 4) {
+                            const uint4 qv = *reinterpret_cast<const uint4 *>(wrow + jj);
+                            wv[jj] = qv.x;
+                            wv[jj + 1] = qv.y;
+                            wv[jj + 2] = qv.z;
+                            wv[jj + 3] = qv.w;
+                        }
+#pragma unroll
+                        for (int p = 0; p < P; ++p)
+#pragma unroll
+                            for (int jj = 0; jj < JB; ++jj) acc[p][jj] = dot2<T>(xv[p], wv[jj], acc[p][jj]);
+                    }
+            }
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj) {
+                if (j0 + jj >= a.Cog) break;
+                T *yc = Y + ybase + (g * a.Cog + j0 + jj) * f.ys_c;
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+                    if (ow0 + p * a.tpr < a.OW) yc[p * a.tpr * f.ys_w] = from_f32<T>(acc[p][jj]);
+            }
         }
     }
 }
@@ -251,6 +421,46 @@ int launch_grp(const conv_plan_t &p, const void *x, const void *w, const void *b
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)p.grid[0]), block(256);
     const size_t lds = (size_t)p.lds_bytes;
+    // Persistent schedule: unit dilation, a compiled kernel extent, 32-bit
+    // offsets, at most 8 staged words per thread.
+    const int64_t lim = 0x7fffffffLL - 4096;
+    auto span = [&](const conv_tensor &t) {
+        int64_t o = 0;
+        for (int i = 0; i < t.rank; ++i)
+            if (t.sizes[i] > 0) o += (t.sizes[i] - 1) * t.strides[i];
+        return o + 1;
+    };
+    const bool ext = (a.KW == 3 || a.KW == 5 || a.KW == 7) && (a.KH == 1 || a.KH == a.KW);
+    const int64_t tiles = (int64_t)a.N * a.tiles_h * a.tiles_w;
+    if (ext && a.DH == 1 && a.DW == 1 && span(d.x) * esize(d.dtype) < lim && span(p.y) < lim &&
+        (int64_t)a.npairs * a.IH * a.IW <= 8 * 256 && a.IH < 32768 && a.IW < 32768) {
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 256;
+        GpPers f;
+        f.xs_n = (int32_t)a.xs_n;
+        f.xs_c = (int32_t)a.xs_c;
+        f.xs_h = (int32_t)a.xs_h;
+        f.xs_w = (int32_t)a.xs_w;
+        f.ys_n = (int32_t)a.ys_n;
+        f.ys_c = (int32_t)a.ys_c;
+        f.ys_h = (int32_t)a.ys_h;
+        f.ys_w = (int32_t)a.ys_w;
+        f.x_bytes = (int32_t)(span(d.x) * esize(d.dtype));
+        // Four workgroups per CU, spread over the groups.
+        f.wpg = (int32_t)std::max<int64_t>(1, std::min<int64_t>(tiles, cdiv(4LL * cus, a.G)));
+        const dim3 pgrid((unsigned)((int64_t)a.G * f.wpg));
+#define MICONV_GP(KH_, KW_)                                                                                      \
+    if (a.KH == KH_ && a.KW == KW_) {                                                                           \
+        if (d.dtype == CONV_F16)                                                                                \
+            hipLaunchKernelGGL((grp_pers_kernel<f16_t, KH_, KW_, kP, kJB>), pgrid, block, lds, s, a, f);        \
+        else                                                                                                    \
+            hipLaunchKernelGGL((grp_pers_kernel<bf16_t, KH_, KW_, kP, kJB>), pgrid, block, lds, s, a, f);       \
+        return hipGetLastError() == hipSuccess ? CONV_OK : CONV_EDEVICE;                                        \
+    }
+        MICONV_GP(3, 3) MICONV_GP(5, 5) MICONV_GP(7, 7) MICONV_GP(1, 3) MICONV_GP(1, 5) MICONV_GP(1, 7)
+#undef MICONV_GP
+    }
     if (d.dtype == CONV_F16)
         hipLaunchKernelGGL((grp_kernel<f16_t, kP, kJB>), grid, block, lds, s, a);
     else if (d.dtype == CONV_BF16)
