@@ -30,9 +30,23 @@ struct IgemmCfg {
 };
 const IgemmCfg &igemm_cfg(int variant);
 int igemm_num_cfgs();
+// The 64-row schedule that runs the rows a sparse last round would leave to a
+// few CUs; the planner does not choose it for whole calls.
+constexpr int IG_TAIL_CFG = 11;
 
 // Plan-field indices for the implicit GEMM (plan.tile[]).
-enum { IG_CIG_PAD = 0, IG_COG_PAD = 1, IG_PHASES = 2, IG_MTILES = 3, IG_NTILES = 4, IG_ROWS = 5, IG_XBYTES = 6 };
+// IG_TAIL: 0, or (row tiles of the full-size launch) | (K ranges of the
+// 64-row launch that covers the remaining rows) << 24.
+enum { IG_CIG_PAD = 0, IG_COG_PAD = 1, IG_PHASES = 2, IG_MTILES = 3, IG_NTILES = 4, IG_ROWS = 5, IG_XBYTES = 6,
+       IG_TAIL = 7 };
+// CUs the planner assumes when it sizes the implicit GEMM's rounds of
+// workgroups (MI355X; the plan makes no device calls).
+constexpr int kIgCus = 256;
+// Bytes of the repacked weights at the start of the workspace.
+inline int64_t igemm_wbytes(int64_t groups, int64_t cog_pad, int64_t taps, int64_t cig_pad, int64_t es)
+{
+    return (groups * cog_pad * taps * cig_pad * es + 255) / 256 * 256;
+}
 
 // Depthwise channels-last stencil (kernel CONV_K_DW_CL).  A workgroup of 256
 // threads owns CW consecutive 32-bit channel words, OCOLS consecutive output

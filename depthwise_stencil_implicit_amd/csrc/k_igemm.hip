@@ -63,6 +63,9 @@ struct IgArgs {
     int32_t L[3], K[3], O[3], S[3], PB[3], D[3], J[3];
     int32_t G, phases, m_tiles, n_tiles, transposed, has_bias;
     int32_t total_tiles, y_vec4;
+    int32_t row0;                 // first row (of every phase) this launch covers
+    int32_t ksplit;               // K ranges per tile (> 1: fp32 partial sums into part)
+    float *part;                  // [ksplit][G][phases][rows - row0][cog_pad] partial sums
     int32_t w_bytes;              // bytes of the repacked weights (buffer range)
 };
 
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgArgs a)
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
         const int row = (tid >> 3) + i * (NT / 8);
-        const int m = m_tile * BM + row;
+        const int m = a.row0 + m_tile * BM + row;
         bool ok = m < a.rows;
         const int mm = ok ? m : 0;
         const int n = mm / JJ;
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgArgs a)
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int m = m_tile * BM + wr * TM + i * 16 + lr;
+        const int m = a.row0 + m_tile * BM + wr * TM + i * 16 + lr;
         if (m >= a.rows) continue;
         const int n = m / JJ;
         const int r = m - n * JJ;
@@ -431,8 +434,10 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int tile = xcd_tile(blockIdx.x, a.total_tiles);
-    // Tile order (fastest first): column tile, phase, row tile, group.
+    const int tile_k = xcd_tile(blockIdx.x, a.total_tiles);
+    // Tile order (fastest first): K range, column tile, phase, row tile, group.
+    const int ks = tile_k % a.ksplit;
+    const int tile = tile_k / a.ksplit;
     const int n_tile = tile % a.n_tiles;
     int rest = tile / a.n_tiles;
     const int phase = rest % a.phases;
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
         const int row = i * NW * RPI + wave * RPI + lane / KC;
-        const int m = m_tile * BM + row;
+        const int m = a.row0 + m_tile * BM + row;
         bool ok = m < a.rows;
         const int mm = ok ? m : 0;
         const int n = mm / JJ;
@@ -517,12 +522,23 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     const int ncb = a.cig_pad / BK;
     int it_t = 0, it_cb = 0, it_o0 = 0, it_o1 = 0, it_o2 = 0;
     while (it_t < a.taps && !tap_offsets(it_t, it_o0, it_o1, it_o2)) ++it_t;
-    // Number of steps: valid taps x channel blocks (uniform).
-    int nsteps = 0;
+    // Number of steps: valid taps x channel blocks (uniform); this workgroup
+    // runs steps [kb, kb + nsteps) of them (its K range).
+    int nall = 0;
     if (ncb > 0) {
         int dummy0, dummy1, dummy2;
-        for (int t = 0; t < a.taps; ++t) nsteps += tap_offsets(t, dummy0, dummy1, dummy2) ? ncb : 0;
+        for (int t = 0; t < a.taps; ++t) nall += tap_offsets(t, dummy0, dummy1, dummy2) ? ncb : 0;
     }
+    const int kb = ks * nall / a.ksplit;
+    const int nsteps = (ks + 1) * nall / a.ksplit - kb;
+    auto advance = [&]() {
+        if (++it_cb == ncb) {
+            it_cb = 0;
+            ++it_t;
+            while (it_t < a.taps && !tap_offsets(it_t, it_o0, it_o1, it_o2)) ++it_t;
+        }
+    };
+    for (int k = 0; k < kb; ++k) advance();
 
     auto issue = [&](unsigned char *A) {
         unsigned char *B = A + BM * RB;
@@ -542,12 +558,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
         for (int i = 0; i < B_IT; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(B + (i * NW * RPI + wave * RPI) * RB), 16,
                                                      b_off[i], step_off, 0, 0);
-        // advance the cursor
-        if (++it_cb == ncb) {
-            it_cb = 0;
-            ++it_t;
-            while (it_t < a.taps && !tap_offsets(it_t, it_o0, it_o1, it_o2)) ++it_t;
-        }
+        advance();
     };
 
     const int wr = wave / WN, wc = wave % WN;
@@ -619,6 +630,23 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
 #undef MICONV_DMA_STEP
 
     // ---- epilogue: lane holds 4 consecutive channels of one output position ----
+    if (a.ksplit > 1) {
+        // Partial sums of this K range, fp32, bias and rounding left to the
+        // reduction.
+        const int prow = a.rows - a.row0;
+        float *P = a.part + ((int64_t)(ks * a.G + g) * a.phases + phase) * prow * a.cog_pad;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = a.row0 + m_tile * BM + wr * TM + i * 16 + lr;
+            if (m >= a.rows) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int co = n_tile * BN + wc * TN + j * 16 + lg * 4;
+                *reinterpret_cast<f32x4 *>(P + (int64_t)(m - a.row0) * a.cog_pad + co) = acc[i][j];
+            }
+        }
+        return;
+    }
     T *__restrict__ Y = static_cast<T *>(a.y);
     const T *__restrict__ Bias = static_cast<const T *>(a.b);
     float bias[FN][4];
@@ -631,7 +659,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int m = m_tile * BM + wr * TM + i * 16 + lr;
+        const int m = a.row0 + m_tile * BM + wr * TM + i * 16 + lr;
         if (m >= a.rows) continue;
         const int n = m / JJ;
         const int r = m - n * JJ;
@@ -668,6 +696,68 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
         }
     }
 #endif  // __HIP_DEVICE_COMPILE__
+}
+
+// Split-K reduction: y = bias + sum over the K ranges of the fp32 partial
+// sums, rounded once; one thread per 4 consecutive output channels of one
+// row (of one group and phase), stored at y's strides like the epilogue.
+template <typename T>
+__global__ __launch_bounds__(256) void igemm_splitk_reduce(IgArgs a)
+{
+    const int quads = (a.Cog + 3) / 4;
+    const int prow = a.rows - a.row0;
+    const int64_t total = (int64_t)a.G * a.phases * prow * quads;
+    const int64_t plane = (int64_t)a.G * a.phases * prow * a.cog_pad;   // one K range
+    T *__restrict__ Y = static_cast<T *>(a.y);
+    const T *__restrict__ Bias = static_cast<const T *>(a.b);
+    const int JJ = a.J[0] * a.J[1] * a.J[2];
+    const int J12 = a.J[1] * a.J[2];
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int qd = (int)(idx % quads);
+        int64_t r0 = idx / quads;
+        const int mr = (int)(r0 % prow);
+        r0 /= prow;
+        const int phase = (int)(r0 % a.phases);
+        const int g = (int)(r0 / a.phases);
+        const int co = qd * 4;
+        const float *P = a.part + (((int64_t)g * a.phases + phase) * prow + mr) * a.cog_pad + co;
+        f32x4 s = *reinterpret_cast<const f32x4 *>(P);
+        for (int k = 1; k < a.ksplit; ++k) s += *reinterpret_cast<const f32x4 *>(P + k * plane);
+        const int m = a.row0 + mr;
+        const int n = m / JJ;
+        const int r = m - n * JJ;
+        int q0 = r / J12;
+        const int r2 = r - q0 * J12;
+        int q1 = r2 / a.J[2], q2 = r2 - q1 * a.J[2];
+        if (a.transposed) {
+            int p = phase;
+            const int rho2 = p % a.S[2];
+            p /= a.S[2];
+            const int rho1 = p % a.S[1];
+            const int rho0 = p / a.S[1];
+            q0 = a.S[0] * q0 + rho0;
+            q1 = a.S[1] * q1 + rho1;
+            q2 = a.S[2] * q2 + rho2;
+            if (q0 >= a.O[0] || q1 >= a.O[1] || q2 >= a.O[2]) continue;
+        }
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = s[e] + ((a.has_bias && co + e < a.Cog) ? to_f32(Bias[g * a.Cog + co + e]) : 0.f);
+        T *dst = Y + (int64_t)n * a.ys_n + q0 * a.ys_l[0] + q1 * a.ys_l[1] + q2 * a.ys_l[2] +
+                 (int64_t)(g * a.Cog + co) * a.ys_c;
+        if (a.y_vec4) {
+            uint2 u;
+            u.x = pack2<T>(v[0], v[1]);
+            u.y = pack2<T>(v[2], v[3]);
+            *reinterpret_cast<uint2 *>(dst) = u;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (co + e < a.Cog) dst[(int64_t)e * a.ys_c] = from_f32<T>(v[e]);
+        }
+    }
 }
 
 // Weight repack: w (any strides) -> [G][Cog_pad][taps][Cig_pad], zero padded.
@@ -715,6 +805,7 @@ constexpr IgemmCfg kCfgs[] = {
     {128, 256, 64, 2, 4, 3, 70},   // 8: 8 waves, wave tile 64 x 64
     {256, 256, 32, 2, 4, 4, 93},   // 9: 8 waves, K step 32, 4 stages (deeper prefetch)
     {256, 256, 32, 2, 4, 3, 88},   // 10: 8 waves, K step 32, 3 stages
+    {64, 256, 64, 1, 4, 3, 40},    // 11: 4 waves, wave tile 64 x 64 (rows left after the full rounds)
 };
 
 template <typename T, int V, bool VEC>
@@ -755,6 +846,7 @@ hipError_t launch_typed(const IgArgs &a, int variant, bool vec, hipStream_t s)
         case 8: return vec ? launch_cfg<T, 8, true>(a, s) : launch_cfg<T, 8, false>(a, s);
         case 9: return vec ? launch_cfg<T, 9, true>(a, s) : launch_cfg<T, 9, false>(a, s);
         case 10: return vec ? launch_cfg<T, 10, true>(a, s) : launch_cfg<T, 10, false>(a, s);
+        case 11: return vec ? launch_cfg<T, 11, true>(a, s) : launch_cfg<T, 11, false>(a, s);
         default: return hipErrorInvalidValue;
         }
     }
@@ -824,7 +916,7 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
     a.transposed = d.transposed;
     a.has_bias = d.has_bias;
     a.total_tiles = (int32_t)p.grid[0];
-    a.w_bytes = (int32_t)p.workspace_bytes;
+    a.w_bytes = (int32_t)igemm_wbytes(d.groups, p.tile[IG_COG_PAD], a.taps, p.tile[IG_CIG_PAD], esize(d.dtype));
     // 4 consecutive output channels form one aligned vector in y.
     a.y_vec4 = (p.y.strides[1] == 1 && (reinterpret_cast<uintptr_t>(y) & (4 * esize(d.dtype) - 1)) == 0 &&
                 p.y.strides[0] % 4 == 0 && (r < 1 || p.y.strides[2] % 4 == 0) &&
@@ -833,6 +925,8 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
                    ? 1
                    : 0;
 
+    a.row0 = 0;
+
     hipError_t e;
     switch (d.dtype) {
     case CONV_F32: e = launch_repack<float>(p, w, ws, s); break;
@@ -840,10 +934,47 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
     default: e = launch_repack<bf16_t>(p, w, ws, s); break;
     }
     if (e != hipSuccess) return CONV_EDEVICE;
-    switch (d.dtype) {
-    case CONV_F32: e = launch_typed<float>(a, p.variant, vec, s); break;
-    case CONV_F16: e = launch_typed<f16_t>(a, p.variant, vec, s); break;
-    default: e = launch_typed<bf16_t>(a, p.variant, vec, s); break;
+    auto run = [&](const IgArgs &args, int variant) {
+        switch (d.dtype) {
+        case CONV_F32: return launch_typed<float>(args, variant, vec, s);
+        case CONV_F16: return launch_typed<f16_t>(args, variant, vec, s);
+        default: return launch_typed<bf16_t>(args, variant, vec, s);
+        }
+    };
+    a.ksplit = 1;
+    a.part = nullptr;
+    const int64_t tail = p.tile[IG_TAIL];
+    if (tail > 0) {
+        // The planner split the rows: full-size tiles for whole rounds of
+        // workgroups, then the rows left as 64-row tiles, their K split into
+        // ksplit ranges whose fp32 partial sums a reduction adds up (with the
+        // bias) -- so the rows that would leave most CUs idle in a last round
+        // spread over all of them.
+        const IgemmCfg &cm = igemm_cfg(p.variant);
+        const int per_m = a.n_tiles * a.phases * a.G;
+        IgArgs main = a;
+        main.m_tiles = (int)(tail & 0xffffff);
+        main.total_tiles = main.m_tiles * per_m;
+        IgArgs t = a;
+        t.row0 = main.m_tiles * cm.bm;
+        t.m_tiles = (int)cdiv(a.rows - t.row0, igemm_cfg(IG_TAIL_CFG).bm);
+        t.ksplit = vec ? (int)(tail >> 24) : 1;
+        t.total_tiles = t.m_tiles * per_m * t.ksplit;
+        if (t.ksplit > 1)
+            t.part = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + a.w_bytes);
+        e = main.m_tiles > 0 ? run(main, p.variant) : hipSuccess;
+        if (e == hipSuccess) e = run(t, IG_TAIL_CFG);
+        if (e == hipSuccess && t.ksplit > 1) {
+            const int64_t total = (int64_t)a.G * a.phases * (a.rows - t.row0) * ((a.Cog + 3) / 4);
+            const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(total, 256), 8192);
+            switch (d.dtype) {
+            case CONV_F16: hipLaunchKernelGGL((igemm_splitk_reduce<f16_t>), dim3(blocks), dim3(256), 0, s, t); break;
+            default: hipLaunchKernelGGL((igemm_splitk_reduce<bf16_t>), dim3(blocks), dim3(256), 0, s, t); break;
+            }
+            e = hipGetLastError();
+        }
+    } else {
+        e = run(a, p.variant);
     }
     return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
 }

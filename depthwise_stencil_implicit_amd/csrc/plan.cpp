@@ -238,12 +238,19 @@ bool geom_igemm(const conv_desc &d, conv_plan_t &p)
     double best_cost = 0;
     const int lo = d.dtype == CONV_F32 ? 5 : 0, hi = d.dtype == CONV_F32 ? 5 : igemm_num_cfgs() - 1;
     for (int v = lo; v <= hi; ++v) {
-        if ((v == 5) != (d.dtype == CONV_F32)) continue;
+        if ((v == 5) != (d.dtype == CONV_F32) || v == IG_TAIL_CFG) continue;
         const IgemmCfg &c = igemm_cfg(v);
         const int64_t lds = (int64_t)c.stages * (c.bm + c.bn) * 128;
         const int64_t occ = lds > 80 * 1024 ? 1 : 2;
         const int64_t tiles = d.groups * phases * cdiv(rows, c.bm) * cdiv(cog(d) > 0 ? cog(d) : 1, c.bn);
-        const double rounds = (double)cdiv(tiles, 256 * occ);
+        double rounds = (double)cdiv(tiles, kIgCus * occ);
+        // A sparse last round of one-per-CU tiles runs split over all CUs (the
+        // 64-row split-K launch below), at about a third of the efficiency.
+        const IgemmCfg &ct = igemm_cfg(IG_TAIL_CFG);
+        const int64_t left = tiles % kIgCus;
+        if (occ == 1 && d.dtype != CONV_F32 && c.bm > ct.bm && c.bn == ct.bn && tiles > kIgCus && left > 0 &&
+            4 * left <= kIgCus)
+            rounds = (double)(tiles / kIgCus) + 3.0 * (double)left / kIgCus;
         // CU time of one resident round, over the schedule's measured efficiency.
         const double cost = rounds * occ * c.bm * c.bn / (double)c.eff;
         if (best < 0 || cost < best_cost) {
@@ -274,8 +281,40 @@ bool geom_igemm(const conv_desc &d, conv_plan_t &p)
     p.grid[0] = d.groups * phases * p.tile[IG_MTILES] * p.tile[IG_NTILES];
     p.block = 64 * c.wm * c.wn;
     p.lds_bytes = (int32_t)(c.stages * (c.bm + c.bn) * 128);
-    p.workspace_bytes = round_up(d.groups * cog_pad * taps * cig_pad * es, 256);
+    p.workspace_bytes = igemm_wbytes(d.groups, cog_pad, taps, cig_pad, es);
     if (p.workspace_bytes >= kI32) return false;   // 32-bit buffer offsets into the weights
+    // Rows whose tiles would leave a last round that keeps at most a quarter
+    // of the CUs busy go to 64-row tiles with their K split over the CUs
+    // (fp32 partial sums in the workspace after the weights).
+    p.tile[IG_TAIL] = 0;
+    const IgemmCfg &ct = igemm_cfg(IG_TAIL_CFG);
+    const int64_t per_m = p.tile[IG_NTILES] * phases * d.groups;
+    const int64_t total = p.grid[0];
+    const int64_t left = total % kIgCus;
+    if (d.dtype != CONV_F32 && c.bm > ct.bm && c.bn == ct.bn && total > kIgCus && left > 0 && 4 * left <= kIgCus) {
+        const int64_t m_tail = cdiv(left, per_m);
+        const int64_t main_m = p.tile[IG_MTILES] - m_tail;
+        const int64_t tail_rows = rows - main_m * c.bm;
+        const int64_t tail_tiles = cdiv(tail_rows, ct.bm) * per_m;
+        // Fewest K steps of any phase (valid taps x 64-channel blocks).
+        int64_t min_taps = 1;
+        for (int i = 0; i < d.spatial; ++i) {
+            int64_t lo = d.k[i];
+            if (d.transposed) {
+                for (int64_t rho = 0; rho < d.stride[i]; ++rho) {
+                    int64_t cnt = 0;
+                    for (int64_t t = 0; t < d.k[i]; ++t)
+                        if ((((rho + d.padding_before[i] - t * d.dilation[i]) % d.stride[i]) + d.stride[i]) % d.stride[i] == 0) ++cnt;
+                    lo = std::min(lo, cnt);
+                }
+            }
+            min_taps *= lo;
+        }
+        const int64_t min_steps = min_taps * (cig_pad / ct.bk);
+        int64_t ks = std::max<int64_t>(1, std::min<int64_t>({8, kIgCus / std::max<int64_t>(tail_tiles, 1), min_steps}));
+        p.tile[IG_TAIL] = main_m | (ks << 24);
+        if (ks > 1) p.workspace_bytes += round_up(ks * d.groups * phases * tail_rows * cog_pad * 4, 256);
+    }
     // 16-byte buffer-load path: contiguous, chunk-aligned channels, span < 2 GB.
     const int64_t ev = 16 / es;
     bool vec = d.x.strides[1] == 1 && cig(d) % ev == 0 && d.x.strides[0] % ev == 0 && p.tile[IG_XBYTES] > 0;

@@ -269,3 +269,49 @@ def test_aten_style_overloads_match_reference():
     yr2, A2 = oracle.conv(x.double().numpy(), w.permute(1, 0, 2).double().numpy(), None, padding_before=2,
                           padding_after=2)
     assert_close(y2, yr2, A2, EPS["bf16"], "convolution")
+
+
+# ------------------------------------------------ rows past the full rounds --
+
+def _tail_case(transposed):
+    if not transposed:
+        # 22 x 56 x 56 rows in 256-row tiles: 270 tiles, 14 past one round of
+        # 256 CUs -> their rows run as split-K 64-row tiles.
+        return synth.random_case(7001, rank=2, transposed=False, dtype="bf16", channels_last=True, N=22,
+                                 C_in=256, C_out=256, groups=1, L=[56, 56], k=[3, 3], stride=[1, 1],
+                                 padding_before=[1, 1], padding_after=[1, 1], dilation=[1, 1],
+                                 output_padding=[0, 0], has_bias=True)
+    # Transposed 1-D, stride 2: 2 phases x 32 row tiles x 2 column tiles ...
+    return synth.random_case(7002, rank=1, transposed=True, dtype="bf16", channels_last=True, N=1,
+                             C_in=512, C_out=512, groups=1, L=[66000], k=[4], stride=[2], padding_before=[1],
+                             padding_after=[2], dilation=[1], output_padding=[0], has_bias=True)
+
+
+@pytest.mark.parametrize("transposed", [False, True], ids=["forward", "transposed"])
+def test_tail_rows_split_k(transposed):
+    """Calls whose last round of full-size tiles would be sparse: the rows past
+    the full rounds (64-row tiles with K split, partial sums reduced with the
+    bias) against the reference, sampled densely there and at the boundary."""
+    wl = _tail_case(transposed)
+    _flush(f"tail rows: {_desc(wl)}")
+    x, w, b, y = run_gpu(wl)
+    plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in expand_kw(wl).items()
+                                                  if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=wl.transposed)).plan
+    tail = int(plan.tile[7])
+    if not transposed:
+        assert tail != 0 and (tail >> 24) > 1, "shape chosen to exercise the split-K rows"
+    xr, wr, br = ref_inputs(x, w, b)
+    rng = np.random.default_rng(11)
+    shape = tuple(y.shape)
+    n = 12000
+    pts = np.stack([rng.integers(0, s, n) for s in shape], axis=1)
+    # Half the points in the last images / positions (the rows past the full rounds).
+    if not transposed:
+        pts[: n // 2, 0] = shape[0] - 1 - rng.integers(0, 2, n // 2)
+    else:
+        pts[: n // 2, 2] = shape[2] - 1 - rng.integers(0, 9000, n // 2)
+    yr, A = oracle.conv_points(xr, wr, br, pts, **expand_kw(wl))
+    yg = y.detach()[tuple(torch.as_tensor(pts.T, device=y.device))].double().cpu().numpy()
+    bad = ~(np.abs(yg - yr) <= EPS[wl.dtype] * A)
+    assert not bad.any(), f"{int(bad.sum())} outputs outside the bound, e.g. {pts[bad][:3].tolist()}"
