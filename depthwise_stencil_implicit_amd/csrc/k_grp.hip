@@ -162,9 +162,12 @@ __global__ __launch_bounds__(256) void grp_kernel(GpArgs a)
 // every tap unrolled (ds_read immediate column offsets).
 struct GpPers {
     int32_t xs_n, xs_c, xs_h, xs_w, ys_n, ys_c, ys_h, ys_w;
-    int32_t x_bytes;   // buffer range of x
-    int32_t wpg;       // workgroups per group
+    int32_t x_bytes, y_bytes;   // buffer ranges of x and y
+    int32_t wpg;                // workgroups per group
+    uint32_t m_plane, m_iw;     // ceil(2^32 / plane), ceil(2^32 / IW): quotients of operands below 2^16
 };
+
+__device__ __forceinline__ int qdiv(int a, uint32_t m) { return (int)__umulhi((uint32_t)a, m); }
 
 template <typename T, int KH, int KW, int P, int JB>
 __global__ __launch_bounds__(256) void grp_pers_kernel(GpArgs a, GpPers f)
@@ -209,8 +212,8 @@ __global__ __launch_bounds__(256) void grp_pers_kernel(GpArgs a, GpPers f)
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
         const int e = tid + 256 * k;
-        const int p = e / plane, i = e - p * plane;
-        const int r = i / a.IW, q = i - r * a.IW;
+        const int p = qdiv(e, f.m_plane), i = e - p * plane;
+        const int r = qdiv(i, f.m_iw), q = i - r * a.IW;
         soff[k] = r * f.xs_h + q * f.xs_w + 2 * p * f.xs_c;
         // bit 31: slot unused; bit 30: no partner channel; then r << 15 | q.
         srq[k] = (e >= words ? (1 << 31) : 0) | (2 * p + 1 >= a.Cig ? (1 << 30) : 0) | (r << 15) | q;
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(256) void grp_pers_kernel(GpArgs a, GpPers f)
     const int tx = tid - ty * a.tpr;
     const bool active = ty < a.TH;
     const T *__restrict__ Bp = static_cast<const T *>(a.b);
-    T *__restrict__ Y = static_cast<T *>(a.y);
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, f.y_bytes, 0x00020000);
     int xa[KH][P];
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh)
@@ -305,13 +308,22 @@ __global__ __launch_bounds__(256) void grp_pers_kernel(GpArgs a, GpPers f)
                             for (int jj = 0; jj < JB; ++jj) acc[p][jj] = dot2<T>(xv[p], wv[jj], acc[p][jj]);
                     }
             }
+            // 16-bit buffer stores at 32-bit offsets; absent columns and
+            // channels get an out-of-range vector offset (dropped) -- the
+            // scalar offset, which the range check does not cover, stays a
+            // real channel offset.
+            int yo[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                yo[p] = ow0 + p * a.tpr < a.OW ? (ybase + (g * a.Cog + j0) * f.ys_c + p * a.tpr * f.ys_w) * ES
+                                               : 0x7fffff00;
 #pragma unroll
             for (int jj = 0; jj < JB; ++jj) {
-                if (j0 + jj >= a.Cog) break;
-                T *yc = Y + ybase + (g * a.Cog + j0 + jj) * f.ys_c;
+                const bool cok = j0 + jj < a.Cog;
 #pragma unroll
                 for (int p = 0; p < P; ++p)
-                    if (ow0 + p * a.tpr < a.OW) yc[p * a.tpr * f.ys_w] = from_f32<T>(acc[p][jj]);
+                    __builtin_amdgcn_raw_buffer_store_b16(from_f32<T>(acc[p][jj]).u, yr, cok ? yo[p] : 0x7fffff00,
+                                                          cok ? jj * f.ys_c * ES : 0, 0);
             }
         }
     }
@@ -432,7 +444,7 @@ int launch_grp(const conv_plan_t &p, const void *x, const void *w, const void *b
     };
     const bool ext = (a.KW == 3 || a.KW == 5 || a.KW == 7) && (a.KH == 1 || a.KH == a.KW);
     const int64_t tiles = (int64_t)a.N * a.tiles_h * a.tiles_w;
-    if (ext && a.DH == 1 && a.DW == 1 && span(d.x) * esize(d.dtype) < lim && span(p.y) < lim &&
+    if (ext && a.DH == 1 && a.DW == 1 && span(d.x) * esize(d.dtype) < lim && span(p.y) * esize(d.dtype) < lim &&
         (int64_t)a.npairs * a.IH * a.IW <= 8 * 256 && a.IH < 32768 && a.IW < 32768) {
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -447,6 +459,9 @@ int launch_grp(const conv_plan_t &p, const void *x, const void *w, const void *b
         f.ys_h = (int32_t)a.ys_h;
         f.ys_w = (int32_t)a.ys_w;
         f.x_bytes = (int32_t)(span(d.x) * esize(d.dtype));
+        f.y_bytes = (int32_t)(span(p.y) * esize(d.dtype));
+        f.m_plane = (uint32_t)(((1ULL << 32) + (uint64_t)a.IH * a.IW - 1) / ((uint64_t)a.IH * a.IW));
+        f.m_iw = (uint32_t)(((1ULL << 32) + a.IW - 1) / a.IW);
         // Four workgroups per CU, spread over the groups.
         f.wpg = (int32_t)std::max<int64_t>(1, std::min<int64_t>(tiles, cdiv(4LL * cus, a.G)));
         const dim3 pgrid((unsigned)((int64_t)a.G * f.wpg));
