@@ -94,6 +94,26 @@ template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi)
 
 template <typename T> __device__ __forceinline__ T load_elem(const T *p) { return *p; }
 
+// Raw buffer descriptor (the same fields __builtin_amdgcn_make_buffer_rsrc
+// fills: base, stride 0, byte range, the flags word) as an SGPR quad for
+// inline assembly.
+__device__ __forceinline__ u32x4 raw_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// 16-byte raw buffer store followed by two wait states.  The hardware may
+// still be reading the data registers of a store wider than 8 bytes when the
+// next instruction issues, and a VALU write to them in that cycle changes
+// what is stored (seen on gfx950: the next store's address landed in the
+// first word of the previous one's data, and the compiler did not pad the
+// pair).  In one asm block nothing can be scheduled between the two.
+__device__ __forceinline__ void store_b128(u32x4 v, u32x4 rsrc, int voff, int soff)
+{
+    asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 1" ::"v"(v), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+
 // 8-element MFMA step: D(16x16) += A(16x32) * B(32x16) for 2-byte types, with
 // the A/B fragments holding 8 consecutive K elements of one row / column.
 __device__ __forceinline__ void mma_16x16x32(const uint4 &a, const uint4 &b, f32x4 &c, bf16_t)

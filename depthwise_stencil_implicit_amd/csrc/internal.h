@@ -21,6 +21,11 @@ inline int64_t esize(int32_t dtype) { return dtype == CONV_F32 ? 4 : 2; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
+// Grouped-stencil schedules (kernel CONV_K_GRP, plan.variant): the vector
+// dot2 schedules, or the matrix-core plane schedule for small 3x3 groups
+// whose planes are contiguous.
+enum { GRP_SCHED_VALU = 0, GRP_SCHED_MMA = 1 };
+
 // Implicit GEMM schedule table (kernel CONV_K_IGEMM / CONV_K_IGEMM_T).
 struct IgemmCfg {
     int bm, bn, bk;     // workgroup tile: rows, columns, K per step

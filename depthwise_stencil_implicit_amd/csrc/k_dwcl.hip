@@ -132,26 +132,6 @@ __device__ __forceinline__ void wg_barrier()
     asm volatile("" ::: "memory");
 }
 
-// Raw buffer descriptor (the same fields __builtin_amdgcn_make_buffer_rsrc
-// fills: base, stride 0, byte range, the flags word) as an SGPR quad for
-// inline assembly.
-__device__ __forceinline__ u32x4 raw_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-// 16-byte raw buffer store followed by two wait states.  The hardware may
-// still be reading the data registers of a store wider than 8 bytes when the
-// next instruction issues, and a VALU write to them in that cycle changes
-// what is stored (seen on gfx950: the next store's address landed in the
-// first word of the previous one's data, and the compiler did not pad the
-// pair).  In one asm block nothing can be scheduled between the two.
-__device__ __forceinline__ void store_b128(u32x4 v, u32x4 rsrc, int voff, int soff)
-{
-    asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 1" ::"v"(v), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory");
-}
-
 // Packed 16-bit column pairs of one channel, built with one byte permute:
 // lo(a, b) = (a.lo, b.lo) and hi(a, b) = (a.hi, b.hi) for channel words a, b
 // of two neighbouring columns.

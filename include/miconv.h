@@ -78,7 +78,9 @@ typedef enum conv_kernel {
     CONV_K_AUTO = -1,
     CONV_K_DW_CL = 1,   /* depthwise, channel-contiguous input: per-lane register sliding window */
     CONV_K_PLANE = 2,   /* depthwise / few-channel grouped, any layout: LDS halo tile, fan-out */
-    CONV_K_GRP = 3,     /* few-channel grouped, half types: packed dot2 over input-channel pairs */
+    CONV_K_GRP = 3,     /* few-channel grouped, half types: packed dot2 over input-channel pairs, or
+                           (plan variant 1) small 3x3 groups with contiguous planes as a per-group
+                           matrix-core contraction over (tap, channel) */
     CONV_K_REDUCE = 4,  /* depthwise / few-channel grouped, few outputs: wavefront reduction over taps */
     CONV_K_IGEMM = 5,   /* implicit GEMM, forward: on-the-fly im2col tile in LDS, MFMA */
     CONV_K_IGEMM_T = 6  /* implicit GEMM with the transposed gather, phase-split by stride */

@@ -119,6 +119,116 @@ def _geom_cases(kind, n, seed):
     return out
 
 
+def _grp_flat_cases(n, seed):
+    """Grouped calls inside the flat grouped schedule's domain: 3x3 with equal
+    strides 1 or 2, or one row of 1, 3, 5 or 7 taps at stride 1 or 2, unit
+    dilation; any channel counts, pads, layouts and ragged sizes."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        i = len(out)
+        dtype = ["f16", "bf16"][i % 2]
+        r = 2 if i % 3 else 1
+        ss = int(rng.integers(1, 3))
+        if r == 2:
+            k = [3, 3] if i % 4 else [1, int(rng.choice([1, 3, 5, 7]))]
+            s = [ss, ss] if k[0] == 3 else [int(rng.integers(1, 4)), ss]
+            L = [int(rng.integers(3, 30)), int(rng.integers(max(3, k[1]), 70))]
+        else:
+            k = [int(rng.choice([1, 3, 5, 7]))]
+            s = [ss]
+            L = [int(rng.integers(k[0], 300))]
+        cig = int(rng.integers(1, 9))
+        groups = int(rng.integers(2, 7))
+        cog = int(rng.choice([1, 2, 3, 8, 9, 16, 17]))
+        pb = [int(rng.integers(0, kk)) if kk > 1 else 0 for kk in k]
+        pa = [int(rng.integers(0, kk)) if kk > 1 else 0 for kk in k]
+        if not all(Li + pbi + pai - (ki - 1) - 1 >= 0 for Li, pbi, pai, ki in zip(L, pb, pa, k)):
+            continue
+        out.append(synth.random_case(5000 + i + 100 * seed, rank=r, transposed=False, dtype=dtype,
+                                     channels_last=bool(rng.integers(0, 2)), N=int(rng.integers(1, 4)),
+                                     C_in=groups * cig, C_out=groups * cog, groups=groups, L=L, k=k, stride=s,
+                                     padding_before=pb, padding_after=pa, dilation=[1] * r,
+                                     output_padding=[0] * r, has_bias=bool(rng.integers(0, 2))))
+    return out
+
+
+GRP_FLAT = _grp_flat_cases(24, 7)
+
+
+def _grp_plane_cases(n, seed):
+    """Grouped 3x3 calls inside the one-plane-per-workgroup schedule's domain:
+    contiguous NCHW x and y whose per-group planes are whole 16-byte chunks,
+    equal strides 1 or 2, unit dilation, small planes; any pads, channel
+    counts (odd ones included) and bias."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        i = len(out)
+        s = int(rng.integers(1, 3))
+        cig = int(rng.integers(1, 9))
+        cog = int(rng.choice([1, 2, 3, 4, 8, 9, 16]))
+        groups = int(rng.integers(1, 5)) * 2
+        H, W = int(rng.integers(3, 33)), int(rng.integers(3, 33))
+        pb = [int(rng.integers(0, 3)) for _ in range(2)]
+        pa = [int(rng.integers(0, 3)) for _ in range(2)]
+        OH = (H + pb[0] + pa[0] - 3) // s + 1
+        OW = (W + pb[1] + pa[1] - 3) // s + 1
+        if OH < 1 or OW < 1:
+            continue
+        N = int(rng.integers(1, 4))
+        threads = -(-cog * -(-OH // 2) * -(-OW // 7) // 64) * 64
+        if (cig * H * W) % 8 or (cog * OH * OW) % 8 or threads > 512 or -(-(cig * H * W * 2) // 16) > threads:
+            continue
+        out.append(synth.random_case(6000 + i + 100 * seed, rank=2, transposed=False,
+                                     dtype=["f16", "bf16"][i % 2], channels_last=False, N=N,
+                                     C_in=groups * cig, C_out=groups * cog, groups=groups, L=[H, W], k=[3, 3],
+                                     stride=[s, s], padding_before=pb, padding_after=pa, dilation=[1, 1],
+                                     output_padding=[0, 0], has_bias=bool(rng.integers(0, 2))))
+    return out
+
+
+GRP_PLANE = _grp_plane_cases(24, 8)
+
+
+def _grp_mma_cases(n, seed):
+    """Grouped 3x3 calls inside the matrix-core plane schedule's domain:
+    contiguous NCHW planes in whole 16-byte (input) and 8-byte (output)
+    pieces, output rows of a multiple of 4 columns, up to 16 output
+    channels per group, equal strides 1 or 2; odd channel counts and both
+    channel-slot widths (Cig <= 4 and 5..8)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        i = len(out)
+        s = int(rng.integers(1, 3))
+        cig = int(rng.integers(1, 9))
+        cog = int(rng.choice([1, 2, 3, 5, 8, 12, 16]))
+        groups = int(rng.integers(1, 6))
+        H, W = int(rng.integers(3, 40)), int(rng.integers(3, 40))
+        pb = [int(rng.integers(0, 3)) for _ in range(2)]
+        pa = [int(rng.integers(0, 3)) for _ in range(2)]
+        OH = (H + pb[0] + pa[0] - 3) // s + 1
+        OW = (W + pb[1] + pa[1] - 3) // s + 1
+        if OH < 1 or OW < 1 or groups * cig < 2:
+            continue
+        if (cig * H * W) % 8 or OW % 4 or cig * H * W > 4096 or cog * OH * OW > 8192:
+            continue
+        cp = 4 if cig <= 4 else 8
+        IHh, IWh = (OH - 1) * s + 3, (OW - 1) * s + 3
+        if IHh * IWh * cp * 2 + cog * OH * OW * 2 + 64 > 64 * 1024:
+            continue
+        out.append(synth.random_case(7000 + i + 100 * seed, rank=2, transposed=False,
+                                     dtype=["f16", "bf16"][i % 2], channels_last=False,
+                                     N=int(rng.integers(1, 4)), C_in=groups * cig, C_out=groups * cog,
+                                     groups=groups, L=[H, W], k=[3, 3], stride=[s, s], padding_before=pb,
+                                     padding_after=pa, dilation=[1, 1], output_padding=[0, 0],
+                                     has_bias=bool(rng.integers(0, 2))))
+    return out
+
+
+GRP_MMA = _grp_mma_cases(20, 9)
+
 SWEEP = {kind: _geom_cases(kind, n, seed) for kind, n, seed in
          [("igemm", 24, 1), ("igemm_t", 24, 2), ("plane", 24, 3), ("dw_cl", 24, 4), ("reduce", 9, 5),
           ("grp", 24, 6)]}
@@ -136,6 +246,12 @@ def _desc(wl):
 def test_forced_kernel_sweep(kind, wl):
     _flush(f"sweep {kind}: {_desc(wl)}")
     check_full(wl, force=kind)
+
+
+@pytest.mark.parametrize("wl", GRP_FLAT + GRP_PLANE + GRP_MMA, ids=lambda v: v.name)
+def test_grp_flat_sweep(wl):
+    _flush(f"sweep grp (flat / plane domain): {_desc(wl)}")
+    check_full(wl, force="grp")
 
 
 # ------------------------------------------------------------- exactness --
@@ -156,6 +272,10 @@ EXACT_CASES = [
     ("grp", synth.random_case(13, rank=1, transposed=False, dtype="f16", channels_last=True, N=3, C_in=14,
                               C_out=21, groups=7, L=[33], k=[5], stride=[1], padding_before=[2],
                               padding_after=[1], dilation=[2], output_padding=[0], has_bias=False)),
+    ("grp", synth.random_case(14, rank=2, transposed=False, dtype="f16", channels_last=False, N=3, C_in=15,
+                              C_out=45, groups=5, L=[14, 19], k=[3, 3], stride=[2, 2],
+                              padding_before=[1, 0], padding_after=[0, 1], dilation=[1, 1],
+                              output_padding=[0, 0], has_bias=True)),
     ("igemm", synth.random_case(9, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=64,
                                 C_out=48, groups=1, L=[9, 10], k=[3, 3], stride=[1, 2],
                                 padding_before=[1, 0], padding_after=[2, 1], dilation=[1, 1],
@@ -186,7 +306,9 @@ def test_exact_results(kind, wl, values):
 
 # ------------------------------------------------------------ memory safety --
 
-@pytest.mark.parametrize("kind,wl", [(k, ws[i]) for k, ws in SWEEP.items() for i in (0, 1)],
+@pytest.mark.parametrize("kind,wl", [(k, ws[i]) for k, ws in SWEEP.items() for i in (0, 1)] +
+                         [("grp", GRP_FLAT[i]) for i in (0, 1, 2)] + [("grp", GRP_PLANE[i]) for i in (0, 1, 2)] +
+                         [("grp", GRP_MMA[i]) for i in (0, 1, 2)],
                          ids=lambda v: v if isinstance(v, str) else v.name)
 def test_writes_stay_inside_output(kind, wl):
     """y sits inside a canary-filled buffer and starts as NaN: afterwards the
