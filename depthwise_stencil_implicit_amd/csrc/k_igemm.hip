@@ -531,28 +531,43 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     }
     const int kb = ks * nall / a.ksplit;
     const int nsteps = (ks + 1) * nall / a.ksplit - kb;
+    // Byte offsets of this lane's A rows at the current tap (channel chunk
+    // kc of channel block 0), or the out-of-range marker for an absent
+    // input position: recomputed only when the tap changes.  The channel
+    // block rides in the scalar offset; the marker exceeds the buffer range
+    // with any scalar offset added.
+    int a_off[A_IT];
+    auto set_tap = [&]() {
+#pragma unroll
+        for (int i = 0; i < A_IT; ++i) {
+            const int i0 = a_b0[i] + it_o0, i1 = a_b1[i] + it_o1, i2 = a_b2[i] + it_o2;
+            const bool inb = a_ok[i] && (unsigned)i0 < (unsigned)a.L[0] && (unsigned)i1 < (unsigned)a.L[1] &&
+                             (unsigned)i2 < (unsigned)a.L[2];
+            const int pix = a_nb[i] + i0 * a.xs_l[0] + i1 * a.xs_l[1] + i2 * a.xs_l[2];
+            a_off[i] = inb ? (pix + kc * EV) * ES : 0x7fffff00;
+        }
+    };
     auto advance = [&]() {
         if (++it_cb == ncb) {
             it_cb = 0;
             ++it_t;
             while (it_t < a.taps && !tap_offsets(it_t, it_o0, it_o1, it_o2)) ++it_t;
+            set_tap();
         }
     };
+    set_tap();
     for (int k = 0; k < kb; ++k) advance();
+    // Channel chunks past Cig (a padded last block) read zeros.
+    const bool cig_full = a.Cig % BK == 0;
 
     auto issue = [&](unsigned char *A) {
         unsigned char *B = A + BM * RB;
         const int c = it_cb * BK + kc * EV;
+        const bool cok = cig_full || c < a.Cig;
 #pragma unroll
-        for (int i = 0; i < A_IT; ++i) {
-            const int i0 = a_b0[i] + it_o0, i1 = a_b1[i] + it_o1, i2 = a_b2[i] + it_o2;
-            const bool inb = a_ok[i] && (unsigned)i0 < (unsigned)a.L[0] && (unsigned)i1 < (unsigned)a.L[1] &&
-                             (unsigned)i2 < (unsigned)a.L[2] && c < a.Cig;
-            const int pix = a_nb[i] + i0 * a.xs_l[0] + i1 * a.xs_l[1] + i2 * a.xs_l[2];
-            const int off = inb ? (pix + c) * ES : 0x7fffff00;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(A + (i * NW * RPI + wave * RPI) * RB), 16, off,
-                                                     0, 0, 0);
-        }
+        for (int i = 0; i < A_IT; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(A + (i * NW * RPI + wave * RPI) * RB), 16,
+                                                     cok ? a_off[i] : 0x7fffff00, it_cb * BK * ES, 0, 0);
         const int step_off = wtile0 + (it_t * a.cig_pad + it_cb * BK) * ES;
 #pragma unroll
         for (int i = 0; i < B_IT; ++i)
@@ -569,10 +584,10 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const unsigned char *A) {
+    auto compute = [&](const unsigned char *A, int k0, int k1) {
         const unsigned char *B = A + BM * RB;
 #pragma unroll
-        for (int kk = 0; kk < KC / 4; ++kk) {
+        for (int kk = k0; kk < k1; ++kk) {
             uint4 af[FM], bf[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -586,9 +601,11 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
                 for (int j = 0; j < FN; ++j) mma_16x16x32(bf[j], af[i], acc[i][j], T{});
         }
     };
-    // One step: wait for this wave's loads of the stage, barrier, refill the
-    // stage read one step ago, multiply.  Stages are named arrays, so after
-    // inlining each access targets one known LDS object.
+    // One step: wait for this wave's loads of the stage, barrier, multiply
+    // the first half of the stage, refill the stage read one step ago (its
+    // address work then overlaps the MFMAs in flight), multiply the rest.
+    // Stages are named arrays, so after inlining each access targets one
+    // known LDS object.
     auto wait_own = [&](int s) {
         if (s + STAGES - 2 < nsteps) {
             constexpr int N = (STAGES - 2) * LPS;
@@ -597,12 +614,14 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
             __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
         }
     };
+    constexpr int KH1 = KC / 8 > 0 ? KC / 8 : 1;
 #define MICONV_DMA_STEP(CUR, NEXT, S)                 \
     if ((S) < nsteps) {                               \
         wait_own(S);                                  \
         lds_barrier();                                \
+        compute(CUR, 0, KH1);                         \
         if ((S) + STAGES - 1 < nsteps) issue(NEXT);   \
-        compute(CUR);                                 \
+        compute(CUR, KH1, KC / 4);                    \
     }
 
     // Prologue: steps 0 .. STAGES-2 into stages 0 .. STAGES-2.
