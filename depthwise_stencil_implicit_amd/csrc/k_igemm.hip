@@ -584,21 +584,52 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const unsigned char *A, int k0, int k1) {
+    // Fragment reads interleaved with the MFMAs, as one stream over the
+    // step's K slices: the first slice's B fragments and first two A
+    // fragments are read up front, then each group of FN MFMAs (one A
+    // fragment) is followed by the read of the A fragment two groups ahead --
+    // and, two groups before a slice starts, by that slice's B fragments --
+    // so every read has two MFMA groups to land.  The scheduling groups pin
+    // that order (the compiler's own schedule reads one A fragment and waits
+    // for it before every group).  The refill of the stage read one step ago
+    // is issued after the first slice's MFMAs.
+    constexpr int KSL = KC / 4;                 // K slices (of 32) per step
+    auto compute = [&](const unsigned char *A, unsigned char *next, bool refill) {
         const unsigned char *B = A + BM * RB;
-#pragma unroll
-        for (int kk = k0; kk < k1; ++kk) {
-            uint4 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const uint4 *>(A + swz_k<KC>(wr * TM + i * 16 + lr, kk * 4 + lg));
+        uint4 af[KSL][FM], bf[KSL][FN];
+        auto read_a = [&](int kk, int i) {
+            af[kk][i] = *reinterpret_cast<const uint4 *>(A + swz_k<KC>(wr * TM + i * 16 + lr, kk * 4 + lg));
+        };
+        auto read_b = [&](int kk) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bf[j] = *reinterpret_cast<const uint4 *>(B + swz_k<KC>(wc * TN + j * 16 + lr, kk * 4 + lg));
+                bf[kk][j] = *reinterpret_cast<const uint4 *>(B + swz_k<KC>(wc * TN + j * 16 + lr, kk * 4 + lg));
+        };
+        read_b(0);
+        read_a(0, 0);
+        if constexpr (FM > 1) read_a(0, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, FN + (FM > 1 ? 2 : 1), 0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+        for (int kk = 0; kk < KSL; ++kk) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) mma_16x16x32(bf[j], af[i], acc[i][j], T{});
+            for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) mma_16x16x32(bf[kk][j], af[kk][i], acc[i][j], T{});
+                __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+                const int g2 = kk * FM + i + 2;       // the A fragment two groups ahead
+                if (g2 < KSL * FM) {
+                    const int k2 = g2 / FM, i2 = g2 % FM;
+                    if (i2 == 0) {
+                        read_b(k2);
+                        read_a(k2, i2);
+                        __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);
+                    } else {
+                        read_a(k2, i2);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                }
+                if (kk == 0 && i == FM - 1 && refill) issue(next);
+            }
         }
     };
     // One step: wait for this wave's loads of the stage, barrier, multiply
@@ -614,14 +645,11 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
             __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
         }
     };
-    constexpr int KH1 = KC / 8 > 0 ? KC / 8 : 1;
 #define MICONV_DMA_STEP(CUR, NEXT, S)                 \
     if ((S) < nsteps) {                               \
         wait_own(S);                                  \
         lds_barrier();                                \
-        compute(CUR, 0, KH1);                         \
-        if ((S) + STAGES - 1 < nsteps) issue(NEXT);   \
-        compute(CUR, KH1, KC / 4);                    \
+        compute(CUR, NEXT, (S) + STAGES - 1 < nsteps); \
     }
 
     // Prologue: steps 0 .. STAGES-2 into stages 0 .. STAGES-2.
