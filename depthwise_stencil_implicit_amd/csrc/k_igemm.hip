@@ -808,30 +808,42 @@ __global__ __launch_bounds__(256) void igemm_splitk_reduce(IgArgs a)
 }
 
 // Weight repack: w (any strides) -> [G][Cog_pad][taps][Cig_pad], zero padded.
+// One thread per 16-byte chunk of a packed row (Cig_pad is a multiple of the
+// chunk): 32-bit index arithmetic (the packed weights stay below 2 GiB, the
+// planner checks) once per chunk, the chunk's elements gathered at w's
+// strides and stored as one vector.
 template <typename T>
-__global__ void igemm_repack(const T *__restrict__ w, T *__restrict__ wr, int64_t total, int32_t Cig, int32_t Cog,
+__global__ void igemm_repack(const T *__restrict__ w, T *__restrict__ wr, int32_t chunks, int32_t Cig, int32_t Cog,
                              int32_t cig_pad, int32_t cog_pad, int32_t taps, int32_t K1, int32_t K2, int64_t ws0,
                              int64_t ws1, int64_t wk0, int64_t wk1, int64_t wk2, int32_t transposed)
 {
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int c = (int)(idx % cig_pad);
-        int64_t r = idx / cig_pad;
-        const int t = (int)(r % taps);
+    constexpr int EV = 16 / sizeof(T);
+    const int cpr = cig_pad / EV;   // chunks per packed row (g, j, t)
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < chunks; q += gridDim.x * blockDim.x) {
+        const int cc = q % cpr;
+        int r = q / cpr;
+        const int t = r % taps;
         r /= taps;
-        const int j = (int)(r % cog_pad);
-        const int64_t g = r / cog_pad;
-        T v;
-        __builtin_memset(&v, 0, sizeof(T));
-        if (j < Cog && c < Cig) {
+        const int j = r % cog_pad;
+        const int g = r / cog_pad;
+        T v[EV];
+        __builtin_memset(v, 0, sizeof(v));
+        if (j < Cog) {
             const int t2 = t % K2, t1 = (t / K2) % K1, t0 = t / (K2 * K1);
             const int64_t toff = t0 * wk0 + t1 * wk1 + t2 * wk2;
-            if (!transposed)
-                v = w[(g * Cog + j) * ws0 + (int64_t)c * ws1 + toff];
-            else
-                v = w[(g * Cig + c) * ws0 + (int64_t)j * ws1 + toff];
+            // Forward: w[g*Cog + j][c][t]; transposed: w[g*Cig + c][j][t].
+            const int64_t base = transposed ? (int64_t)g * Cig * ws0 + (int64_t)j * ws1 + toff
+                                            : ((int64_t)g * Cog + j) * ws0 + toff;
+            const int64_t sc = transposed ? ws0 : ws1;
+#pragma unroll
+            for (int e = 0; e < EV; ++e) {
+                const int c = cc * EV + e;
+                if (c < Cig) v[e] = w[base + (int64_t)c * sc];
+            }
         }
-        wr[idx] = v;
+        uint4 u;
+        __builtin_memcpy(&u, v, 16);
+        reinterpret_cast<uint4 *>(wr)[q] = u;
     }
 }
 
@@ -909,9 +921,10 @@ hipError_t launch_repack(const conv_plan_t &p, const void *w, void *ws, hipStrea
     const int r = d.spatial;
     int64_t wk[3] = {0, 0, 0};
     for (int i = 0; i < r; ++i) wk[i] = d.w.strides[2 + i];
-    const int64_t blocks = std::min<int64_t>(cdiv(total, 256), 4096);
+    const int64_t chunks = total / (16 / (int64_t)sizeof(T));
+    const int64_t blocks = std::min<int64_t>(cdiv(chunks, 256), 4096);
     hipLaunchKernelGGL((igemm_repack<T>), dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const T *>(w),
-                       static_cast<T *>(ws), total, (int32_t)(d.C_in / d.groups), (int32_t)(d.C_out / d.groups),
+                       static_cast<T *>(ws), (int32_t)chunks, (int32_t)(d.C_in / d.groups), (int32_t)(d.C_out / d.groups),
                        (int32_t)p.tile[IG_CIG_PAD], (int32_t)p.tile[IG_COG_PAD], (int32_t)taps, (int32_t)d.k[1],
                        (int32_t)d.k[2], d.w.strides[0], d.w.strides[1], wk[0], wk[1], wk[2], d.transposed);
     return hipGetLastError();
