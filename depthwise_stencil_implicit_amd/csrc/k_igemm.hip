@@ -560,10 +560,14 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     // Channel chunks past Cig (a padded last block) read zeros.
     const bool cig_full = a.Cig % BK == 0;
 
-    auto issue = [&](unsigned char *A) {
+    // Loads of the next step into stage A.  A dead issue (past the last
+    // step) loads out of range everywhere, which fills the stage with zeros;
+    // the cursor then runs past the last tap, harmlessly, so that the loads
+    // stay on one path.
+    auto issue = [&](unsigned char *A, bool live) {
         unsigned char *B = A + BM * RB;
         const int c = it_cb * BK + kc * EV;
-        const bool cok = cig_full || c < a.Cig;
+        const bool cok = live && (cig_full || c < a.Cig);
 #pragma unroll
         for (int i = 0; i < A_IT; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(A + (i * NW * RPI + wave * RPI) * RB), 16,
@@ -572,7 +576,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
 #pragma unroll
         for (int i = 0; i < B_IT; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(B + (i * NW * RPI + wave * RPI) * RB), 16,
-                                                     b_off[i], step_off, 0, 0);
+                                                     live ? b_off[i] : 0x7fffff00, step_off, 0, 0);
         advance();
     };
 
@@ -594,16 +598,29 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     // for it before every group).  The refill of the stage read one step ago
     // is issued after the first slice's MFMAs.
     constexpr int KSL = KC / 4;                 // K slices (of 32) per step
+    // This lane's fragment offsets within a stage, per K slice: fragment i
+    // (rows 16 i on) adds the constant 16 i RB, as the swizzle depends only
+    // on the row modulo 16.  The empty asm makes each offset one opaque
+    // value, so every fragment address is the stage plus two terms; a deeper
+    // chain of address arithmetic loses the per-array alias scope of the
+    // stage, and the read then waits for every LDS load in flight.
+    int offa[KSL], offb[KSL];
+#pragma unroll
+    for (int kk = 0; kk < KSL; ++kk) {
+        offa[kk] = swz_k<KC>(wr * TM + lr, kk * 4 + lg);
+        offb[kk] = BM * RB + swz_k<KC>(wc * TN + lr, kk * 4 + lg);
+        asm("" : "+v"(offa[kk]));
+        asm("" : "+v"(offb[kk]));
+    }
     auto compute = [&](const unsigned char *A, unsigned char *next, bool refill) {
-        const unsigned char *B = A + BM * RB;
         uint4 af[KSL][FM], bf[KSL][FN];
         auto read_a = [&](int kk, int i) {
-            af[kk][i] = *reinterpret_cast<const uint4 *>(A + swz_k<KC>(wr * TM + i * 16 + lr, kk * 4 + lg));
+            af[kk][i] = *reinterpret_cast<const uint4 *>(A + offa[kk] + i * 16 * RB);
         };
         auto read_b = [&](int kk) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bf[kk][j] = *reinterpret_cast<const uint4 *>(B + swz_k<KC>(wc * TN + j * 16 + lr, kk * 4 + lg));
+                bf[kk][j] = *reinterpret_cast<const uint4 *>(A + offb[kk] + j * 16 * RB);
         };
         read_b(0);
         read_a(0, 0);
@@ -628,7 +645,13 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
                         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     }
                 }
-                if (kk == 0 && i == FM - 1 && refill) issue(next);
+                if (kk == 0 && i == FM - 1) {
+                    if constexpr (STAGES == 2) {
+                        if (refill) issue(next, true);
+                    } else {
+                        issue(next, refill);
+                    }
+                }
             }
         }
     };
@@ -637,42 +660,51 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     // address work then overlaps the MFMAs in flight), multiply the rest.
     // Stages are named arrays, so after inlining each access targets one
     // known LDS object.
-    auto wait_own = [&](int s) {
-        if (s + STAGES - 2 < nsteps) {
-            constexpr int N = (STAGES - 2) * LPS;
-            __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-        } else {
-            __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-        }
+    auto wait_own = [&]() {
+        constexpr int N = (STAGES - 2) * LPS;
+        __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
     };
-#define MICONV_DMA_STEP(CUR, NEXT, S)                 \
-    if ((S) < nsteps) {                               \
-        wait_own(S);                                  \
-        lds_barrier();                                \
+#define MICONV_DMA_STEP(CUR, NEXT, S)             \
+    {                                             \
+        wait_own();                               \
+        lds_barrier();                            \
         compute(CUR, NEXT, (S) + STAGES - 1 < nsteps); \
     }
 
-    // Prologue: steps 0 .. STAGES-2 into stages 0 .. STAGES-2.
-    if (0 < nsteps) issue(st0);
-    if constexpr (STAGES > 2)
-        if (1 < nsteps) issue(st1);
-    if constexpr (STAGES > 3)
-        if (2 < nsteps) issue(st2);
-
-    for (int s = 0; s < nsteps; s += STAGES) {
-        if constexpr (STAGES == 2) {
+    if constexpr (STAGES == 2) {
+        // Two stages: each step waits for every load in flight, so steps
+        // past the end are simply skipped.
+        if (0 < nsteps) issue(st0, true);
+        for (int s = 0; s < nsteps; s += 2) {
             MICONV_DMA_STEP(st0, st1, s)
-            MICONV_DMA_STEP(st1, st0, s + 1)
-        } else if constexpr (STAGES == 3) {
-            MICONV_DMA_STEP(st0, st2, s)
-            MICONV_DMA_STEP(st1, st0, s + 1)
-            MICONV_DMA_STEP(st2, st1, s + 2)
-        } else {
-            MICONV_DMA_STEP(st0, st3, s)
-            MICONV_DMA_STEP(st1, st0, s + 1)
-            MICONV_DMA_STEP(st2, st1, s + 2)
-            MICONV_DMA_STEP(st3, st2, s + 3)
+            if (s + 1 < nsteps) MICONV_DMA_STEP(st1, st0, s + 1)
         }
+    } else {
+        // Three or four stages.  Every step issues a refill, a dead one past
+        // the last step, and the step count is rounded up to whole rounds of
+        // stages (the extra steps multiply zeros), so that no path through
+        // the loop differs in the loads it has in flight: where such paths
+        // join, the compiler loses track of which stage each pending load
+        // writes and waits for all of them before the next LDS read.  Each
+        // step waits for its own stage only, the later stages still loading.
+        const int nsp = (nsteps + STAGES - 1) / STAGES * STAGES;
+        issue(st0, 0 < nsteps);
+        issue(st1, 1 < nsteps);
+        if constexpr (STAGES > 3) issue(st2, 2 < nsteps);
+        for (int s = 0; s < nsp; s += STAGES) {
+            if constexpr (STAGES == 3) {
+                MICONV_DMA_STEP(st0, st2, s)
+                MICONV_DMA_STEP(st1, st0, s + 1)
+                MICONV_DMA_STEP(st2, st1, s + 2)
+            } else {
+                MICONV_DMA_STEP(st0, st3, s)
+                MICONV_DMA_STEP(st1, st0, s + 1)
+                MICONV_DMA_STEP(st2, st1, s + 2)
+                MICONV_DMA_STEP(st3, st2, s + 3)
+            }
+        }
+        // The dead loads of the last round still write LDS.
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
     }
 #undef MICONV_DMA_STEP
 
