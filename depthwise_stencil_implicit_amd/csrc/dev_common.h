@@ -108,9 +108,16 @@ __device__ __forceinline__ u32x4 raw_rsrc(const void *base, uint32_t bytes)
 // what is stored (seen on gfx950: the next store's address landed in the
 // first word of the previous one's data, and the compiler did not pad the
 // pair).  In one asm block nothing can be scheduled between the two.
+// Stores of whole output lines are non-temporal (nt): a kernel never reads
+// back what it writes, and streaming those lines out of the L2 measured 6-11%
+// faster on the depthwise and grouped kernels.  (Stores of partial lines --
+// the implicit GEMM's 8-byte pieces -- keep the default policy: there the L2
+// merges the pieces, and nt measured 11-15% slower.)
+constexpr int kStoreNT = 2;   // cache-policy operand of the buffer-store builtins: nt
 __device__ __forceinline__ void store_b128(u32x4 v, u32x4 rsrc, int voff, int soff)
 {
-    asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 1" ::"v"(v), "v"(voff), "s"(rsrc), "s"(soff)
+    asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen nt\n\ts_nop 1" ::"v"(v), "v"(voff), "s"(rsrc),
+                 "s"(soff)
                  : "memory");
 }
 

@@ -712,7 +712,7 @@ __global__ __launch_bounds__(512) void grp_lds_kernel(GpArgs a, GpLds f)
             const bool ok = q < f.pieces_out;
             typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
             const u32x2 v = *reinterpret_cast<const u32x2 *>(sout + (ok ? q : 0) * 8);
-            __builtin_amdgcn_raw_buffer_store_b64(v, yr, ok ? yoff + q * 8 : INVALID, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(v, yr, ok ? yoff + q * 8 : INVALID, 0, kStoreNT);
         }
     }
 }
@@ -938,7 +938,7 @@ __global__ __launch_bounds__(256) void grp_mma_kernel(GpArgs a, GpMma f)
             const int q = tid + r * 256;
             const bool ok = q < f.pieces_out;
             const u32x2 v = *reinterpret_cast<const u32x2 *>(sout + (ok ? q : 0) * 8);
-            __builtin_amdgcn_raw_buffer_store_b64(v, yr, ok ? yoff + r * 256 * 8 : INVALID, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(v, yr, ok ? yoff + r * 256 * 8 : INVALID, 0, kStoreNT);
         }
     }
 }
