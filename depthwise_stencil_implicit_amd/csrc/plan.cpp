@@ -147,10 +147,12 @@ void geom_dwcl(const conv_desc &d, conv_plan_t &p)
     p.tile[DW_COLCHUNKS] = cdiv(d.out[1], dw_ocols(s));
     p.tile[DW_XBYTES] = span_bytes(d.x, es);
     p.tile[DW_YBYTES] = span_bytes(p.y, es);
-    // Row blocks: enough workgroups for two per CU, each one block of output
-    // rows of one image (no block crosses an image).
+    // Row blocks: enough workgroups to fill every CU once (two or three per
+    // CU), each one block of output rows of one image (no block crosses an
+    // image).
     const int64_t tasks = d.N * p.tile[DW_CHCHUNKS] * p.tile[DW_COLCHUNKS];
-    int64_t rb = std::max<int64_t>(1, std::min<int64_t>(d.out[0], cdiv(512, std::max<int64_t>(tasks, 1))));
+    const int64_t want = 256 * dw_wgs_per_cu(k, s);
+    int64_t rb = std::max<int64_t>(1, std::min<int64_t>(d.out[0], cdiv(want, std::max<int64_t>(tasks, 1))));
     const int64_t rpb = cdiv(d.out[0], rb);
     rb = cdiv(d.out[0], rpb);
     p.tile[DW_RBLOCKS] = rb;
