@@ -749,12 +749,13 @@ struct GpMma {
     int32_t wpg;                 // workgroups per group
 };
 
-template <typename T, int CP, int S>
+template <typename T, int CP, int S, bool PM>
 __global__ __launch_bounds__(256) void grp_mma_kernel(GpArgs a, GpMma f)
 {
     constexpr int ES = Dt<T>::size;
     constexpr int KS = (9 * CP + 31) / 32;      // MFMA K steps
-    constexpr int IN_IT = 2, OUT_IT = 8;        // chunks / pieces per thread (host-checked)
+    constexpr int IN_IT = PM ? CP : 2;          // chunks per thread (host-checked)
+    constexpr int OUT_IT = 8;                   // output pieces per thread (host-checked)
     constexpr int INVALID = 0x7fffff00;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char *sin = lds;                   // [IHh][IWh][CP] stored values
@@ -771,15 +772,20 @@ __global__ __launch_bounds__(256) void grp_mma_kernel(GpArgs a, GpMma f)
 
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.x), (short)0, f.x_bytes, 0x00020000);
+    // PM (planes of whole 16-byte chunks, HW / 8 <= 256): thread t < HW / 8
+    // loads the 8 positions 8t .. 8t + 7 of every channel (chunk c = channel
+    // c), so it holds each position's channels together and writes them to
+    // LDS as one 8- or 16-byte vector.  Otherwise chunk r of thread t is the
+    // group's 16-byte chunk t + 256 r, whose 8 elements go to LDS one by one.
     const int xoff0 = g * item * ES + tid * 16;
     u32x4 chunk[IN_IT];
     auto fetch = [&](int n) {
 #pragma unroll
         for (int r = 0; r < IN_IT; ++r) {
-            const bool ok = n < a.N && tid + r * 256 < f.chunks_in;
+            const bool ok = PM ? n < a.N && tid * 8 < HW && r < a.Cig : n < a.N && tid + r * 256 < f.chunks_in;
+            const int off = PM ? xoff0 + r * HW * ES : xoff0 + r * 256 * 16;
             chunk[r] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                           xr, ok ? xoff0 + r * 256 * 16 + n * f.xs_n * ES : INVALID, 0, 0));
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? off + n * f.xs_n * ES : INVALID, 0, 0));
         }
     };
     int n = blockIdx.x / a.G;
@@ -788,9 +794,10 @@ __global__ __launch_bounds__(256) void grp_mma_kernel(GpArgs a, GpMma f)
     // LDS byte address of each element of this thread's chunks (channel c,
     // row h, column w -> slot c of position (h + PH, w + PW)), or -1 for
     // elements past the group or outside the haloed plane.
-    int saddr[IN_IT][8];
+    constexpr int SR = PM ? 1 : IN_IT;          // chunk rows with their own addresses
+    int saddr[SR][8];
 #pragma unroll
-    for (int r = 0; r < IN_IT; ++r) {
+    for (int r = 0; r < SR; ++r) {
         const int e0 = (tid + r * 256) * 8;
         int c = e0 / HW;
         const int rem = e0 - c * HW;
@@ -799,7 +806,8 @@ __global__ __launch_bounds__(256) void grp_mma_kernel(GpArgs a, GpMma f)
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int hh = h + a.PH, ww = w + a.PW;
-            saddr[r][k] = (e0 + k < item && hh < f.IHh && ww < f.IWh) ? ((hh * f.IWh + ww) * CP + c) * ES : -1;
+            const int lim = PM ? HW : item;
+            saddr[r][k] = (e0 + k < lim && hh < f.IHh && ww < f.IWh) ? ((hh * f.IWh + ww) * CP + c) * ES : -1;
             if (++w == a.W) {
                 w = 0;
                 if (++h == a.H) {
@@ -868,22 +876,44 @@ __global__ __launch_bounds__(256) void grp_mma_kernel(GpArgs a, GpMma f)
     for (; n < a.N; n += f.wpg) {
         // The previous image's tiles were read before its last barrier: the
         // plane is free.  Scatter this image's chunks, fetch the next ones.
+        if constexpr (PM) {
+            // Position k of the thread's block: its CP channel values, low
+            // or high halves of word k / 2 of each chunk, paired by one byte
+            // permute per two channels.
+            const uint32_t sel = 0x05040100u;
 #pragma unroll
-        for (int r = 0; r < IN_IT; ++r)
+            for (int k = 0; k < 8; ++k) {
+                if (saddr[0][k] < 0) continue;
+                const uint32_t sk = (k & 1) ? sel + 0x02020202u : sel;
+                uint32_t wv[CP / 2];
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (saddr[r][k] >= 0) {
-                    const uint32_t word = chunk[r][k >> 1];
-                    *reinterpret_cast<uint16_t *>(sin + saddr[r][k]) = (k & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
-                }
+                for (int q = 0; q < CP / 2; ++q)
+                    wv[q] = __builtin_amdgcn_perm(chunk[2 * q + 1][k >> 1], chunk[2 * q][k >> 1], sk);
+                if constexpr (CP == 4)
+                    *reinterpret_cast<uint2 *>(sin + saddr[0][k]) = uint2{wv[0], wv[1]};
+                else
+                    *reinterpret_cast<uint4 *>(sin + saddr[0][k]) = uint4{wv[0], wv[1], wv[2], wv[3]};
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < IN_IT; ++r)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (saddr[r][k] >= 0) {
+                        const uint32_t word = chunk[r][k >> 1];
+                        *reinterpret_cast<uint16_t *>(sin + saddr[r][k]) =
+                            (k & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
+                    }
+        }
         fetch(n + f.wpg);
         __syncthreads();
 
-        // Four independent tiles per pass (w, w + 4, w + 8, w + 12), so their
-        // LDS reads, MFMAs and stores overlap; a tile past the plane repeats
-        // the last one and keeps nothing.
-        for (int t0 = wave; t0 < ntiles; t0 += 16) {
-            constexpr int TU = 4;
+        // Two independent tiles per pass (w and w + 4), so their LDS reads,
+        // MFMAs and stores overlap; a tile past the plane repeats the last one
+        // and keeps nothing.  (Four per pass measured 5% slower: the extra
+        // registers cost a resident workgroup per CU.)
+        constexpr int TU = 2;
+        for (int t0 = wave; t0 < ntiles; t0 += 4 * TU) {
             f32x4 acc[TU];
             uint4 av[TU][KS];
             int oh[TU], ow0[TU];
@@ -1133,9 +1163,18 @@ int launch_grp(const conv_plan_t &p, const void *x, const void *w, const void *b
                 hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)a.G * f.wpg)), dim3(256), mlds, s, a, f);
                 return hipGetLastError() == hipSuccess ? CONV_OK : CONV_EDEVICE;
             };
-#define MICONV_GM(CP_, S_)                                                                                      \
-    if (CP == CP_ && S == S_)                                                                                   \
-        return d.dtype == CONV_F16 ? go(grp_mma_kernel<f16_t, CP_, S_>) : go(grp_mma_kernel<bf16_t, CP_, S_>);
+            // Position-major chunks when every channel plane is whole 16-byte
+            // chunks and one thread per 8 positions suffices.
+            const int64_t HW = (int64_t)a.H * a.W;
+            const bool pm = (HW * es) % 16 == 0 && HW % 8 == 0 && HW / 8 <= 256;
+#define MICONV_GM(CP_, S_)                                                                             \
+    if (CP == CP_ && S == S_) {                                                                        \
+        if (pm)                                                                                        \
+            return d.dtype == CONV_F16 ? go(grp_mma_kernel<f16_t, CP_, S_, true>)                      \
+                                       : go(grp_mma_kernel<bf16_t, CP_, S_, true>);                    \
+        return d.dtype == CONV_F16 ? go(grp_mma_kernel<f16_t, CP_, S_, false>)                         \
+                                   : go(grp_mma_kernel<bf16_t, CP_, S_, false>);                       \
+    }
             MICONV_GM(4, 1) MICONV_GM(8, 1) MICONV_GM(4, 2) MICONV_GM(8, 2)
 #undef MICONV_GM
         }
