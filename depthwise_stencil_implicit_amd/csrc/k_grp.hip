@@ -759,7 +759,7 @@ __global__ __launch_bounds__(256) void grp_mma_kernel(GpArgs a, GpMma f)
     constexpr int INVALID = 0x7fffff00;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char *sin = lds;                   // [IHh][IWh][CP] stored values
-    unsigned char *sout = lds + f.in_bytes;     // [Cog][OH][OW] stored values, then a spare slot
+    unsigned char *sout = lds + f.in_bytes;     // [Cog][OH][OW] stored values
 
     const int tid = threadIdx.x;
     // The wave index is uniform: in a scalar register, so tile arithmetic
@@ -868,7 +868,6 @@ __global__ __launch_bounds__(256) void grp_mma_kernel(GpArgs a, GpMma f)
 
     // Tiles: (output row, 16-column block), wave w takes tiles w, w + 4, ...
     const int ntiles = a.OH * f.ctiles;
-    uint16_t *spare = reinterpret_cast<uint16_t *>(sout + f.pieces_out * 8);
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, f.y_bytes, 0x00020000);
     const int yoff0 = g * a.Cog * OHW * ES + tid * 8;
     typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
@@ -949,12 +948,15 @@ __global__ __launch_bounds__(256) void grp_mma_kernel(GpArgs a, GpMma f)
                 // Lane l holds columns ow0 + 4 (l / 16) + i of channel l % 16
                 // (OW % 4 == 0: all four columns valid or none).
                 const int oc = ow0[u] + 4 * kq;
+                // Lanes past Cog (or past the plane) store nothing: a shared
+                // spare slot would put every one of them on one LDS bank.
                 const bool keep = jn < a.Cog && oc < a.OW && t0 + 4 * u < ntiles;
-                uint16_t *dst = keep ? reinterpret_cast<uint16_t *>(sout) + (jn * a.OH + oh[u]) * a.OW + oc : spare;
-                uint2 v;
-                v.x = pack2<T>(acc[u][0], acc[u][1]);
-                v.y = pack2<T>(acc[u][2], acc[u][3]);
-                *reinterpret_cast<uint2 *>(dst) = v;
+                if (keep) {
+                    uint2 v;
+                    v.x = pack2<T>(acc[u][0], acc[u][1]);
+                    v.y = pack2<T>(acc[u][2], acc[u][3]);
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(sout) + (jn * a.OH + oh[u]) * a.OW + oc) = v;
+                }
             }
         }
         __syncthreads();
