@@ -260,12 +260,18 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
         const int soff = ok ? (ybase + out_row(j) * a.ys_h) * ES : 0;
         const int vbad = ok ? 0 : INVALID;
         const unsigned char *src = stg + (j & 1) * STGB;
+        if constexpr (CB == 16) {
+            // All staged reads first, then the stores: one LDS round trip
+            // instead of one per store (the asm stores are barriers to the
+            // compiler's scheduling).
+            u32x4 v[NS];
 #pragma unroll
-        for (int r = 0; r < NS; ++r) {
-            if constexpr (CB == 16) {
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(src + soff_l[r]);
-                store_b128(v, yq, yoff[r] + vbad, soff);
-            } else {
+            for (int r = 0; r < NS; ++r) v[r] = *reinterpret_cast<const u32x4 *>(src + soff_l[r]);
+#pragma unroll
+            for (int r = 0; r < NS; ++r) store_b128(v[r], yq, yoff[r] + vbad, soff);
+        } else {
+#pragma unroll
+            for (int r = 0; r < NS; ++r) {
                 const uint32_t v = *reinterpret_cast<const uint32_t *>(src + soff_l[r]);
                 __builtin_amdgcn_raw_buffer_store_b32(v, yr, yoff[r] + vbad, soff, kStoreNT);
             }
