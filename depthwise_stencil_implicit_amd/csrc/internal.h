@@ -82,13 +82,13 @@ constexpr int dw_pending(int K, int S, int CB, int D)
 {
     return (D - 2) * dw_lpw(K, S, CB) + ((D - 1 + S - 1) / S) * dw_ns(S, CB);
 }
-// Workgroups resident per CU: three for the light stride-1 stencils (k <= 5
-// fits 12 waves per CU in registers, and a 4-row ring keeps three rings in
-// LDS), two with a 6-row ring otherwise.
-constexpr int dw_wgs_per_cu(int K, int S) { return S == 1 && K <= 5 ? 3 : 2; }
+// Workgroups resident per CU: three for the light stride-1 stencils (k3, and
+// k5 on the 16-byte path, fit 12 waves per CU in registers, and a 4-row ring
+// keeps three rings in LDS), two with a 6-row ring otherwise.
+constexpr int dw_wgs_per_cu(int K, int S, int CB) { return S == 1 && (K == 3 || (K == 5 && CB == 16)) ? 3 : 2; }
 constexpr int dw_depth(int K, int S, int CB)
 {
-    int d = dw_wgs_per_cu(K, S) == 3 ? 4 : 6;
+    int d = dw_wgs_per_cu(K, S, CB) == 3 ? 4 : 6;
     while (d > 3 && (dw_pending(K, S, CB, d) > 63 || d * dw_row_bytes(K, S, CB) + dw_tail_bytes(K, S) > 80 * 1024))
         --d;
     return d;

@@ -147,11 +147,17 @@ void geom_dwcl(const conv_desc &d, conv_plan_t &p)
     p.tile[DW_COLCHUNKS] = cdiv(d.out[1], dw_ocols(s));
     p.tile[DW_XBYTES] = span_bytes(d.x, es);
     p.tile[DW_YBYTES] = span_bytes(p.y, es);
+    // variant 1: 16-byte direct-to-LDS loads and 16-byte stores, which need
+    // 16-byte aligned channel runs (x and y must also be 16-byte aligned at run
+    // time; y is dense with x's channel count); variant 0 moves 4-byte channel
+    // words.
+    bool q = (d.C_in * es) % 16 == 0;
+    for (int i : {0, 2, 3}) q = q && (d.x.strides[i] * es) % 16 == 0;
     // Row blocks: enough workgroups to fill every CU once (two or three per
     // CU), each one block of output rows of one image (no block crosses an
     // image).
     const int64_t tasks = d.N * p.tile[DW_CHCHUNKS] * p.tile[DW_COLCHUNKS];
-    const int64_t want = 256 * dw_wgs_per_cu(k, s);
+    const int64_t want = 256 * dw_wgs_per_cu(k, s, q ? 16 : 4);
     int64_t rb = std::max<int64_t>(1, std::min<int64_t>(d.out[0], cdiv(want, std::max<int64_t>(tasks, 1))));
     const int64_t rpb = cdiv(d.out[0], rb);
     rb = cdiv(d.out[0], rpb);
@@ -159,12 +165,6 @@ void geom_dwcl(const conv_desc &d, conv_plan_t &p)
     p.tile[DW_RPB] = rpb;
     p.grid[0] = tasks * rb;
     p.block = 256;
-    // variant 1: 16-byte direct-to-LDS loads and 16-byte stores, which need
-    // 16-byte aligned channel runs (x and y must also be 16-byte aligned at run
-    // time; y is dense with x's channel count); variant 0 moves 4-byte channel
-    // words.
-    bool q = (d.C_in * es) % 16 == 0;
-    for (int i : {0, 2, 3}) q = q && (d.x.strides[i] * es) % 16 == 0;
     p.variant = q ? 1 : 0;
     p.lds_bytes = dw_lds_bytes(k, s, q ? 16 : 4);
     p.vec_ok = 1;
