@@ -437,3 +437,50 @@ def test_tail_rows_split_k(transposed):
     yg = y.detach()[tuple(torch.as_tensor(pts.T, device=y.device))].double().cpu().numpy()
     bad = ~(np.abs(yg - yr) <= EPS[wl.dtype] * A)
     assert not bad.any(), f"{int(bad.sum())} outputs outside the bound, e.g. {pts[bad][:3].tolist()}"
+
+
+# ---------------------------------------------- every implicit-GEMM tiling --
+
+def _cfg_cases():
+    """16-bit implicit-GEMM calls whose K ranges are 1, 2, 3 and 5 steps of 64
+    channels (2, 4, 6 and 10 of 32), so every stage count meets step counts
+    below it and ones that are not a multiple of it; plus a transposed call
+    and a grouped one with a ragged channel block."""
+    out = []
+    for i, (cig, k, cog) in enumerate([(64, 1, 16), (128, 1, 70), (64, 3, 33), (320, 1, 5)]):
+        out.append(synth.random_case(7100 + i, rank=1, transposed=False, dtype=["bf16", "f16"][i % 2],
+                                     channels_last=True, N=2, C_in=cig, C_out=cog, groups=1, L=[37], k=[k],
+                                     stride=[1], padding_before=[k // 2], padding_after=[k // 2], dilation=[1],
+                                     output_padding=[0], has_bias=bool(i % 2)))
+    out.append(synth.random_case(7104, rank=1, transposed=True, dtype="bf16", channels_last=True, N=2, C_in=96,
+                                 C_out=40, groups=1, L=[29], k=[4], stride=[2], padding_before=[1],
+                                 padding_after=[2], dilation=[1], output_padding=[0], has_bias=True))
+    out.append(synth.random_case(7105, rank=2, transposed=False, dtype="f16", channels_last=False, N=1, C_in=2 * 72,
+                                 C_out=2 * 24, groups=2, L=[9, 11], k=[3, 3], stride=[1, 2], padding_before=[1, 0],
+                                 padding_after=[1, 2], dilation=[1, 1], output_padding=[0, 0], has_bias=False))
+    return out
+
+
+CFG_CASES = _cfg_cases()
+# Tile configurations of the 16-bit path (index 5 is the fp32 register-staged
+# one); the test checks that the plan took each index.
+CFGS_16 = [0, 1, 2, 3, 4, 6, 7, 8, 9, 10, 11]
+
+
+@pytest.mark.parametrize("cfg", CFGS_16)
+@pytest.mark.parametrize("wl", CFG_CASES, ids=lambda v: v.name)
+def test_igemm_every_tile_config(wl, cfg, monkeypatch):
+    """The planner's tile choice forced to every configuration (the
+    MICONV_IGEMM_CFG tuning knob), whole output against the reference:
+    two-stage tiles, and three- and four-stage tiles whose step counts are
+    padded to whole rounds with dead refills."""
+    monkeypatch.setenv("MICONV_IGEMM_CFG", str(cfg))
+    kind = "igemm_t" if wl.transposed else "igemm"
+    _flush(f"tile config {cfg}: {_desc(wl)}")
+    x, w, b = synth.make_inputs(wl, device="cuda")
+    kw = expand_kw(wl)
+    plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=wl.transposed),
+                        force_kernel=kind).plan
+    assert int(plan.variant) == cfg, f"the plan did not take tile configuration {cfg}"
+    check_full(wl, force=kind)
