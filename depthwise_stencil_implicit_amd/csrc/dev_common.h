@@ -60,6 +60,25 @@ template <> __device__ __forceinline__ float dot2<bf16_t>(uint32_t a, uint32_t b
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// The same sum written to a fresh register: the VOP3P encoding, whose
+// accumulator input is an operand of its own.  The compiler always picks the
+// tied v_dot2c form and, for an accumulator that stays live (a bias starting
+// several chains), first copies it into the destination; this form needs no
+// copy.  Bit-identical to dot2 (compared on 2^20 random bf16 operand sets).
+template <typename T> __device__ __forceinline__ float dot2_to(uint32_t a, uint32_t b, float c);
+template <> __device__ __forceinline__ float dot2_to<f16_t>(uint32_t a, uint32_t b, float c)
+{
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+template <> __device__ __forceinline__ float dot2_to<bf16_t>(uint32_t a, uint32_t b, float c)
+{
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Narrow fp32 to the storage type, rounding to nearest even.
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }

@@ -411,14 +411,21 @@ __global__ __launch_bounds__(256) void dwcl_kernel(DwArgs a)
 #pragma unroll
                         for (int t = 0; t < TO; ++t) {
                             if constexpr (DOT) {
-                                float a0 = kh == 0 ? bias[0] : acc[slot][t][0];
-                                float a1 = kh == 0 ? bias[1] : acc[slot][t][1];
+                                float a0 = acc[slot][t][0];
+                                float a1 = acc[slot][t][1];
 #pragma unroll
                                 for (int pp = 0; pp < KP; ++pp) {
                                     const int col = t * S + 2 * pp;
                                     const bool two = 2 * pp + 1 < K;
-                                    a0 = dot2<T>(two ? plo[col] : zlo[col], wpl[kh][pp], a0);
-                                    a1 = dot2<T>(two ? phi[col] : zhi[col], wph[kh][pp], a1);
+                                    const uint32_t x0 = two ? plo[col] : zlo[col], x1 = two ? phi[col] : zhi[col];
+                                    if (kh == 0 && pp == 0) {
+                                        // The output's first product starts from the bias.
+                                        a0 = dot2_to<T>(x0, wpl[kh][pp], bias[0]);
+                                        a1 = dot2_to<T>(x1, wph[kh][pp], bias[1]);
+                                    } else {
+                                        a0 = dot2<T>(x0, wpl[kh][pp], a0);
+                                        a1 = dot2<T>(x1, wph[kh][pp], a1);
+                                    }
                                 }
                                 acc[slot][t][0] = a0;
                                 acc[slot][t][1] = a1;
