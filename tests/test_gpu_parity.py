@@ -484,3 +484,39 @@ def test_igemm_every_tile_config(wl, cfg, monkeypatch):
                         force_kernel=kind).plan
     assert int(plan.variant) == cfg, f"the plan did not take tile configuration {cfg}"
     check_full(wl, force=kind)
+
+
+# ------------------------------------------- every depthwise ring kernel --
+
+def _dw_every_case():
+    """One channels-last depthwise call per compiled ring kernel: kernel 3, 5
+    and 7, stride 1 and 2, fp32 / fp16 / bf16, channel runs of whole 16-byte
+    chunks (the 16-byte path) and not (the 4-byte path; 12 channels of 16-bit
+    or 6 of fp32 are 24 bytes), asymmetric padding and a ragged column chunk
+    (72 output columns at stride 1, more than one 56-column chunk)."""
+    out = []
+    i = 0
+    for k in (3, 5, 7):
+        for s in (1, 2):
+            for dtype in ("f32", "f16", "bf16"):
+                for aligned in (True, False):
+                    es = 4 if dtype == "f32" else 2
+                    C = (64 // es) if aligned else (24 // es)
+                    W = 72 * s + k
+                    out.append(synth.random_case(7300 + i, rank=2, transposed=False, dtype=dtype,
+                                                 channels_last=True, N=2, C_in=C, C_out=C, groups=C,
+                                                 L=[9 + k, W], k=[k, k], stride=[s, s],
+                                                 padding_before=[k // 2, max(0, k // 2 - 1)],
+                                                 padding_after=[k // 2, k // 2], dilation=[1, 1],
+                                                 output_padding=[0, 0], has_bias=bool(i % 2)))
+                    i += 1
+    return out
+
+
+@pytest.mark.parametrize("wl", _dw_every_case(), ids=lambda v: v.name)
+def test_dw_cl_every_ring_kernel(wl):
+    """Whole output of each compiled depthwise ring kernel (kernel size,
+    stride, dtype, access width) against the reference; the stride-1 k3 and
+    k5 16-byte kernels run three workgroups per CU with a 4-row ring."""
+    _flush(f"dw_cl kernel: {_desc(wl)}")
+    check_full(wl, force="dw_cl")
