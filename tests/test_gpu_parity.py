@@ -520,3 +520,45 @@ def test_dw_cl_every_ring_kernel(wl):
     k5 16-byte kernels run three workgroups per CU with a 4-row ring."""
     _flush(f"dw_cl kernel: {_desc(wl)}")
     check_full(wl, force="dw_cl")
+
+
+# ------------------------------------- every grouped matrix-core kernel --
+
+def _grp_mma_every_case():
+    """One grouped 3x3 call per compiled matrix-core kernel: 4 or 8 channel
+    slots (Cig 3 / 4 and 6 / 8), stride 1 and 2, fp16 / bf16, and planes of
+    whole 16-byte chunks (position-major writes, HW % 8 == 0) or not."""
+    out = []
+    i = 0
+    for pm in (True, False):
+        for cp in (4, 8):
+            for s in (1, 2):
+                for dtype in ("f16", "bf16"):
+                    cig = (3 if cp == 4 else 6) if pm else (4 if cp == 4 else 8)
+                    if pm:
+                        H, W, pa = (8, 12, 1) if s == 1 else (8, 16, 1)
+                    else:
+                        H, W, pa = (5, 12, 1) if s == 1 else (5, 14, 2)
+                    cog = (8, 5)[i % 2]
+                    out.append(synth.random_case(7400 + i, rank=2, transposed=False, dtype=dtype,
+                                                 channels_last=False, N=3, C_in=2 * cig, C_out=2 * cog, groups=2,
+                                                 L=[H, W], k=[3, 3], stride=[s, s], padding_before=[1, 1],
+                                                 padding_after=[1, pa], dilation=[1, 1], output_padding=[0, 0],
+                                                 has_bias=bool(i % 2)))
+                    i += 1
+    return out
+
+
+@pytest.mark.parametrize("wl", _grp_mma_every_case(), ids=lambda v: v.name)
+def test_grp_mma_every_kernel(wl):
+    """Each compiled matrix-core grouped kernel (channel slots, stride, dtype,
+    position-major or element-wise plane writes), checked to take that
+    schedule, whole output against the reference."""
+    _flush(f"grp matrix-core kernel: {_desc(wl)}")
+    x, w, b = synth.make_inputs(wl, device="cuda")
+    kw = expand_kw(wl)
+    plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=wl.transposed),
+                        force_kernel="grp").plan
+    assert int(plan.variant) == 1, "shape chosen for the matrix-core schedule"
+    check_full(wl, force="grp")
