@@ -53,10 +53,14 @@ class ConvPlan(ctypes.Structure):
                 ("block", _i32), ("lds_bytes", _i32), ("flops", _i64), ("bytes", _i64)]
 
 
+class ConvPlanOpts(ctypes.Structure):
+    _fields_ = [("force_kernel", _i32), ("force_variant", _i32), ("reserved", _i32 * 6)]
+
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmiconv.so")
 
 # Every symbol include/miconv.h declares.
-EXPORTS = ("conv_bind", "conv_out_shape", "conv_plan", "conv_run", "conv_kernel_name",
+EXPORTS = ("conv_bind", "conv_out_shape", "conv_plan", "conv_plan_ex", "conv_run", "conv_kernel_name",
            "conv_status_string", "conv_abi_version")
 
 _lib = None
@@ -79,6 +83,8 @@ def lib():
         L.conv_out_shape.restype = ctypes.c_int
         L.conv_plan.argtypes = [P(ConvDesc), P(ConvTensor), _i32, P(ConvPlan)]
         L.conv_plan.restype = ctypes.c_int
+        L.conv_plan_ex.argtypes = [P(ConvDesc), P(ConvTensor), P(ConvPlanOpts), P(ConvPlan)]
+        L.conv_plan_ex.restype = ctypes.c_int
         L.conv_run.argtypes = [P(ConvPlan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.conv_run.restype = ctypes.c_int

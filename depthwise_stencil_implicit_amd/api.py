@@ -12,7 +12,6 @@ ATen convolution overload maps onto the one canonical op).
 from __future__ import annotations
 
 import ctypes
-import os
 from typing import Optional, Sequence, Tuple, Union
 
 import torch
@@ -113,16 +112,21 @@ def conv_out_shape(d: A.ConvDesc) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
     return tuple(y.sizes[: y.rank]), tuple(y.strides[: y.rank])
 
 
-def conv_plan(d: A.ConvDesc, y: A.ConvTensor, force_kernel: Union[int, str, None] = None) -> A.ConvPlan:
+def conv_plan(d: A.ConvDesc, y: A.ConvTensor, force_kernel: Union[int, str, None] = None,
+              force_variant: Optional[int] = None) -> A.ConvPlan:
+    """``conv_plan``, or ``conv_plan_ex`` when a schedule is forced too."""
     if force_kernel is None:
-        force_kernel = os.environ.get("MICONV_FORCE_KERNEL", "auto")
+        force_kernel = "auto"
     if isinstance(force_kernel, str):
         force_kernel = A.KERNELS[force_kernel]
     p = A.ConvPlan()
-    _check(A.lib().conv_plan(ctypes.byref(d), ctypes.byref(y), int(force_kernel), ctypes.byref(p)))
-    if os.environ.get("MICONV_LOG"):
-        print(f"[miconv] plan kernel={kernel_name(p.kernel)} variant={p.variant} grid={p.grid[0]} "
-              f"block={p.block} vec_ok={p.vec_ok} ws={p.workspace_bytes}", flush=True)
+    if force_variant is None:
+        _check(A.lib().conv_plan(ctypes.byref(d), ctypes.byref(y), int(force_kernel), ctypes.byref(p)))
+    else:
+        o = A.ConvPlanOpts()
+        o.force_kernel = int(force_kernel)
+        o.force_variant = int(force_variant)
+        _check(A.lib().conv_plan_ex(ctypes.byref(d), ctypes.byref(y), ctypes.byref(o), ctypes.byref(p)))
     return p
 
 
@@ -141,11 +145,12 @@ class Prepared:
     """bind + out_shape + plan for fixed tensor descriptors (reusable)."""
 
     def __init__(self, x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], args: A.ConvArgs,
-                 force_kernel=None):
+                 force_kernel=None, force_variant: Optional[int] = None):
         self.desc = conv_bind(describe(x), describe(w), describe(b), args)
         self.sizes, self.strides = conv_out_shape(self.desc)
         self.dtype = x.dtype
-        self.plan = conv_plan(self.desc, tensor_desc(self.sizes, self.strides, x.dtype), force_kernel)
+        self.plan = conv_plan(self.desc, tensor_desc(self.sizes, self.strides, x.dtype), force_kernel,
+                              force_variant)
 
     def empty_output(self, device) -> torch.Tensor:
         return torch.empty_strided(self.sizes, self.strides, dtype=self.dtype, device=device)
@@ -166,7 +171,8 @@ class Prepared:
 
 def conv(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None, *, stride=1,
          padding_before=0, padding_after=0, dilation=1, groups: int = 1, transposed: bool = False,
-         output_padding=0, padding_mode: str = "explicit", force_kernel=None) -> torch.Tensor:
+         output_padding=0, padding_mode: str = "explicit", force_kernel=None,
+         force_variant: Optional[int] = None) -> torch.Tensor:
     """The canonical convolution on GPU tensors (x, w, b share one dtype)."""
     for t in (x, w) + ((b,) if b is not None else ()):
         if not t.is_cuda:
@@ -177,7 +183,7 @@ def conv(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None, *, 
                      padding_before=padding_before, padding_after=padding_after,
                      dilation=dilation, output_padding=output_padding if transposed else None,
                      padding_mode=padding_mode)
-    prep = Prepared(x, w, b, args, force_kernel)
+    prep = Prepared(x, w, b, args, force_kernel, force_variant)
     y = prep.empty_output(x.device)
     return prep.run(x, w, b, y, prep.workspace(x.device))
 

@@ -1024,8 +1024,27 @@ bool grp_supported(const conv_desc &d)
     return cig >= 1 && cig <= 8;
 }
 
-void grp_geometry(const conv_desc &d, conv_plan_t &p)
+// LDS of the tiled schedule's smallest tile (one output row of kP columns):
+// the group's weights (input-channel pairs x taps x padded outputs, one word
+// each) plus the halo rows.  Every grouped schedule stages the weights.
+static int64_t grp_min_lds(const conv_desc &d)
 {
+    const bool two = d.spatial == 2;
+    const int64_t KH = two ? d.k[0] : 1, KW = two ? d.k[1] : d.k[0];
+    const int64_t SW = two ? d.stride[1] : d.stride[0];
+    const int64_t DW = two ? d.dilation[1] : d.dilation[0];
+    const int64_t DH = two ? d.dilation[0] : 1;
+    const int64_t npairs = (d.C_in / d.groups + 1) / 2;
+    const int64_t cog_pad = round_up(d.C_out / d.groups, kJB);
+    const int64_t ih = (KH - 1) * DH + 1, iw = (kP - 1) * SW + (KW - 1) * DW + 1;
+    return 4 * (npairs * KH * KW * cog_pad + npairs * ih * iw);
+}
+
+bool grp_fits(const conv_desc &d) { return grp_min_lds(d) <= kLds; }
+
+bool grp_geometry(const conv_desc &d, conv_plan_t &p)
+{
+    if (!grp_fits(d)) return false;
     const bool two = d.spatial == 2;
     const int64_t OH = two ? d.out[0] : 1, OW = two ? d.out[1] : d.out[0];
     const int64_t KH = two ? d.k[0] : 1, KW = two ? d.k[1] : d.k[0];
@@ -1059,6 +1078,7 @@ void grp_geometry(const conv_desc &d, conv_plan_t &p)
     p.block = 256;
     p.lds_bytes = (int32_t)lds(TH, TW);
     p.variant = grp_mma_plane_ok(d, p.y) ? GRP_SCHED_MMA : GRP_SCHED_VALU;
+    return p.lds_bytes <= kLds;
 }
 
 int launch_grp(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream)

@@ -23,7 +23,6 @@
 //       otherwise                                      -> PLANE
 //   everything else                                   -> IGEMM
 #include <cstring>
-#include <cstdlib>
 #include <algorithm>
 #include <initializer_list>
 
@@ -32,7 +31,8 @@
 namespace miconv {
 bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw);
 bool grp_supported(const conv_desc &d);
-void grp_geometry(const conv_desc &d, conv_plan_t &p);
+bool grp_geometry(const conv_desc &d, conv_plan_t &p);
+bool grp_fits(const conv_desc &d);
 void reduce_geometry(const conv_desc &d, conv_plan_t &p);
 }  // namespace miconv
 
@@ -127,7 +127,12 @@ int route(const conv_desc &d, const conv_tensor &y)
     if (stencil_domain(d) && all_dil1(d) && d.groups > 1) {
         if (few_outputs(d)) return CONV_K_REDUCE;
         if (supports_dwcl(d, y)) return CONV_K_DW_CL;
-        if (cig(d) >= 2 && grp_supported(d)) return CONV_K_GRP;
+        if (cig(d) >= 2 && grp_supported(d)) {
+            // Every grouped schedule keeps the group's weights in LDS; a
+            // wide per-group product that does not fit is a GEMM.
+            if (!grp_fits(d)) return CONV_K_IGEMM;
+            return CONV_K_GRP;
+        }
         return CONV_K_PLANE;
     }
     return CONV_K_IGEMM;
@@ -221,7 +226,7 @@ bool geom_plane(const conv_desc &d, conv_plan_t &p)
 
 // Implicit GEMM: choose the tile shape with the least estimated CU time,
 // rounds of workgroups over the 256 CUs times the tile area each runs.
-bool geom_igemm(const conv_desc &d, conv_plan_t &p)
+bool geom_igemm(const conv_desc &d, conv_plan_t &p, int force_variant)
 {
     int64_t phases = 1, rows = d.N;
     for (int i = 0; i < 3; ++i) {
@@ -260,11 +265,12 @@ bool geom_igemm(const conv_desc &d, conv_plan_t &p)
             best_cost = cost;
         }
     }
-    // Tuning knob: MICONV_IGEMM_CFG=<index> forces a tile configuration of the
-    // same dtype class (used to sweep schedules; the default is the estimate).
-    if (const char *env = std::getenv("MICONV_IGEMM_CFG")) {
-        const int v = std::atoi(env);
-        if (v >= lo && v < igemm_num_cfgs() && (v == 5) == (d.dtype == CONV_F32)) best = v;
+    // An explicit schedule (conv_plan_ex): a tile configuration of the same
+    // dtype class, or the call is refused.
+    if (force_variant >= 0) {
+        if (force_variant < lo || force_variant >= igemm_num_cfgs() || (force_variant == 5) != (d.dtype == CONV_F32))
+            return false;
+        best = force_variant;
     }
     const IgemmCfg &c = igemm_cfg(best);
     const int64_t taps = d.k[0] * d.k[1] * d.k[2];
@@ -358,9 +364,14 @@ bool same_layout(const conv_tensor &a, const conv_tensor &b)
 
 }  // namespace
 
-extern "C" int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force_kernel, conv_plan_t *p)
+extern "C" int conv_plan_ex(const conv_desc *d, const conv_tensor *y, const conv_plan_opts *o, conv_plan_t *p)
 {
     if (!d || !y || !p) return CONV_EINVAL;
+    const int32_t force_kernel = o ? o->force_kernel : CONV_K_AUTO;
+    const int32_t force_variant = o ? o->force_variant : -1;
+    if (force_variant >= 0 && force_kernel != CONV_K_IGEMM && force_kernel != CONV_K_IGEMM_T &&
+        force_kernel != CONV_K_GRP)
+        return CONV_EINVAL;
     if (d->spatial < 1 || d->spatial > 3 || d->groups < 1 || d->x.rank != d->spatial + 2) return CONV_EINVAL;
     conv_tensor expect;
     if (conv_out_shape(d, &expect) != CONV_OK) return CONV_EINVAL;
@@ -381,7 +392,7 @@ extern "C" int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force
         switch (k) {
         case CONV_K_DW_CL: ok = supports_dwcl(*d, yb); break;
         case CONV_K_PLANE: ok = supports_plane(*d); break;
-        case CONV_K_GRP: ok = stencil_domain(*d) && grp_supported(*d); break;
+        case CONV_K_GRP: ok = stencil_domain(*d) && grp_supported(*d) && grp_fits(*d); break;
         case CONV_K_REDUCE: ok = supports_reduce(*d); break;
         case CONV_K_IGEMM: ok = supports_igemm(*d); break;
         case CONV_K_IGEMM_T: ok = supports_igemm_t(*d); break;
@@ -396,13 +407,21 @@ extern "C" int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force
         if (!geom_plane(*d, plan)) {
             if (force_kernel != CONV_K_AUTO) return CONV_EUNSUPPORTED;
             plan.kernel = CONV_K_IGEMM;
-            if (!geom_igemm(*d, plan)) return CONV_EUNSUPPORTED;
+            if (!geom_igemm(*d, plan, -1)) return CONV_EUNSUPPORTED;
         }
         break;
-    case CONV_K_GRP: grp_geometry(*d, plan); break;
+    case CONV_K_GRP:
+        if (!grp_geometry(*d, plan)) return CONV_EUNSUPPORTED;
+        if (force_variant >= 0) {
+            // The matrix-core schedule only where its own conditions hold.
+            if (force_variant == GRP_SCHED_MMA && plan.variant != GRP_SCHED_MMA) return CONV_EUNSUPPORTED;
+            if (force_variant > GRP_SCHED_MMA) return CONV_EUNSUPPORTED;
+            plan.variant = force_variant;
+        }
+        break;
     case CONV_K_REDUCE: reduce_geometry(*d, plan); break;
     default:
-        if (!geom_igemm(*d, plan)) return CONV_EUNSUPPORTED;
+        if (!geom_igemm(*d, plan, force_variant)) return CONV_EUNSUPPORTED;
         break;
     }
     if (plan.grid[0] > kI32) return CONV_EUNSUPPORTED;
@@ -418,4 +437,13 @@ extern "C" int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force
     plan.bytes = (numel(d->x) + numel(d->w) + (d->has_bias ? d->C_out : 0) + ny) * esize(d->dtype);
     *p = plan;
     return CONV_OK;
+}
+
+extern "C" int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force_kernel, conv_plan_t *p)
+{
+    conv_plan_opts o;
+    std::memset(&o, 0, sizeof(o));
+    o.force_kernel = force_kernel;
+    o.force_variant = -1;
+    return conv_plan_ex(d, y, &o, p);
 }

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "internal.h"
 
@@ -17,6 +18,19 @@ int64_t numel(const conv_tensor &t)
     int64_t n = 1;
     for (int i = 0; i < t.rank; ++i) n *= t.sizes[i];
     return n;
+}
+
+// Whether the process sees a GPU: asked once, on the first launch.
+bool have_device()
+{
+    static std::once_flag once;
+    static bool ok = false;
+    std::call_once(once, [] {
+        int n = 0;
+        ok = hipGetDeviceCount(&n) == hipSuccess && n > 0;
+        if (!ok) (void)hipGetLastError();
+    });
+    return ok;
 }
 
 }  // namespace
@@ -35,11 +49,7 @@ extern "C" int conv_run(const conv_plan_t *p, const void *x, const void *w, cons
         if (!workspace || workspace_bytes < (size_t)p->workspace_bytes) return CONV_EINVAL;
         if (!aligned(workspace, 16)) return CONV_EALIGN;
     }
-    int ndev = 0;
-    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
-        (void)hipGetLastError();
-        return CONV_EDEVICE;
-    }
+    if (!have_device()) return CONV_EDEVICE;
     const bool vec = p->vec_ok && aligned(x, 16) && aligned(y, 16);
     switch (p->kernel) {
     case CONV_K_DW_CL:

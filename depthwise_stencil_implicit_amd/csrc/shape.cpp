@@ -7,6 +7,12 @@
 // torch/_inductor/kernel/conv.py (conv_layout, channels_last_order): the
 // output layout follows the input's memory format, channels-last meaning the
 // channel dim has the smallest stride, then the last spatial dim, ..., then N.
+//
+// The rule, as ATen's convolution applies it: a 2-D or 3-D output is
+// channels-last when x or w is channels-last-like and not also
+// contiguous-like, else contiguous.  A 1-D call is run by ATen as a 2-D one
+// with H = 1 after x has been made contiguous, so only the weight can make a
+// 1-D output channels-last (NLC); an NLC x alone gives a contiguous output.
 #include <cstring>
 
 #include "internal.h"
@@ -63,7 +69,7 @@ void batched_out(const conv_desc &d, conv_tensor &y)
     y.sizes[0] = d.N;
     y.sizes[1] = d.C_out;
     for (int i = 0; i < d.spatial; ++i) y.sizes[2 + i] = d.out[i];
-    const bool cl = channels_last_like(d.x) || channels_last_like(d.w);
+    const bool cl = (d.spatial >= 2 && channels_last_like(d.x)) || channels_last_like(d.w);
     int order[CONV_MAX_RANK], n = 0;
     if (cl) {
         order[n++] = 1;

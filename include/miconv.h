@@ -197,11 +197,38 @@ MICONV_API int conv_out_shape(const conv_desc *d, conv_tensor *y);
  *   y            output descriptor; must equal conv_out_shape(d) exactly.
  *   force_kernel CONV_K_AUTO, or a conv_kernel to run (tests pin schedules).
  *   p            receives the plan.
+ *   Same as conv_plan_ex with { force_kernel, -1 }.
  *
  * Returns CONV_OK, CONV_ELAYOUT (y differs from conv_out_shape),
  * CONV_EUNSUPPORTED (forced kernel outside its domain) or CONV_EINVAL.
  */
 MICONV_API int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force_kernel, conv_plan_t *p);
+
+/* Options of conv_plan_ex.  Zero-initialise, then set what is wanted. */
+typedef struct conv_plan_opts {
+    int32_t force_kernel;             /* CONV_K_AUTO (-1) or a conv_kernel to run */
+    int32_t force_variant;            /* -1 = the planner's schedule; else a schedule of the forced
+                                         kernel: CONV_K_IGEMM / CONV_K_IGEMM_T take an index of the
+                                         implicit GEMM's tile table (0..11 for 16-bit types except
+                                         5, which is the fp32 one), CONV_K_GRP takes 0 (packed dot2)
+                                         or 1 (matrix-core plane) */
+    int32_t reserved[6];              /* must be zero */
+} conv_plan_opts;
+
+/*
+ * conv_plan_ex -- conv_plan with explicit options: the forced kernel and,
+ * for a forced kernel, one of its schedules (executorch PR #25084,
+ * description: tests pin a single schedule of a template).  The planner
+ * reads no environment; these fields are the only overrides.
+ *
+ *   o  NULL = { CONV_K_AUTO, -1 } (the same plan as conv_plan).
+ *
+ * Returns as conv_plan; CONV_EUNSUPPORTED also when the forced schedule
+ * cannot run the call (a tile of another dtype class, the matrix-core
+ * grouped schedule outside its conditions), CONV_EINVAL when a schedule is
+ * given without a kernel that has schedules.
+ */
+MICONV_API int conv_plan_ex(const conv_desc *d, const conv_tensor *y, const conv_plan_opts *o, conv_plan_t *p);
 
 /*
  * conv_run -- launch the planned kernels on the caller's HIP stream.

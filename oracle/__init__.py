@@ -152,14 +152,19 @@ def out_strides(y_shape: Sequence[int], x_sizes: Sequence[int], x_strides: Seque
                 w_sizes: Sequence[int], w_strides: Sequence[int]) -> Tuple[int, ...]:
     """Element strides of the output (batched shapes).
 
-    Reading of "the output layout ATen's CUDA convolution returns" (executorch
-    PR #25084, description): the output is dense; it is channels-last
-    (C fastest, then the last spatial dim, ..., then N) when x or w is
-    channels-last-like and not also contiguous-like, and contiguous
-    otherwise.  Products use max(size, 1), as ATen does for empty dims.
+    Reading of the output layout the pages name (executorch PR #25084, "Add
+    triton::convolution and the conv routing framework", description: the op
+    returns the layout ATen's convolution returns).  The output is dense.  For
+    2-D and 3-D calls it is channels-last (C fastest, then the last spatial
+    dim, ..., then N) when x or w is channels-last-like and not also
+    contiguous-like, and contiguous otherwise.  ATen runs a 1-D call as a 2-D
+    one with H = 1 after making x contiguous, so for 1-D calls only w counts:
+    an NLC x alone gives a contiguous output.  Products use max(size, 1), as
+    ATen does for empty dims.
     """
     nd = len(y_shape)
-    if is_channels_last(x_sizes, x_strides) or is_channels_last(w_sizes, w_strides):
+    x_counts = nd >= 4
+    if (x_counts and is_channels_last(x_sizes, x_strides)) or is_channels_last(w_sizes, w_strides):
         order = [1] + list(range(nd - 1, 1, -1)) + [0]
     else:
         order = list(range(nd - 1, -1, -1))

@@ -23,13 +23,13 @@ def expand_kw(wl):
                 transposed=wl.transposed, output_padding=ex(wl.output_padding))
 
 
-def run_gpu(wl, force=None, inputs=None):
+def run_gpu(wl, force=None, inputs=None, variant=None):
     x, w, b = inputs if inputs is not None else synth.make_inputs(wl, device="cuda")
     kw = expand_kw(wl)
     y = api.conv(x, w, b, stride=kw["stride"], padding_before=kw["padding_before"],
                  padding_after=kw["padding_after"], dilation=kw["dilation"], groups=kw["groups"],
                  transposed=kw["transposed"], output_padding=kw["output_padding"],
-                 force_kernel=force)
+                 force_kernel=force, force_variant=variant)
     torch.cuda.synchronize()
     return x, w, b, y
 
@@ -46,11 +46,11 @@ def assert_close(y_gpu: torch.Tensor, y_ref: np.ndarray, A: np.ndarray, eps: flo
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside eps*A ({eps}); {detail}")
 
 
-def check_full(wl, force=None, exact=False):
+def check_full(wl, force=None, exact=False, variant=None):
     """Whole output against the reference.  ``exact``: inputs whose fp32 sums
     are exact, so the result must equal the reference rounded once (nearest
     even) to the output dtype."""
-    x, w, b, y = run_gpu(wl, force)
+    x, w, b, y = run_gpu(wl, force, variant=variant)
     xr, wr, br = ref_inputs(x, w, b)
     yr, A = oracle.conv(xr, wr, br, **expand_kw(wl))
     if exact:

@@ -174,7 +174,7 @@ EXPECTED = {  # (sizes, strides, kernel) of the five workloads
     "dw_bf16_nhwc_32x256x56x56_k7s2": ((32, 256, 28, 28), (200704, 1, 7168, 256), "dw_cl"),
     "grp_f16_nchw_32x256x28x28_g64_m2": ((32, 512, 28, 28), (401408, 784, 28, 1), ("grp", "plane")),
     "dense_bf16_nhwc_64x256x56x56_k3": ((64, 256, 56, 56), (802816, 1, 14336, 256), "igemm"),
-    "convT1d_bf16_nlc_16x512x8192_k4s2": ((16, 512, 16383), (8388096, 1, 512), "igemm_t"),
+    "convT1d_bf16_nlc_16x512x8192_k4s2": ((16, 512, 16383), (8388096, 16383, 1), "igemm_t"),
 }
 
 
@@ -286,3 +286,66 @@ def test_empty_output_runs_as_a_noop_without_a_device():
 def test_cpu_tensors_are_refused_by_the_product_path():
     with pytest.raises(ValueError, match="GPU only"):
         api.conv(torch.zeros((1, 2, 5)), torch.zeros((2, 2, 3)))
+
+
+# ------------------------------------------- explicit schedules, LDS budget --
+
+def test_wide_grouped_product_goes_to_the_gemm():
+    """A grouped call with few input channels per group but a wide per-group
+    output: the grouped stencil keeps every group's weights in LDS, which do
+    not fit, so the planner picks the implicit GEMM, and forcing the grouped
+    kernel is refused."""
+    x, w = T((1, 16, 32, 32), torch.float16), T((2048, 8, 9, 9), torch.float16)
+    p = prep(x, w, groups=2, padding_before=4, padding_after=4).plan
+    assert api.kernel_name(p.kernel) == "igemm" and p.lds_bytes <= 160 * 1024
+    with pytest.raises(api.ConvError) as e:
+        prep(x, w, groups=2, padding_before=4, padding_after=4, force="grp")
+    assert e.value.status == A.EUNSUPPORTED
+    x2, w2 = T((1, 16, 32, 32), torch.float16), T((1024, 8, 3, 3), torch.float16)
+    p2 = prep(x2, w2, groups=2, padding_before=1, padding_after=1).plan
+    assert api.kernel_name(p2.kernel) == "igemm"
+    # A narrow per-group output still runs on the grouped stencil.
+    p3 = prep(T((1, 16, 32, 32), torch.float16), T((32, 8, 3, 3), torch.float16), groups=2,
+              padding_before=1, padding_after=1).plan
+    assert api.kernel_name(p3.kernel) == "grp" and p3.lds_bytes <= 64 * 1024
+
+
+def test_forced_schedule_is_explicit():
+    """conv_plan_ex takes the implicit GEMM's tile index and the grouped
+    kernel's schedule; a schedule of the wrong dtype class is refused, a
+    schedule without a kernel is invalid, and the environment plays no part."""
+    import os
+    x, w = T((2, 64, 12, 12), cl=True), T((64, 64, 3, 3))
+    for v in (0, 3, 9, 11):
+        p = api.Prepared(x, w, None, api.make_args(padding_before=1, padding_after=1), force_kernel="igemm",
+                         force_variant=v).plan
+        assert p.variant == v
+    with pytest.raises(api.ConvError) as e:
+        api.Prepared(x, w, None, api.make_args(padding_before=1, padding_after=1), force_kernel="igemm",
+                     force_variant=5)       # the fp32 tile
+    assert e.value.status == A.EUNSUPPORTED
+    with pytest.raises(api.ConvError) as e:
+        api.Prepared(x, w, None, api.make_args(padding_before=1, padding_after=1), force_variant=0)
+    assert e.value.status == A.EINVAL
+    base = bytes(prep(x, w, padding_before=1, padding_after=1).plan)
+    old = os.environ.get("MICONV_IGEMM_CFG")
+    os.environ["MICONV_IGEMM_CFG"] = "4"
+    try:
+        assert bytes(prep(x, w, padding_before=1, padding_after=1).plan) == base
+    finally:
+        if old is None:
+            del os.environ["MICONV_IGEMM_CFG"]
+        else:
+            os.environ["MICONV_IGEMM_CFG"] = old
+    # The grouped kernel: the matrix-core schedule only where it applies.
+    xg, wg = T((2, 8, 8, 16), torch.float16), T((16, 4, 3, 3), torch.float16)
+    pg = api.Prepared(xg, wg, None, api.make_args(groups=2, padding_before=1, padding_after=1),
+                      force_kernel="grp").plan
+    assert pg.variant == 1
+    pv = api.Prepared(xg, wg, None, api.make_args(groups=2, padding_before=1, padding_after=1),
+                      force_kernel="grp", force_variant=0).plan
+    assert pv.variant == 0
+    with pytest.raises(api.ConvError):
+        api.Prepared(T((2, 8, 8, 15), torch.float16), wg, None,
+                     api.make_args(groups=2, padding_before=1, padding_after=1), force_kernel="grp",
+                     force_variant=1)

@@ -55,6 +55,30 @@ def test_workload_reduced_batch_full_output(wl):
     check_full(wl)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("wl", [synth.dense_bf16_cl(), synth.transposed_bf16_nlc()], ids=lambda w: w.name)
+def test_workload_full_size_whole_output(wl):
+    """The dense and transposed workloads at full size, in the launch
+    configuration the benchmark times (full-size tiles, and for the dense call
+    the split-K rows past the last full round), every output element against
+    the reference.  The reference runs a few images at a time to bound host
+    memory."""
+    _flush(f"workload {wl.name} (whole output, full size)")
+    x, w, b, y = run_gpu(wl)
+    kw = expand_kw(wl)
+    plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=wl.transposed)).plan
+    _flush(f"  plan {api.kernel_name(plan.kernel)} variant {plan.variant} tail {int(plan.tile[7])}")
+    xr, wr, br = ref_inputs(x, w, b)
+    N = x.shape[0]
+    step = 8 if not wl.transposed else 2
+    for n0 in range(0, N, step):
+        n1 = min(N, n0 + step)
+        yr, A = oracle.conv(xr[n0:n1], wr, br, **kw)
+        assert_close(y[n0:n1], yr, A, EPS[wl.dtype], f"{wl.name} images {n0}..{n1 - 1}")
+        _flush(f"  images {n0}..{n1 - 1} ok")
+
+
 # ----------------------------------------------------------------- sweeps --
 
 def _geom_cases(kind, n, seed):
@@ -290,18 +314,55 @@ EXACT_CASES = [
 ]
 
 
+EXACT_CASES += [
+    ("dw_cl", synth.random_case(15, rank=2, transposed=False, dtype="f16", channels_last=True, N=2, C_in=64,
+                                C_out=64, groups=64, L=[11, 30], k=[7, 7], stride=[1, 1],
+                                padding_before=[3, 3], padding_after=[3, 3], dilation=[1, 1],
+                                output_padding=[0, 0], has_bias=True)),
+    ("dw_cl", synth.random_case(16, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=48,
+                                C_out=48, groups=48, L=[12, 33], k=[3, 3], stride=[2, 2],
+                                padding_before=[0, 0], padding_after=[1, 1], dilation=[1, 1],
+                                output_padding=[0, 0], has_bias=True)),
+    ("plane", synth.random_case(17, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=16,
+                                C_out=16, groups=16, L=[15, 13], k=[5, 5], stride=[1, 1],
+                                padding_before=[2, 2], padding_after=[2, 2], dilation=[1, 1],
+                                output_padding=[0, 0], has_bias=True)),
+    # The grouped matrix-core plane schedule (3x3, NCHW planes, 12 columns).
+    ("grp", synth.random_case(18, rank=2, transposed=False, dtype="f16", channels_last=False, N=3, C_in=6,
+                              C_out=16, groups=2, L=[8, 12], k=[3, 3], stride=[1, 1],
+                              padding_before=[1, 1], padding_after=[1, 1], dilation=[1, 1],
+                              output_padding=[0, 0], has_bias=True)),
+    ("grp", synth.random_case(19, rank=2, transposed=False, dtype="bf16", channels_last=False, N=3, C_in=8,
+                              C_out=10, groups=2, L=[8, 16], k=[3, 3], stride=[2, 2],
+                              padding_before=[1, 1], padding_after=[1, 1], dilation=[1, 1],
+                              output_padding=[0, 0], has_bias=False)),
+]
+
+
 @pytest.mark.parametrize("kind,wl", EXACT_CASES, ids=lambda v: v if isinstance(v, str) else v.name)
-@pytest.mark.parametrize("values", ["ones", "ints"])
+@pytest.mark.parametrize("values", ["ones", "ints", "wide"])
 def test_exact_results(kind, wl, values):
-    """All-ones and small-integer inputs have exact fp32 sums in any order, and
-    results small enough to be exact in the output dtype."""
+    """Integer inputs have exact fp32 sums in any order, so every kernel must
+    return the exact sum rounded once, to nearest even, to the output dtype.
+    "ones" and "ints" stay small enough to be exact in every dtype; "wide"
+    (x in [-127, 127], w in [-31, 31]) gives sums well above 256 (bf16) and
+    2048 (fp16) with odd low bits, so each output needs a rounding -- a
+    truncating or twice-rounding epilogue fails it."""
     import dataclasses
     if values == "ones":
         wl = dataclasses.replace(wl, x_dist=("ones",), w_dist=("ones",), b_dist=("ones",))
-    else:
+    elif values == "ints":
         wl = dataclasses.replace(wl, x_dist=("ints", -3, 3), w_dist=("ints", -2, 2), b_dist=("ints", -4, 4))
+    else:
+        wl = dataclasses.replace(wl, x_dist=("ints", -127, 127), w_dist=("ints", -31, 31),
+                                 b_dist=("ints", -500, 500))
     _flush(f"exact {values} {kind}: {_desc(wl)}")
-    check_full(wl, force=kind, exact=True)
+    y = check_full(wl, force=kind, exact=True)
+    if values == "wide" and wl.dtype != "f32":
+        # The case really exercises the rounding: many outputs beyond the
+        # range where every integer is representable.
+        lim = 256 if wl.dtype == "bf16" else 2048
+        assert (y.abs().float() > lim).float().mean().item() > 0.2
 
 
 # ------------------------------------------------------------ memory safety --
@@ -439,6 +500,46 @@ def test_tail_rows_split_k(transposed):
     assert not bad.any(), f"{int(bad.sum())} outputs outside the bound, e.g. {pts[bad][:3].tolist()}"
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("transposed", [False, True], ids=["forward", "transposed"])
+def test_tail_rows_whole_output(transposed):
+    """The same calls, every output element: the 256x256 tile (configuration
+    0) over whole rounds of full tiles, and the rows past them (64-row tiles;
+    for the forward call their K range split over several workgroups and the
+    fp32 partial sums reduced with the bias)."""
+    wl = _tail_case(transposed)
+    _flush(f"tail rows, whole output: {_desc(wl)}")
+    x, w, b, y = run_gpu(wl)
+    kw = expand_kw(wl)
+    plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=wl.transposed)).plan
+    assert int(plan.variant) == 0, "shape chosen for the 256x256 tile"
+    if not transposed:
+        assert (int(plan.tile[7]) >> 24) > 1 and (int(plan.tile[7]) & 0xffffff) >= 2
+    xr, wr, br = ref_inputs(x, w, b)
+    step = 6 if not transposed else 1
+    for n0 in range(0, x.shape[0], step):
+        n1 = min(x.shape[0], n0 + step)
+        yr, A = oracle.conv(xr[n0:n1], wr, br, **kw)
+        assert_close(y[n0:n1], yr, A, EPS[wl.dtype], f"{wl.name} images {n0}..{n1 - 1}")
+
+
+def test_wide_grouped_product_on_the_gemm():
+    """Few input channels per group but a wide per-group output: the weights
+    would not fit the grouped stencil's LDS, so the call runs on the implicit
+    GEMM; whole output against the reference."""
+    wl = synth.random_case(7501, rank=2, transposed=False, dtype="f16", channels_last=False, N=2, C_in=16,
+                           C_out=2048, groups=2, L=[13, 11], k=[9, 9], stride=[1, 1], padding_before=[4, 4],
+                           padding_after=[4, 3], dilation=[1, 1], output_padding=[0, 0], has_bias=True)
+    _flush(f"wide grouped: {_desc(wl)}")
+    x, w, b = synth.make_inputs(wl, device="cuda")
+    kw = expand_kw(wl)
+    plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=wl.transposed)).plan
+    assert api.kernel_name(plan.kernel) == "igemm"
+    check_full(wl)
+
+
 # ---------------------------------------------- every implicit-GEMM tiling --
 
 def _cfg_cases():
@@ -469,21 +570,20 @@ CFGS_16 = [0, 1, 2, 3, 4, 6, 7, 8, 9, 10, 11]
 
 @pytest.mark.parametrize("cfg", CFGS_16)
 @pytest.mark.parametrize("wl", CFG_CASES, ids=lambda v: v.name)
-def test_igemm_every_tile_config(wl, cfg, monkeypatch):
-    """The planner's tile choice forced to every configuration (the
-    MICONV_IGEMM_CFG tuning knob), whole output against the reference:
-    two-stage tiles, and three- and four-stage tiles whose step counts are
-    padded to whole rounds with dead refills."""
-    monkeypatch.setenv("MICONV_IGEMM_CFG", str(cfg))
+def test_igemm_every_tile_config(wl, cfg):
+    """The planner's tile choice forced to every configuration (conv_plan_ex's
+    force_variant), whole output against the reference: two-stage tiles, and
+    three- and four-stage tiles whose step counts are padded to whole rounds
+    with dead refills."""
     kind = "igemm_t" if wl.transposed else "igemm"
     _flush(f"tile config {cfg}: {_desc(wl)}")
     x, w, b = synth.make_inputs(wl, device="cuda")
     kw = expand_kw(wl)
     plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
                                                groups=wl.groups, transposed=wl.transposed),
-                        force_kernel=kind).plan
+                        force_kernel=kind, force_variant=cfg).plan
     assert int(plan.variant) == cfg, f"the plan did not take tile configuration {cfg}"
-    check_full(wl, force=kind)
+    check_full(wl, force=kind, variant=cfg)
 
 
 # ------------------------------------------- every depthwise ring kernel --

@@ -404,32 +404,34 @@ def test_points_match_full_output(oracle_mod):
 
 # --------------------------------------------------------------- layout --
 
-@pytest.mark.parametrize("r", [2, 3])
-@pytest.mark.parametrize("cl", [False, True])
+@pytest.mark.parametrize("r", [1, 2, 3])
+@pytest.mark.parametrize("xl", ["contiguous", "channels_last"])
+@pytest.mark.parametrize("wl", ["contiguous", "channels_last"])
 @pytest.mark.parametrize("transposed", [False, True])
-def test_out_strides_match_torch_cpu(oracle_mod, r, cl, transposed):
-    """CPU ATen follows the same memory-format rule for 2-D inputs, and for
-    contiguous 3-D inputs.  Its 1-D and 3-D channels-last CPU paths return
-    contiguous outputs, so those cases are pinned by the rule cases below."""
-    if r == 3 and cl:
-        pytest.skip("CPU ATen's 3-D path ignores channels-last; the rule is the spec here")
-    x = torch.randn((2, 4) + (5,) * r, dtype=torch.float64)
-    if cl:
+def test_out_strides_match_torch_cpu(oracle_mod, r, xl, wl, transposed):
+    """CPU ATen's convolution (fp32: its channels-last-aware path) returns
+    the layout of the rule for every rank and both layouts of x and w: 1-D
+    calls ignore an NLC x (ATen makes x contiguous before running the call as
+    2-D) but follow an NLC weight."""
+    x = torch.randn((2, 4) + (5,) * r, dtype=torch.float32)
+    if xl == "channels_last":
         x = synth.channels_last_copy(x)
-    if transposed:
-        w = torch.randn((4, 3) + (3,) * r, dtype=torch.float64)
-        y = CONVT[r](x, w, stride=2, padding=1)
-    else:
-        w = torch.randn((6, 4) + (3,) * r, dtype=torch.float64)
-        y = CONV[r](x, w, stride=2, padding=1)
+    w = torch.randn(((4, 3) if transposed else (6, 4)) + (3,) * r, dtype=torch.float32)
+    if wl == "channels_last":
+        w = synth.channels_last_copy(w)
+    y = (CONVT if transposed else CONV)[r](x, w, stride=2, padding=1)
     assert oracle_mod.out_strides(tuple(y.shape), tuple(x.shape), tuple(x.stride()),
                                   tuple(w.shape), tuple(w.stride())) == tuple(y.stride())
 
 
 def test_out_strides_rule_cases(oracle_mod):
-    # NLC input -> NLC output (the rule; CPU ATen differs for 1-D, so it is not used here)
+    # 1-D: an NLC input with a contiguous weight -> contiguous output (the
+    # transposed 1-D upsampling workload's layout)
     assert oracle_mod.out_strides((16, 512, 16383), (16, 512, 8192), (4194304, 1, 512),
-                                  (512, 512, 4), (2048, 4, 1)) == (8388096, 1, 512)
+                                  (512, 512, 4), (2048, 4, 1)) == (8388096, 16383, 1)
+    # 1-D: an NLC weight -> NLC output
+    assert oracle_mod.out_strides((2, 6, 20), (2, 8, 20), (160, 20, 1),
+                                  (6, 8, 3), (24, 1, 8)) == (120, 1, 6)
     # C == 1: both formats describe x -> contiguous
     assert oracle_mod.out_strides((2, 3, 4, 4), (2, 1, 4, 4), (16, 16, 4, 1),
                                   (3, 1, 1, 1), (1, 1, 1, 1)) == (48, 16, 4, 1)
