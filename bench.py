@@ -2,6 +2,7 @@
 """Throughput of the canonical convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --probe-copy MIB | --probe-mfma | --probe-lds
 
 A step is one pass over the workload's calls (kernels only: binding, output
 layout and planning run once per call before timing, and their host time is
@@ -11,14 +12,22 @@ buffer more than ~1 GiB of traffic apart, so the 256 MB Infinity Cache cannot
 serve them.  One JSON line is printed.
 
 Workloads
-  dw_bf16_cl   (default) depthwise bf16 channels-last, N=32, C=256, 56x56,
+  all          (default) every measured workload below in one step: the
+               depthwise fp32 call, the six depthwise bf16 calls, the grouped
+               call, the dense call and the transposed call.  ``value`` is the
+               step's percentage of the MI355X roofline: the sum over the
+               calls of their time at the roofline (algorithmic bytes at
+               8 TB/s or algorithmic FLOPs at the relevant compute peak,
+               whichever is longer) over the measured step time.  Each
+               workload also gets its own row (GB/s or TFLOP/s, fraction).
+  dw_bf16_cl   depthwise bf16 channels-last, N=32, C=256, 56x56,
                k in {3,5,7} x stride in {1,2}: six calls per step.  GB/s.
   dw_f32_small depthwise fp32 NCHW, 1x32x32x32, 3x3.  GB/s.
   grp_f16      grouped fp16 NCHW, 32x256x28x28 -> 512, 64 groups.  GB/s.
   dense_bf16   dense 3x3 bf16 channels-last, 64x256x56x56 -> 256.  TFLOP/s.
   convT1d_bf16 transposed 1-D bf16 NLC, 16x512x8192 -> 16383, k=4, s=2.  TFLOP/s.
 
-``roofline`` describes the kernel with the largest average duration: its
+``roofline`` describes the call with the largest average duration: its
 algorithmic bytes (or FLOPs) per launch over that average, measured with HIP
 events on the launch stream.  ``cpu_baseline`` times the double-precision
 reference (test infrastructure) on the host cores over a bounded sample.
@@ -36,26 +45,34 @@ import time
 METRIC = "HBM GB/s (stencil) and TFLOP/s (implicit GEMM), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6        # dense bf16/fp16 MFMA, 256 CUs x 2048 FMA/clk x 2.4 GHz x 2
+MFMA_F32_PEAK_TFLOPS = 157.3          # dense fp32 MFMA
 VALU_FP32_PEAK_TFLOPS = 78.6          # 256 CUs x 64 lanes x 2 FLOP/FMA x 2.4 GHz (no packed fp32)
 VALU_DOT2_PEAK_TFLOPS = 157.3         # the same lanes issuing v_dot2_f32_{bf16,f16}: two FMAs each
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 
-WORKLOADS = ("dw_bf16_cl", "dw_f32_small", "grp_f16", "dense_bf16", "convT1d_bf16")
+WORKLOADS = ("all", "dw_f32_small", "dw_bf16_cl", "grp_f16", "dense_bf16", "convT1d_bf16")
+UNITS = {"dw_f32_small": "GB/s", "dw_bf16_cl": "GB/s", "grp_f16": "GB/s", "dense_bf16": "TFLOP/s",
+         "convT1d_bf16": "TFLOP/s"}
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dw_bf16_cl", choices=WORKLOADS)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all", choices=WORKLOADS)
     ap.add_argument("--rotate", type=int, default=0, help="rotation copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work for the baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU work for the baseline")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="MIB",
                     help="instead of a workload, time a plain device copy of MIB mebibytes (the "
                          "measured bandwidth ceiling, and the reference for HBM byte counters)")
+    ap.add_argument("--probe-mfma", action="store_true",
+                    help="instead of a workload, time a kernel of independent bf16 MFMAs (the "
+                         "measured matrix-core ceiling)")
+    ap.add_argument("--probe-lds", action="store_true",
+                    help="instead of a workload, time a kernel of conflict-free 16-byte LDS reads")
     return ap.parse_args()
 
 
@@ -81,17 +98,79 @@ def copy_probe(mib, steps, warmup):
                       "avg_us": round(us, 2), "GBps": round(moved / us / 1e3, 1)}), flush=True)
 
 
+def unit_probe(kind, steps, warmup):
+    """MFMA issue rate or LDS read bandwidth from the probe library's kernels
+    (8 workgroups of 256 threads per CU, 256 CUs).  The MFMA probe also reads
+    the shader clock against the 100 MHz real-time counter inside its loop,
+    which gives the clock the units ran at."""
+    import ctypes
+    import torch
+    from depthwise_stencil_implicit_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        raise SystemExit(f"{build.PROBE_LIB} is missing: run the build first")
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    blocks = 256 * 8
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    clk = torch.zeros(blocks * 2, dtype=torch.int64, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    if kind == "mfma":
+        lib.probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+        lib.probe_mfma.restype = ctypes.c_int
+        iters = 4096
+        shapes = [("mfma_bf16_16x16x32", 0, 8 * 16 * 16 * 32 * 2), ("mfma_bf16_32x32x16", 1, 4 * 32 * 32 * 16 * 2)]
+        for name, big, flop_per_round in shapes:
+            fn = lambda: lib.probe_mfma(out.data_ptr(), clk.data_ptr(), blocks, iters, big, stream.cuda_stream)
+            for _ in range(warmup):
+                assert fn() == 0
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(steps):
+                assert fn() == 0
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            us = ev0.elapsed_time(ev1) * 1e3 / steps
+            flops = blocks * 4 * iters * flop_per_round
+            rate = flops / us / 1e6
+            c = clk.view(-1, 2).double()
+            mhz = float((c[:, 0] / c[:, 1].clamp(min=1)).median()) * 100.0
+            cyc = float(c[:, 0].median()) / iters / (8 if not big else 4)
+            print(json.dumps({"probe": name, "flops_per_launch": flops, "avg_us": round(us, 2),
+                              "TFLOPs": round(rate, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                              "frac": round(rate / MFMA_BF16_PEAK_TFLOPS, 4), "shader_clock_MHz": round(mhz),
+                              "clocks_per_mfma_per_wave": round(cyc, 2)}), flush=True)
+    else:
+        lib.probe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.probe_lds.restype = ctypes.c_int
+        iters = 2048
+        fn = lambda: lib.probe_lds(out.data_ptr(), blocks, iters, stream.cuda_stream)
+        for _ in range(warmup):
+            assert fn() == 0
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            assert fn() == 0
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / steps
+        nbytes = blocks * 256 * iters * 8 * 16
+        rate = nbytes / us / 1e6
+        print(json.dumps({"probe": "lds_read_b128", "bytes_per_launch": nbytes, "avg_us": round(us, 2),
+                          "TBps": round(rate, 2),
+                          "bytes_per_clk_per_cu_at_2.4GHz": round(nbytes / (us * 1e-6) / 2.4e9 / 256, 1)}),
+              flush=True)
+
+
 def workload_calls(name):
+    """[(workload name, call)] for a bench workload."""
     from depthwise_stencil_implicit_amd import synth
-    if name == "dw_bf16_cl":
-        return synth.depthwise_bf16_cl_all(), "GB/s"
-    if name == "dw_f32_small":
-        return [synth.depthwise_f32_small()], "GB/s"
-    if name == "grp_f16":
-        return [synth.grouped_f16()], "GB/s"
-    if name == "dense_bf16":
-        return [synth.dense_bf16_cl()], "TFLOP/s"
-    return [synth.transposed_bf16_nlc()], "TFLOP/s"
+    table = {"dw_f32_small": [synth.depthwise_f32_small()], "dw_bf16_cl": synth.depthwise_bf16_cl_all(),
+             "grp_f16": [synth.grouped_f16()], "dense_bf16": [synth.dense_bf16_cl()],
+             "convT1d_bf16": [synth.transposed_bf16_nlc()]}
+    names = [n for n in WORKLOADS if n != "all"] if name == "all" else [name]
+    return [(n, wl) for n in names for wl in table[n]]
 
 
 def expand(wl):
@@ -132,45 +211,16 @@ def measured_traffic(kernel_name, call_name):
         return None
 
 
-def cpu_baseline(calls, unit, target_s):
-    """The reference on a bounded sample of the workload: the leading images
-    of each call, sized from a one-image timing so the whole sample takes about
-    ``target_s``; when even the full batch is quicker, the full batch is run
-    repeatedly until ``target_s`` has passed."""
-    import oracle
-    from depthwise_stencil_implicit_amd import synth
-    cores = len(os.sched_getaffinity(0))
-    f = lambda t: None if t is None else t.double().contiguous().numpy()
-    plan = []
-    for wl in calls:
-        one = wl.with_batch(1)
-        x, w, b = synth.make_inputs(one)
-        t0 = time.perf_counter()
-        oracle.conv(f(x), f(w), f(b), nthreads=cores, **expand(one))
-        t_one = time.perf_counter() - t0
-        n = max(1, min(wl.x_shape[0], int(target_s / len(calls) / max(t_one, 1e-6))))
-        sub = wl.with_batch(n)
-        plan.append((sub, synth.make_inputs(sub), call_work(sub, unit)))
-    total_t, total_work, rounds = 0.0, 0.0, 0
-    while rounds == 0 or total_t < 0.5 * target_s:
-        for sub, (x, w, b), work in plan:
-            t0 = time.perf_counter()
-            oracle.conv(f(x), f(w), f(b), nthreads=cores, **expand(sub))
-            total_t += time.perf_counter() - t0
-            total_work += work
-        rounds += 1
-    value = total_work / total_t / (1e9 if unit == "GB/s" else 1e12)
-    samples = ", ".join(f"{sub.name.split('@')[0]}:N={sub.x_shape[0]}" for sub, _, _ in plan)
-    return {"value": round(value, 4), "unit": unit, "cores": int(oracle.max_threads()), "kind": "oracle",
-            "sample": f"double-precision reference over {samples}, {rounds} pass(es), {total_t:.1f} s wall"}
+def make_args(wl):
+    from depthwise_stencil_implicit_amd import api
+    kw = expand(wl)
+    return api.make_args(transposed=kw["transposed"], groups=kw["groups"], stride=kw["stride"],
+                         padding_before=kw["padding_before"], padding_after=kw["padding_after"],
+                         dilation=kw["dilation"], output_padding=kw["output_padding"] if kw["transposed"] else None)
 
 
-def wl0_dtype(calls):
-    return calls[0].dtype
-
-
-def call_work(wl, unit):
-    """Algorithmic bytes or FLOPs of one call, from the library's plan."""
+def call_plan(wl):
+    """The library's plan of a call (host only), for its algorithmic units."""
     import torch
     from depthwise_stencil_implicit_amd import api, synth
     dt = synth.DTYPES[wl.dtype]
@@ -180,13 +230,86 @@ def call_work(wl, unit):
     w = torch.empty(wl.w_shape, dtype=dt)
     c_out = wl.w_shape[1] * wl.groups if wl.transposed else wl.w_shape[0]
     b = torch.empty((c_out,), dtype=dt) if wl.has_bias else None
-    kw = expand(wl)
-    args = api.make_args(transposed=kw["transposed"], groups=kw["groups"], stride=kw["stride"],
-                         padding_before=kw["padding_before"], padding_after=kw["padding_after"],
-                         dilation=kw["dilation"],
-                         output_padding=kw["output_padding"] if kw["transposed"] else None)
-    p = api.Prepared(x, w, b, args).plan
-    return float(p.bytes if unit == "GB/s" else p.flops)
+    return api.Prepared(x, w, b, make_args(wl)).plan
+
+
+def roof_of(kernel, variant, dtype, flops, nbytes):
+    """(bound, peak, time at the roofline in us) of one call: the longer of
+    its algorithmic bytes at 8 TB/s and its FLOPs at the compute peak of the
+    units the kernel multiplies on."""
+    if kernel in ("igemm", "igemm_t") or (kernel == "grp" and variant == 1):
+        cpeak, cbound = (MFMA_F32_PEAK_TFLOPS if dtype == "f32" else MFMA_BF16_PEAK_TFLOPS), "mfma"
+    elif dtype == "f32":
+        cpeak, cbound = VALU_FP32_PEAK_TFLOPS, "alu"
+    else:
+        cpeak, cbound = VALU_DOT2_PEAK_TFLOPS, "alu"
+    t_mem = nbytes / (HBM_PEAK_GBS * 1e3)          # us
+    t_cmp = flops / (cpeak * 1e6)                    # us
+    if kernel in ("igemm", "igemm_t") or t_cmp > t_mem:
+        return cbound, cpeak, max(t_cmp, t_mem)
+    return "hbm", HBM_PEAK_GBS, t_mem
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(calls, target_s, headline_pct):
+    """The reference on a bounded sample of the workload: the leading images
+    of each call, sized from a one-image timing so the whole sample takes
+    about ``target_s``; when even the full batch is quicker, the full batch is
+    run repeatedly.  Reported in the headline's unit (percent of the GPU's
+    roofline for the sampled calls) and per workload in GB/s or TFLOP/s."""
+    import oracle
+    from depthwise_stencil_implicit_amd import api, synth
+    cores = len(os.sched_getaffinity(0))
+    f = lambda t: None if t is None else t.double().contiguous().numpy()
+    plan = []
+    for wname, wl in calls:
+        one = wl.with_batch(1)
+        x, w, b = synth.make_inputs(one)
+        t0 = time.perf_counter()
+        oracle.conv(f(x), f(w), f(b), nthreads=cores, **expand(one))
+        t_one = time.perf_counter() - t0
+        n = max(1, min(wl.x_shape[0], int(target_s / len(calls) / max(t_one, 1e-6))))
+        sub = wl.with_batch(n)
+        p = call_plan(sub)
+        plan.append((wname, sub, synth.make_inputs(sub), p))
+    total_t, rounds = 0.0, 0
+    per = {}
+    while rounds == 0 or total_t < 0.5 * target_s:
+        for wname, sub, (x, w, b), p in plan:
+            t0 = time.perf_counter()
+            oracle.conv(f(x), f(w), f(b), nthreads=cores, **expand(sub))
+            dt = time.perf_counter() - t0
+            total_t += dt
+            _, _, t_roof = roof_of(api.kernel_name(p.kernel), int(p.variant), sub.dtype, float(p.flops),
+                                   float(p.bytes))
+            e = per.setdefault(wname, [0.0, 0.0, 0.0, 0.0])
+            e[0] += dt
+            e[1] += float(p.bytes)
+            e[2] += float(p.flops)
+            e[3] += t_roof * 1e-6
+        rounds += 1
+    rows = []
+    for wname, (t, nb, fl, tr) in per.items():
+        unit = UNITS[wname]
+        rows.append({"workload": wname, "unit": unit,
+                     "value": round(nb / t / 1e9 if unit == "GB/s" else fl / t / 1e12, 5)})
+    pct = 100.0 * sum(e[3] for e in per.values()) / sum(e[0] for e in per.values())
+    samples = ", ".join(f"{sub.name.split('@')[0]}:N={sub.x_shape[0]}" for _, sub, _, _ in plan)
+    out = {"value": round(pct, 6), "unit": "% of MI355X roofline", "cores": int(oracle.max_threads()),
+           "kind": "oracle", "cpu_model": cpu_model(), "per_workload": rows,
+           "sample": f"double-precision reference over {samples}, {rounds} pass(es), {total_t:.1f} s wall"}
+    if headline_pct is not None and pct > 0:
+        out["gpu_over_cpu"] = round(headline_pct / pct, 1)
+    return out
 
 
 def main():
@@ -205,32 +328,29 @@ def main():
     if a.probe_copy:
         copy_probe(a.probe_copy, a.steps, a.warmup)
         return
-    calls, unit = workload_calls(a.workload)
+    if a.probe_mfma or a.probe_lds:
+        unit_probe("mfma" if a.probe_mfma else "lds", a.steps, a.warmup)
+        return
+    calls = workload_calls(a.workload)
 
     # ---- bind / out_shape / plan once per call (host time reported) ----
-    preps, host_us = [], []
-    per_call_bytes = []
-    for wl in calls:
+    preps, host_us, per_call_bytes = [], [], []
+    for wname, wl in calls:
         x, w, b = synth.make_inputs(wl)
-        kw = expand(wl)
         t0 = time.perf_counter()
-        args = api.make_args(transposed=kw["transposed"], groups=kw["groups"], stride=kw["stride"],
-                             padding_before=kw["padding_before"], padding_after=kw["padding_after"],
-                             dilation=kw["dilation"],
-                             output_padding=kw["output_padding"] if kw["transposed"] else None)
-        p = api.Prepared(x, w, b, args)
+        p = api.Prepared(x, w, b, make_args(wl))
         host_us.append((time.perf_counter() - t0) * 1e6)
         footprint = (x.numel() + w.numel() + (b.numel() if b is not None else 0)) * x.element_size() + \
             int(torch.Size(p.sizes).numel()) * x.element_size()
         per_call_bytes.append(footprint)
-        preps.append((wl, p, (x, w, b)))
+        preps.append((wname, wl, p, (x, w, b)))
 
     # ---- device buffers, rotated so a buffer's reuse is >= ~1 GiB apart ----
     step_bytes = sum(per_call_bytes)
     R = a.rotate or max(2, -(-(1 << 30) // max(step_bytes, 1)) + 1)
     R = min(R, 64)
     sets = []
-    for (wl, p, (x, w, b)) in preps:
+    for (_, wl, p, (x, w, b)) in preps:
         rs = []
         for _ in range(R):
             xd = torch.empty_strided(x.shape, x.stride(), dtype=x.dtype, device=dev)
@@ -246,7 +366,7 @@ def main():
 
     def step(i, evs=None):
         r = i % R
-        for c, (wl, p, _) in enumerate(preps):
+        for c, (_, wl, p, _) in enumerate(preps):
             xd, wd, bd, yd, ws = sets[c][r]
             if evs is not None:
                 evs[c][0].record(stream)
@@ -266,65 +386,78 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / a.steps
 
-    # ---- per-kernel durations with events on the launch stream ----
+    # ---- per-call durations with events on the launch stream ----
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
            for _ in preps] for _ in range(a.steps)]
     for i in range(a.steps):
         step(a.warmup + a.steps + i, ev[i])
     torch.cuda.synchronize()
     per_call = []
-    for c, (wl, p, _) in enumerate(preps):
+    for c, (wname, wl, p, _) in enumerate(preps):
         durs = sorted(ev[i][c][0].elapsed_time(ev[i][c][1]) for i in range(a.steps))
         avg_us = 1e3 * sum(durs) / len(durs)
         med_us = 1e3 * durs[len(durs) // 2]
         kname = api.kernel_name(p.plan.kernel)
         flops, nbytes = float(p.plan.flops), float(p.plan.bytes)
-        per_call.append(dict(call=wl.name, kernel=kname, variant=int(p.plan.variant), avg_us=round(avg_us, 2),
-                             median_us=round(med_us, 2),
+        bound, peak, t_roof = roof_of(kname, int(p.plan.variant), wl.dtype, flops, nbytes)
+        achieved = nbytes / avg_us / 1e3 if bound == "hbm" else flops / avg_us / 1e6
+        per_call.append(dict(workload=wname, call=wl.name, kernel=kname, variant=int(p.plan.variant),
+                             avg_us=round(avg_us, 2), median_us=round(med_us, 2),
                              GBps=round(nbytes / avg_us / 1e3, 1), TFLOPs=round(flops / avg_us / 1e6, 2),
-                             bytes=int(nbytes), flops=int(flops), host_plan_us=round(host_us[c], 1)))
+                             bytes=int(nbytes), flops=int(flops), bound=bound, roof_us=round(t_roof, 3),
+                             frac=round(achieved / peak, 4), host_plan_us=round(host_us[c], 1)))
 
-    total_bytes = sum(c["bytes"] for c in per_call)
-    total_flops = sum(c["flops"] for c in per_call)
-    if unit == "GB/s":
-        value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    # ---- per-workload rows and the headline ----
+    rows = []
+    for wname in dict.fromkeys(c["workload"] for c in per_call):
+        cs = [c for c in per_call if c["workload"] == wname]
+        t = sum(c["avg_us"] for c in cs)
+        unit = UNITS[wname]
+        val = sum(c["bytes"] for c in cs) / t / 1e3 if unit == "GB/s" else sum(c["flops"] for c in cs) / t / 1e6
+        rows.append({"workload": wname, "calls": len(cs), "unit": unit, "value": round(val, 2),
+                     "us": round(t, 2), "roof_us": round(sum(c["roof_us"] for c in cs), 3),
+                     "frac_of_roofline": round(sum(c["roof_us"] for c in cs) / t, 4)})
+    roof_total_us = sum(c["roof_us"] for c in per_call)
+    if a.workload == "all":
+        value, unit = 100.0 * roof_total_us / (ms_per_step * 1e3), "% of MI355X roofline"
     else:
-        value = total_flops / (ms_per_step * 1e-3) / 1e12
+        unit = UNITS[a.workload]
+        tot = sum(c["bytes"] for c in per_call) if unit == "GB/s" else sum(c["flops"] for c in per_call)
+        value = tot / (ms_per_step * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
 
-    # ---- roofline of the dominant kernel ----
+    # ---- roofline of the dominant call ----
     dom = max(per_call, key=lambda c: c["avg_us"])
-    ai = dom["flops"] / dom["bytes"]
-    # The 16-bit stencils (dw_cl, grp) multiply through packed dot2, two FMAs
-    # per lane and instruction; every other vector path issues one FMA.  The
-    # grouped kernel's matrix-core schedule (plan variant 1) multiplies on
-    # MFMA, whose ridge (~315 FLOP/B) puts every stencil on the HBM side.
-    valu_peak = VALU_DOT2_PEAK_TFLOPS if (dom["kernel"] in ("dw_cl", "grp") and wl0_dtype(calls) != "f32") \
-        else VALU_FP32_PEAK_TFLOPS
-    if dom["kernel"] == "grp" and dom["variant"] == 1:
-        valu_peak = MFMA_BF16_PEAK_TFLOPS
-    if dom["kernel"] in ("igemm", "igemm_t"):
-        roof = dict(bound="mfma", achieved=dom["TFLOPs"], peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s")
-    elif ai > valu_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof = dict(bound="alu", achieved=dom["TFLOPs"], peak=valu_peak, unit="TFLOP/s")
-    else:
+    if dom["bound"] == "hbm":
         roof = dict(bound="hbm", achieved=dom["GBps"], peak=HBM_PEAK_GBS, unit="GB/s")
+    else:
+        _, peak, _ = roof_of(dom["kernel"], dom["variant"], next(wl.dtype for _, wl, _, _ in preps
+                                                                   if wl.name == dom["call"]),
+                             dom["flops"], dom["bytes"])
+        roof = dict(bound=dom["bound"], achieved=dom["TFLOPs"], peak=peak, unit="TFLOP/s")
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(dom["kernel"], dom["call"])
     roof["kernel"] = dom["kernel"]
     roof["call"] = dom["call"]
     roof["avg_us"] = dom["avg_us"]
+    roof["units_per_launch"] = dom["flops"] if roof["unit"] == "TFLOP/s" else dom["bytes"]
 
-    wl0 = calls[0]
-    config = {"workload": a.workload, "calls": [c.name for c in calls], "dtype": wl0.dtype,
-              "rotation_sets": R, "timing": "wall clock over K steps; per-kernel HIP events"}
+    dtypes = sorted({wl.dtype for _, wl, _, _ in preps})
+    config = {"workload": a.workload, "calls": [wl.name for _, wl, _, _ in preps], "dtypes": dtypes,
+              "rotation_sets": R, "timing": "wall clock over K steps; per-call HIP events on the launch stream",
+              "headline": ("sum over the calls of their time at the roofline / measured step time"
+                           if a.workload == "all" else "algorithmic units of a step / measured step time")}
     out = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": wl0.dtype, "data": "synthetic",
-           "config": config, "roofline": roof, "per_call": per_call}
+           "scaling": "weak", "vs_baseline": None, "dtype": dtypes[0] if len(dtypes) == 1 else "mixed",
+           "data": "synthetic", "config": config, "roofline": roof, "per_workload": rows, "per_call": per_call}
     if a.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:
-        out["cpu_baseline"] = cpu_baseline(calls, unit, a.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(calls, a.cpu_seconds, value if a.workload == "all" else None)
+        if a.workload != "all":
+            # Single-workload runs: the CPU figure in the workload's own unit.
+            pw = out["cpu_baseline"]["per_workload"][0]
+            out["cpu_baseline"].update(value=pw["value"], unit=pw["unit"])
     print(json.dumps(out), flush=True)
 
 

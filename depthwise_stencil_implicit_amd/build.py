@@ -16,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmiconv.so")
+PROBE_SRC = os.path.join(PKG, "probe", "probe.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libmiconv_probe.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
@@ -71,7 +73,25 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The measurement probes (MFMA issue rate, LDS read bandwidth): a small
+    library of their own, loaded only by the benchmark's probe modes."""
+    tmp = PROBE_LIB + ".tmp"
+    # MFMA results in VGPRs: with accumulation registers the allocator moves
+    # the probe's accumulators between rounds, which would time the moves.
+    cmd = [os.path.join(ROCM, "bin", "hipcc"), *HIP_FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form", "-shared", PROBE_SRC,
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
