@@ -12,7 +12,8 @@ MAX_RANK = 5
 MAX_SPATIAL = 3
 
 F32, F16, BF16 = 0, 1, 2
-OK, EINVAL, EUNSUPPORTED, ELAYOUT, EALIGN, EDEVICE = range(6)
+OK, EINVAL, EUNSUPPORTED, ELAYOUT, EALIGN, EDEVICE, ENOSPACE = range(7)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 PAD_EXPLICIT, PAD_SAME, PAD_VALID = 0, 1, 2
 K_AUTO, K_DW_CL, K_PLANE, K_GRP, K_REDUCE, K_IGEMM, K_IGEMM_T = -1, 1, 2, 3, 4, 5, 6
 KERNELS = {"auto": K_AUTO, "dw_cl": K_DW_CL, "plane": K_PLANE, "grp": K_GRP, "reduce": K_REDUCE,
@@ -60,8 +61,8 @@ class ConvPlanOpts(ctypes.Structure):
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmiconv.so")
 
 # Every symbol include/miconv.h declares.
-EXPORTS = ("conv_bind", "conv_out_shape", "conv_plan", "conv_plan_ex", "conv_run", "conv_kernel_name",
-           "conv_status_string", "conv_abi_version")
+EXPORTS = ("conv_bind", "conv_out_shape", "conv_plan", "conv_plan_ex", "conv_run", "conv_run_noalloc",
+           "conv_kernel_name", "conv_status_string", "conv_abi_version")
 
 _lib = None
 
@@ -88,6 +89,9 @@ def lib():
         L.conv_run.argtypes = [P(ConvPlan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.conv_run.restype = ctypes.c_int
+        L.conv_run_noalloc.argtypes = [P(ConvPlan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+        L.conv_run_noalloc.restype = ctypes.c_int
         L.conv_kernel_name.argtypes = [_i32]
         L.conv_kernel_name.restype = ctypes.c_char_p
         L.conv_status_string.argtypes = [_i32]

@@ -102,8 +102,9 @@ extern "C" const char *conv_status_string(int32_t status)
     case CONV_ELAYOUT: return "output layout differs from conv_out_shape";
     case CONV_EALIGN: return "pointer not aligned to its element size";
     case CONV_EDEVICE: return "no usable GPU or HIP launch error";
+    case CONV_ENOSPACE: return "the plan needs more scratch than conv_run_noalloc's fixed device array holds";
     default: return "unknown status";
     }
 }
 
-extern "C" int32_t conv_abi_version(void) { return 1; }
+extern "C" int32_t conv_abi_version(void) { return 2; }

@@ -64,7 +64,8 @@ typedef enum conv_status {
     CONV_EUNSUPPORTED = 2, /* forced kernel outside its supported domain */
     CONV_ELAYOUT = 3,      /* y's sizes/strides differ from conv_out_shape */
     CONV_EALIGN = 4,       /* a pointer is not aligned to its element size */
-    CONV_EDEVICE = 5       /* no usable GPU, or a HIP launch/runtime error */
+    CONV_EDEVICE = 5,      /* no usable GPU, or a HIP launch/runtime error */
+    CONV_ENOSPACE = 6      /* conv_run_noalloc: the plan needs more scratch than the fixed array */
 } conv_status;
 
 typedef enum conv_padding_mode {
@@ -249,6 +250,28 @@ MICONV_API int conv_plan_ex(const conv_desc *d, const conv_tensor *y, const conv
  */
 MICONV_API int conv_run(const conv_plan_t *p, const void *x, const void *w, const void *b, void *y,
              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Size of the device-resident scratch array of conv_run_noalloc, MiB. */
+#define MICONV_NOALLOC_SCRATCH_MIB 32
+
+/*
+ * conv_run_noalloc -- conv_run for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels, with the workspace taken from a
+ * file-scope device array of MICONV_NOALLOC_SCRATCH_MIB MiB that each GPU
+ * holds until the process ends.  It calls no allocating routine.
+ *
+ *   p, x, w, b, y, stream   as for conv_run.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents: calls that overlap in time on one GPU race.  Plans whose
+ * kernels need no workspace run exactly as with conv_run.
+ *
+ * Returns as conv_run, or CONV_ENOSPACE when p->workspace_bytes exceeds the
+ * array (nothing is launched).
+ */
+MICONV_API int conv_run_noalloc(const conv_plan_t *p, const void *x, const void *w, const void *b, void *y,
+                                void *stream);
 
 /* Name of a conv_kernel value ("dw_cl", "plane", ...), or "?" . */
 MICONV_API const char *conv_kernel_name(int32_t kernel);

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_names():
     lib = A.lib()
-    assert lib.conv_abi_version() == 1
+    assert lib.conv_abi_version() == 2
     for name, val in A.KERNELS.items():
         assert lib.conv_kernel_name(val).decode() == name
     assert lib.conv_kernel_name(99).decode() == "?"
@@ -48,8 +48,10 @@ PROBE = r"""
 #include "miconv.h"
 #define P(T, F) printf(#T "." #F " %zu\n", offsetof(T, F))
 int main(void) {
-  printf("conv_tensor %zu\nconv_args %zu\nconv_desc %zu\nconv_plan_t %zu\n",
-         sizeof(conv_tensor), sizeof(conv_args), sizeof(conv_desc), sizeof(conv_plan_t));
+  printf("conv_tensor %zu\nconv_args %zu\nconv_desc %zu\nconv_plan_t %zu\nconv_plan_opts %zu\n",
+         sizeof(conv_tensor), sizeof(conv_args), sizeof(conv_desc), sizeof(conv_plan_t),
+         sizeof(conv_plan_opts));
+  P(conv_plan_opts, force_variant); P(conv_plan_opts, reserved);
   P(conv_args, groups); P(conv_args, stride); P(conv_args, output_padding);
   P(conv_desc, N); P(conv_desc, in); P(conv_desc, output_padding); P(conv_desc, x); P(conv_desc, b);
   P(conv_plan_t, y); P(conv_plan_t, kernel); P(conv_plan_t, workspace_bytes); P(conv_plan_t, tile);
@@ -66,8 +68,10 @@ def test_struct_layout_matches_ctypes(tmp_path):
     subprocess.check_call(["gcc", "-std=c99", f"-I{os.path.dirname(HEADER)}", str(src), "-o", str(exe)])
     got = dict(ln.rsplit(" ", 1) for ln in subprocess.check_output([str(exe)], text=True).splitlines())
     expect = {"conv_tensor": ctypes.sizeof(A.ConvTensor), "conv_args": ctypes.sizeof(A.ConvArgs),
-              "conv_desc": ctypes.sizeof(A.ConvDesc), "conv_plan_t": ctypes.sizeof(A.ConvPlan)}
-    fields = {"conv_args": A.ConvArgs, "conv_desc": A.ConvDesc, "conv_plan_t": A.ConvPlan}
+              "conv_desc": ctypes.sizeof(A.ConvDesc), "conv_plan_t": ctypes.sizeof(A.ConvPlan),
+              "conv_plan_opts": ctypes.sizeof(A.ConvPlanOpts)}
+    fields = {"conv_args": A.ConvArgs, "conv_desc": A.ConvDesc, "conv_plan_t": A.ConvPlan,
+              "conv_plan_opts": A.ConvPlanOpts}
     for key, val in got.items():
         if "." in key:
             struct, field = key.split(".")
