@@ -166,4 +166,37 @@ __device__ __forceinline__ void mma_16x16x32_f32(const float (&a)[8], const floa
     for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin; block b is remapped so
+// that each XCD gets one contiguous range of tiles (tiles that share input
+// rows or weight slices then share that XCD's L2).
+__device__ __forceinline__ int xcd_tile(int b, int total)
+{
+    const int q = total >> 3, r = total & 7;
+    const int xcd = b & 7, local = b >> 3;
+    const int off = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+    return off + local;
+}
+
+// A workgroup barrier without a memory fence: a compiler-only memory
+// clobber keeps LDS accesses on their side of it.  Before it each wave waits
+// for its own direct-to-LDS loads of the stage about to be read, so after it
+// every wave's loads have landed; a fenced __syncthreads() would instead
+// drain every load in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Byte offset of 16-byte chunk c of LDS row r with KC chunks per row.  KC = 8:
+// c ^ (r & 7); KC = 4: c ^ ((r >> 1) & 3).  Either way the 8 lanes of one
+// ds_read_b128 cycle (8 consecutive rows, one logical chunk) land on 8
+// different 16-byte bank groups.
+template <int KC> __device__ __forceinline__ int swz_k(int r, int c)
+{
+    if constexpr (KC == 8) return (r * 8 + (c ^ (r & 7))) * 16;
+    else return (r * 4 + (c ^ ((r >> 1) & 3))) * 16;
+}
+
 }  // namespace miconv

@@ -38,6 +38,16 @@ int igemm_num_cfgs();
 // The 64-row schedule that runs the rows a sparse last round would leave to a
 // few CUs; the planner does not choose it for whole calls.
 constexpr int IG_TAIL_CFG = 11;
+// Transposed 1-D calls with stride 2: both output phases per workgroup from
+// one halo tile of input rows (a kernel of its own, not a table entry).
+constexpr int IG_T1_CFG = 12;   // four waves, two stages, 256 rows j per tile
+constexpr int IG_T1B_CFG = 13;  // eight waves, three stages, 448 rows j (2 or 4 taps)
+// Smallest halo shift of such a call and the spread of the shifts (span may
+// be NULL); false when they spread over more than the kernel's 64 spare halo
+// rows.
+bool igemm_t1_shifts(const conv_desc &d, int *dmin, int *span);
+int igemm_t1_lds_bytes(int taps, int variant);
+int igemm_t1_rows(int variant);
 
 // Plan-field indices for the implicit GEMM (plan.tile[]).
 // IG_TAIL: 0, or (row tiles of the full-size launch) | (K ranges of the
@@ -104,6 +114,8 @@ enum { DW_CW = 0, DW_OCOLS = 1, DW_CHCHUNKS = 2, DW_COLCHUNKS = 3, DW_XBYTES = 4
 // Launchers (defined in the .hip files).  `vec` selects the 16-byte path.
 int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *ws,
                  void *stream, bool vec);
+int launch_igemm_t1(const conv_plan_t &p, const void *x, const void *wpacked, const void *b, void *y,
+                    void *stream);
 int launch_plane(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream);
 int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream,
                 bool vec);

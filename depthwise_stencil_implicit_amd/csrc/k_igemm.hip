@@ -69,14 +69,6 @@ struct IgArgs {
     int32_t w_bytes;              // bytes of the repacked weights (buffer range)
 };
 
-__device__ __forceinline__ int xcd_tile(int b, int total)
-{
-    const int q = total >> 3, r = total & 7;
-    const int xcd = b & 7, local = b >> 3;
-    const int off = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
-    return off + local;
-}
-
 // Byte offset of 16-byte chunk `c` of LDS row `r` (rows of 8 chunks).
 __device__ __forceinline__ int swz(int r, int c) { return (r * 8 + (c ^ (r & 7))) * 16; }
 
@@ -387,23 +379,6 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgArgs a)
 // accesses on their side of it); before it each wave waits for its own loads of
 // the stage about to be read, so after it every wave's loads have landed.  A
 // fenced __syncthreads() would instead drain every load in flight.
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Byte offset of 16-byte chunk c of LDS row r with KC chunks per row.  KC = 8:
-// c ^ (r & 7); KC = 4: c ^ ((r >> 1) & 3).  Either way the 8 lanes of one
-// ds_read_b128 cycle (8 consecutive rows, one logical chunk) land on 8
-// different 16-byte bank groups.
-template <int KC> __device__ __forceinline__ int swz_k(int r, int c)
-{
-    if constexpr (KC == 8) return (r * 8 + (c ^ (r & 7))) * 16;
-    else return (r * 4 + (c ^ ((r >> 1) & 3))) * 16;
-}
-
 template <typename T, int BM, int BN, int WM, int WN, int STAGES, int KC>
 __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
 {
@@ -1026,6 +1001,11 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
     default: e = launch_repack<bf16_t>(p, w, ws, s); break;
     }
     if (e != hipSuccess) return CONV_EDEVICE;
+    if (p.variant == IG_T1_CFG || p.variant == IG_T1B_CFG) {
+        // Both phases per workgroup; it needs the 16-byte loads of x.
+        if (!vec) return CONV_EALIGN;
+        return launch_igemm_t1(p, x, ws, b, y, stream);
+    }
     auto run = [&](const IgArgs &args, int variant) {
         switch (d.dtype) {
         case CONV_F32: return launch_typed<float>(args, variant, vec, s);

@@ -241,6 +241,38 @@ bool geom_igemm(const conv_desc &d, conv_plan_t &p, int force_variant)
     const int64_t xspan = span_bytes(d.x, es);
     // Element offsets into x are 32-bit in the kernel.
     if (xspan / es >= kI32 || rows >= kI32) return false;
+    const int64_t cig_v = cig(d);
+    // Transposed 1-D calls with stride 2 and channel-contiguous 16-byte chunks
+    // of x: both output phases per workgroup from one halo tile of input rows.
+    {
+        int dmin = 0;
+        const int64_t ev = 16 / es;
+        const bool t1 = d.transposed && d.spatial == 1 && d.stride[0] == 2 && d.dtype != CONV_F32 && d.k[0] >= 2 &&
+                        d.k[0] <= 8 && igemm_t1_shifts(d, &dmin, nullptr) && d.x.strides[1] == 1 && cig_v % ev == 0 &&
+                        d.x.strides[0] % ev == 0 && d.x.strides[2] % ev == 0 && xspan < kI32 - 4096;
+        const bool t1b = t1 && (d.k[0] == 2 || d.k[0] == 4);
+        if ((force_variant == IG_T1_CFG && !t1) || (force_variant == IG_T1B_CFG && !t1b)) return false;
+        if (t1 && (force_variant < 0 || force_variant == IG_T1_CFG || force_variant == IG_T1B_CFG)) {
+            const int v = force_variant >= 0 ? force_variant : IG_T1_CFG;
+            const int64_t cig_pad = round_up(cig_v, 64), cog_pad = round_up(cog(d) > 0 ? cog(d) : 1, 64);
+            const int64_t J = cdiv(d.out[0], 2), jtiles = cdiv(J, igemm_t1_rows(v));
+            p.variant = v;
+            p.tile[IG_CIG_PAD] = cig_pad;
+            p.tile[IG_COG_PAD] = cog_pad;
+            p.tile[IG_PHASES] = 2;
+            p.tile[IG_MTILES] = d.N * jtiles;
+            p.tile[IG_NTILES] = cog_pad / 64;
+            p.tile[IG_ROWS] = d.N * J;
+            p.tile[IG_XBYTES] = xspan;
+            p.tile[IG_TAIL] = 0;
+            p.grid[0] = d.groups * d.N * jtiles * (cog_pad / 64);
+            p.block = v == IG_T1_CFG ? 256 : 512;
+            p.lds_bytes = igemm_t1_lds_bytes((int)d.k[0], v);
+            p.workspace_bytes = igemm_wbytes(d.groups, cog_pad, d.k[0], cig_pad, es);
+            p.vec_ok = 1;
+            return p.workspace_bytes < kI32;
+        }
+    }
     int best = -1;
     double best_cost = 0;
     const int lo = d.dtype == CONV_F32 ? 5 : 0, hi = d.dtype == CONV_F32 ? 5 : igemm_num_cfgs() - 1;

@@ -477,10 +477,14 @@ def test_tail_rows_split_k(transposed):
     bias) against the reference, sampled densely there and at the boundary."""
     wl = _tail_case(transposed)
     _flush(f"tail rows: {_desc(wl)}")
-    x, w, b, y = run_gpu(wl)
+    # The transposed call runs the phase-split tiles (configuration 0); by
+    # default it would take the both-phases kernel, which has tests of its own.
+    v = 0 if transposed else None
+    x, w, b, y = run_gpu(wl, force="igemm_t" if transposed else None, variant=v)
     plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in expand_kw(wl).items()
                                                   if k not in ("groups", "transposed")},
-                                               groups=wl.groups, transposed=wl.transposed)).plan
+                                               groups=wl.groups, transposed=wl.transposed),
+                        force_kernel="igemm_t" if transposed else None, force_variant=v).plan
     tail = int(plan.tile[7])
     if not transposed:
         assert tail != 0 and (tail >> 24) > 1, "shape chosen to exercise the split-K rows"
@@ -509,10 +513,12 @@ def test_tail_rows_whole_output(transposed):
     fp32 partial sums reduced with the bias)."""
     wl = _tail_case(transposed)
     _flush(f"tail rows, whole output: {_desc(wl)}")
-    x, w, b, y = run_gpu(wl)
+    v = 0 if transposed else None
+    x, w, b, y = run_gpu(wl, force="igemm_t" if transposed else None, variant=v)
     kw = expand_kw(wl)
     plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
-                                               groups=wl.groups, transposed=wl.transposed)).plan
+                                               groups=wl.groups, transposed=wl.transposed),
+                        force_kernel="igemm_t" if transposed else None, force_variant=v).plan
     assert int(plan.variant) == 0, "shape chosen for the 256x256 tile"
     if not transposed:
         assert (int(plan.tile[7]) >> 24) > 1 and (int(plan.tile[7]) & 0xffffff) >= 2
@@ -662,3 +668,64 @@ def test_grp_mma_every_kernel(wl):
                         force_kernel="grp").plan
     assert int(plan.variant) == 1, "shape chosen for the matrix-core schedule"
     check_full(wl, force="grp")
+
+
+# ------------------- transposed 1-D, stride 2, both phases per workgroup --
+
+def _t1_cases():
+    """Transposed 1-D stride-2 calls inside the both-phases kernel's domain
+    (16-bit, channel-contiguous x in whole 16-byte chunks): 2 to 8 taps,
+    dilation 1 to 3 (an even dilation leaves one phase without taps),
+    padding_before from 0 to 5, output_padding, groups, channel counts that are
+    not multiples of the 32-channel block or the 64-channel tile, lengths below
+    and above one 256-row tile, and both output layouts (contiguous, and
+    channels-last through a channels-last weight)."""
+    rng = np.random.default_rng(12)
+    out = []
+    i = 0
+    while len(out) < 20:
+        k = int(rng.integers(2, 9))
+        dil = int(rng.choice([1, 1, 1, 2, 3]))
+        pb = int(rng.integers(0, 6))
+        pa = int(rng.integers(0, 6))
+        op = int(rng.integers(0, max(2, dil)))
+        L = int(rng.choice([5, 37, 256, 300, 777]))
+        groups = int(rng.choice([1, 1, 2]))
+        cig = int(rng.choice([8, 16, 40, 64, 104]))
+        cog = int(rng.choice([1, 9, 64, 70, 130]))
+        if (L - 1) * 2 - pb - pa + dil * (k - 1) + op + 1 < 1:
+            continue
+        wl = synth.random_case(7600 + i, rank=1, transposed=True, dtype=["bf16", "f16"][i % 2], channels_last=True,
+                               N=int(rng.integers(1, 3)), C_in=groups * cig, C_out=groups * cog, groups=groups,
+                               L=[L], k=[k], stride=[2], padding_before=[pb], padding_after=[pa], dilation=[dil],
+                               output_padding=[op], has_bias=bool(i % 3))
+        out.append((wl, i % 4 == 3))
+        i += 1
+    return out
+
+
+@pytest.mark.parametrize("variant", [12, 13])
+@pytest.mark.parametrize("wl,w_cl", _t1_cases(), ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_transposed_both_phases_kernel(wl, w_cl, variant):
+    """Whole output of the both-phases transposed kernels against the
+    reference: plan variant 12 (four waves, two stages) and 13 (eight waves,
+    three stages, 2 or 4 taps); w_cl stores the weight channels-last, which
+    makes y channels-last too (channel-fastest write-out)."""
+    if variant == 13 and wl.w_shape[2] not in (2, 4):
+        pytest.skip("the eight-wave kernel takes 2 or 4 taps")
+    _flush(f"transposed both phases, variant {variant} (w_cl={w_cl}): {_desc(wl)}")
+    x, w, b = synth.make_inputs(wl, device="cuda")
+    if w_cl:
+        w = synth.channels_last_copy(w)
+    kw = expand_kw(wl)
+    prep = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=True),
+                        force_kernel="igemm_t", force_variant=variant)
+    assert api.kernel_name(prep.plan.kernel) == "igemm_t" and int(prep.plan.variant) == variant
+    y = prep.run(x, w, b, prep.empty_output(x.device), prep.workspace(x.device))
+    torch.cuda.synchronize()
+    assert tuple(y.stride()) == oracle.out_strides(tuple(y.shape), tuple(x.shape), tuple(x.stride()),
+                                                   tuple(w.shape), tuple(w.stride()))
+    xr, wr, br = ref_inputs(x, w, b)
+    yr, A = oracle.conv(xr, wr, br, **kw)
+    assert_close(y, yr, A, EPS[wl.dtype], wl.name)
