@@ -10,6 +10,8 @@ Contents
     contiguous) -- see ``out_strides`` for the reading.
   * ``conv``: full output and per-element bound A, computed by ``oracle.c``.
   * ``conv_points``: the same for selected output elements only.
+  * ``conv_backward``: the input, weight and bias gradients for a given
+    output gradient, each with its bound.
 
 Semantics follow executorch PR #25084 ("Add triton::convolution and the conv
 routing framework", description), the forward index map printed in
@@ -74,6 +76,9 @@ def _load():
         lib.oracle_conv_points_f64.restype = ctypes.c_int
         lib.oracle_out_len.argtypes = [ctypes.c_int32] + [ctypes.c_int64] * 7
         lib.oracle_out_len.restype = ctypes.c_int64
+        lib.oracle_conv_backward_f64.argtypes = [ctypes.POINTER(_Geom), dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                                 ctypes.c_int]
+        lib.oracle_conv_backward_f64.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -265,3 +270,30 @@ def conv_points(x, w, b, points, *, stride=1, padding_before=0, padding_after=0,
         if rc != 0:
             raise ValueError("oracle rejected the geometry or a point")
     return y, A
+
+
+def conv_backward(x, w, gy, *, with_bias=True, stride=1, padding_before=0, padding_after=0, dilation=1,
+                  groups=1, transposed=False, output_padding=0, nthreads: int = 0):
+    """Gradients of the canonical op for an output gradient ``gy`` (float64).
+
+    Returns (dx, Adx, dw, Adw, db, Adb): dx like x, dw like w, db [C_out]
+    (None when ``with_bias`` is false), each with the sum of the absolute
+    values of its terms.  Follows the backward of the convolution lowering in
+    torch/_inductor/kernel/conv.py (convolution_backward): input, weight and
+    bias gradients of the same op, stated in ``oracle.c``.
+    """
+    x, w, gy = _prep(x), _prep(w), _prep(gy)
+    g = _geom(x, w, stride, padding_before, padding_after, dilation, groups, transposed, output_padding)
+    shape = (g.N, g.C_out) + tuple(g.O[i] for i in range(g.rank))
+    if gy.shape != shape:
+        raise ValueError(f"gy has shape {gy.shape}, the output is {shape}")
+    dx, Adx = np.empty_like(x), np.empty_like(x)
+    dw, Adw = np.empty_like(w), np.empty_like(w)
+    db = np.empty(g.C_out) if with_bias else None
+    Adb = np.empty(g.C_out) if with_bias else None
+    rc = _load().oracle_conv_backward_f64(ctypes.byref(g), _dptr(x), _dptr(w), _dptr(gy), _dptr(dx), _dptr(Adx),
+                                          _dptr(dw), _dptr(Adw), _dptr(db) if with_bias else None,
+                                          _dptr(Adb) if with_bias else None, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the geometry")
+    return dx, Adx, dw, Adw, db, Adb

@@ -38,6 +38,17 @@
  * Loops are the definition written out: no blocking, no reordering of a
  * single element's sum beyond the natural (input channel, tap) order.
  * Threads (OpenMP) split independent (n, output channel) pairs only.
+ *
+ * Gradients (torch/_inductor/kernel/conv.py, convolution_backward: the
+ * input, weight and bias gradients of the op).  Both the forward and the
+ * transposed op are sums of terms x[n, ci, i] * w(co, c, t) over the pairs
+ * (o, t) whose term reads input position i; with gy the gradient of y,
+ *   dx[n, ci, i]  = sum over (co of ci's group, t, o whose term reads i) of gy[n, co, o] * w(co, c, t)
+ *   dw(co, c, t)  = sum over (n, o whose term at t exists) of gy[n, co, o] * x[n, ci, i(o, t)]
+ *   db[co]        = sum over (n, o) of gy[n, co, o]
+ * where w(co, c, t) is the weight element the term uses (forward w[co, c, t],
+ * transposed w[ci, j, t]).  Beside each gradient element the oracle returns
+ * the sum of the absolute values of its terms, the bound the tests use.
  */
 #include <math.h>
 #include <stdint.h>
@@ -91,6 +102,25 @@ static int64_t src_index(int32_t transposed, int64_t o, int64_t t, int64_t L,
         i = num / s;
     }
     return (i >= 0 && i < L) ? i : -1;
+}
+
+/* The output position whose term reads input position i at tap t in one
+ * dimension, or -1: the exact inverse of src_index (for a forward term
+ * i = o*s - pb + t*d, so o = (i + pb - t*d)/s when exact; for a transposed
+ * term i = (o + pb - t*d)/s, so o = i*s - pb + t*d), limited to [0, O). */
+static int64_t dst_index(int32_t transposed, int64_t i, int64_t t, int64_t O,
+                         int64_t s, int64_t pb, int64_t d)
+{
+    int64_t o;
+    if (!transposed) {
+        int64_t num = i + pb - t * d;
+        if (num < 0) return -1;
+        if (num % s != 0) return -1;
+        o = num / s;
+    } else {
+        o = i * s - pb + t * d;
+    }
+    return (o >= 0 && o < O) ? o : -1;
 }
 
 /* One output element y[n, co, o0, o1, o2] and its bound A. */
@@ -197,6 +227,109 @@ int oracle_conv_points_f64(const oracle_geom *g, const double *x, const double *
         const int64_t *r = idx + 5 * p;
         int64_t o[3] = {r[2], r[3], r[4]};
         conv_point(g, x, w, b, r[0], r[1], o, &y[p], &A[p]);
+    }
+    return 0;
+}
+
+/* Index of the weight element w(co, c, t) a term uses: forward
+ * w[co, c, t], transposed w[g*Cig + c, j, t] (co = g*Cog + j). */
+static int64_t w_index(const oracle_geom *g, int64_t co, int64_t c, int64_t t0, int64_t t1, int64_t t2)
+{
+    const int64_t Cig = g->C_in / g->groups, Cog = g->C_out / g->groups;
+    const int64_t grp = co / Cog, j = co % Cog;
+    if (!g->transposed) return (((co * Cig + c) * g->K[0] + t0) * g->K[1] + t1) * g->K[2] + t2;
+    return ((((grp * Cig + c) * Cog + j) * g->K[0] + t0) * g->K[1] + t1) * g->K[2] + t2;
+}
+
+/* Gradients of the op for a given gradient gy of its output.  x: [N, C_in,
+ * L...], w: the op's weight, gy: [N, C_out, O...], all contiguous.  dx, Adx:
+ * [N, C_in, L...]; dw, Adw: w's shape; db, Adb: [C_out] (db may be NULL).
+ * Returns 0, or -1 for an inconsistent geometry. */
+int oracle_conv_backward_f64(const oracle_geom *g, const double *x, const double *w, const double *gy,
+                             double *dx, double *Adx, double *dw, double *Adw, double *db, double *Adb,
+                             int nthreads)
+{
+    if (!geom_ok(g)) return -1;
+    const int64_t Cig = g->C_in / g->groups, Cog = g->C_out / g->groups;
+    const int64_t SL = g->L[0] * g->L[1] * g->L[2];
+    const int64_t SO = g->O[0] * g->O[1] * g->O[2];
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    /* dx: each input element gathers the terms that read it. */
+    const int64_t xpairs = g->N * g->C_in;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < xpairs; ++p) {
+        const int64_t n = p / g->C_in, ci = p % g->C_in;
+        const int64_t grp = ci / Cig, c = ci % Cig;
+        for (int64_t f = 0; f < SL; ++f) {
+            const int64_t i2 = f % g->L[2], i1 = (f / g->L[2]) % g->L[1], i0 = f / (g->L[2] * g->L[1]);
+            double sum = 0.0, asum = 0.0;
+            for (int64_t j = 0; j < Cog; ++j) {
+                const int64_t co = grp * Cog + j;
+                for (int64_t t0 = 0; t0 < g->K[0]; ++t0) {
+                    const int64_t o0 = dst_index(g->transposed, i0, t0, g->O[0], g->s[0], g->pb[0], g->d[0]);
+                    if (o0 < 0) continue;
+                    for (int64_t t1 = 0; t1 < g->K[1]; ++t1) {
+                        const int64_t o1 = dst_index(g->transposed, i1, t1, g->O[1], g->s[1], g->pb[1], g->d[1]);
+                        if (o1 < 0) continue;
+                        for (int64_t t2 = 0; t2 < g->K[2]; ++t2) {
+                            const int64_t o2 = dst_index(g->transposed, i2, t2, g->O[2], g->s[2], g->pb[2], g->d[2]);
+                            if (o2 < 0) continue;
+                            const double gv = gy[(((n * g->C_out + co) * g->O[0] + o0) * g->O[1] + o1) * g->O[2] + o2];
+                            const double pr = gv * w[w_index(g, co, c, t0, t1, t2)];
+                            sum += pr;
+                            asum += fabs(pr);
+                        }
+                    }
+                }
+            }
+            dx[p * SL + f] = sum;
+            Adx[p * SL + f] = asum;
+        }
+    }
+    /* dw: each weight element sums its terms over images and output positions. */
+    const int64_t wpairs = g->C_out * Cig;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < wpairs; ++p) {
+        const int64_t co = p / Cig, c = p % Cig;
+        const int64_t ci = (co / Cog) * Cig + c;
+        for (int64_t t0 = 0; t0 < g->K[0]; ++t0)
+            for (int64_t t1 = 0; t1 < g->K[1]; ++t1)
+                for (int64_t t2 = 0; t2 < g->K[2]; ++t2) {
+                    double sum = 0.0, asum = 0.0;
+                    for (int64_t n = 0; n < g->N; ++n)
+                        for (int64_t f = 0; f < SO; ++f) {
+                            const int64_t o2 = f % g->O[2], o1 = (f / g->O[2]) % g->O[1], o0 = f / (g->O[2] * g->O[1]);
+                            const int64_t i0 = src_index(g->transposed, o0, t0, g->L[0], g->s[0], g->pb[0], g->d[0]);
+                            const int64_t i1 = src_index(g->transposed, o1, t1, g->L[1], g->s[1], g->pb[1], g->d[1]);
+                            const int64_t i2 = src_index(g->transposed, o2, t2, g->L[2], g->s[2], g->pb[2], g->d[2]);
+                            if (i0 < 0 || i1 < 0 || i2 < 0) continue;
+                            const double pr = gy[(n * g->C_out + co) * SO + f] *
+                                              x[(((n * g->C_in + ci) * g->L[0] + i0) * g->L[1] + i1) * g->L[2] + i2];
+                            sum += pr;
+                            asum += fabs(pr);
+                        }
+                    const int64_t wi = w_index(g, co, c, t0, t1, t2);
+                    dw[wi] = sum;
+                    Adw[wi] = asum;
+                }
+    }
+    /* db: the output gradient summed over images and positions. */
+    if (db) {
+        for (int64_t co = 0; co < g->C_out; ++co) {
+            double sum = 0.0, asum = 0.0;
+            for (int64_t n = 0; n < g->N; ++n)
+                for (int64_t f = 0; f < SO; ++f) {
+                    const double v = gy[(n * g->C_out + co) * SO + f];
+                    sum += v;
+                    asum += fabs(v);
+                }
+            db[co] = sum;
+            Adb[co] = asum;
+        }
     }
     return 0;
 }

@@ -447,3 +447,115 @@ def test_out_strides_rule_cases(oracle_mod):
     # zero-size batch: contiguous, products over max(size, 1)
     assert oracle_mod.out_strides((0, 5, 3), (0, 5, 3), (15, 3, 1), (5, 5, 1),
                                   (5, 1, 1)) == (15, 3, 1)
+
+
+# ------------------------------------------------------------- gradients --
+
+def _torch_fn(x, w, b, *, stride, padding_before, padding_after, dilation, groups, transposed, output_padding):
+    """The op as differentiable torch CPU float64 ops (asymmetric padding by an
+    explicit pad for forward calls, a crop of the uncropped output for
+    transposed ones)."""
+    r = x.dim() - 2
+    if not transposed:
+        pads = []
+        for i in reversed(range(r)):
+            pads += [padding_before[i], padding_after[i]]
+        y = CONV[r](F.pad(x, pads), w, None, stride=tuple(stride), padding=0, dilation=tuple(dilation),
+                    groups=groups)
+    else:
+        full = CONVT[r](x, w, None, stride=tuple(stride), padding=0, output_padding=0, groups=groups,
+                        dilation=tuple(dilation))
+        ext = []
+        for i in reversed(range(r)):
+            ext += [0, output_padding[i]]
+        full = F.pad(full, ext)
+        sl = [slice(None), slice(None)]
+        for i in range(r):
+            L_full = full.shape[2 + i] - output_padding[i]
+            sl.append(slice(padding_before[i], L_full - padding_after[i] + output_padding[i]))
+        y = full[tuple(sl)]
+    if b is not None:
+        y = y + b.reshape((1, -1) + (1,) * r)
+    return y
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda wl: f"{wl.name}-r{len(wl.x_shape)-2}"
+                         f"{'T' if wl.transposed else 'F'}")
+def test_gradients_match_torch_autograd(oracle_mod, wl):
+    """dx, dw, db against torch CPU float64 autograd of the same op, for
+    forward and transposed calls of every rank (groups, dilation, strides,
+    asymmetric padding, output_padding)."""
+    x, w, b = synth.make_inputs(wl)
+    kw = kw_of(wl)
+    xt = x.double().requires_grad_(True)
+    wt = w.double().requires_grad_(True)
+    bt = b.double().requires_grad_(True) if b is not None else None
+    y = _torch_fn(xt, wt, bt, **kw)
+    gy = torch.randn(y.shape, dtype=torch.float64, generator=torch.Generator().manual_seed(wl.seed))
+    y.backward(gy)
+    dx, Adx, dw, Adw, db, Adb = oracle_mod.conv_backward(as64(x), as64(w), gy.numpy(), with_bias=b is not None,
+                                                         **kw)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=0, atol=1e-12 * (1 + Adx.max()))
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=0, atol=1e-12 * (1 + Adw.max()))
+    if b is not None:
+        np.testing.assert_allclose(db, bt.grad.numpy(), rtol=0, atol=1e-12 * (1 + Adb.max()))
+    # The bounds are the same sums over absolute values.
+    assert np.all(Adx >= np.abs(dx) - 1e-12) and np.all(Adw >= np.abs(dw) - 1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("transposed", [False, True])
+def test_gradient_adjoint_identities(oracle_mod, seed, transposed):
+    """For the bias-free op f(x, w), linear in each argument,
+    <f(x, w), gy> = <x, dx> = <w, dw>, and <1, gy> = sum(db)."""
+    rng = np.random.default_rng(40 + seed)
+    r = 1 + seed % 3
+    groups = 1 + seed % 2
+    cig, cog = 2, 3
+    L = tuple(int(v) for v in rng.integers(4, 8, r))
+    k = tuple(int(v) for v in rng.integers(1, 4, r))
+    s = tuple(int(v) for v in rng.integers(1, 4, r))
+    d = tuple(int(v) for v in rng.integers(1, 3, r))
+    pb = tuple(int(v) for v in rng.integers(0, 3, r))
+    pa = tuple(int(v) for v in rng.integers(0, 3, r))
+    op = tuple(int(rng.integers(0, max(si, di))) for si, di in zip(s, d)) if transposed else (0,) * r
+    x = rng.standard_normal((2, groups * cig) + L)
+    w = rng.standard_normal(((groups * cig, cog) if transposed else (groups * cog, cig)) + k)
+    kw = dict(stride=s, padding_before=pb, padding_after=pa, dilation=d, groups=groups, transposed=transposed,
+              output_padding=op)
+    try:
+        y, _ = oracle_mod.conv(x, w, None, **kw)
+    except ValueError:
+        pytest.skip("empty output for this draw")
+    gy = rng.standard_normal(y.shape)
+    dx, _, dw, _, db, _ = oracle_mod.conv_backward(x, w, gy, **kw)
+    f = float(np.sum(y * gy))
+    scale = max(1.0, float(np.sum(np.abs(y * gy))))
+    assert abs(float(np.sum(x * dx)) - f) <= 1e-12 * scale
+    assert abs(float(np.sum(w * dw)) - f) <= 1e-12 * scale
+    assert abs(float(np.sum(db)) - float(np.sum(gy))) <= 1e-12 * max(1.0, float(np.sum(np.abs(gy))))
+
+
+@pytest.mark.parametrize("transposed", [False, True])
+def test_gradients_brute_force(oracle_mod, transposed):
+    """Tiny shapes, integer values: dx = M^T gy and dw = Mw^T gy exactly,
+    with M and Mw the op's matrices in x and in w built column by column
+    from unit impulses through the (separately pinned) forward op."""
+    rng = np.random.default_rng(5)
+    kw = dict(stride=(2, 1), padding_before=(1, 0), padding_after=(0, 1), dilation=(1, 2), groups=2,
+              transposed=transposed, output_padding=(1, 0) if transposed else (0, 0))
+    x = rng.integers(-5, 6, (2, 4, 3, 4)).astype(float)
+    w = rng.integers(-5, 6, (4, 3, 2, 2) if transposed else (6, 2, 2, 2)).astype(float)
+    y, _ = oracle_mod.conv(x, w, None, **kw)
+    gy = rng.integers(-5, 6, y.shape).astype(float)
+    dx, _, dw, _, db, _ = oracle_mod.conv_backward(x, w, gy, **kw)
+    for arr, grad, which in ((x, dx, "x"), (w, dw, "w")):
+        exp = np.zeros(arr.size)
+        for j in range(arr.size):
+            e = np.zeros(arr.size)
+            e[j] = 1.0
+            col = oracle_mod.conv(e.reshape(arr.shape) if which == "x" else x,
+                                  w if which == "x" else e.reshape(arr.shape), None, **kw)[0]
+            exp[j] = float(np.sum(col * gy))
+        np.testing.assert_array_equal(grad.ravel(), exp, err_msg=which)
+    np.testing.assert_array_equal(db, gy.sum(axis=(0, 2, 3)))
