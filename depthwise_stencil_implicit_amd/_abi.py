@@ -54,6 +54,13 @@ class ConvPlan(ctypes.Structure):
                 ("block", _i32), ("lds_bytes", _i32), ("flops", _i64), ("bytes", _i64)]
 
 
+class ConvBwdPlan(ctypes.Structure):
+    _fields_ = [("d", ConvDesc), ("gy", ConvTensor), ("dx", ConvTensor), ("dw", ConvTensor), ("db", ConvTensor),
+                ("need_dx", _i32), ("need_dw", _i32), ("need_db", _i32), ("reserved0", _i32),
+                ("dgrad", ConvPlan), ("wg_tile", _i64 * 8), ("db_splits", _i64), ("workspace_bytes", _i64),
+                ("flops", _i64 * 3), ("bytes", _i64 * 3)]
+
+
 class ConvPlanOpts(ctypes.Structure):
     _fields_ = [("force_kernel", _i32), ("force_variant", _i32), ("reserved", _i32 * 6)]
 
@@ -62,6 +69,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmiconv.s
 
 # Every symbol include/miconv.h declares.
 EXPORTS = ("conv_bind", "conv_out_shape", "conv_plan", "conv_plan_ex", "conv_run", "conv_run_noalloc",
+           "conv_backward_layout", "conv_plan_backward", "conv_run_backward",
            "conv_kernel_name", "conv_status_string", "conv_abi_version")
 
 _lib = None
@@ -92,6 +100,12 @@ def lib():
         L.conv_run_noalloc.argtypes = [P(ConvPlan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
         L.conv_run_noalloc.restype = ctypes.c_int
+        L.conv_backward_layout.argtypes = [P(ConvDesc), P(ConvTensor), P(ConvTensor), P(ConvTensor), P(ConvTensor)]
+        L.conv_backward_layout.restype = ctypes.c_int
+        L.conv_plan_backward.argtypes = [P(ConvDesc), P(ConvTensor), _i32, _i32, _i32, P(ConvBwdPlan)]
+        L.conv_plan_backward.restype = ctypes.c_int
+        L.conv_run_backward.argtypes = [P(ConvBwdPlan)] + [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]
+        L.conv_run_backward.restype = ctypes.c_int
         L.conv_kernel_name.argtypes = [_i32]
         L.conv_kernel_name.restype = ctypes.c_char_p
         L.conv_status_string.argtypes = [_i32]

@@ -188,6 +188,68 @@ def conv(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None, *, 
     return prep.run(x, w, b, y, prep.workspace(x.device))
 
 
+# -------------------------------------------------------------- gradients --
+
+def _tensor_of(d: A.ConvTensor):
+    return tuple(d.sizes[: d.rank]), tuple(d.strides[: d.rank])
+
+
+class PreparedBackward:
+    """conv_plan_backward for fixed descriptors (reusable): the input, weight
+    and bias gradients of one call (torch/_inductor/kernel/conv.py,
+    convolution_backward)."""
+
+    def __init__(self, x: torch.Tensor, w: torch.Tensor, gy: torch.Tensor, args: A.ConvArgs, *,
+                 need_dx: bool = True, need_dw: bool = True, need_db: bool = True):
+        self.desc = conv_bind(describe(x), describe(w), None, args)
+        self.dtype = x.dtype
+        gyd = describe(gy)
+        self.plan = A.ConvBwdPlan()
+        _check(A.lib().conv_plan_backward(ctypes.byref(self.desc), ctypes.byref(gyd), int(need_dx), int(need_dw),
+                                          int(need_db), ctypes.byref(self.plan)))
+        dx, dw, db = A.ConvTensor(), A.ConvTensor(), A.ConvTensor()
+        _check(A.lib().conv_backward_layout(ctypes.byref(self.desc), ctypes.byref(gyd), ctypes.byref(dx) if need_dx
+                                            else None, ctypes.byref(dw), ctypes.byref(db)))
+        self.dx_layout = _tensor_of(dx) if need_dx else None
+        self.dw_layout = _tensor_of(dw) if need_dw else None
+        self.db_layout = _tensor_of(db) if need_db else None
+
+    def outputs(self, device):
+        mk = lambda lay: None if lay is None else torch.empty_strided(lay[0], lay[1], dtype=self.dtype, device=device)
+        return mk(self.dx_layout), mk(self.dw_layout), mk(self.db_layout)
+
+    def workspace(self, device) -> Optional[torch.Tensor]:
+        n = int(self.plan.workspace_bytes)
+        return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+    def run(self, x, w, gy, dx=None, dw=None, db=None, ws=None, stream: Optional[int] = None):
+        if stream is None:
+            stream = torch.cuda.current_stream(gy.device).cuda_stream
+        ptr = lambda t: t.data_ptr() if t is not None else None
+        _check(A.lib().conv_run_backward(ctypes.byref(self.plan), ptr(x), ptr(w), ptr(gy), ptr(dx), ptr(dw), ptr(db),
+                                         ptr(ws), ws.numel() if ws is not None else 0, stream))
+        return dx, dw, db
+
+
+def conv_backward(x: torch.Tensor, w: torch.Tensor, gy: torch.Tensor, *, stride=1, padding_before=0,
+                  padding_after=0, dilation=1, groups: int = 1, transposed: bool = False, output_padding=0,
+                  padding_mode: str = "explicit", need_dx: bool = True, need_dw: bool = True,
+                  need_db: bool = True):
+    """Gradients (dx, dw, db) of the canonical convolution for an output
+    gradient gy (GPU tensors; a gradient not asked for is None)."""
+    for t in (x, w, gy):
+        if not t.is_cuda:
+            raise ValueError("the canonical convolution runs on the GPU only; move tensors to cuda")
+    if padding_mode != "explicit":
+        padding_before = padding_after = None
+    args = make_args(transposed=transposed, groups=groups, stride=stride, padding_before=padding_before,
+                     padding_after=padding_after, dilation=dilation,
+                     output_padding=output_padding if transposed else None, padding_mode=padding_mode)
+    prep = PreparedBackward(x, w, gy, args, need_dx=need_dx, need_dw=need_dw, need_db=need_db)
+    dx, dw, db = prep.outputs(gy.device)
+    return prep.run(x, w, gy, dx, dw, db, prep.workspace(gy.device))
+
+
 # ------------------------------------------------------- ATen-style overloads --
 
 def _pad_args(padding):

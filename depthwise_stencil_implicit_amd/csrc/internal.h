@@ -111,6 +111,12 @@ constexpr int dw_lds_bytes(int K, int S, int CB)
 enum { DW_CW = 0, DW_OCOLS = 1, DW_CHCHUNKS = 2, DW_COLCHUNKS = 3, DW_XBYTES = 4, DW_YBYTES = 5, DW_RBLOCKS = 6,
        DW_RPB = 7 };
 
+// Weight-gradient schedule fields (conv_bwd_plan_t.wg_tile[]): WB_MFMA is 0
+// for the simple kernel, else 1 | 2 (P read position-major) | 4 (Q read
+// position-major) for the matrix-core one; padded a / b extents, ranges of
+// positions, and the byte ranges of the two operands for the 16-byte loads.
+enum { WB_MFMA = 0, WB_APAD = 1, WB_BPAD = 2, WB_SPLITS = 3, WB_PBYTES = 4, WB_QBYTES = 5 };
+
 // Launchers (defined in the .hip files).  `vec` selects the 16-byte path.
 int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *ws,
                  void *stream, bool vec);
@@ -120,6 +126,9 @@ int launch_plane(const conv_plan_t &p, const void *x, const void *w, const void 
 int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream,
                 bool vec);
 int launch_grp(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream);
+int launch_wgrad(const conv_bwd_plan_t &p, const void *x, const void *gy, void *dw, void *ws, void *stream);
+int launch_bgrad(const conv_bwd_plan_t &p, const void *gy, void *db, void *ws, void *stream);
+int launch_fill_zero(void *out, const conv_tensor &t, void *stream);
 int launch_reduce(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream);
 
 }  // namespace miconv

@@ -1,0 +1,599 @@
+// Weight and bias gradients of the canonical op (conv_run_backward).
+//
+// torch/_inductor/kernel/conv.py (convolution_backward): the weight gradient
+// is a GEMM whose reduction runs over images and positions, and the bias
+// gradient sums the output gradient over them.  For the forward op the
+// terms are x[n, ci, o*s - pb + t*dil] * w[co, c, t]; for the transposed op
+// x[n, ci, i] * w[ci, j, t] with output position o = i*s - pb + t*dil.  In
+// both the weight gradient reads one dense operand P over a set of
+// positions m and one operand Q gathered at m*s - pb + t*dil:
+//
+//   dW[g*PC + a, b, t] = sum_m P[n, g*PC + a, m] * Q[n, g*QC + b, m*s - pb + t*dil]
+//
+//   forward:    P = gy (positions: y's), Q = x  (zero outside x),  PC = Cog, QC = Cig
+//   transposed: P = x  (positions: x's), Q = gy (zero outside y),  PC = Cig, QC = Cog
+//
+// which is exactly the weight layout of each op ([C_out, Cig, k] forward,
+// [C_in, Cog, k] transposed: first index g*PC + a, second b).
+//
+// Kernels
+//   wgrad_mfma    16-bit, channel-contiguous P and Q in 16-byte chunks: a
+//                 workgroup owns (group, tap, 128 a x 128 b) and one range of
+//                 m; per 32-position step it loads [32 m x 128 ch] of each
+//                 operand (16-byte chunks of 8 channels) and writes them
+//                 transposed into LDS as [ch][m], so the MFMA operands hold 8
+//                 consecutive positions per lane (v_mfma_f32_16x16x32); the
+//                 next step's chunks are loaded into registers while the
+//                 current one is multiplied.
+//   wgrad_simple  any dtype and layout: one thread per weight element and
+//                 range of m, fp32 sums.
+//   bgrad         per-channel sums of gy over one range of positions.
+//   bwd_reduce    sums the fp32 partial sums of the ranges, rounds once to
+//                 the dtype and stores at the gradient's strides.
+#include "dev_common.h"
+#include "internal.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace miconv {
+
+struct WgArgs {
+    const void *P;
+    const void *Q;
+    float *part;                 // [S][G][T][apad][bpad] partial sums
+    int64_t ps_n, ps_c, ps_l[3]; // element strides of P
+    int64_t qs_n, qs_c, qs_l[3]; // element strides of Q
+    int32_t N, G, PC, QC, T, apad, bpad;
+    int32_t E[3];                // P's spatial extents (positions m)
+    int32_t F[3];                // Q's spatial extents
+    int32_t K[3], S[3], PB[3], D[3];
+    int32_t splits;              // ranges of m
+    int64_t M;                   // N * E0 * E1 * E2
+    int32_t p_bytes, q_bytes;    // buffer ranges (16-byte path)
+};
+
+namespace {
+
+// Position m -> (n, e0, e1, e2).
+__device__ __forceinline__ void split_m(int64_t m, const WgArgs &a, int &n, int &e0, int &e1, int &e2)
+{
+    const int64_t E12 = (int64_t)a.E[1] * a.E[2];
+    const int64_t per = E12 * a.E[0];
+    n = (int)(m / per);
+    const int64_t r = m - (int64_t)n * per;
+    e0 = (int)(r / E12);
+    const int64_t r2 = r - (int64_t)e0 * E12;
+    e1 = (int)(r2 / a.E[2]);
+    e2 = (int)(r2 - (int64_t)e1 * a.E[2]);
+}
+
+// Range [m_lo, m_hi) of split `sp`, in whole 32-position steps.
+__device__ __forceinline__ void m_range(const WgArgs &a, int sp, int64_t &lo, int64_t &hi)
+{
+    const int64_t steps = (a.M + 31) / 32;
+    lo = steps * sp / a.splits * 32;
+    hi = std::min<int64_t>(steps * (sp + 1) / a.splits * 32, a.M);
+}
+
+// LDS offset of 16-byte chunk c (8 positions) of channel row r, rows of 32
+// positions: rows are 64 bytes, every 8 rows one spare row so that rows r
+// and r + 8 use opposite halves of the banks, and the chunk is XORed with
+// bits 1-2 of the row, so the 8 lanes of one ds_read_b128 cycle (8
+// consecutive rows, one chunk) hit 8 different 16-byte bank groups.
+__device__ __forceinline__ int wg_off(int r, int c) { return (r + (r >> 3)) * 64 + ((c ^ ((r >> 1) & 3)) * 16); }
+
+}  // namespace
+
+constexpr int WG_TILE = 128;
+constexpr int WG_ROWS = WG_TILE + WG_TILE / 8;   // LDS rows per operand with the spare rows
+
+// PM_P / PM_Q: that operand is read position-major (8 consecutive positions
+// of one channel per chunk, gathered element by element: any strides, the
+// last spatial extent a multiple of 8 so a chunk stays in one row) instead of
+// channel-major (16-byte chunks of 8 channels at one position, transposed on
+// the way into LDS).
+template <typename T, bool PM_P, bool PM_Q>
+__global__ __launch_bounds__(256) void wgrad_mfma_kernel(WgArgs a)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __attribute__((aligned(16))) unsigned char sm[2][2][WG_ROWS * 64];   // [buffer][P/Q]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Block order (fastest first): split, b tile, a tile, tap, group.
+    int blk = blockIdx.x;
+    const int sp = blk % a.splits;
+    blk /= a.splits;
+    const int btiles = a.bpad / WG_TILE, atiles = a.apad / WG_TILE;
+    const int bt = blk % btiles;
+    blk /= btiles;
+    const int at = blk % atiles;
+    blk /= atiles;
+    const int t = blk % a.T;
+    const int g = blk / a.T;
+    const int t2 = t % a.K[2], t1 = (t / a.K[2]) % a.K[1], t0 = t / (a.K[2] * a.K[1]);
+    const int toff0 = t0 * a.D[0] - a.PB[0], toff1 = t1 * a.D[1] - a.PB[1], toff2 = t2 * a.D[2] - a.PB[2];
+
+    int64_t m_lo, m_hi;
+    m_range(a, sp, m_lo, m_hi);
+
+    const __amdgpu_buffer_rsrc_t pr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.P), (short)0, a.p_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t qr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.Q), (short)0, a.q_bytes, 0x00020000);
+    const T *__restrict__ Pe = static_cast<const T *>(a.P);
+    const T *__restrict__ Qe = static_cast<const T *>(a.Q);
+    const int a0 = at * WG_TILE, b0 = bt * WG_TILE;
+    // Registers of the next step: per operand two 16-byte chunks.  Channel
+    // mode: thread -> position lm = tid & 31 and channel chunks (tid >> 5) and
+    // (tid >> 5) + 8.  Position mode: chunk id tid + 256h -> 8-position block
+    // (id & 3) of channel (id >> 2).
+    const int lm = tid & 31, lc = tid >> 5;
+    uint4 rp[2], rq[2];
+    auto gload = [&](int64_t mbase) {
+        // Channel-major chunks of both operands at position mbase + lm.
+        if constexpr (!PM_P || !PM_Q) {
+            const int64_t m = mbase + lm;
+            int n = 0, e0 = 0, e1 = 0, e2 = 0;
+            const bool live = m < m_hi;
+            if (live) split_m(m, a, n, e0, e1, e2);
+            const int64_t pbase = (int64_t)n * a.ps_n + e0 * a.ps_l[0] + e1 * a.ps_l[1] + e2 * a.ps_l[2];
+            const int q0 = e0 * a.S[0] + toff0, q1 = e1 * a.S[1] + toff1, q2 = e2 * a.S[2] + toff2;
+            const bool qin = live && (unsigned)q0 < (unsigned)a.F[0] && (unsigned)q1 < (unsigned)a.F[1] &&
+                             (unsigned)q2 < (unsigned)a.F[2];
+            const int64_t qbase = (int64_t)n * a.qs_n + q0 * a.qs_l[0] + q1 * a.qs_l[1] + q2 * a.qs_l[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int ch = 8 * (lc + 8 * h);
+                if constexpr (!PM_P) {
+                    const bool pok = live && a0 + ch < a.PC;
+                    const int po = pok ? (int)((pbase + (int64_t)(g * a.PC + a0 + ch) * a.ps_c) * 2) : 0x7fffff00;
+                    rp[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pr, po, 0, 0));
+                }
+                if constexpr (!PM_Q) {
+                    const bool qok = qin && b0 + ch < a.QC;
+                    const int qo = qok ? (int)((qbase + (int64_t)(g * a.QC + b0 + ch) * a.qs_c) * 2) : 0x7fffff00;
+                    rq[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, qo, 0, 0));
+                }
+            }
+        }
+        // Position-major chunks: 8 consecutive positions of one channel, all
+        // in one row of the last spatial dim.
+        if constexpr (PM_P || PM_Q) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int id = tid + 256 * h, blk8 = id & 3, ch = id >> 2;
+                const int64_t m = mbase + 8 * blk8;
+                int n = 0, e0 = 0, e1 = 0, e2 = 0;
+                const bool live = m < m_hi;
+                if (live) split_m(m, a, n, e0, e1, e2);
+                uint16_t v[8];
+                if constexpr (PM_P) {
+                    const bool ok = live && a0 + ch < a.PC;
+                    const int64_t base = (int64_t)n * a.ps_n + (int64_t)(g * a.PC + a0 + ch) * a.ps_c +
+                                         e0 * a.ps_l[0] + e1 * a.ps_l[1] + e2 * a.ps_l[2];
+                    const int64_t st = a.ps_l[2];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const T val = (ok && m + e < m_hi) ? Pe[base + e * st] : T{};
+                        __builtin_memcpy(&v[e], &val, 2);
+                    }
+                    __builtin_memcpy(&rp[h], v, 16);
+                }
+                if constexpr (PM_Q) {
+                    const bool ok = live && b0 + ch < a.QC;
+                    const int q0 = e0 * a.S[0] + toff0, q1 = e1 * a.S[1] + toff1;
+                    const bool rowin = ok && (unsigned)q0 < (unsigned)a.F[0] && (unsigned)q1 < (unsigned)a.F[1];
+                    const int64_t base = (int64_t)n * a.qs_n + (int64_t)(g * a.QC + b0 + ch) * a.qs_c +
+                                         q0 * a.qs_l[0] + q1 * a.qs_l[1];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int q2 = (e2 + e) * a.S[2] + toff2;
+                        const bool in = rowin && m + e < m_hi && (unsigned)q2 < (unsigned)a.F[2];
+                        const T val = in ? Qe[base + (int64_t)q2 * a.qs_l[2]] : T{};
+                        __builtin_memcpy(&v[e], &val, 2);
+                    }
+                    __builtin_memcpy(&rq[h], v, 16);
+                }
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if constexpr (!PM_P || !PM_Q) {
+                // Channel-major chunk: element e is channel ch + e at position lm.
+                const int ch = 8 * (lc + 8 * h);
+                uint16_t vp[8], vq[8];
+                __builtin_memcpy(vp, &rp[h], 16);
+                __builtin_memcpy(vq, &rq[h], 16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int off = wg_off(ch + e, lm >> 3) + (lm & 7) * 2;
+                    if constexpr (!PM_P) *reinterpret_cast<uint16_t *>(&sm[buf][0][off]) = vp[e];
+                    if constexpr (!PM_Q) *reinterpret_cast<uint16_t *>(&sm[buf][1][off]) = vq[e];
+                }
+            }
+            if constexpr (PM_P || PM_Q) {
+                const int id = tid + 256 * h, blk8 = id & 3, ch = id >> 2;
+                if constexpr (PM_P) *reinterpret_cast<uint4 *>(&sm[buf][0][wg_off(ch, blk8)]) = rp[h];
+                if constexpr (PM_Q) *reinterpret_cast<uint4 *>(&sm[buf][1][wg_off(ch, blk8)]) = rq[h];
+            }
+        }
+    };
+
+    const int wa = wave >> 1, wb = wave & 1;   // wave tile: a rows 64*wa.., b rows 64*wb..
+    const int lr = lane & 15, lg = lane >> 4;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int buf) {
+        uint4 af[4], bf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4 *>(&sm[buf][0][wg_off(64 * wa + 16 * i + lr, lg)]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4 *>(&sm[buf][1][wg_off(64 * wb + 16 * j + lr, lg)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mma_16x16x32(af[i], bf[j], acc[i][j], T{});
+    };
+
+    const int nsteps = (int)((m_hi - m_lo + 31) / 32);
+    if (nsteps > 0) {
+        gload(m_lo);
+        sstore(0);
+        __syncthreads();
+        for (int s = 0; s < nsteps; ++s) {
+            const bool more = s + 1 < nsteps;
+            if (more) gload(m_lo + 32 * (s + 1));
+            compute(s & 1);
+            if (more) sstore((s + 1) & 1);
+            __syncthreads();
+        }
+    }
+    // Partial sums of this range: lane holds a rows 64*wa + 16i + 4*lg + e of
+    // b column 64*wb + 16j + lr.
+    float *Pt = a.part + ((((int64_t)sp * a.G + g) * a.T + t) * a.apad) * a.bpad;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ar = a0 + 64 * wa + 16 * i + 4 * lg + e, bc = b0 + 64 * wb + 16 * j + lr;
+                Pt[(int64_t)ar * a.bpad + bc] = acc[i][j][e];
+            }
+#endif
+}
+
+// One thread per (group, tap, a, b) and range of m, fp32 sum.
+template <typename T>
+__global__ __launch_bounds__(256) void wgrad_simple_kernel(WgArgs a)
+{
+    const int64_t per = (int64_t)a.G * a.T * a.PC * a.QC;
+    const int64_t total = per * a.splits;
+    const T *__restrict__ P = static_cast<const T *>(a.P);
+    const T *__restrict__ Q = static_cast<const T *>(a.Q);
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int sp = (int)(idx / per);
+        int64_t r = idx - sp * per;
+        const int b = (int)(r % a.QC);
+        r /= a.QC;
+        const int av = (int)(r % a.PC);
+        r /= a.PC;
+        const int t = (int)(r % a.T);
+        const int g = (int)(r / a.T);
+        const int t2 = t % a.K[2], t1 = (t / a.K[2]) % a.K[1], t0 = t / (a.K[2] * a.K[1]);
+        int64_t lo, hi;
+        m_range(a, sp, lo, hi);
+        float sum = 0.f;
+        for (int64_t m = lo; m < hi; ++m) {
+            int n, e0, e1, e2;
+            split_m(m, a, n, e0, e1, e2);
+            const int q0 = e0 * a.S[0] - a.PB[0] + t0 * a.D[0];
+            const int q1 = e1 * a.S[1] - a.PB[1] + t1 * a.D[1];
+            const int q2 = e2 * a.S[2] - a.PB[2] + t2 * a.D[2];
+            if ((unsigned)q0 >= (unsigned)a.F[0] || (unsigned)q1 >= (unsigned)a.F[1] || (unsigned)q2 >= (unsigned)a.F[2])
+                continue;
+            const float pv = to_f32(P[(int64_t)n * a.ps_n + (int64_t)(g * a.PC + av) * a.ps_c + e0 * a.ps_l[0] +
+                                      e1 * a.ps_l[1] + e2 * a.ps_l[2]]);
+            const float qv = to_f32(Q[(int64_t)n * a.qs_n + (int64_t)(g * a.QC + b) * a.qs_c + q0 * a.qs_l[0] +
+                                      q1 * a.qs_l[1] + q2 * a.qs_l[2]]);
+            sum = fmaf(pv, qv, sum);
+        }
+        a.part[((((int64_t)sp * a.G + g) * a.T + t) * a.apad + av) * a.bpad + b] = sum;
+    }
+}
+
+struct BgArgs {
+    const void *gy;
+    float *part;                 // [S][C] partial sums
+    int64_t gs_n, gs_c, gs_l[3];
+    int32_t N, C, O[3], splits;
+    int64_t M;                   // N * O0 * O1 * O2
+};
+
+// Block (split, 64-channel chunk): 4 groups of 64 threads, thread = channel;
+// each group walks every 4th position of the split's range.  Channel-fastest
+// lanes read consecutive channels of one position (channels-last gy); the
+// partial sums of the 4 groups are added in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void bgrad_kernel(BgArgs a)
+{
+    __shared__ float red[4][64];
+    const int chunks = (a.C + 63) / 64;
+    const int sp = blockIdx.x / chunks, ck = blockIdx.x % chunks;
+    const int c = ck * 64 + (threadIdx.x & 63), grp = threadIdx.x >> 6;
+    const int64_t per = (a.M + a.splits - 1) / a.splits;
+    const int64_t lo = per * sp, hi = std::min<int64_t>(lo + per, a.M);
+    const T *__restrict__ G = static_cast<const T *>(a.gy);
+    const int64_t O12 = (int64_t)a.O[1] * a.O[2], O012 = O12 * a.O[0];
+    float sum = 0.f;
+    if (c < a.C)
+        for (int64_t m = lo + grp; m < hi; m += 4) {
+            const int64_t n = m / O012, r = m - n * O012;
+            const int64_t o0 = r / O12, r2 = r - o0 * O12;
+            const int64_t o1 = r2 / a.O[2], o2 = r2 - o1 * a.O[2];
+            sum += to_f32(G[n * a.gs_n + (int64_t)c * a.gs_c + o0 * a.gs_l[0] + o1 * a.gs_l[1] + o2 * a.gs_l[2]]);
+        }
+    red[grp][threadIdx.x & 63] = sum;
+    __syncthreads();
+    if (grp == 0 && c < a.C)
+        a.part[(int64_t)sp * a.C + c] = red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] +
+                                        red[3][threadIdx.x];
+}
+
+struct RdArgs {
+    const float *part;
+    void *out;
+    int64_t count;               // elements of the gradient
+    int64_t plane;               // floats per split
+    int32_t splits;
+    // gradient element e -> (g, t, a, b) for the weight gradient; -> c for db
+    int32_t is_w, G, T, PC, QC, apad, bpad, K1, K2;
+    int64_t os0, os1, osk[3];    // the gradient's strides (weight: [g*PC + a, b, k...]; db: os0)
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(RdArgs a)
+{
+    T *__restrict__ out = static_cast<T *>(a.out);
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < a.count;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        int64_t src, dst;
+        if (a.is_w) {
+            int64_t r = e;
+            const int b = (int)(r % a.QC);
+            r /= a.QC;
+            const int av = (int)(r % a.PC);
+            r /= a.PC;
+            const int t = (int)(r % a.T);
+            const int g = (int)(r / a.T);
+            src = (((int64_t)g * a.T + t) * a.apad + av) * a.bpad + b;
+            const int t2 = t % a.K2, t1 = (t / a.K2) % a.K1, t0 = t / (a.K2 * a.K1);
+            dst = (int64_t)(g * a.PC + av) * a.os0 + (int64_t)b * a.os1 + t0 * a.osk[0] + t1 * a.osk[1] +
+                  t2 * a.osk[2];
+        } else {
+            src = e;
+            dst = e * a.os0;
+        }
+        float s = 0.f;
+        for (int k = 0; k < a.splits; ++k) s += a.part[(int64_t)k * a.plane + src];
+        out[dst] = from_f32<T>(s);
+    }
+}
+
+namespace {
+
+template <typename T>
+hipError_t launch_wgrad_t(const WgArgs &a, bool mfma, bool pm_p, bool pm_q, hipStream_t s)
+{
+    if constexpr (Dt<T>::size == 2) {
+        if (mfma) {
+            const dim3 blocks(a.G * a.T * (a.apad / WG_TILE) * (a.bpad / WG_TILE) * a.splits);
+            if (!pm_p && !pm_q) hipLaunchKernelGGL((wgrad_mfma_kernel<T, false, false>), blocks, dim3(256), 0, s, a);
+            else if (pm_p && !pm_q) hipLaunchKernelGGL((wgrad_mfma_kernel<T, true, false>), blocks, dim3(256), 0, s, a);
+            else if (!pm_p && pm_q) hipLaunchKernelGGL((wgrad_mfma_kernel<T, false, true>), blocks, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((wgrad_mfma_kernel<T, true, true>), blocks, dim3(256), 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    {
+        const int64_t total = (int64_t)a.G * a.T * a.PC * a.QC * a.splits;
+        const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(total, 256), 65536);
+        hipLaunchKernelGGL((wgrad_simple_kernel<T>), dim3(blocks), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_reduce_t(const RdArgs &r, hipStream_t s)
+{
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(r.count, 256), 16384);
+    hipLaunchKernelGGL((bwd_reduce_kernel<T>), dim3(blocks), dim3(256), 0, s, r);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bgrad_t(const BgArgs &b, hipStream_t s)
+{
+    const int blocks = b.splits * (int)cdiv(b.C, 64);
+    hipLaunchKernelGGL((bgrad_kernel<T>), dim3(blocks), dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Zeros at a tensor's strides (a gradient with no terms).
+template <typename T>
+__global__ void fill_zero_kernel(T *out, int64_t count, int rank, int64_t s0, int64_t s1, int64_t s2, int64_t s3,
+                                 int64_t s4, int64_t z1, int64_t z2, int64_t z3, int64_t z4)
+{
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += (int64_t)gridDim.x * blockDim.x) {
+        int64_t r = e, off = 0;
+        const int64_t sz[5] = {0, z1, z2, z3, z4}, st[5] = {s0, s1, s2, s3, s4};
+        for (int i = rank - 1; i >= 1; --i) {
+            off += (r % sz[i]) * st[i];
+            r /= sz[i];
+        }
+        off += r * st[0];
+        out[off] = from_f32<T>(0.f);
+    }
+}
+
+int launch_fill_zero(void *out, const conv_tensor &t, void *stream)
+{
+    int64_t count = 1;
+    for (int i = 0; i < t.rank; ++i) count *= t.sizes[i];
+    if (count == 0) return CONV_OK;
+    int64_t sz[5] = {1, 1, 1, 1, 1}, st[5] = {0, 0, 0, 0, 0};
+    for (int i = 0; i < t.rank; ++i) {
+        sz[i] = t.sizes[i];
+        st[i] = t.strides[i];
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(count, 256), 8192);
+    switch (t.dtype) {
+    case CONV_F32:
+        hipLaunchKernelGGL((fill_zero_kernel<float>), dim3(blocks), dim3(256), 0, s, static_cast<float *>(out), count,
+                           t.rank, st[0], st[1], st[2], st[3], st[4], sz[1], sz[2], sz[3], sz[4]);
+        break;
+    case CONV_F16:
+        hipLaunchKernelGGL((fill_zero_kernel<f16_t>), dim3(blocks), dim3(256), 0, s, static_cast<f16_t *>(out), count,
+                           t.rank, st[0], st[1], st[2], st[3], st[4], sz[1], sz[2], sz[3], sz[4]);
+        break;
+    default:
+        hipLaunchKernelGGL((fill_zero_kernel<bf16_t>), dim3(blocks), dim3(256), 0, s, static_cast<bf16_t *>(out),
+                           count, t.rank, st[0], st[1], st[2], st[3], st[4], sz[1], sz[2], sz[3], sz[4]);
+        break;
+    }
+    return hipGetLastError() == hipSuccess ? CONV_OK : CONV_EDEVICE;
+}
+
+int launch_wgrad(const conv_bwd_plan_t &p, const void *x, const void *gy, void *dw, void *ws, void *stream)
+{
+    const conv_desc &d = p.d;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool tr = d.transposed != 0;
+    // P: the operand dense over the positions m; Q: the gathered one.
+    const conv_tensor &P = tr ? d.x : p.gy;
+    const conv_tensor &Q = tr ? p.gy : d.x;
+    WgArgs a;
+    a.P = tr ? x : gy;
+    a.Q = tr ? gy : x;
+    a.part = static_cast<float *>(ws);
+    a.ps_n = P.strides[0];
+    a.ps_c = P.strides[1];
+    a.qs_n = Q.strides[0];
+    a.qs_c = Q.strides[1];
+    // The used spatial dims are right-aligned in the three slots (unused
+    // leading slots: extent 1, stride 0), so the fastest slot is the last
+    // spatial dim of every rank -- the one a position-major chunk runs along.
+    // The flat tap order (t0*K1 + t1)*K2 + t2 is unchanged by leading 1s.
+    const int lead = 3 - d.spatial;
+    for (int i = 0; i < 3; ++i) {
+        const int j = i - lead;          // spatial dim held by slot i, or < 0
+        const bool on = j >= 0;
+        a.ps_l[i] = on ? P.strides[2 + j] : 0;
+        a.qs_l[i] = on ? Q.strides[2 + j] : 0;
+        a.E[i] = on ? (int32_t)(tr ? d.in[j] : d.out[j]) : 1;
+        a.F[i] = on ? (int32_t)(tr ? d.out[j] : d.in[j]) : 1;
+        a.K[i] = on ? (int32_t)d.k[j] : 1;
+        a.S[i] = on ? (int32_t)d.stride[j] : 1;
+        a.PB[i] = on ? (int32_t)d.padding_before[j] : 0;
+        a.D[i] = on ? (int32_t)d.dilation[j] : 1;
+    }
+    a.N = (int32_t)d.N;
+    a.G = (int32_t)d.groups;
+    const int32_t Cig = (int32_t)(d.C_in / d.groups), Cog = (int32_t)(d.C_out / d.groups);
+    a.PC = tr ? Cig : Cog;
+    a.QC = tr ? Cog : Cig;
+    a.T = (int32_t)(d.k[0] * d.k[1] * d.k[2]);
+    a.apad = (int32_t)p.wg_tile[WB_APAD];
+    a.bpad = (int32_t)p.wg_tile[WB_BPAD];
+    a.splits = (int32_t)p.wg_tile[WB_SPLITS];
+    a.M = (int64_t)d.N * a.E[0] * a.E[1] * a.E[2];
+    a.p_bytes = (int32_t)p.wg_tile[WB_PBYTES];
+    a.q_bytes = (int32_t)p.wg_tile[WB_QBYTES];
+    const bool mfma = p.wg_tile[WB_MFMA] != 0;
+    const bool pm_p = (p.wg_tile[WB_MFMA] & 2) != 0, pm_q = (p.wg_tile[WB_MFMA] & 4) != 0;
+    hipError_t e;
+    switch (d.dtype) {
+    case CONV_F32: e = launch_wgrad_t<float>(a, false, false, false, s); break;
+    case CONV_F16: e = launch_wgrad_t<f16_t>(a, mfma, pm_p, pm_q, s); break;
+    default: e = launch_wgrad_t<bf16_t>(a, mfma, pm_p, pm_q, s); break;
+    }
+    if (e != hipSuccess) return CONV_EDEVICE;
+    RdArgs r;
+    r.part = a.part;
+    r.out = dw;
+    r.count = (int64_t)a.G * a.T * a.PC * a.QC;
+    r.plane = (int64_t)a.G * a.T * a.apad * a.bpad;
+    r.splits = a.splits;
+    r.is_w = 1;
+    r.G = a.G;
+    r.T = a.T;
+    r.PC = a.PC;
+    r.QC = a.QC;
+    r.apad = a.apad;
+    r.bpad = a.bpad;
+    r.K1 = a.K[1];
+    r.K2 = a.K[2];
+    r.os0 = p.dw.strides[0];
+    r.os1 = p.dw.strides[1];
+    for (int i = 0; i < 3; ++i) r.osk[i] = i >= lead ? p.dw.strides[2 + i - lead] : 0;   // the slots of a.K
+    switch (d.dtype) {
+    case CONV_F32: e = launch_reduce_t<float>(r, s); break;
+    case CONV_F16: e = launch_reduce_t<f16_t>(r, s); break;
+    default: e = launch_reduce_t<bf16_t>(r, s); break;
+    }
+    return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
+}
+
+int launch_bgrad(const conv_bwd_plan_t &p, const void *gy, void *db, void *ws, void *stream)
+{
+    const conv_desc &d = p.d;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    BgArgs b;
+    b.gy = gy;
+    b.part = static_cast<float *>(ws);
+    b.gs_n = p.gy.strides[0];
+    b.gs_c = p.gy.strides[1];
+    for (int i = 0; i < 3; ++i) {
+        b.gs_l[i] = i < d.spatial ? p.gy.strides[2 + i] : 0;
+        b.O[i] = (int32_t)d.out[i];
+    }
+    b.N = (int32_t)d.N;
+    b.C = (int32_t)d.C_out;
+    b.splits = (int32_t)p.db_splits;
+    b.M = (int64_t)d.N * b.O[0] * b.O[1] * b.O[2];
+    hipError_t e;
+    switch (d.dtype) {
+    case CONV_F32: e = launch_bgrad_t<float>(b, s); break;
+    case CONV_F16: e = launch_bgrad_t<f16_t>(b, s); break;
+    default: e = launch_bgrad_t<bf16_t>(b, s); break;
+    }
+    if (e != hipSuccess) return CONV_EDEVICE;
+    RdArgs r;
+    std::memset(&r, 0, sizeof(r));
+    r.part = b.part;
+    r.out = db;
+    r.count = b.C;
+    r.plane = b.C;
+    r.splits = b.splits;
+    r.is_w = 0;
+    r.os0 = p.db.rank > 0 ? p.db.strides[0] : 1;
+    switch (d.dtype) {
+    case CONV_F32: e = launch_reduce_t<float>(r, s); break;
+    case CONV_F16: e = launch_reduce_t<f16_t>(r, s); break;
+    default: e = launch_reduce_t<bf16_t>(r, s); break;
+    }
+    return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
+}
+
+}  // namespace miconv

@@ -251,6 +251,79 @@ MICONV_API int conv_plan_ex(const conv_desc *d, const conv_tensor *y, const conv
 MICONV_API int conv_run(const conv_plan_t *p, const void *x, const void *w, const void *b, void *y,
              void *workspace, size_t workspace_bytes, void *stream);
 
+/* A plan of the gradients of one call (conv_plan_backward).  Caller-owned,
+ * no destroy call; host-only to produce. */
+typedef struct conv_bwd_plan_t {
+    conv_desc d;                      /* the call whose gradients are computed */
+    conv_tensor gy;                   /* batched view of the output gradient */
+    conv_tensor dx;                   /* batched input gradient (layout of conv_backward_layout) */
+    conv_tensor dw;                   /* weight gradient: w's sizes, dense in w's memory format */
+    conv_tensor db;                   /* [C_out] contiguous, or rank 0 */
+    int32_t need_dx, need_dw, need_db, reserved0;
+    conv_plan_t dgrad;                /* the adjoint call that computes dx */
+    int64_t wg_tile[8];               /* weight-gradient schedule */
+    int64_t db_splits;                /* ranges of positions of the bias gradient */
+    int64_t workspace_bytes;          /* device scratch conv_run_backward needs */
+    int64_t flops[3];                 /* algorithmic FLOPs of dx, dw, db */
+    int64_t bytes[3];                 /* algorithmic bytes of dx, dw, db */
+} conv_bwd_plan_t;
+
+/*
+ * conv_backward_layout -- layouts of the gradients of a call
+ * (torch/_inductor/kernel/conv.py, convolution_backward: the input, weight
+ * and bias gradients of the convolution).
+ *
+ *   d   the call (conv_bind).
+ *   gy  descriptor of the output gradient: y's sizes (batched, or unbatched
+ *       for an unbatched call), any non-negative strides.
+ *   dx  receives the input gradient's layout: the output layout of the
+ *       adjoint call (forward and transposed exchanged, gy as its input, the
+ *       same weight tensor), which has x's sizes.  May be NULL.
+ *   dw  receives w's sizes, dense in w's memory format.  May be NULL.
+ *   db  receives [C_out], stride 1.  May be NULL.
+ *
+ * Returns CONV_OK, CONV_EINVAL, CONV_ELAYOUT (gy's sizes or dtype differ
+ * from y's) or CONV_EUNSUPPORTED (a transposed call with output_padding >=
+ * stride, whose adjoint is longer than x).
+ */
+MICONV_API int conv_backward_layout(const conv_desc *d, const conv_tensor *gy, conv_tensor *dx, conv_tensor *dw,
+                                    conv_tensor *db);
+
+/*
+ * conv_plan_backward -- plan the gradients of a call (same passage).
+ *
+ *   dx = the adjoint call of gy: for a forward call the transposed call
+ *        with output_padding (L + pb + pa - dil(k-1) - 1) mod s, for a
+ *        transposed call the forward call; planned by conv_plan.
+ *   dw[g*PC + a, b, t] = sum over positions m of P[m, g*PC + a] *
+ *        Q[m*s - pb + t*dil, g*QC + b] with (P, Q) = (gy, x) for a forward
+ *        call and (x, gy) for a transposed one.
+ *   db[co] = sum of gy over images and positions.
+ *   need_dx / need_dw / need_db select the gradients.  Host only.
+ *
+ * Returns as conv_backward_layout, or CONV_EUNSUPPORTED when the adjoint
+ * call cannot be planned.
+ */
+MICONV_API int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int32_t need_dx, int32_t need_dw,
+                                  int32_t need_db, conv_bwd_plan_t *p);
+
+/*
+ * conv_run_backward -- enqueue the planned gradients on the caller's stream.
+ *
+ *   x, w, gy         device pointers as the plan's descriptors say (x is
+ *                    needed for dw, w for dx).
+ *   dx, dw, db       device outputs at the layouts of conv_backward_layout
+ *                    (NULL for a gradient the plan does not compute).
+ *   workspace        device scratch of at least p->workspace_bytes bytes,
+ *                    16-byte aligned (NULL when 0).  Overwritten.
+ *
+ * Each gradient is accumulated in fp32 and rounded once.  Asynchronous.
+ * Returns CONV_OK, CONV_EINVAL (a NULL pointer the plan needs, a short
+ * workspace), CONV_EALIGN or CONV_EDEVICE.
+ */
+MICONV_API int conv_run_backward(const conv_bwd_plan_t *p, const void *x, const void *w, const void *gy, void *dx,
+                                 void *dw, void *db, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Size of the device-resident scratch array of conv_run_noalloc, MiB. */
 #define MICONV_NOALLOC_SCRATCH_MIB 32
 

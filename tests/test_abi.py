@@ -52,6 +52,9 @@ int main(void) {
          sizeof(conv_tensor), sizeof(conv_args), sizeof(conv_desc), sizeof(conv_plan_t),
          sizeof(conv_plan_opts));
   P(conv_plan_opts, force_variant); P(conv_plan_opts, reserved);
+  printf("conv_bwd_plan_t %zu\n", sizeof(conv_bwd_plan_t));
+  P(conv_bwd_plan_t, gy); P(conv_bwd_plan_t, need_dx); P(conv_bwd_plan_t, dgrad); P(conv_bwd_plan_t, wg_tile);
+  P(conv_bwd_plan_t, workspace_bytes); P(conv_bwd_plan_t, bytes);
   P(conv_args, groups); P(conv_args, stride); P(conv_args, output_padding);
   P(conv_desc, N); P(conv_desc, in); P(conv_desc, output_padding); P(conv_desc, x); P(conv_desc, b);
   P(conv_plan_t, y); P(conv_plan_t, kernel); P(conv_plan_t, workspace_bytes); P(conv_plan_t, tile);
@@ -69,9 +72,9 @@ def test_struct_layout_matches_ctypes(tmp_path):
     got = dict(ln.rsplit(" ", 1) for ln in subprocess.check_output([str(exe)], text=True).splitlines())
     expect = {"conv_tensor": ctypes.sizeof(A.ConvTensor), "conv_args": ctypes.sizeof(A.ConvArgs),
               "conv_desc": ctypes.sizeof(A.ConvDesc), "conv_plan_t": ctypes.sizeof(A.ConvPlan),
-              "conv_plan_opts": ctypes.sizeof(A.ConvPlanOpts)}
+              "conv_plan_opts": ctypes.sizeof(A.ConvPlanOpts), "conv_bwd_plan_t": ctypes.sizeof(A.ConvBwdPlan)}
     fields = {"conv_args": A.ConvArgs, "conv_desc": A.ConvDesc, "conv_plan_t": A.ConvPlan,
-              "conv_plan_opts": A.ConvPlanOpts}
+              "conv_plan_opts": A.ConvPlanOpts, "conv_bwd_plan_t": A.ConvBwdPlan}
     for key, val in got.items():
         if "." in key:
             struct, field = key.split(".")

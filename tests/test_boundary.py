@@ -349,3 +349,73 @@ def test_forced_schedule_is_explicit():
         api.Prepared(T((2, 8, 8, 15), torch.float16), wg, None,
                      api.make_args(groups=2, padding_before=1, padding_after=1), force_kernel="grp",
                      force_variant=1)
+
+
+# -------------------------------------------------------------- gradients --
+
+def _bwd(wl, gy_strides=None):
+    x, w, b = wl_tensors(wl)
+    p = prep(x, w, b, **wl_args(wl))
+    gy = torch.empty_strided(p.sizes, gy_strides or p.strides, dtype=x.dtype)
+    return x, w, api.PreparedBackward(x, w, gy, api.make_args(**wl_args(wl)))
+
+
+def test_gradient_layouts_of_the_workloads():
+    """dx has the layout of the adjoint call's output (channels-last for the
+    channels-last 2-D calls, contiguous for the 1-D transposed call whose gy
+    is contiguous), dw is dense in w's format, db is [C_out]."""
+    want = {"dense_bf16_nhwc_64x256x56x56_k3": (802816, 1, 14336, 256),
+            "convT1d_bf16_nlc_16x512x8192_k4s2": (4194304, 8192, 1),
+            "grp_f16_nchw_32x256x28x28_g64_m2": (200704, 784, 28, 1),
+            "dw_bf16_nhwc_32x256x56x56_k7s2": (802816, 1, 14336, 256)}
+    for wl in synth.all_workloads():
+        x, w, bp = _bwd(wl)
+        assert bp.dx_layout[0] == tuple(x.shape)
+        if wl.name in want:
+            assert bp.dx_layout[1] == want[wl.name], wl.name
+        assert bp.dw_layout == (tuple(w.shape), tuple(w.stride()))
+        c_out = wl.w_shape[1] * wl.groups if wl.transposed else wl.w_shape[0]
+        assert bp.db_layout == ((c_out,), (1,))
+
+
+def test_gradient_schedules():
+    """The dense call's weight gradient runs on the matrix cores with both
+    operands channel-major; the transposed 1-D call's with its contiguous gy
+    read position-major; depthwise weight gradients use the simple kernel;
+    the input gradient of a forward call is a transposed call and vice versa."""
+    _, _, dense = _bwd(synth.dense_bf16_cl())
+    assert dense.plan.wg_tile[0] == 1 and api.kernel_name(dense.plan.dgrad.kernel) == "igemm_t"
+    _, _, tr = _bwd(synth.transposed_bf16_nlc())
+    assert tr.plan.wg_tile[0] == 1 | 4 and api.kernel_name(tr.plan.dgrad.kernel) == "igemm"
+    _, _, dw = _bwd(synth.depthwise_bf16_cl(3, 1))
+    assert dw.plan.wg_tile[0] == 0
+    assert dense.plan.flops[1] == dense.plan.flops[0] == 2 * 200704 * 256 * 2304
+    assert dense.plan.workspace_bytes >= dense.plan.wg_tile[3] * 9 * 256 * 256 * 4
+
+
+def test_gradient_plan_errors():
+    x, w = T((1, 4, 9)), T((4, 2, 3))
+    # A transposed call whose output_padding reaches the stride: its forward
+    # adjoint would be longer than x.
+    a = api.make_args(transposed=True, stride=2, dilation=3, output_padding=2, padding_before=0, padding_after=0)
+    d = api.conv_bind(api.describe(x), api.describe(w), None, a)
+    sizes, strides = api.conv_out_shape(d)
+    gy = api.tensor_desc(sizes, strides, torch.bfloat16)
+    p = A.ConvBwdPlan()
+    assert A.lib().conv_plan_backward(ctypes.byref(d), ctypes.byref(gy), 1, 0, 0, ctypes.byref(p)) == A.EUNSUPPORTED
+    # ... though its weight and bias gradients can be planned.
+    assert A.lib().conv_plan_backward(ctypes.byref(d), ctypes.byref(gy), 0, 1, 1, ctypes.byref(p)) == A.OK
+    # gy of the wrong shape.
+    bad = api.tensor_desc((1, 2, sizes[2] + 1), (sizes[2] + 1, 1, 1), torch.bfloat16)
+    assert A.lib().conv_plan_backward(ctypes.byref(d), ctypes.byref(bad), 1, 1, 1, ctypes.byref(p)) == A.ELAYOUT
+
+
+def test_gradient_run_checks_before_touching_the_device():
+    x, w, bp = _bwd(synth.dense_bf16_cl().with_batch(1))
+    L = A.lib()
+    run = lambda *a: L.conv_run_backward(ctypes.byref(bp.plan), *a)
+    ws = bp.plan.workspace_bytes
+    assert run(0x1000, 0x2000, None, 0x3000, 0x4000, 0x5000, 0x6000, ws, None) == A.EINVAL        # no gy
+    assert run(0x1000, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, ws, None) == A.EINVAL        # dx needs w
+    assert run(0x1000, 0x2000, 0x2200, 0x3000, 0x4000, 0x5000, None, 0, None) == A.EINVAL         # workspace
+    assert run(0x1001, 0x2000, 0x2200, 0x3000, 0x4000, 0x5000, 0x6000, ws, None) == A.EALIGN
