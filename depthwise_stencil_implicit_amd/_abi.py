@@ -14,6 +14,7 @@ MAX_SPATIAL = 3
 F32, F16, BF16 = 0, 1, 2
 OK, EINVAL, EUNSUPPORTED, ELAYOUT, EALIGN, EDEVICE, ENOSPACE = range(7)
 NOALLOC_SCRATCH_BYTES = 32 << 20
+PLAN_ONE_BY_ONE = 1
 PAD_EXPLICIT, PAD_SAME, PAD_VALID = 0, 1, 2
 K_AUTO, K_DW_CL, K_PLANE, K_GRP, K_REDUCE, K_IGEMM, K_IGEMM_T = -1, 1, 2, 3, 4, 5, 6
 KERNELS = {"auto": K_AUTO, "dw_cl": K_DW_CL, "plane": K_PLANE, "grp": K_GRP, "reduce": K_REDUCE,
@@ -51,7 +52,8 @@ class ConvPlan(ctypes.Structure):
     _fields_ = [("d", ConvDesc), ("y", ConvTensor),
                 ("kernel", _i32), ("variant", _i32), ("vec_ok", _i32), ("index64", _i32),
                 ("workspace_bytes", _i64), ("tile", _i64 * 8), ("grid", _i64 * 3),
-                ("block", _i32), ("lds_bytes", _i32), ("flops", _i64), ("bytes", _i64)]
+                ("block", _i32), ("lds_bytes", _i32), ("flags", _i32), ("reserved1", _i32), ("flops", _i64),
+                ("bytes", _i64)]
 
 
 class ConvBwdPlan(ctypes.Structure):

@@ -67,6 +67,7 @@ struct IgArgs {
     int32_t ksplit;               // K ranges per tile (> 1: fp32 partial sums into part)
     float *part;                  // [ksplit][G][phases][rows - row0][cog_pad] partial sums
     int32_t w_bytes;              // bytes of the repacked weights (buffer range)
+    int32_t one;                  // 1x1 plain GEMM: row m of A is x's row m (m * Cig elements)
 };
 
 // Byte offset of 16-byte chunk `c` of LDS row `r` (rows of 8 chunks).
@@ -513,6 +514,15 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
     // with any scalar offset added.
     int a_off[A_IT];
     auto set_tap = [&]() {
+        if (a.one) {
+            // 1x1: A is x's dense [rows, Cig] matrix.
+#pragma unroll
+            for (int i = 0; i < A_IT; ++i) {
+                const int m = a.row0 + m_tile * BM + i * NW * RPI + wave * RPI + lane / KC;
+                a_off[i] = m < a.rows ? (m * a.Cig + kc * EV) * ES : 0x7fffff00;
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < A_IT; ++i) {
             const int i0 = a_b0[i] + it_o0, i1 = a_b1[i] + it_o1, i2 = a_b2[i] + it_o2;
@@ -994,11 +1004,18 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
 
     a.row0 = 0;
 
-    hipError_t e;
-    switch (d.dtype) {
-    case CONV_F32: e = launch_repack<float>(p, w, ws, s); break;
-    case CONV_F16: e = launch_repack<f16_t>(p, w, ws, s); break;
-    default: e = launch_repack<bf16_t>(p, w, ws, s); break;
+    a.one = (p.flags & CONV_PLAN_ONE_BY_ONE) && vec ? 1 : 0;
+    hipError_t e = hipSuccess;
+    if (p.flags & CONV_PLAN_ONE_BY_ONE) {
+        // The weight tensor is the packed B operand: read in place.
+        a.w = w;
+        a.w_bytes = (int32_t)(d.C_out * d.C_in * esize(d.dtype));
+    } else {
+        switch (d.dtype) {
+        case CONV_F32: e = launch_repack<float>(p, w, ws, s); break;
+        case CONV_F16: e = launch_repack<f16_t>(p, w, ws, s); break;
+        default: e = launch_repack<bf16_t>(p, w, ws, s); break;
+        }
     }
     if (e != hipSuccess) return CONV_EDEVICE;
     if (p.variant == IG_T1_CFG || p.variant == IG_T1B_CFG) {
@@ -1033,7 +1050,8 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
         t.ksplit = vec ? (int)(tail >> 24) : 1;
         t.total_tiles = t.m_tiles * per_m * t.ksplit;
         if (t.ksplit > 1)
-            t.part = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + a.w_bytes);
+            t.part = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) +
+                                               ((p.flags & CONV_PLAN_ONE_BY_ONE) ? 0 : a.w_bytes));
         e = main.m_tiles > 0 ? run(main, p.variant) : hipSuccess;
         if (e == hipSuccess) e = run(t, IG_TAIL_CFG);
         if (e == hipSuccess && t.ksplit > 1) {

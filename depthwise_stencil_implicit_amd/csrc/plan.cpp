@@ -321,7 +321,25 @@ bool geom_igemm(const conv_desc &d, conv_plan_t &p, int force_variant)
     p.grid[0] = d.groups * phases * p.tile[IG_MTILES] * p.tile[IG_NTILES];
     p.block = 64 * c.wm * c.wn;
     p.lds_bytes = (int32_t)(c.stages * (c.bm + c.bn) * 128);
-    p.workspace_bytes = igemm_wbytes(d.groups, cog_pad, taps, cig_pad, es);
+    // A forward 1x1 call with stride 1 and no padding on dense channels-last
+    // x (row m of the GEMM is x's pixel m) and a contiguous [C_out, C_in]
+    // weight with C_in a multiple of the 64-channel block (then the weight
+    // already has the packed layout): a plain GEMM, no repack, no position
+    // arithmetic (Inductor conv.py, conv1x1_via_mm).
+    bool one = !d.transposed && d.groups == 1 && d.dtype != CONV_F32 && cig(d) == cig_pad && taps == 1 &&
+               d.x.strides[1] == 1 && d.w.strides[1] == 1 && d.w.strides[0] == d.C_in &&
+               d.C_out * d.C_in * es < kI32 - 4096;
+    {
+        int64_t acc = d.C_in;
+        for (int i = d.spatial - 1; i >= 0 && one; --i) {
+            one = d.stride[i] == 1 && d.padding_before[i] == 0 && d.padding_after[i] == 0 &&
+                  (d.in[i] == 1 || d.x.strides[2 + i] == acc);
+            acc *= d.in[i];
+        }
+        one = one && (d.N == 1 || d.x.strides[0] == acc);
+    }
+    p.flags = one ? CONV_PLAN_ONE_BY_ONE : 0;
+    p.workspace_bytes = one ? 0 : igemm_wbytes(d.groups, cog_pad, taps, cig_pad, es);
     if (p.workspace_bytes >= kI32) return false;   // 32-bit buffer offsets into the weights
     // Rows whose tiles would leave a last round that keeps at most a quarter
     // of the CUs busy go to 64-row tiles with their K split over the CUs

@@ -132,6 +132,13 @@ typedef struct conv_desc {
     conv_tensor x, w, b;
 } conv_desc;
 
+/* Plan flags.  CONV_PLAN_ONE_BY_ONE: a forward 1x1 call with stride 1 and no
+ * padding on dense channels-last x and a contiguous [C_out, C_in] weight
+ * (C_in a multiple of 64): a plain GEMM on the implicit GEMM's tiles whose A
+ * rows are x's rows and whose B operand is the weight tensor in place (no
+ * position arithmetic, no weight repack). */
+#define CONV_PLAN_ONE_BY_ONE 1
+
 /* A launch plan.  Produced by conv_plan on the host without any device call. */
 typedef struct conv_plan_t {
     conv_desc d;
@@ -145,6 +152,8 @@ typedef struct conv_plan_t {
     int64_t grid[3];
     int32_t block;
     int32_t lds_bytes;
+    int32_t flags;                    /* CONV_PLAN_* bits */
+    int32_t reserved1;
     int64_t flops;                    /* algorithmic FLOPs of the call */
     int64_t bytes;                    /* algorithmic bytes: x + w + b read once, y written once */
 } conv_plan_t;

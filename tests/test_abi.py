@@ -58,7 +58,7 @@ int main(void) {
   P(conv_args, groups); P(conv_args, stride); P(conv_args, output_padding);
   P(conv_desc, N); P(conv_desc, in); P(conv_desc, output_padding); P(conv_desc, x); P(conv_desc, b);
   P(conv_plan_t, y); P(conv_plan_t, kernel); P(conv_plan_t, workspace_bytes); P(conv_plan_t, tile);
-  P(conv_plan_t, grid); P(conv_plan_t, block); P(conv_plan_t, flops); P(conv_plan_t, bytes);
+  P(conv_plan_t, grid); P(conv_plan_t, block); P(conv_plan_t, flags); P(conv_plan_t, flops); P(conv_plan_t, bytes);
   return 0;
 }
 """

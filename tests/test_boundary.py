@@ -419,3 +419,25 @@ def test_gradient_run_checks_before_touching_the_device():
     assert run(0x1000, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, ws, None) == A.EINVAL        # dx needs w
     assert run(0x1000, 0x2000, 0x2200, 0x3000, 0x4000, 0x5000, None, 0, None) == A.EINVAL         # workspace
     assert run(0x1001, 0x2000, 0x2200, 0x3000, 0x4000, 0x5000, 0x6000, ws, None) == A.EALIGN
+
+
+# ------------------------------------------------------------ 1x1 calls --
+
+def test_one_by_one_plain_gemm_plan():
+    """A forward 1x1 call with stride 1 and no padding on dense
+    channels-last x, with a contiguous weight and C_in a multiple of 64, is a
+    plain GEMM: the plan flags it and needs no weight workspace."""
+    x, w, b = T((4, 256, 28, 28), cl=True), T((384, 256, 1, 1)), T((384,))
+    p = prep(x, w, b).plan
+    assert p.flags & A.PLAN_ONE_BY_ONE and api.kernel_name(p.kernel) == "igemm"
+    assert p.workspace_bytes == 0 or (p.tile[7] >> 24) > 1      # only split-K partial sums, if any
+    p1 = prep(T((2, 128, 50), cl=True), T((64, 128, 1))).plan
+    assert p1.flags & A.PLAN_ONE_BY_ONE
+    # Not a plain GEMM: NCHW x, padding, stride, C_in not a multiple of 64,
+    # transposed, grouped.
+    assert not prep(T((4, 256, 28, 28)), w).plan.flags
+    assert not prep(x, w, padding_before=1, padding_after=1).plan.flags
+    assert not prep(x, w, stride=2).plan.flags
+    assert not prep(T((4, 96, 28, 28), cl=True), T((64, 96, 1, 1))).plan.flags
+    assert not prep(T((4, 256, 28, 28), cl=True), T((256, 64, 1, 1)), transposed=True).plan.flags
+    assert not prep(x, T((384, 128, 1, 1)), groups=2).plan.flags

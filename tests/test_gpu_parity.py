@@ -729,3 +729,43 @@ def test_transposed_both_phases_kernel(wl, w_cl, variant):
     xr, wr, br = ref_inputs(x, w, b)
     yr, A = oracle.conv(xr, wr, br, **kw)
     assert_close(y, yr, A, EPS[wl.dtype], wl.name)
+
+
+# ----------------------------------------------------- 1x1 plain GEMM --
+
+def _one_cases():
+    out = []
+    shapes = [(2, [56, 56], 256, 256, "bf16"), (3, [30, 20], 128, 70, "f16"), (1, [1000], 64, 16, "bf16"),
+              (2, [6, 7, 9], 192, 130, "f16"), (22, [56, 56], 256, 256, "bf16")]
+    for i, (N, L, cin, cout, dt) in enumerate(shapes):
+        r = len(L)
+        out.append(synth.random_case(7700 + i, rank=r, transposed=False, dtype=dt, channels_last=True, N=N,
+                                     C_in=cin, C_out=cout, groups=1, L=L, k=[1] * r, stride=[1] * r,
+                                     padding_before=[0] * r, padding_after=[0] * r, dilation=[1] * r,
+                                     output_padding=[0] * r, has_bias=bool(i % 2)))
+    return out
+
+
+@pytest.mark.parametrize("wl", _one_cases(), ids=lambda v: v.name)
+def test_one_by_one_plain_gemm(wl):
+    """1x1 calls on the plain-GEMM path (x's rows as A, the weight in place),
+    whole output against the reference; the last case is large enough for
+    the split-K rows past the last full round."""
+    _flush(f"1x1: {_desc(wl)}")
+    x, w, b = synth.make_inputs(wl, device="cuda")
+    kw = expand_kw(wl)
+    plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=1)).plan
+    assert plan.flags & _abi.PLAN_ONE_BY_ONE
+    if wl.x_shape[0] == 22:
+        assert (int(plan.tile[7]) >> 24) > 1
+    y = check_full(wl)
+    # The same call with x at an odd element offset: the general gather
+    # (no 16-byte loads) with the weight still read in place.
+    buf = torch.zeros(x.numel() + 8, dtype=x.dtype, device="cuda")
+    xm = torch.as_strided(buf, x.shape, x.stride(), 1)
+    xm.copy_(x)
+    ym = api.conv(xm, w, b)
+    torch.cuda.synchronize()
+    yr, A = oracle.conv(*ref_inputs(x, w, b))
+    assert_close(ym, yr, A, EPS[wl.dtype], "1x1 misaligned x")
