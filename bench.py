@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--workload", default="all", choices=WORKLOADS)
     ap.add_argument("--rotate", type=int, default=0, help="rotation copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rule", action="store_true",
+                    help="run the planner's rule-based schedules (default: time every candidate schedule of each "
+                         "call once while planning, conv_tune, and run the fastest)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU work for the baseline")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="MIB",
                     help="instead of a workload, time a plain device copy of MIB mebibytes (the "
@@ -339,6 +342,10 @@ def main():
         x, w, b = synth.make_inputs(wl)
         t0 = time.perf_counter()
         p = api.Prepared(x, w, b, make_args(wl))
+        if not a.rule:
+            xd, wd = x.to(dev), w.to(dev)          # .to keeps x's strides
+            p.tune(xd, wd, b.to(dev) if b is not None else None, reps=3)
+            del xd, wd
         host_us.append((time.perf_counter() - t0) * 1e6)
         footprint = (x.numel() + w.numel() + (b.numel() if b is not None else 0)) * x.element_size() + \
             int(torch.Size(p.sizes).numel()) * x.element_size()
@@ -444,6 +451,7 @@ def main():
     dtypes = sorted({wl.dtype for _, wl, _, _ in preps})
     config = {"workload": a.workload, "calls": [wl.name for _, wl, _, _ in preps], "dtypes": dtypes,
               "rotation_sets": R, "timing": "wall clock over K steps; per-call HIP events on the launch stream",
+              "schedules": "planner rule" if a.rule else "timed at plan time (conv_tune), fastest kept",
               "headline": ("sum over the calls of their time at the roofline / measured step time"
                            if a.workload == "all" else "algorithmic units of a step / measured step time")}
     out = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": a.steps,

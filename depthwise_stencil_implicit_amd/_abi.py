@@ -15,6 +15,7 @@ F32, F16, BF16 = 0, 1, 2
 OK, EINVAL, EUNSUPPORTED, ELAYOUT, EALIGN, EDEVICE, ENOSPACE = range(7)
 NOALLOC_SCRATCH_BYTES = 32 << 20
 PLAN_ONE_BY_ONE = 1
+PLAN_TUNED = 2
 PAD_EXPLICIT, PAD_SAME, PAD_VALID = 0, 1, 2
 K_AUTO, K_DW_CL, K_PLANE, K_GRP, K_REDUCE, K_IGEMM, K_IGEMM_T = -1, 1, 2, 3, 4, 5, 6
 KERNELS = {"auto": K_AUTO, "dw_cl": K_DW_CL, "plane": K_PLANE, "grp": K_GRP, "reduce": K_REDUCE,
@@ -72,6 +73,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmiconv.s
 # Every symbol include/miconv.h declares.
 EXPORTS = ("conv_bind", "conv_out_shape", "conv_plan", "conv_plan_ex", "conv_run", "conv_run_noalloc",
            "conv_backward_layout", "conv_plan_backward", "conv_run_backward",
+           "conv_plan_candidates", "conv_tune", "conv_plan_tuned",
            "conv_kernel_name", "conv_status_string", "conv_abi_version")
 
 _lib = None
@@ -108,6 +110,14 @@ def lib():
         L.conv_plan_backward.restype = ctypes.c_int
         L.conv_run_backward.argtypes = [P(ConvBwdPlan)] + [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]
         L.conv_run_backward.restype = ctypes.c_int
+        L.conv_plan_candidates.argtypes = [P(ConvDesc), P(ConvTensor), P(ConvPlan), _i32, P(_i32)]
+        L.conv_plan_candidates.restype = ctypes.c_int
+        L.conv_tune.argtypes = [P(ConvDesc), P(ConvTensor)] + [ctypes.c_void_p] * 5 + [ctypes.c_size_t,
+                                                                                        ctypes.c_void_p, _i32,
+                                                                                        P(ConvPlan)]
+        L.conv_tune.restype = ctypes.c_int
+        L.conv_plan_tuned.argtypes = [P(ConvDesc), P(ConvTensor), P(ConvPlan)]
+        L.conv_plan_tuned.restype = ctypes.c_int
         L.conv_kernel_name.argtypes = [_i32]
         L.conv_kernel_name.restype = ctypes.c_char_p
         L.conv_status_string.argtypes = [_i32]

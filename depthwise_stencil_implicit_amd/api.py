@@ -135,6 +135,21 @@ def conv_run(p: A.ConvPlan, x_ptr: int, w_ptr: int, b_ptr: Optional[int], y_ptr:
     _check(A.lib().conv_run(ctypes.byref(p), x_ptr, w_ptr, b_ptr, y_ptr, ws_ptr, ws_bytes, stream))
 
 
+def conv_plan_candidates(d: A.ConvDesc, y: A.ConvTensor):
+    """Every plan that can run the call (the rule's plan first)."""
+    n = ctypes.c_int32(0)
+    _check(A.lib().conv_plan_candidates(ctypes.byref(d), ctypes.byref(y), None, 0, ctypes.byref(n)))
+    arr = (A.ConvPlan * max(1, n.value))()
+    _check(A.lib().conv_plan_candidates(ctypes.byref(d), ctypes.byref(y), arr, n.value, ctypes.byref(n)))
+    return list(arr[: n.value])
+
+
+def conv_plan_tuned(d: A.ConvDesc, y: A.ConvTensor) -> A.ConvPlan:
+    p = A.ConvPlan()
+    _check(A.lib().conv_plan_tuned(ctypes.byref(d), ctypes.byref(y), ctypes.byref(p)))
+    return p
+
+
 def kernel_name(k: int) -> str:
     return A.lib().conv_kernel_name(k).decode()
 
@@ -145,15 +160,34 @@ class Prepared:
     """bind + out_shape + plan for fixed tensor descriptors (reusable)."""
 
     def __init__(self, x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], args: A.ConvArgs,
-                 force_kernel=None, force_variant: Optional[int] = None):
+                 force_kernel=None, force_variant: Optional[int] = None, tuned: bool = False):
         self.desc = conv_bind(describe(x), describe(w), describe(b), args)
         self.sizes, self.strides = conv_out_shape(self.desc)
         self.dtype = x.dtype
-        self.plan = conv_plan(self.desc, tensor_desc(self.sizes, self.strides, x.dtype), force_kernel,
-                              force_variant)
+        ydesc = tensor_desc(self.sizes, self.strides, x.dtype)
+        if tuned and force_kernel is None and force_variant is None:
+            self.plan = conv_plan_tuned(self.desc, ydesc)
+        else:
+            self.plan = conv_plan(self.desc, ydesc, force_kernel, force_variant)
 
     def empty_output(self, device) -> torch.Tensor:
         return torch.empty_strided(self.sizes, self.strides, dtype=self.dtype, device=device)
+
+    def tune(self, x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], reps: int = 5) -> A.ConvPlan:
+        """Time every candidate schedule on these buffers (conv_tune) and keep
+        the fastest; later Prepared(..., tuned=True) of the same descriptors
+        on this device get it from the library's cache."""
+        y = self.empty_output(x.device)
+        ydesc = tensor_desc(self.sizes, self.strides, self.dtype)
+        need = max(int(p.workspace_bytes) for p in conv_plan_candidates(self.desc, ydesc))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        best = A.ConvPlan()
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(A.lib().conv_tune(ctypes.byref(self.desc), ctypes.byref(ydesc), x.data_ptr(), w.data_ptr(),
+                                 b.data_ptr() if b is not None else None, y.data_ptr(), ws.data_ptr(), ws.numel(),
+                                 stream, int(reps), ctypes.byref(best)))
+        self.plan = best
+        return best
 
     def workspace(self, device) -> Optional[torch.Tensor]:
         n = int(self.plan.workspace_bytes)
@@ -172,8 +206,10 @@ class Prepared:
 def conv(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None, *, stride=1,
          padding_before=0, padding_after=0, dilation=1, groups: int = 1, transposed: bool = False,
          output_padding=0, padding_mode: str = "explicit", force_kernel=None,
-         force_variant: Optional[int] = None) -> torch.Tensor:
-    """The canonical convolution on GPU tensors (x, w, b share one dtype)."""
+         force_variant: Optional[int] = None, tune: bool = False) -> torch.Tensor:
+    """The canonical convolution on GPU tensors (x, w, b share one dtype).
+    ``tune``: use the schedule conv_tune chose for these descriptors, timing
+    the candidates first if they have not been timed on this device."""
     for t in (x, w) + ((b,) if b is not None else ()):
         if not t.is_cuda:
             raise ValueError("the canonical convolution runs on the GPU only; move tensors to cuda")
@@ -183,7 +219,9 @@ def conv(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None, *, 
                      padding_before=padding_before, padding_after=padding_after,
                      dilation=dilation, output_padding=output_padding if transposed else None,
                      padding_mode=padding_mode)
-    prep = Prepared(x, w, b, args, force_kernel, force_variant)
+    prep = Prepared(x, w, b, args, force_kernel, force_variant, tuned=tune)
+    if tune and force_kernel is None and force_variant is None and not (prep.plan.flags & A.PLAN_TUNED):
+        prep.tune(x, w, b)
     y = prep.empty_output(x.device)
     return prep.run(x, w, b, y, prep.workspace(x.device))
 

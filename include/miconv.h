@@ -31,8 +31,9 @@
  *     ([C_in, L...]) is accepted and gives an unbatched y.
  *   - x, w, b and y share one dtype.  Accumulation is fp32; the bias is
  *     added in fp32 and the result rounded once (nearest even) to the dtype.
- *   - The library keeps no mutable global state and never allocates device
- *     memory: the caller owns every buffer, the workspace and the stream.
+ *   - The library never allocates device memory: the caller owns every
+ *     buffer, the workspace and the stream.  Its only mutable global state
+ *     is the cache of timed schedules (conv_tune), guarded by a mutex.
  *     conv_desc and conv_plan_t are plain caller-owned structs (no destroy
  *     call); a plan may be reused for any call with the same descriptors.
  *   - Every function is reentrant.  conv_run does not synchronise.
@@ -138,6 +139,8 @@ typedef struct conv_desc {
  * rows are x's rows and whose B operand is the weight tensor in place (no
  * position arithmetic, no weight repack). */
 #define CONV_PLAN_ONE_BY_ONE 1
+/* Set by conv_plan_tuned on a plan that comes from the cache of conv_tune. */
+#define CONV_PLAN_TUNED 2
 
 /* A launch plan.  Produced by conv_plan on the host without any device call. */
 typedef struct conv_plan_t {
@@ -332,6 +335,48 @@ MICONV_API int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int
  */
 MICONV_API int conv_run_backward(const conv_bwd_plan_t *p, const void *x, const void *w, const void *gy, void *dx,
                                  void *dw, void *db, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * conv_plan_candidates -- every plan that can run a call: the rule's plan
+ * first, then each kernel whose supports() holds and each schedule of the
+ * kernels that have several (the implicit GEMM's tile table, the grouped
+ * stencil's schedules, the transposed both-phases kernels), as conv_plan_ex
+ * accepts them (executorch PR #25085, description: the stencil's schedules
+ * are timed when the call is compiled; torch/_inductor/kernel/conv.py,
+ * autotune_select_algorithm).  Host only.
+ *
+ *   out, max   caller array of max plans (may be NULL when max is 0).
+ *   count      receives the number of candidates (may exceed max).
+ *
+ * Returns as conv_plan.
+ */
+MICONV_API int conv_plan_candidates(const conv_desc *d, const conv_tensor *y, conv_plan_t *out, int32_t max,
+                                    int32_t *count);
+
+/*
+ * conv_tune -- time the candidates on the caller's buffers and stream and
+ * keep the fastest (same passages).
+ *
+ *   x, w, b, yptr    device buffers of the call (y is overwritten).
+ *   workspace        device scratch; candidates needing more than
+ *                    workspace_bytes are skipped.
+ *   reps             timed launches per candidate (after one untimed one).
+ *   best             receives the fastest plan.
+ *
+ * The choice is cached per (descriptors, y, device) for conv_plan_tuned.
+ * Synchronises the stream.  Returns CONV_OK, the planning errors of
+ * conv_plan, or CONV_EDEVICE (no candidate ran).
+ */
+MICONV_API int conv_tune(const conv_desc *d, const conv_tensor *y, const void *x, const void *w, const void *b,
+                         void *yptr, void *workspace, size_t workspace_bytes, void *stream, int32_t reps,
+                         conv_plan_t *best);
+
+/*
+ * conv_plan_tuned -- the plan conv_tune chose for these descriptors on the
+ * current device (flag CONV_PLAN_TUNED set), or conv_plan's when the call
+ * has not been tuned.  Returns as conv_plan.
+ */
+MICONV_API int conv_plan_tuned(const conv_desc *d, const conv_tensor *y, conv_plan_t *p);
 
 /* Size of the device-resident scratch array of conv_run_noalloc, MiB. */
 #define MICONV_NOALLOC_SCRATCH_MIB 32

@@ -441,3 +441,36 @@ def test_one_by_one_plain_gemm_plan():
     assert not prep(T((4, 96, 28, 28), cl=True), T((64, 96, 1, 1))).plan.flags
     assert not prep(T((4, 256, 28, 28), cl=True), T((256, 64, 1, 1)), transposed=True).plan.flags
     assert not prep(x, T((384, 128, 1, 1)), groups=2).plan.flags
+
+
+# ------------------------------------------------------ schedule timing --
+
+def _cands(wl):
+    x, w, b = wl_tensors(wl)
+    p = prep(x, w, b, **wl_args(wl))
+    return p, api.conv_plan_candidates(p.desc, api.tensor_desc(p.sizes, p.strides, x.dtype))
+
+
+def test_candidates_cover_every_schedule():
+    """The rule's plan comes first; the dense call lists every 16-bit tile
+    configuration; the transposed 1-D call adds the both-phases kernels; the
+    depthwise call lists the ring stencil, the plane stencil and the GEMM;
+    each candidate is a plan conv_plan_ex accepts, listed once."""
+    p, c = _cands(synth.dense_bf16_cl())
+    assert bytes(c[0]) == bytes(p.plan)
+    assert sorted({int(q.variant) for q in c if api.kernel_name(q.kernel) == "igemm"}) == [0, 1, 2, 3, 4, 6, 7, 8, 9, 10]
+    _, c = _cands(synth.transposed_bf16_nlc())
+    assert {12, 13} <= {int(q.variant) for q in c}
+    _, c = _cands(synth.depthwise_bf16_cl(5, 1))
+    assert {"dw_cl", "plane", "igemm"} <= {api.kernel_name(q.kernel) for q in c}
+    assert "reduce" not in {api.kernel_name(q.kernel) for q in c}
+    keys = [(q.kernel, q.variant, q.flags) for q in c]
+    assert len(keys) == len(set(keys))
+    _, c = _cands(synth.grouped_f16())
+    assert {(api.kernel_name(q.kernel), int(q.variant)) for q in c} >= {("grp", 0), ("grp", 1), ("plane", 0)}
+
+
+def test_untuned_call_plans_by_the_rule():
+    p, _ = _cands(synth.dense_bf16_cl())
+    t = api.conv_plan_tuned(p.desc, api.tensor_desc(p.sizes, p.strides, torch.bfloat16))
+    assert not (t.flags & A.PLAN_TUNED) and bytes(t) == bytes(p.plan)
