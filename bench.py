@@ -185,10 +185,10 @@ def expand(wl):
 
 
 def kernel_source_sha(kernel_name):
-    files = {"dw_cl": "k_dwcl.hip", "plane": "k_plane.hip", "grp": "k_grp.hip", "reduce": "k_reduce.hip",
-             "igemm": "k_igemm.hip", "igemm_t": "k_igemm.hip"}
+    files = {"dw_cl": ("k_dwcl.hip",), "plane": ("k_plane.hip",), "grp": ("k_grp.hip",),
+             "reduce": ("k_reduce.hip",), "igemm": ("k_igemm.hip",), "igemm_t": ("k_igemm.hip", "k_igemm_t1.hip")}
     h = hashlib.sha256()
-    for f in (files.get(kernel_name, ""), "dev_common.h"):
+    for f in files.get(kernel_name, ()) + ("dev_common.h",):
         p = os.path.join(ROOT, "depthwise_stencil_implicit_amd", "csrc", f)
         if os.path.isfile(p):
             h.update(open(p, "rb").read())
