@@ -1019,8 +1019,10 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
     }
     if (e != hipSuccess) return CONV_EDEVICE;
     if (p.variant == IG_T1_CFG || p.variant == IG_T1B_CFG) {
-        // Both phases per workgroup; it needs the 16-byte loads of x.
-        if (!vec) return CONV_EALIGN;
+        // Both phases per workgroup; it needs the 16-byte loads of x (conv_run
+        // sends a misaligned x to the phase-split tile), and writes y at any
+        // element alignment.
+        if (reinterpret_cast<uintptr_t>(x) & 15) return CONV_EALIGN;
         return launch_igemm_t1(p, x, ws, b, y, stream);
     }
     auto run = [&](const IgArgs &args, int variant) {

@@ -27,10 +27,12 @@
 // load waits overlap the other's matrix work.
 //
 // Epilogue: the 64 x 512 output tile (bias added in fp32, rounded once) is
-// staged in LDS as [channel][o] and written with consecutive lanes on
-// consecutive elements along whichever of y's dims has stride 1, so a
-// contiguous [N, C, L] output is written as whole 128-byte runs of each
-// channel's row (its rows of an odd length are not vector-aligned).
+// staged in LDS as [channel][o] and written along whichever of y's dims has
+// stride 1.  For a contiguous [N, C, L] output each channel row is staged
+// shifted by its own offset from a 16-byte boundary of y (rows of an odd
+// length start at every even offset), so the row leaves as 16-byte chunks
+// aligned to y -- one non-temporal store per lane -- plus the few elements
+// of its two partial end chunks.
 #include "dev_common.h"
 #include "internal.h"
 
@@ -60,7 +62,7 @@ constexpr int T1_RB = 64;                   // LDS row bytes: 32 channels of 16-
 constexpr int t1_fm(int nw) { return nw == 4 ? 8 : 7; }
 constexpr int t1_bm(int nw) { return nw / 2 * 16 * t1_fm(nw); }             // rows j per tile
 constexpr int t1_hr(int nw) { return (t1_bm(nw) + 64 + 16 * nw - 1) / (16 * nw) * (16 * nw); }  // halo rows
-constexpr int t1_sr(int nw) { return 2 * (2 * t1_bm(nw)) + 4; }             // staging row bytes (+ pad)
+constexpr int t1_sr(int nw) { return 2 * (2 * t1_bm(nw)) + 16; }            // staging row bytes (+ shift room)
 constexpr int t1_ab(int nt, int nw) { return t1_hr(nw) * T1_RB + nt * T1_BN * T1_RB; }
 // A stage holds the halo and the weights, and at the end whole staging rows:
 // all stages together hold the 64 channel rows of the output tile.
@@ -85,7 +87,10 @@ constexpr int t1_wgs_per_cu(int nt, int nw, int stages)
     return nw == 4 && stages * t1_stage_bytes(nt, nw, stages) <= 80 * 1024 ? 2 : 1;
 }
 
-template <typename T, int NT, int NW, int STAGES>
+// REG: an even number of taps and an odd dilation, so each phase owns
+// exactly NT/2 taps, every other one (t = t0, t0 + 2, ...): the fragment
+// reads of a step then form one static stream over the wave's taps.
+template <typename T, int NT, int NW, int STAGES, bool REG>
 __global__ __launch_bounds__(NW * 64, t1_wgs_per_cu(NT, NW, STAGES)) void igemm_t1_kernel(T1Args a)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -191,7 +196,65 @@ __global__ __launch_bounds__(NW * 64, t1_wgs_per_cu(NT, NW, STAGES)) void igemm_
         offb[t] = A_BYTES + swz_k<4>(t * BN + lr, lg);
         asm("" : "+v"(offb[t]));
     }
+    // The regular case: this wave's taps t_u = t0 + 2u and their halo
+    // shifts are known before the K loop, so each tap's A and B fragment
+    // offsets are computed once.  The reads run as one stream interleaved with
+    // the MFMAs (as in the forward tile): the first tap's B fragments and
+    // first two A fragments up front, then after each group of FN MFMAs the
+    // A fragment two groups ahead -- with, where that fragment opens the next
+    // tap, that tap's B fragments -- pinned by scheduling groups.
+    constexpr int TPH = REG ? NT / 2 : 1;
+    int offa_r[TPH], offb_r[TPH];
+    if constexpr (REG) {
+        const int t0 = (rho + a.pb) & 1;
+#pragma unroll
+        for (int u = 0; u < TPH; ++u) {
+            const int t = t0 + 2 * u;
+            const int h = ((rho + a.pb - t * a.dil) >> 1) - a.dmin;
+            offa_r[u] = swz_k<4>(wr * WR + lr + h, lg);
+            offb_r[u] = A_BYTES + swz_k<4>(t * BN + lr, lg);
+            asm("" : "+v"(offa_r[u]));
+            asm("" : "+v"(offb_r[u]));
+        }
+    }
+    auto compute_reg = [&](const unsigned char *S) {
+        uint4 af[TPH][FM], bf[TPH][FN];
+        auto read_a = [&](int u, int i) { af[u][i] = *reinterpret_cast<const uint4 *>(S + offa_r[u] + i * 16 * RB); };
+        auto read_b = [&](int u) {
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) bf[u][jj] = *reinterpret_cast<const uint4 *>(S + offb_r[u] + jj * 16 * RB);
+        };
+        read_b(0);
+        read_a(0, 0);
+        read_a(0, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, FN + 2, 0);
+#pragma unroll
+        for (int u = 0; u < TPH; ++u) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                for (int jj = 0; jj < FN; ++jj) mma_16x16x32(af[u][i], bf[u][jj], acc[i][jj], T{});
+                __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+                const int g2 = u * FM + i + 2;
+                if (g2 < TPH * FM) {
+                    const int u2 = g2 / FM, i2 = g2 % FM;
+                    if (i2 == 0) {
+                        read_b(u2);
+                        read_a(u2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, FN + 1, 0);
+                    } else {
+                        read_a(u2, i2);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                }
+            }
+        }
+    };
     auto compute = [&](const unsigned char *S) {
+        if constexpr (REG) {
+            compute_reg(S);
+            return;
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int num = rho + a.pb - t * a.dil;
@@ -257,20 +320,35 @@ __global__ __launch_bounds__(NW * 64, t1_wgs_per_cu(NT, NW, STAGES)) void igemm_
 
     // ---- epilogue: stage [channel][o] in LDS (RPS channel rows per stage),
     // then write along y's unit-stride dim ----
+    //
+    // Positions contiguous in y (pvec): each channel row of the tile is
+    // staged shifted by sh, the offset in elements of its first output from
+    // a 16-byte boundary of y, so that LDS chunk q of the row is exactly the
+    // 16-byte-aligned chunk q of y's row segment; full chunks then leave as
+    // single 16-byte stores and only the two partial end chunks element by
+    // element.  (Rows of an odd length start at every even byte offset.)
     wait_all();
     __syncthreads();
+    T *__restrict__ Y = static_cast<T *>(a.y);
+    const int o0 = 2 * j0;
+    const int cbase = g * a.Cog + n_tile * BN;
+    const int64_t ybase = (int64_t)n * a.ys_n + (int64_t)cbase * a.ys_c + (int64_t)o0 * a.ys_l;
+    const bool pvec = !a.co_fast && a.ys_l == 1;
+    auto shift_of = [&](int col) -> int {
+        const uint64_t addr = reinterpret_cast<uintptr_t>(Y) + 2 * (uint64_t)(ybase + (int64_t)col * a.ys_c);
+        return pvec ? (int)((addr & 15) >> 1) : 0;
+    };
     auto srow = [&](int col) -> unsigned char * {
         const int sidx = col / RPS, r = col - sidx * RPS;
         unsigned char *base = sidx == 0 ? st0 : (sidx == 1 ? st1 : st2);
         return base + r * SR;
     };
     const T *__restrict__ Bias = static_cast<const T *>(a.b);
-    const int cbase = g * a.Cog + n_tile * BN;
 #pragma unroll
     for (int jj = 0; jj < FN; ++jj) {
         const int col = 16 * jj + lr;
         const float bias = (a.has_bias && n_tile * BN + col < a.Cog) ? to_f32(Bias[cbase + col]) : 0.f;
-        unsigned char *row = srow(col);
+        unsigned char *row = srow(col) + 2 * shift_of(col);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -280,15 +358,58 @@ __global__ __launch_bounds__(NW * 64, t1_wgs_per_cu(NT, NW, STAGES)) void igemm_
             }
     }
     __syncthreads();
-    T *__restrict__ Y = static_cast<T *>(a.y);
-    const int o0 = 2 * j0;
-    const int64_t ybase = (int64_t)n * a.ys_n + (int64_t)cbase * a.ys_c + (int64_t)o0 * a.ys_l;
     const int ncol = min(BN, a.Cog - n_tile * BN), nout = min(2 * BM, a.O - o0);
-    // Each wave writes its share with eight staged reads in flight before
-    // their eight stores.
-    if (!a.co_fast) {
-        // Positions fastest: wave w writes channel rows w, w+NW, ..., lane l
-        // elements l, l+64, ... of a row (128-byte runs of y's rows).
+    if (pvec) {
+        // Full chunks first: wave w takes channel rows w, w+NW, ..., four at a
+        // time (their staged reads in flight together), lane l chunks l,
+        // l+64, ...; chunk q is full when outputs 8q - sh .. 8q - sh + 7 all
+        // lie in [0, nout).  The stores are non-temporal: whole lines that
+        // nothing here reads again, kept out of the L2 that holds the
+        // weights and the halo rows the neighbouring channel tiles share.
+        constexpr int NQ = 2 * BM / 8;           // chunks per row that can be full
+        for (int c0 = wave; c0 < ncol; c0 += 4 * NW) {
+            u32x4 v[4][(NQ + 63) / 64];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int col = c0 + r * NW;
+                const unsigned char *row = srow(col < ncol ? col : 0);
+#pragma unroll
+                for (int h = 0; h < (NQ + 63) / 64; ++h)
+                    if (64 * h + lane < NQ) v[r][h] = *reinterpret_cast<const u32x4 *>(row + 16 * (64 * h + lane));
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int col = c0 + r * NW;
+                if (col >= ncol) break;
+                const int sh = shift_of(col);
+                unsigned char *ab = reinterpret_cast<unsigned char *>(Y + ybase + (int64_t)col * a.ys_c) - 2 * sh;
+#pragma unroll
+                for (int h = 0; h < (NQ + 63) / 64; ++h) {
+                    const int q = 64 * h + lane, first = 8 * q - sh;
+                    if (q < NQ && first >= 0 && first + 8 <= nout)
+                        __builtin_nontemporal_store(v[r][h], reinterpret_cast<u32x4 *>(ab + 16 * q));
+                }
+            }
+        }
+        // Then the partial chunks at each row's two ends, element by element:
+        // the head, outputs [0, hd) before the first chunk boundary, and the
+        // tail, outputs [8 ql - sh, nout) after the last full chunk.  Thread
+        // t takes slots t, t + 64 NW, ...: slot = 16 row + k, k < 8 the head's
+        // k-th output, k >= 8 the tail's (k-8)-th.
+        for (int slot = tid; slot < ncol * 16; slot += 64 * NW) {
+            const int col = slot >> 4, k = slot & 15;
+            const int sh = shift_of(col);
+            const int hd = min((8 - sh) & 7, nout), ql = (nout + sh) >> 3;
+            const int o = k < 8 ? k : max(8 * ql - sh, hd) + (k - 8);
+            if ((k < 8 && o < hd) || (k >= 8 && o < nout)) {
+                const T e = *reinterpret_cast<const T *>(srow(col) + 2 * (o + sh));
+                Y[ybase + (int64_t)col * a.ys_c + o] = e;
+            }
+        }
+    } else if (!a.co_fast) {
+        // Positions fastest at a stride: wave w writes channel rows w, w+NW,
+        // ..., lane l elements l, l+64, ... of a row, eight staged reads in
+        // flight before their eight stores.
         for (int col = wave; col < ncol; col += NW) {
             const unsigned char *row = srow(col);
             T *dst = Y + ybase + (int64_t)col * a.ys_c;
@@ -324,6 +445,22 @@ __global__ __launch_bounds__(NW * 64, t1_wgs_per_cu(NT, NW, STAGES)) void igemm_
 
 // Halo-tile geometry of a call: the smallest shift delta over all taps, and
 // whether the shifts span at most 64 rows.
+namespace {
+
+template <typename T, int NT, int NW, int STAGES>
+void t1_launch(const T1Args &a, bool reg, dim3 grid, hipStream_t s)
+{
+    if constexpr (NT % 2 == 0) {
+        if (reg) {
+            hipLaunchKernelGGL((igemm_t1_kernel<T, NT, NW, STAGES, true>), grid, dim3(NW * 64), 0, s, a);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((igemm_t1_kernel<T, NT, NW, STAGES, false>), grid, dim3(NW * 64), 0, s, a);
+}
+
+}  // namespace
+
 bool igemm_t1_shifts(const conv_desc &d, int *dmin, int *span)
 {
     int lo = 1 << 30, hi = -(1 << 30);
@@ -382,22 +519,24 @@ int launch_igemm_t1(const conv_plan_t &p, const void *x, const void *wpacked, co
     // Eight waves and three stages for 2 or 4 taps (the weights of a step
     // split evenly over eight waves, three stages within the LDS); four waves
     // and two stages otherwise.
-#define MICONV_T1(K_)                                                                                       \
-    case K_:                                                                                                \
-        if (big) {                                                                                          \
-            if constexpr (K_ == 2 || K_ == 4) {                                                             \
-                if (d.dtype == CONV_F16)                                                                    \
-                    hipLaunchKernelGGL((igemm_t1_kernel<f16_t, K_, 8, 3>), grid, dim3(512), 0, s, a);       \
-                else                                                                                        \
-                    hipLaunchKernelGGL((igemm_t1_kernel<bf16_t, K_, 8, 3>), grid, dim3(512), 0, s, a);      \
-            } else {                                                                                        \
-                return CONV_EUNSUPPORTED;                                                                   \
-            }                                                                                               \
-        } else if (d.dtype == CONV_F16) {                                                                   \
-            hipLaunchKernelGGL((igemm_t1_kernel<f16_t, K_, 4, 2>), grid, dim3(256), 0, s, a);               \
-        } else {                                                                                            \
-            hipLaunchKernelGGL((igemm_t1_kernel<bf16_t, K_, 4, 2>), grid, dim3(256), 0, s, a);              \
-        }                                                                                                   \
+    // Even tap counts with an odd dilation take the static read stream.
+    const bool reg = k % 2 == 0 && (d.dilation[0] & 1);
+#define MICONV_T1(K_)                                                                 \
+    case K_:                                                                          \
+        if (big) {                                                                    \
+            if constexpr (K_ == 2 || K_ == 4) {                                       \
+                if (d.dtype == CONV_F16)                                              \
+                    t1_launch<f16_t, K_, 8, 3>(a, reg, grid, s);                      \
+                else                                                                  \
+                    t1_launch<bf16_t, K_, 8, 3>(a, reg, grid, s);                     \
+            } else {                                                                  \
+                return CONV_EUNSUPPORTED;                                             \
+            }                                                                         \
+        } else if (d.dtype == CONV_F16) {                                             \
+            t1_launch<f16_t, K_, 4, 2>(a, reg, grid, s);                              \
+        } else {                                                                      \
+            t1_launch<bf16_t, K_, 4, 2>(a, reg, grid, s);                             \
+        }                                                                             \
         break;
     switch (k) {
         MICONV_T1(2) MICONV_T1(3) MICONV_T1(4) MICONV_T1(5) MICONV_T1(6) MICONV_T1(7) MICONV_T1(8)

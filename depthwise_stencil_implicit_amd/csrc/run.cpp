@@ -5,6 +5,8 @@
 #include <cstdint>
 #include <mutex>
 
+#include <cstring>
+
 #include "internal.h"
 
 namespace {
@@ -73,8 +75,32 @@ extern "C" int conv_run(const conv_plan_t *p, const void *x, const void *w, cons
     case CONV_K_PLANE: return launch_plane(*p, x, w, b, y, stream);
     case CONV_K_GRP: return launch_grp(*p, x, w, b, y, stream);
     case CONV_K_REDUCE: return launch_reduce(*p, x, w, b, y, stream);
-    case CONV_K_IGEMM:
-    case CONV_K_IGEMM_T: return launch_igemm(*p, x, w, b, y, workspace, stream, vec);
+    case CONV_K_IGEMM_T:
+        // The both-phases tile loads x in 16-byte chunks.  An x view off a
+        // 16-byte boundary runs on the phase-split tile of 64 output channels
+        // (configuration 3), whose repacked weights have the same layout and
+        // size, so the plan's workspace serves it.
+        if ((p->variant == IG_T1_CFG || p->variant == IG_T1B_CFG) && !aligned(x, 16)) {
+            conv_tensor yc = p->y;
+            if (d.unbatched) {
+                for (int i = 1; i < yc.rank; ++i) {
+                    yc.sizes[i - 1] = yc.sizes[i];
+                    yc.strides[i - 1] = yc.strides[i];
+                }
+                yc.rank -= 1;
+            }
+            conv_plan_opts o;
+            std::memset(&o, 0, sizeof(o));
+            o.force_kernel = CONV_K_IGEMM_T;
+            o.force_variant = 3;
+            conv_plan_t q;
+            const int st = conv_plan_ex(&d, &yc, &o, &q);
+            if (st != CONV_OK) return st;
+            if (q.workspace_bytes > p->workspace_bytes) return CONV_EALIGN;
+            return launch_igemm(q, x, w, b, y, workspace, stream, false);
+        }
+        return launch_igemm(*p, x, w, b, y, workspace, stream, vec);
+    case CONV_K_IGEMM: return launch_igemm(*p, x, w, b, y, workspace, stream, vec);
     default: return CONV_EINVAL;
     }
 }

@@ -704,15 +704,18 @@ def _t1_cases():
     return out
 
 
-@pytest.mark.parametrize("variant", [12, 13])
-@pytest.mark.parametrize("wl,w_cl", _t1_cases(), ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def _t1_params():
+    # Variant 12 on every case; variant 13 (eight waves) takes 2 or 4 taps.
+    return [(wl, w_cl, v) for wl, w_cl in _t1_cases() for v in (12, 13) if v == 12 or wl.w_shape[2] in (2, 4)]
+
+
+@pytest.mark.parametrize("wl,w_cl,variant", _t1_params(),
+                         ids=lambda v: v.name if hasattr(v, "name") else str(v))
 def test_transposed_both_phases_kernel(wl, w_cl, variant):
     """Whole output of the both-phases transposed kernels against the
     reference: plan variant 12 (four waves, two stages) and 13 (eight waves,
     three stages, 2 or 4 taps); w_cl stores the weight channels-last, which
     makes y channels-last too (channel-fastest write-out)."""
-    if variant == 13 and wl.w_shape[2] not in (2, 4):
-        pytest.skip("the eight-wave kernel takes 2 or 4 taps")
     _flush(f"transposed both phases, variant {variant} (w_cl={w_cl}): {_desc(wl)}")
     x, w, b = synth.make_inputs(wl, device="cuda")
     if w_cl:
@@ -727,6 +730,63 @@ def test_transposed_both_phases_kernel(wl, w_cl, variant):
     assert tuple(y.stride()) == oracle.out_strides(tuple(y.shape), tuple(x.shape), tuple(x.stride()),
                                                    tuple(w.shape), tuple(w.stride()))
     xr, wr, br = ref_inputs(x, w, b)
+    yr, A = oracle.conv(xr, wr, br, **kw)
+    assert_close(y, yr, A, EPS[wl.dtype], wl.name)
+
+
+@pytest.mark.parametrize("offset", [0, 1, 3, 6])
+@pytest.mark.parametrize("variant", [12, 13])
+def test_both_phases_writes_stay_inside_output(variant, offset):
+    """The both-phases kernels write contiguous output rows as 16-byte
+    chunks aligned to y's memory, with the partial chunks at each row's ends
+    element by element.  Here y (rows of the odd length 601, so every row
+    starts at another alignment) sits at element offset `offset` inside a
+    canary-filled buffer and starts as NaN: afterwards the canary is intact,
+    no element is left NaN, and every element matches the reference (two
+    row tiles, the second partial; two channel tiles, the second partial)."""
+    wl = synth.random_case(7700 + offset, rank=1, transposed=True, dtype="bf16", channels_last=True, N=2, C_in=64,
+                           C_out=70, groups=1, L=[301], k=[4], stride=[2], padding_before=[1], padding_after=[2],
+                           dilation=[1], output_padding=[0], has_bias=True)
+    _flush(f"both phases guard, variant {variant}, offset {offset}: {_desc(wl)}")
+    x, w, b = synth.make_inputs(wl, device="cuda")
+    kw = expand_kw(wl)
+    prep = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=True),
+                        force_kernel="igemm_t", force_variant=variant)
+    assert tuple(prep.sizes) == (2, 70, 601) and tuple(prep.strides) == (70 * 601, 601, 1)
+    span = 1 + sum((s - 1) * st for s, st in zip(prep.sizes, prep.strides))
+    guard = 4096
+    buf = torch.full((span + 2 * guard + 8,), 7.0, dtype=x.dtype, device="cuda")
+    y = torch.as_strided(buf, prep.sizes, prep.strides, guard + offset)
+    y.fill_(float("nan"))
+    prep.run(x, w, b, y, prep.workspace(x.device))
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    assert (buf[:guard + offset] == 7.0).all() and (buf[guard + offset + span:] == 7.0).all()
+    xr, wr, br = ref_inputs(x, w, b)
+    yr, A = oracle.conv(xr, wr, br, **kw)
+    assert_close(y, yr, A, EPS[wl.dtype], wl.name)
+
+
+def test_both_phases_plan_with_misaligned_x():
+    """A both-phases plan whose x view starts off a 16-byte boundary (one
+    element in): conv_run runs the call on the phase-split tile instead, with
+    the same workspace, and the result is the reference's."""
+    wl = synth.random_case(7710, rank=1, transposed=True, dtype="f16", channels_last=True, N=2, C_in=64, C_out=72,
+                           groups=1, L=[300], k=[4], stride=[2], padding_before=[1], padding_after=[2], dilation=[1],
+                           output_padding=[1], has_bias=True)
+    _flush(f"both phases, misaligned x: {_desc(wl)}")
+    x0, w, b = synth.make_inputs(wl, device="cuda")
+    buf = torch.zeros(x0.numel() + 8, dtype=x0.dtype, device="cuda")
+    x = torch.as_strided(buf, x0.shape, x0.stride(), 1)
+    x.copy_(x0)
+    kw = expand_kw(wl)
+    prep = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=True))
+    assert api.kernel_name(prep.plan.kernel) == "igemm_t" and int(prep.plan.variant) == 12
+    y = prep.run(x, w, b, prep.empty_output(x.device), prep.workspace(x.device))
+    torch.cuda.synchronize()
+    xr, wr, br = ref_inputs(x0, w, b)
     yr, A = oracle.conv(xr, wr, br, **kw)
     assert_close(y, yr, A, EPS[wl.dtype], wl.name)
 
