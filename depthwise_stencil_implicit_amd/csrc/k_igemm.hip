@@ -68,6 +68,8 @@ struct IgArgs {
     float *part;                  // [ksplit][G][phases][rows - row0][cog_pad] partial sums
     int32_t w_bytes;              // bytes of the repacked weights (buffer range)
     int32_t one;                  // 1x1 plain GEMM: row m of A is x's row m (m * Cig elements)
+    int32_t y_lin;                // 16-bit forward output whose row m starts at element m * y_rs (+ channel)
+    int32_t y_rs;
 };
 
 // Byte offset of 16-byte chunk `c` of LDS row `r` (rows of 8 chunks).
@@ -721,6 +723,63 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
         for (int e = 0; e < 4; ++e)
             bias[j][e] = (a.has_bias && co + e < a.Cog) ? to_f32(Bias[g * a.Cog + co + e]) : 0.f;
     }
+    if constexpr (ES == 2) {
+        if (a.y_lin) {
+            // Rows of y are linear (row m at m * y_rs): the tile is staged in
+            // LDS as [row][channel] and leaves as whole 16-byte chunks, lanes
+            // on consecutive chunks of a row, so every store covers whole
+            // lines; non-temporal, as nothing here reads y again and the L2
+            // keeps the gathered input rows the next taps re-read.  Chunks of
+            // a staged row are XOR-swizzled by the row so that the 16 rows
+            // one staging write covers spread over the banks.  Rows go through
+            // in passes of what the stages hold.
+            constexpr int RBY = 2 * BN;                       // staged row bytes
+            constexpr int CPR = BN / 8;                       // chunks per row (a power of two)
+            constexpr int RPS = STAGE_BYTES / RBY;            // staged rows per stage array
+            constexpr int PR0 = STAGES * RPS < BM ? STAGES * RPS : BM;
+            constexpr int PR = PR0 / 16 * 16;                 // rows per pass
+            static_assert(PR >= 16 && (CPR & (CPR - 1)) == 0, "staging geometry");
+            auto srow = [&](int r) -> unsigned char * {
+                const int si = r / RPS;
+                // Only the stage arrays this instance has (si < STAGES).
+                unsigned char *base = si == 0 ? st0
+                                      : (si == 1 || STAGES == 2) ? st1
+                                      : (si == 2 || STAGES == 3) ? st2
+                                                                 : st3;
+                return base + (r - si * RPS) * RBY;
+            };
+            const int mbase = a.row0 + m_tile * BM;
+            T *ytile = Y + (int64_t)mbase * a.y_rs + g * a.Cog + n_tile * BN;
+            __syncthreads();
+            for (int p0 = 0; p0 < BM; p0 += PR) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int r = wr * TM + i * 16 + lr - p0;
+                    if (r < 0 || r >= PR) continue;
+                    unsigned char *row = srow(r);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int c = (wc * TN + j * 16 + lg * 4) >> 3;
+                        uint2 u;
+                        u.x = pack2<T>(acc[i][j][0] + bias[j][0], acc[i][j][1] + bias[j][1]);
+                        u.y = pack2<T>(acc[i][j][2] + bias[j][2], acc[i][j][3] + bias[j][3]);
+                        *reinterpret_cast<uint2 *>(row + ((c ^ (r & (CPR - 1))) << 4) + ((lg & 1) << 3)) = u;
+                    }
+                }
+                __syncthreads();
+                for (int idx = tid; idx < PR * CPR; idx += 64 * NW) {
+                    const int r = idx / CPR, c = idx & (CPR - 1);
+                    if (p0 + r < BM && mbase + p0 + r < a.rows && n_tile * BN + 8 * c < a.Cog) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(srow(r) + ((c ^ (r & (CPR - 1))) << 4));
+                        __builtin_nontemporal_store(
+                            v, reinterpret_cast<u32x4 *>(ytile + (int64_t)(p0 + r) * a.y_rs + 8 * c));
+                    }
+                }
+                if (p0 + PR < BM) __syncthreads();
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = a.row0 + m_tile * BM + wr * TM + i * 16 + lr;
@@ -994,6 +1053,21 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
     a.has_bias = d.has_bias;
     a.total_tiles = (int32_t)p.grid[0];
     a.w_bytes = (int32_t)igemm_wbytes(d.groups, p.tile[IG_COG_PAD], a.taps, p.tile[IG_CIG_PAD], esize(d.dtype));
+    // Linear 16-byte output rows: a forward 16-bit call whose y is dense
+    // channels-last (row m at m * C_out), channel counts in whole 8-channel
+    // chunks, y 16-byte aligned.
+    {
+        bool lin = !d.transposed && esize(d.dtype) == 2 && p.y.strides[1] == 1 && d.C_out % 8 == 0 &&
+                   (d.C_out / d.groups) % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+        int64_t e = d.C_out;
+        for (int i = r - 1; i >= 0 && lin; --i) {
+            lin = d.out[i] == 1 || p.y.strides[2 + i] == e;
+            e *= d.out[i];
+        }
+        lin = lin && (d.N == 1 || p.y.strides[0] == e);
+        a.y_lin = lin ? 1 : 0;
+        a.y_rs = (int32_t)d.C_out;
+    }
     // 4 consecutive output channels form one aligned vector in y.
     a.y_vec4 = (p.y.strides[1] == 1 && (reinterpret_cast<uintptr_t>(y) & (4 * esize(d.dtype) - 1)) == 0 &&
                 p.y.strides[0] % 4 == 0 && (r < 1 || p.y.strides[2] % 4 == 0) &&

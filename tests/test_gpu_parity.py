@@ -592,6 +592,32 @@ def test_igemm_every_tile_config(wl, cfg):
     check_full(wl, force=kind, variant=cfg)
 
 
+def _staged_row_cases():
+    """Forward 16-bit calls with dense channels-last outputs, which leave the
+    tile through the LDS-staged 16-byte row stores: several full row tiles
+    plus a partial one, a partial channel tile, groups (the channel offset of
+    each group), bias and none."""
+    return [synth.random_case(7150, rank=2, transposed=False, dtype="bf16", channels_last=True, N=1, C_in=64,
+                              C_out=264, groups=1, L=[24, 24], k=[3, 3], stride=[1, 1], padding_before=[1, 1],
+                              padding_after=[1, 1], dilation=[1, 1], output_padding=[0, 0], has_bias=True),
+            synth.random_case(7151, rank=2, transposed=False, dtype="f16", channels_last=True, N=2, C_in=2 * 64,
+                              C_out=2 * 136, groups=2, L=[20, 15], k=[3, 3], stride=[1, 1], padding_before=[1, 1],
+                              padding_after=[1, 1], dilation=[1, 1], output_padding=[0, 0], has_bias=False)]
+
+
+@pytest.mark.parametrize("cfg", CFGS_16)
+@pytest.mark.parametrize("wl", _staged_row_cases(), ids=lambda v: v.name)
+def test_igemm_staged_output_rows(wl, cfg):
+    """Every tile configuration on outputs whose rows are linear in y: the
+    tile is staged in LDS (in two passes where the stages hold fewer rows
+    than the tile) and written as whole 16-byte chunks; whole output against
+    the reference, and y's layout is the dense channels-last one this path
+    needs."""
+    _flush(f"staged rows, tile config {cfg}: {_desc(wl)}")
+    y = check_full(wl, force="igemm", variant=cfg)
+    assert y.stride(1) == 1 and y.stride(-1) == y.shape[1]
+
+
 # ------------------------------------------- every depthwise ring kernel --
 
 def _dw_every_case():
