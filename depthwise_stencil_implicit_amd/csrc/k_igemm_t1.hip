@@ -62,7 +62,10 @@ constexpr int T1_RB = 64;                   // LDS row bytes: 32 channels of 16-
 constexpr int t1_fm(int nw) { return nw == 4 ? 8 : 7; }
 constexpr int t1_bm(int nw) { return nw / 2 * 16 * t1_fm(nw); }             // rows j per tile
 constexpr int t1_hr(int nw) { return (t1_bm(nw) + 64 + 16 * nw - 1) / (16 * nw) * (16 * nw); }  // halo rows
-constexpr int t1_sr(int nw) { return 2 * (2 * t1_bm(nw)) + 16; }            // staging row bytes (+ shift room)
+// Staging row bytes: the row, up to 7 elements of shift, and an odd number of
+// dwords in all, so that the 16 channel rows one staging write covers fall on
+// distinct banks.
+constexpr int t1_sr(int nw) { return 2 * (2 * t1_bm(nw)) + 20; }
 constexpr int t1_ab(int nt, int nw) { return t1_hr(nw) * T1_RB + nt * T1_BN * T1_RB; }
 // A stage holds the halo and the weights, and at the end whole staging rows:
 // all stages together hold the 64 channel rows of the output tile.
@@ -375,7 +378,11 @@ __global__ __launch_bounds__(NW * 64, t1_wgs_per_cu(NT, NW, STAGES)) void igemm_
                 const unsigned char *row = srow(col < ncol ? col : 0);
 #pragma unroll
                 for (int h = 0; h < (NQ + 63) / 64; ++h)
-                    if (64 * h + lane < NQ) v[r][h] = *reinterpret_cast<const u32x4 *>(row + 16 * (64 * h + lane));
+                    if (64 * h + lane < NQ) {
+                        // Rows start on 4-byte boundaries: four dword reads.
+                        const uint32_t *src = reinterpret_cast<const uint32_t *>(row + 16 * (64 * h + lane));
+                        v[r][h] = u32x4{src[0], src[1], src[2], src[3]};
+                    }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
