@@ -9,7 +9,9 @@ layout and planning run once per call before timing, and their host time is
 reported as ``host_plan_us``).  Inputs are seeded synthetic tensors already in
 HBM; R rotation copies of every input/output keep consecutive uses of a
 buffer more than ~1 GiB of traffic apart, so the 256 MB Infinity Cache cannot
-serve them.  One JSON line is printed.
+serve them.  ``--graph`` captures each rotation set's step once in a HIP graph
+and times graph replays instead of eager launches (the library's launches
+are capturable: kernels only).  One JSON line is printed.
 
 Workloads
   all          (default) every measured workload below in one step: the
@@ -29,7 +31,7 @@ Workloads
 
 ``roofline`` describes the call with the largest average duration: its
 algorithmic bytes (or FLOPs) per launch over that average, measured with HIP
-events on the launch stream.  ``cpu_baseline`` times the double-precision
+events on the launch stream around eager launches of each call.  ``cpu_baseline`` times the double-precision
 reference (test infrastructure) on the host cores over a bounded sample.
 """
 from __future__ import annotations
@@ -68,6 +70,9 @@ def parse():
                     help="run the planner's rule-based schedules (default: time every candidate schedule of each "
                          "call once while planning, conv_tune, and run the fastest)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU work for the baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each rotation set's step once in a HIP graph and time graph replays (default: "
+                         "eager launches; on the default workload both measure the same step time)")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="MIB",
                     help="instead of a workload, time a plain device copy of MIB mebibytes (the "
                          "measured bandwidth ceiling, and the reference for HBM byte counters)")
@@ -371,24 +376,43 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
-    def step(i, evs=None):
-        r = i % R
+    def launch(r, sp, evs=None, st=None):
         for c, (_, wl, p, _) in enumerate(preps):
             xd, wd, bd, yd, ws = sets[c][r]
             if evs is not None:
-                evs[c][0].record(stream)
-            p.run(xd, wd, bd, yd, ws, sptr)
+                evs[c][0].record(st)
+            p.run(xd, wd, bd, yd, ws, sp)
             if evs is not None:
-                evs[c][1].record(stream)
+                evs[c][1].record(st)
+
+    def step(i, evs=None):
+        launch(i % R, sptr, evs, stream)
 
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # ---- the step as HIP graphs: every call of rotation set r captured once
+    # (the library launches only kernels, no memsets or allocations) ----
+    graphs = []
+    if a.graph:
+        cs = torch.cuda.Stream(dev)
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                launch(r, torch.cuda.current_stream(dev).cuda_stream)
+            graphs.append(g)
+        for i in range(a.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+
     # ---- timed region: exactly K steps, synchronised on both sides ----
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(a.warmup + i)
+        if graphs:
+            graphs[(a.warmup + i) % R].replay()
+        else:
+            step(a.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / a.steps
@@ -450,7 +474,10 @@ def main():
 
     dtypes = sorted({wl.dtype for _, wl, _, _ in preps})
     config = {"workload": a.workload, "calls": [wl.name for _, wl, _, _ in preps], "dtypes": dtypes,
-              "rotation_sets": R, "timing": "wall clock over K steps; per-call HIP events on the launch stream",
+              "rotation_sets": R,
+              "timing": ("wall clock over K steps" + (" (one HIP graph replay per step)" if a.graph else
+                                                      " (eager launches)") +
+                         "; per-call HIP events on the launch stream around eager launches"),
               "schedules": "planner rule" if a.rule else "timed at plan time (conv_tune), fastest kept",
               "headline": ("sum over the calls of their time at the roofline / measured step time"
                            if a.workload == "all" else "algorithmic units of a step / measured step time")}
