@@ -943,6 +943,65 @@ constexpr IgemmCfg kCfgs[] = {
     {64, 256, 64, 1, 4, 3, 40},    // 11: 4 waves, wave tile 64 x 64 (rows left after the full rounds)
 };
 
+// Weight repack through an LDS tile, for weights whose packed rows (g, j, t)
+// lie closer together in w than the channels c of one row -- the contiguous
+// transposed weight [C_in][Cog][k] (rows adjacent, channels Cog*k apart), or
+// the forward [C_out][Cig][k] with taps innermost.  A workgroup takes 64
+// packed rows x 64 channels: lanes on consecutive rows read w (consecutive
+// addresses where the rows are adjacent), the tile is transposed in LDS, and
+// lanes on consecutive 16-byte chunks of each packed row write it.
+template <typename T>
+__global__ __launch_bounds__(256) void igemm_repack_t(const T *__restrict__ w, T *__restrict__ wr, int32_t nrows,
+                                                     int32_t Cig, int32_t Cog, int32_t cig_pad, int32_t cog_pad,
+                                                     int32_t taps, int32_t K1, int32_t K2, int64_t ws0, int64_t ws1,
+                                                     int64_t wk0, int64_t wk1, int64_t wk2, int32_t transposed)
+{
+    constexpr int EV = 16 / sizeof(T);
+    __shared__ T tile[64][65];
+    const int tid = threadIdx.x;
+    const int ctiles = cig_pad / 64;
+    const int r0 = (blockIdx.x / ctiles) * 64, c0 = (blockIdx.x % ctiles) * 64;
+    // Read: lane tr = packed row r0 + tr, channels c0 + tc, tc + 4, ...
+    {
+        const int tr = tid & 63, tc = tid >> 6;
+        const int R = r0 + tr;
+        int64_t base = 0;
+        bool ok = R < nrows;
+        if (ok) {
+            const int t = R % taps;
+            const int gj = R / taps;
+            const int j = gj % cog_pad, g = gj / cog_pad;
+            ok = j < Cog;
+            const int t2 = t % K2, t1 = (t / K2) % K1, t0 = t / (K2 * K1);
+            const int64_t toff = t0 * wk0 + t1 * wk1 + t2 * wk2;
+            base = transposed ? (int64_t)g * Cig * ws0 + (int64_t)j * ws1 + toff : ((int64_t)g * Cog + j) * ws0 + toff;
+        }
+        const int64_t sc = transposed ? ws0 : ws1;
+        // All sixteen reads in flight before the first LDS write.
+        T v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int cc = c0 + tc + 4 * k;
+            v[k] = (ok && cc < Cig) ? w[base + (int64_t)cc * sc] : T{};
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) tile[tc + 4 * k][tr] = v[k];
+    }
+    __syncthreads();
+    // Write: 64 rows x 64 / EV chunks; lane -> (row, chunk), chunks fastest.
+    constexpr int CPT = 64 / EV;
+    for (int q = tid; q < 64 * CPT; q += 256) {
+        const int r = q / CPT, ch = q % CPT;
+        if (r0 + r >= nrows) continue;
+        T v[EV];
+#pragma unroll
+        for (int e = 0; e < EV; ++e) v[e] = tile[ch * EV + e][r];
+        uint4 u;
+        __builtin_memcpy(&u, v, 16);
+        reinterpret_cast<uint4 *>(wr + (int64_t)(r0 + r) * cig_pad + c0)[ch] = u;
+    }
+}
+
 template <typename T, int V, bool VEC>
 hipError_t launch_cfg(const IgArgs &a, hipStream_t s)
 {
@@ -998,6 +1057,20 @@ hipError_t launch_repack(const conv_plan_t &p, const void *w, void *ws, hipStrea
     int64_t wk[3] = {0, 0, 0};
     for (int i = 0; i < r; ++i) wk[i] = d.w.strides[2 + i];
     const int64_t chunks = total / (16 / (int64_t)sizeof(T));
+    // Packed rows (g, j, t) are taps-fastest; the stride of the innermost
+    // tap, and the channel stride, in w.
+    const int64_t row_stride = r > 0 ? wk[r - 1] : 1;
+    const int64_t ch_stride = d.transposed ? d.w.strides[0] : d.w.strides[1];
+    const int64_t nrows = total / p.tile[IG_CIG_PAD];
+    if (row_stride < ch_stride && p.tile[IG_CIG_PAD] % 64 == 0 && nrows < (int64_t)1 << 30) {
+        const int64_t blocks = cdiv(nrows, 64) * (p.tile[IG_CIG_PAD] / 64);
+        hipLaunchKernelGGL((igemm_repack_t<T>), dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const T *>(w),
+                           static_cast<T *>(ws), (int32_t)nrows, (int32_t)(d.C_in / d.groups),
+                           (int32_t)(d.C_out / d.groups), (int32_t)p.tile[IG_CIG_PAD], (int32_t)p.tile[IG_COG_PAD],
+                           (int32_t)taps, (int32_t)d.k[1], (int32_t)d.k[2], d.w.strides[0], d.w.strides[1], wk[0],
+                           wk[1], wk[2], d.transposed);
+        return hipGetLastError();
+    }
     const int64_t blocks = std::min<int64_t>(cdiv(chunks, 256), 4096);
     hipLaunchKernelGGL((igemm_repack<T>), dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const T *>(w),
                        static_cast<T *>(ws), (int32_t)chunks, (int32_t)(d.C_in / d.groups), (int32_t)(d.C_out / d.groups),
