@@ -28,6 +28,10 @@ Workloads
   grp_f16      grouped fp16 NCHW, 32x256x28x28 -> 512, 64 groups.  GB/s.
   dense_bf16   dense 3x3 bf16 channels-last, 64x256x56x56 -> 256.  TFLOP/s.
   convT1d_bf16 transposed 1-D bf16 NLC, 16x512x8192 -> 16383, k=4, s=2.  TFLOP/s.
+  edges        calls at the edges of the fast paths, each its own row (not
+               part of ``all``): depthwise 9x9 and stride 3, a channel
+               multiplier of 2, 1-D depthwise, 3-D dense, 2-D transposed.
+               ``value`` as for ``all``.
 
 ``roofline`` describes the call with the largest average duration: its
 algorithmic bytes (or FLOPs) per launch over that average, measured with HIP
@@ -53,7 +57,10 @@ VALU_DOT2_PEAK_TFLOPS = 157.3         # the same lanes issuing v_dot2_f32_{bf16,
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 
-WORKLOADS = ("all", "dw_f32_small", "dw_bf16_cl", "grp_f16", "dense_bf16", "convT1d_bf16")
+WORKLOADS = ("all", "dw_f32_small", "dw_bf16_cl", "grp_f16", "dense_bf16", "convT1d_bf16", "edges")
+# The five measured workloads (the default run), and the domain-edge calls.
+MEASURED = ("dw_f32_small", "dw_bf16_cl", "grp_f16", "dense_bf16", "convT1d_bf16")
+META = ("all", "edges")
 UNITS = {"dw_f32_small": "GB/s", "dw_bf16_cl": "GB/s", "grp_f16": "GB/s", "dense_bf16": "TFLOP/s",
          "convT1d_bf16": "TFLOP/s"}
 
@@ -177,7 +184,10 @@ def workload_calls(name):
     table = {"dw_f32_small": [synth.depthwise_f32_small()], "dw_bf16_cl": synth.depthwise_bf16_cl_all(),
              "grp_f16": [synth.grouped_f16()], "dense_bf16": [synth.dense_bf16_cl()],
              "convT1d_bf16": [synth.transposed_bf16_nlc()]}
-    names = [n for n in WORKLOADS if n != "all"] if name == "all" else [name]
+    if name == "edges":
+        # Each edge call is a workload of its own, in the unit of its bound.
+        return [(wl.name, wl) for wl in synth.domain_edge_workloads()]
+    names = list(MEASURED) if name == "all" else [name]
     return [(n, wl) for n in names for wl in table[n]]
 
 
@@ -258,6 +268,17 @@ def roof_of(kernel, variant, dtype, flops, nbytes):
     return "hbm", HBM_PEAK_GBS, t_mem
 
 
+def unit_of(wname, plan):
+    """GB/s or TFLOP/s: a measured workload's own unit, else the unit of the
+    call's bound."""
+    if wname in UNITS:
+        return UNITS[wname]
+    from depthwise_stencil_implicit_amd import api
+    bound, _, _ = roof_of(api.kernel_name(plan.kernel), int(plan.variant), "bf16", float(plan.flops),
+                          float(plan.bytes))
+    return "GB/s" if bound == "hbm" else "TFLOP/s"
+
+
 def cpu_model():
     try:
         for ln in open("/proc/cpuinfo"):
@@ -307,7 +328,7 @@ def cpu_baseline(calls, target_s, headline_pct):
         rounds += 1
     rows = []
     for wname, (t, nb, fl, tr) in per.items():
-        unit = UNITS[wname]
+        unit = unit_of(wname, next(p for n, _, _, p in plan if n == wname))
         rows.append({"workload": wname, "unit": unit,
                      "value": round(nb / t / 1e9 if unit == "GB/s" else fl / t / 1e12, 5)})
     pct = 100.0 * sum(e[3] for e in per.values()) / sum(e[0] for e in per.values())
@@ -443,13 +464,13 @@ def main():
     for wname in dict.fromkeys(c["workload"] for c in per_call):
         cs = [c for c in per_call if c["workload"] == wname]
         t = sum(c["avg_us"] for c in cs)
-        unit = UNITS[wname]
+        unit = UNITS.get(wname) or ("GB/s" if cs[0]["bound"] == "hbm" else "TFLOP/s")
         val = sum(c["bytes"] for c in cs) / t / 1e3 if unit == "GB/s" else sum(c["flops"] for c in cs) / t / 1e6
         rows.append({"workload": wname, "calls": len(cs), "unit": unit, "value": round(val, 2),
                      "us": round(t, 2), "roof_us": round(sum(c["roof_us"] for c in cs), 3),
                      "frac_of_roofline": round(sum(c["roof_us"] for c in cs) / t, 4)})
     roof_total_us = sum(c["roof_us"] for c in per_call)
-    if a.workload == "all":
+    if a.workload in META:
         value, unit = 100.0 * roof_total_us / (ms_per_step * 1e3), "% of MI355X roofline"
     else:
         unit = UNITS[a.workload]
@@ -480,7 +501,7 @@ def main():
                          "; per-call HIP events on the launch stream around eager launches"),
               "schedules": "planner rule" if a.rule else "timed at plan time (conv_tune), fastest kept",
               "headline": ("sum over the calls of their time at the roofline / measured step time"
-                           if a.workload == "all" else "algorithmic units of a step / measured step time")}
+                           if a.workload in META else "algorithmic units of a step / measured step time")}
     out = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": dtypes[0] if len(dtypes) == 1 else "mixed",
@@ -488,8 +509,8 @@ def main():
     if a.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:
-        out["cpu_baseline"] = cpu_baseline(calls, a.cpu_seconds, value if a.workload == "all" else None)
-        if a.workload != "all":
+        out["cpu_baseline"] = cpu_baseline(calls, a.cpu_seconds, value if a.workload in META else None)
+        if a.workload not in META:
             # Single-workload runs: the CPU figure in the workload's own unit.
             pw = out["cpu_baseline"]["per_workload"][0]
             out["cpu_baseline"].update(value=pw["value"], unit=pw["unit"])

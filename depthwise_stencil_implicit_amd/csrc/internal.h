@@ -94,8 +94,13 @@ constexpr int dw_pending(int K, int S, int CB, int D)
 }
 // Workgroups resident per CU: three for the light stride-1 stencils (k3, and
 // k5 on the 16-byte path, fit 12 waves per CU in registers, and a 4-row ring
-// keeps three rings in LDS), two with a 6-row ring otherwise.
-constexpr int dw_wgs_per_cu(int K, int S, int CB) { return S == 1 && (K == 3 || (K == 5 && CB == 16)) ? 3 : 2; }
+// keeps three rings in LDS), one for k9 at stride 1 (its nine open output rows
+// of accumulators take more than half the registers), two with a 6-row ring
+// otherwise.
+constexpr int dw_wgs_per_cu(int K, int S, int CB)
+{
+    return S == 1 && (K == 3 || (K == 5 && CB == 16)) ? 3 : (K == 9 && S == 1 ? 1 : 2);
+}
 constexpr int dw_depth(int K, int S, int CB)
 {
     int d = dw_wgs_per_cu(K, S, CB) == 3 ? 4 : 6;

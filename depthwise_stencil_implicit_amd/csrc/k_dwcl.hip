@@ -473,6 +473,7 @@ hipError_t dispatch(const DwArgs &a, int64_t grid, int k, int s, hipStream_t st)
 #define MICONV_DW(KK, SS) \
     if (k == KK && s == SS) return go<T, KK, SS, CB>(a, grid, st);
     MICONV_DW(3, 1) MICONV_DW(5, 1) MICONV_DW(7, 1) MICONV_DW(3, 2) MICONV_DW(5, 2) MICONV_DW(7, 2)
+    MICONV_DW(9, 1) MICONV_DW(9, 2)
 #undef MICONV_DW
     return hipErrorInvalidValue;
 }
@@ -482,7 +483,7 @@ hipError_t dispatch(const DwArgs &a, int64_t grid, int k, int s, hipStream_t st)
 // Kernel sizes and strides with a compiled schedule (square kernels, equal strides).
 bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw)
 {
-    return kh == kw && sh == sw && (kh == 3 || kh == 5 || kh == 7) && (sh == 1 || sh == 2);
+    return kh == kw && sh == sw && (kh == 3 || kh == 5 || kh == 7 || kh == 9) && (sh == 1 || sh == 2);
 }
 
 int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream, bool vec)

@@ -160,6 +160,46 @@ def transposed_bf16_nlc() -> Workload:
                     x_dist=("normal", 1.0), w_dist=("normal", 1.0 / 2048.0), seed=5)
 
 
+# --- Calls at the edges of the fast paths (measured, not part of the five) --
+
+def domain_edge_workloads() -> List[Workload]:
+    """Calls of the canonical domain outside the five measured workloads, with
+    the channel and spatial sizes of the depthwise workload where they apply:
+    depthwise 9x9 and stride 3, a channel multiplier of 2, 1-D depthwise
+    (NLC), 3-D dense forward and 2-D transposed (channels-last), and grouped
+    1-D transposed with dilation 2."""
+    out = []
+    def dw(name, x, w, groups, k, s, pb, pa, seed):
+        r = len(k)
+        taps = 1
+        for v in k:
+            taps *= v
+        return Workload(name, x, w, "bf16", True, True, groups=groups, stride=s, padding_before=pb,
+                        padding_after=pa, dilation=(1,) * r, output_padding=(0,) * r,
+                        x_dist=("normal", 1.0), w_dist=("normal", 1.0 / taps), b_dist=("uniform", -0.1, 0.1),
+                        seed=seed)
+    out.append(dw("edge_dw_bf16_nhwc_32x256x56x56_k9s1", (32, 256, 56, 56), (256, 1, 9, 9), 256, (9, 9), (1, 1),
+                  (4, 4), (4, 4), 3001))
+    out.append(dw("edge_dw_bf16_nhwc_32x256x56x56_k3s3", (32, 256, 56, 56), (256, 1, 3, 3), 256, (3, 3), (3, 3),
+                  (1, 1), (1, 1), 3002))
+    out.append(dw("edge_dw_bf16_nhwc_32x256x56x56_k3s1_m2", (32, 256, 56, 56), (512, 1, 3, 3), 256, (3, 3), (1, 1),
+                  (1, 1), (1, 1), 3003))
+    out.append(Workload("edge_dw1d_bf16_nlc_32x256x3136_k7", (32, 256, 3136), (256, 1, 7), "bf16", True, True,
+                        groups=256, stride=(1,), padding_before=(3,), padding_after=(3,), dilation=(1,),
+                        output_padding=(0,), x_dist=("normal", 1.0), w_dist=("normal", 1.0 / 7.0),
+                        b_dist=("uniform", -0.1, 0.1), seed=3004))
+    out.append(Workload("edge_dense3d_bf16_ndhwc_4x128x16x28x28_k3", (4, 128, 16, 28, 28), (128, 128, 3, 3, 3),
+                        "bf16", True, True, groups=1, stride=(1, 1, 1), padding_before=(1, 1, 1),
+                        padding_after=(1, 1, 1), dilation=(1, 1, 1), output_padding=(0, 0, 0),
+                        x_dist=("normal", 1.0), w_dist=("normal", 1.0 / 3456.0), b_dist=("uniform", -0.1, 0.1),
+                        seed=3005))
+    out.append(Workload("edge_convT2d_bf16_nhwc_16x256x28x28_k4s2", (16, 256, 28, 28), (256, 128, 4, 4), "bf16",
+                        True, True, groups=1, stride=(2, 2), padding_before=(1, 1), padding_after=(1, 1),
+                        dilation=(1, 1), transposed=True, output_padding=(0, 0), x_dist=("normal", 1.0),
+                        w_dist=("normal", 1.0 / 1024.0), b_dist=("uniform", -0.1, 0.1), seed=3006))
+    return out
+
+
 def all_workloads() -> List[Workload]:
     return ([depthwise_f32_small()] + depthwise_bf16_cl_all()
             + [grouped_f16(), dense_bf16_cl(), transposed_bf16_nlc()])

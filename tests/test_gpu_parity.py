@@ -621,14 +621,14 @@ def test_igemm_staged_output_rows(wl, cfg):
 # ------------------------------------------- every depthwise ring kernel --
 
 def _dw_every_case():
-    """One channels-last depthwise call per compiled ring kernel: kernel 3, 5
-    and 7, stride 1 and 2, fp32 / fp16 / bf16, channel runs of whole 16-byte
+    """One channels-last depthwise call per compiled ring kernel: kernel 3, 5,
+    7 and 9, stride 1 and 2, fp32 / fp16 / bf16, channel runs of whole 16-byte
     chunks (the 16-byte path) and not (the 4-byte path; 12 channels of 16-bit
     or 6 of fp32 are 24 bytes), asymmetric padding and a ragged column chunk
     (72 output columns at stride 1, more than one 56-column chunk)."""
     out = []
     i = 0
-    for k in (3, 5, 7):
+    for k in (3, 5, 7, 9):
         for s in (1, 2):
             for dtype in ("f32", "f16", "bf16"):
                 for aligned in (True, False):
