@@ -42,6 +42,13 @@ int add(const conv_desc *d, const conv_tensor *y, int32_t kernel, int32_t varian
     o.force_variant = variant;
     conv_plan_t p;
     if (conv_plan_ex(d, y, &o, &p) != CONV_OK) return 0;
+    // An implicit GEMM that pads each group's input channels more than
+    // fourfold to its channel block (a depthwise or few-channel call, which
+    // the stencils serve) multiplies mostly zeros: one launch can take
+    // milliseconds, so it is not timed.
+    if ((p.kernel == CONV_K_IGEMM || p.kernel == CONV_K_IGEMM_T) && !(p.flags & CONV_PLAN_ONE_BY_ONE) &&
+        p.tile[IG_CIG_PAD] > 4 * (d->C_in / d->groups))
+        return 0;
     // The same schedule reached through another forced kernel (a plane plan
     // can fall back to the implicit GEMM) is listed once.
     for (int i = 0; i < n && i < max; ++i)

@@ -341,7 +341,9 @@ MICONV_API int conv_run_backward(const conv_bwd_plan_t *p, const void *x, const 
  * first, then each kernel whose supports() holds and each schedule of the
  * kernels that have several (the implicit GEMM's tile table, the grouped
  * stencil's schedules, the transposed both-phases kernels), as conv_plan_ex
- * accepts them (executorch PR #25085, description: the stencil's schedules
+ * accepts them -- except implicit-GEMM plans that pad each group's input
+ * channels more than fourfold, which multiply mostly zeros (executorch PR
+ * #25085, description: the stencil's schedules
  * are timed when the call is compiled; torch/_inductor/kernel/conv.py,
  * autotune_select_algorithm).  Host only.
  *
