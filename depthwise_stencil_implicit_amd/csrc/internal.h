@@ -113,6 +113,10 @@ constexpr int dw_lds_bytes(int K, int S, int CB)
     return dw_depth(K, S, CB) * dw_row_bytes(K, S, CB) + dw_tail_bytes(K, S);
 }
 // Plan-field indices for the depthwise stencil (plan.tile[]).
+// dw_cl plan variants: 0 = ring kernel with 4-byte accesses, 1 = ring kernel
+// with 16-byte accesses, DWCL_GENERIC = the generic schedule (any multiplier,
+// kernel shape and stride; no LDS).
+constexpr int DWCL_GENERIC = 2;
 enum { DW_CW = 0, DW_OCOLS = 1, DW_CHCHUNKS = 2, DW_COLCHUNKS = 3, DW_XBYTES = 4, DW_YBYTES = 5, DW_RBLOCKS = 6,
        DW_RPB = 7 };
 

@@ -480,6 +480,191 @@ hipError_t dispatch(const DwArgs &a, int64_t grid, int k, int s, hipStream_t st)
 
 }  // namespace
 
+// ---- generic schedule (plan variant DWCL_GENERIC) ----
+//
+// Channel-contiguous depthwise calls the ring kernels do not cover -- any
+// channel multiplier m (output channel co reads input channel co / m: the
+// multiplier schedule of the PR #25085 description), kernels up to 9 x 9 of
+// any shape, any stride, 1-D calls lifted to one row -- with no LDS: lane
+// (channel word, column strip) of a 256-thread workgroup owns one 32-bit
+// word of output channels (two 16-bit or one fp32) and TO consecutive output
+// columns of one output row; consecutive lanes take consecutive channel
+// words, so every load and store of the workgroup is a run of consecutive
+// channels.  Input values come straight from global memory (the K x K window
+// re-reads hit L1/L2), one word load for both channels of a word when m = 1,
+// one element load when both output channels share an input channel (m
+// even), two otherwise.  fp32 accumulation, bias first, one rounding.
+struct DwgArgs {
+    const void *x, *w, *b;
+    void *y;
+    int64_t xs_n, xs_h, xs_w;     // element strides of x (channel stride 1)
+    int64_t ys_n, ys_h, ys_w;     // element strides of y (channel stride 1)
+    int64_t ws0, ws2, ws3;        // weight strides (output channel, kh, kw)
+    int32_t H, W, M, Cout, OH, OW, KH, KW, SH, SW, PH, PW;
+    int32_t col_blocks, ch_blocks, has_bias;
+};
+
+constexpr int DWG_TO = 8;         // output columns per lane
+
+// KB: kernel width rounded up to 3, 5 or 9 (taps past the width have zero
+// weights); S: the column stride (1..3).  Per kernel row the lane first loads
+// its whole input window -- (TO-1)*S + KB columns, absent ones as zeros --
+// and the kernel row's weights, all loads in flight together, then runs the
+// TO x KB multiply-adds from registers.
+template <typename T, bool WX, int KB, int S>
+__global__ __launch_bounds__(256) void dwg_kernel(DwgArgs a)
+{
+    constexpr int V = Dt<T>::size == 2 ? 2 : 1;
+    constexpr int TO = DWG_TO;
+    constexpr int NX = (TO - 1) * S + KB;        // input columns of the window
+    const int tid = threadIdx.x, cl = tid & 31, st = tid >> 5;
+    int b = blockIdx.x;
+    const int chb = b % a.ch_blocks;
+    b /= a.ch_blocks;
+    const int cb = b % a.col_blocks;
+    b /= a.col_blocks;
+    const int oh = b % a.OH;
+    const int n = b / a.OH;
+    const int co0 = (chb * 32 + cl) * V;          // first output channel of the lane
+    const int ow0 = (cb * 8 + st) * TO;          // first output column of the lane
+    if (co0 >= a.Cout || ow0 >= a.OW) return;    // no barriers below
+    const int nv = min(V, a.Cout - co0);         // output channels of the word
+    int ci[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) ci[v] = min(co0 + v, a.Cout - 1) / a.M;
+    const bool same = V == 2 && ci[0] == ci[V - 1];
+
+    const T *__restrict__ Bp = static_cast<const T *>(a.b);
+    float acc[TO][V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const float bv = (a.has_bias && v < nv) ? to_f32(Bp[co0 + v]) : 0.f;
+#pragma unroll
+        for (int t = 0; t < TO; ++t) acc[t][v] = bv;
+    }
+    const T *__restrict__ X = static_cast<const T *>(a.x) + (int64_t)n * a.xs_n;
+    const T *__restrict__ Wt = static_cast<const T *>(a.w);
+    const int iw0 = ow0 * S - a.PW;
+    const int nx = (min(TO, a.OW - ow0) - 1) * S + a.KW;   // window columns any output uses
+    for (int kh = 0; kh < a.KH; ++kh) {
+        const int ih = oh * a.SH - a.PH + kh;
+        if ((unsigned)ih >= (unsigned)a.H) continue;   // uniform over the workgroup
+        const T *__restrict__ Xr = X + (int64_t)ih * a.xs_h;
+        float wv[KB][V];
+#pragma unroll
+        for (int kw = 0; kw < KB; ++kw)
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                wv[kw][v] = (kw < a.KW && v < nv) ? to_f32(Wt[(int64_t)(co0 + v) * a.ws0 + kh * a.ws2 + kw * a.ws3])
+                                                  : 0.f;
+        float xw[NX][V];
+#pragma unroll
+        for (int j = 0; j < NX; ++j) {
+            const int iw = iw0 + j;
+            const bool ok = j < nx && (unsigned)iw < (unsigned)a.W;
+            const T *px = Xr + (int64_t)(ok ? iw : 0) * a.xs_w;
+            if constexpr (WX) {
+                // m = 1, 16-bit: the word of input channels co0, co0 + 1.
+                const uint32_t u = ok ? *reinterpret_cast<const uint32_t *>(px + co0) : 0u;
+                T lo, hi;
+                lo.u = (uint16_t)u;
+                hi.u = (uint16_t)(u >> 16);
+                xw[j][0] = to_f32(lo);
+                xw[j][V - 1] = to_f32(hi);
+            } else {
+                xw[j][0] = ok ? to_f32(px[ci[0]]) : 0.f;
+                if constexpr (V == 2) xw[j][1] = same ? xw[j][0] : (ok ? to_f32(px[ci[1]]) : 0.f);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TO; ++t)
+#pragma unroll
+            for (int kw = 0; kw < KB; ++kw)
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xw[t * S + kw][v], wv[kw][v], acc[t][v]);
+    }
+    T *__restrict__ Y = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h + co0;
+#pragma unroll
+    for (int t = 0; t < TO; ++t) {
+        const int ow = ow0 + t;
+        if (ow >= a.OW) break;
+        T *py = Y + (int64_t)ow * a.ys_w;
+        if constexpr (V == 2) {
+            if (nv == 2) {
+                *reinterpret_cast<uint32_t *>(py) = pack2<T>(acc[t][0], acc[t][1]);
+                continue;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (v < nv) py[v] = from_f32<T>(acc[t][v]);
+    }
+}
+
+namespace {
+
+template <typename T, bool WX>
+hipError_t dwg_go(const DwgArgs &a, dim3 grid, hipStream_t s)
+{
+    const int kb = a.KW <= 3 ? 3 : (a.KW <= 5 ? 5 : 9);
+#define MICONV_DWG(KB_, S_) \
+    if (kb == KB_ && a.SW == S_) hipLaunchKernelGGL((dwg_kernel<T, WX, KB_, S_>), grid, dim3(256), 0, s, a); else
+    MICONV_DWG(3, 1) MICONV_DWG(5, 1) MICONV_DWG(9, 1) MICONV_DWG(3, 2) MICONV_DWG(5, 2) MICONV_DWG(9, 2)
+    MICONV_DWG(3, 3) MICONV_DWG(5, 3) MICONV_DWG(9, 3) return hipErrorInvalidValue;
+#undef MICONV_DWG
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_dwg(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream)
+{
+    const conv_desc &d = p.d;
+    const bool two = d.spatial == 2;
+    DwgArgs a;
+    a.x = x;
+    a.w = w;
+    a.b = b;
+    a.y = y;
+    a.xs_n = d.x.strides[0];
+    a.xs_h = two ? d.x.strides[2] : 0;
+    a.xs_w = d.x.strides[two ? 3 : 2];
+    a.ys_n = p.y.strides[0];
+    a.ys_h = two ? p.y.strides[2] : 0;
+    a.ys_w = p.y.strides[two ? 3 : 2];
+    a.ws0 = d.w.strides[0];
+    a.ws2 = two ? d.w.strides[2] : 0;
+    a.ws3 = d.w.strides[two ? 3 : 2];
+    a.H = two ? (int32_t)d.in[0] : 1;
+    a.W = (int32_t)d.in[two ? 1 : 0];
+    a.M = (int32_t)(d.C_out / d.C_in);
+    a.Cout = (int32_t)d.C_out;
+    a.OH = two ? (int32_t)d.out[0] : 1;
+    a.OW = (int32_t)d.out[two ? 1 : 0];
+    a.KH = two ? (int32_t)d.k[0] : 1;
+    a.KW = (int32_t)d.k[two ? 1 : 0];
+    a.SH = two ? (int32_t)d.stride[0] : 1;
+    a.SW = (int32_t)d.stride[two ? 1 : 0];
+    a.PH = two ? (int32_t)d.padding_before[0] : 0;
+    a.PW = (int32_t)d.padding_before[two ? 1 : 0];
+    a.col_blocks = (int32_t)p.tile[DW_COLCHUNKS];
+    a.ch_blocks = (int32_t)p.tile[DW_CHCHUNKS];
+    a.has_bias = d.has_bias;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)p.grid[0]);
+    // Word loads of x: multiplier 1 with 16-bit channel pairs on 4-byte
+    // boundaries of x.
+    const bool wx = a.M == 1 && esize(d.dtype) == 2 && (reinterpret_cast<uintptr_t>(x) & 3) == 0 && d.C_in % 2 == 0 &&
+                    a.xs_n % 2 == 0 && a.xs_h % 2 == 0 && a.xs_w % 2 == 0;
+    hipError_t e;
+    switch (d.dtype) {
+    case CONV_F32: e = dwg_go<float, false>(a, grid, s); break;
+    case CONV_F16: e = wx ? dwg_go<f16_t, true>(a, grid, s) : dwg_go<f16_t, false>(a, grid, s); break;
+    default: e = wx ? dwg_go<bf16_t, true>(a, grid, s) : dwg_go<bf16_t, false>(a, grid, s); break;
+    }
+    return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
+}
+
 // Kernel sizes and strides with a compiled schedule (square kernels, equal strides).
 bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw)
 {
@@ -488,6 +673,7 @@ bool dwcl_has_schedule(int64_t kh, int64_t kw, int64_t sh, int64_t sw)
 
 int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream, bool vec)
 {
+    if (p.variant == DWCL_GENERIC) return launch_dwg(p, x, w, b, y, stream);
     const conv_desc &d = p.d;
     DwArgs a;
     a.x = x;

@@ -17,8 +17,9 @@
 //   transposed                                        -> IGEMM_T
 //   r <= 2, dil 1, k <= 9, groups > 1, Cig <= 8:
 //       few outputs (<= 4 positions, >= 32 taps each) -> REDUCE
-//       depthwise, multiplier 1, channel-contiguous,
-//       compiled (k, s) schedule                       -> DW_CL
+//       depthwise, channel-contiguous x and y          -> DW_CL
+//         (ring kernels for multiplier 1 and a compiled square (k, s);
+//          the generic schedule for any multiplier, shape and stride)
 //       grouped (Cig even), fp16/bf16                  -> GRP
 //       otherwise                                      -> PLANE
 //   everything else                                   -> IGEMM
@@ -92,7 +93,25 @@ int64_t span_bytes(const conv_tensor &t, int64_t es)
     return (off + 1) * es;
 }
 
-bool supports_dwcl(const conv_desc &d, const conv_tensor &y)
+// The generic channels-last depthwise schedule: any channel multiplier,
+// kernel shape (within the stencil domain), any row stride and column
+// strides 1..3, 1-D or 2-D, x and y
+// channel-contiguous; 16-bit outputs leave as words of two channels, so y's
+// position strides must keep channel pairs on 4-byte boundaries.
+bool dwcl_generic_ok(const conv_desc &d, const conv_tensor &y)
+{
+    if (!stencil_domain(d) || !all_dil1(d)) return false;
+    if (cig(d) != 1 || d.groups != d.C_in || d.C_out % d.C_in) return false;
+    if (d.stride[d.spatial - 1] > 3) return false;   // compiled column strides 1..3
+    if (d.x.strides[1] != 1 || y.strides[1] != 1) return false;
+    if (esize(d.dtype) == 2)
+        for (int i = 0; i < y.rank; ++i)
+            if (i != 1 && y.sizes[i] > 1 && y.strides[i] % 2) return false;
+    return true;
+}
+
+// The ring kernels: multiplier 1, a compiled square (k, s) schedule.
+bool dwcl_ring_ok(const conv_desc &d, const conv_tensor &y)
 {
     if (!stencil_domain(d) || d.spatial != 2 || !all_dil1(d)) return false;
     if (cig(d) != 1 || d.groups != d.C_in || d.C_out != d.C_in) return false;
@@ -106,6 +125,8 @@ bool supports_dwcl(const conv_desc &d, const conv_tensor &y)
     // 32-bit buffer offsets for loads and stores.
     return span_bytes(d.x, esize(d.dtype)) <= kI32 - 4096 && span_bytes(y, esize(d.dtype)) <= kI32 - 4096;
 }
+
+bool supports_dwcl(const conv_desc &d, const conv_tensor &y) { return dwcl_ring_ok(d, y) || dwcl_generic_ok(d, y); }
 
 bool supports_plane(const conv_desc &d) { return stencil_domain(d); }
 
@@ -140,8 +161,22 @@ int route(const conv_desc &d, const conv_tensor &y)
 
 // ---------------------------------------------------------------- geometry --
 
-void geom_dwcl(const conv_desc &d, conv_plan_t &p)
+void geom_dwcl(const conv_desc &d, conv_plan_t &p, bool generic)
 {
+    if (generic) {
+        // Lane = one word of output channels x DWG 8 output columns; a
+        // workgroup = 32 words x 8 column strips of one output row.
+        const int64_t v = esize(d.dtype) == 2 ? 2 : 1;
+        const int64_t OH = d.spatial == 2 ? d.out[0] : 1, OW = d.out[d.spatial - 1];
+        p.tile[DW_CHCHUNKS] = cdiv(cdiv(d.C_out, v), 32);
+        p.tile[DW_COLCHUNKS] = cdiv(OW, 64);
+        p.grid[0] = d.N * OH * p.tile[DW_COLCHUNKS] * p.tile[DW_CHCHUNKS];
+        p.block = 256;
+        p.variant = DWCL_GENERIC;
+        p.lds_bytes = 0;
+        p.vec_ok = 1;
+        return;
+    }
     const int k = (int)d.k[1], s = (int)d.stride[1];
     const int64_t es = esize(d.dtype);
     const int64_t words = d.C_in * es / 4;
@@ -420,7 +455,7 @@ extern "C" int conv_plan_ex(const conv_desc *d, const conv_tensor *y, const conv
     const int32_t force_kernel = o ? o->force_kernel : CONV_K_AUTO;
     const int32_t force_variant = o ? o->force_variant : -1;
     if (force_variant >= 0 && force_kernel != CONV_K_IGEMM && force_kernel != CONV_K_IGEMM_T &&
-        force_kernel != CONV_K_GRP)
+        force_kernel != CONV_K_GRP && force_kernel != CONV_K_DW_CL)
         return CONV_EINVAL;
     if (d->spatial < 1 || d->spatial > 3 || d->groups < 1 || d->x.rank != d->spatial + 2) return CONV_EINVAL;
     conv_tensor expect;
@@ -452,7 +487,13 @@ extern "C" int conv_plan_ex(const conv_desc *d, const conv_tensor *y, const conv
     }
     plan.kernel = k;
     switch (k) {
-    case CONV_K_DW_CL: geom_dwcl(*d, plan); break;
+    case CONV_K_DW_CL:
+        // The ring kernels where they apply; the generic schedule otherwise
+        // or when forced (the only selectable dw_cl schedule).
+        if (force_variant >= 0 && (force_variant != DWCL_GENERIC || !dwcl_generic_ok(*d, yb)))
+            return CONV_EUNSUPPORTED;
+        geom_dwcl(*d, plan, force_variant == DWCL_GENERIC || !dwcl_ring_ok(*d, yb));
+        break;
     case CONV_K_PLANE:
         if (!geom_plane(*d, plan)) {
             if (force_kernel != CONV_K_AUTO) return CONV_EUNSUPPORTED;

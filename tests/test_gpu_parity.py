@@ -654,6 +654,59 @@ def test_dw_cl_every_ring_kernel(wl):
     check_full(wl, force="dw_cl")
 
 
+def _dw_generic_cases():
+    """Channels-last depthwise calls for the generic dw_cl schedule: channel
+    multipliers 1-4, kernels of any shape up to 9x9, strides 1-3, asymmetric
+    padding, odd and even channel counts, every dtype, bias or not."""
+    rng = np.random.default_rng(77)
+    out = []
+    i = 0
+    while len(out) < 24:
+        kh, kw = int(rng.integers(1, 10)), int(rng.integers(1, 10))
+        sh, sw = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        C = int(rng.choice([3, 8, 13, 64, 70]))
+        m = int(rng.choice([1, 1, 2, 3, 4]))
+        dtype = ["f32", "f16", "bf16"][i % 3]
+        if dtype != "f32" and (C * m) % 2:
+            C += 1
+        H, W = int(rng.integers(kh, kh + 12)), int(rng.integers(kw, kw + 80))
+        pb = [int(rng.integers(0, kh)), int(rng.integers(0, kw))]
+        pa = [int(rng.integers(0, kh)), int(rng.integers(0, kw))]
+        out.append(synth.random_case(7500 + i, rank=2, transposed=False, dtype=dtype, channels_last=True,
+                                     N=int(rng.integers(1, 3)), C_in=C, C_out=C * m, groups=C, L=[H, W],
+                                     k=[kh, kw], stride=[sh, sw], padding_before=pb, padding_after=pa,
+                                     dilation=[1, 1], output_padding=[0, 0], has_bias=bool(i % 2)))
+        i += 1
+    return out
+
+
+@pytest.mark.parametrize("wl", _dw_generic_cases(), ids=lambda v: v.name)
+def test_dw_cl_generic_schedule(wl):
+    """Whole output of the generic channels-last depthwise schedule (plan
+    variant 2 of dw_cl, forced) against the reference."""
+    _flush(f"dw_cl generic: {_desc(wl)}")
+    check_full(wl, force="dw_cl", variant=2)
+
+
+def test_dw_cl_generic_schedule_exact_and_routed():
+    """A multiplier-2 call routes to the generic schedule by the rule, and
+    with wide integer inputs (outputs beyond 256, one rounding each) its
+    bf16 result equals the reference rounded once."""
+    import dataclasses
+    wl = synth.random_case(7590, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=16, C_out=32,
+                           groups=16, L=[12, 40], k=[5, 3], stride=[1, 2], padding_before=[2, 1],
+                           padding_after=[2, 1], dilation=[1, 1], output_padding=[0, 0], has_bias=True)
+    x, w, b = synth.make_inputs(wl)
+    kw = expand_kw(wl)
+    prep = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups))
+    assert api.kernel_name(prep.plan.kernel) == "dw_cl" and int(prep.plan.variant) == 2
+    wl = dataclasses.replace(wl, x_dist=("ints", -127, 127), w_dist=("ints", -31, 31), b_dist=("ints", -500, 500))
+    _flush(f"dw_cl generic exact: {_desc(wl)}")
+    y = check_full(wl, exact=True)
+    assert (y.abs().float() > 256).float().mean().item() > 0.2
+
+
 # ------------------------------------- every grouped matrix-core kernel --
 
 def _grp_mma_every_case():
