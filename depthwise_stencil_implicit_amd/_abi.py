@@ -53,7 +53,7 @@ class ConvPlan(ctypes.Structure):
     _fields_ = [("d", ConvDesc), ("y", ConvTensor),
                 ("kernel", _i32), ("variant", _i32), ("vec_ok", _i32), ("index64", _i32),
                 ("workspace_bytes", _i64), ("tile", _i64 * 8), ("grid", _i64 * 3),
-                ("block", _i32), ("lds_bytes", _i32), ("flags", _i32), ("reserved1", _i32), ("flops", _i64),
+                ("block", _i32), ("lds_bytes", _i32), ("flags", _i32), ("batch_chunk", _i32), ("flops", _i64),
                 ("bytes", _i64)]
 
 

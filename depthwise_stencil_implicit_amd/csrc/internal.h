@@ -132,6 +132,9 @@ int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void 
 int launch_igemm_t1(const conv_plan_t &p, const void *x, const void *wpacked, const void *b, void *y,
                     void *stream);
 int launch_plane(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream);
+// The plan of n images of a plan that runs its batch in chunks
+// (conv_plan_t.batch_chunk).
+int plan_batch_part(const conv_plan_t &whole, int64_t n, conv_plan_t *out);
 int launch_dwcl(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream,
                 bool vec);
 int launch_grp(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream);

@@ -463,6 +463,56 @@ extern "C" int conv_plan_ex(const conv_desc *d, const conv_tensor *y, const conv
     if (!same_layout(*y, expect)) return CONV_ELAYOUT;
     if (!sizes_fit_i32(*d)) return CONV_EUNSUPPORTED;
 
+    // A batch whose x or y spans 2 GiB or more runs in chunks of images (the
+    // kernels take 32-bit buffer offsets): the plan is a chunk's, with d and
+    // y left the whole call, and conv_run steps through the batch.  The
+    // workspace covers the last, smaller chunk as well.
+    {
+        conv_tensor yfull;
+        batched_out(*d, yfull);
+        const int64_t es = esize(d->dtype), lim = kI32 - 4096;
+        if ((span_bytes(d->x, es) > lim || span_bytes(yfull, es) > lim) && d->N > 1 && !d->unbatched) {
+            auto most = [&](const conv_tensor &t) -> int64_t {
+                conv_tensor one = t;
+                one.sizes[0] = 1;
+                const int64_t img = span_bytes(one, es), st = t.strides[0] * es;
+                if (st <= 0 || img > lim) return 0;
+                return (lim - img) / st + 1;
+            };
+            const int64_t nc = std::min<int64_t>(std::min(most(d->x), most(yfull)), d->N);
+            if (nc >= 1 && nc < d->N) {
+                conv_desc cd = *d;
+                conv_tensor cy = yfull;
+                cd.N = nc;
+                cd.x.sizes[0] = nc;
+                cy.sizes[0] = nc;
+                conv_plan_t cp;
+                int st = conv_plan_ex(&cd, &cy, o, &cp);
+                if (st != CONV_OK) return st;
+                int64_t ws = cp.workspace_bytes;
+                if (d->N % nc) {
+                    conv_plan_t whole = cp;
+                    whole.d = *d;
+                    whole.y = yfull;
+                    whole.batch_chunk = (int32_t)nc;
+                    conv_plan_t rp;
+                    st = plan_batch_part(whole, d->N % nc, &rp);
+                    if (st != CONV_OK) return st;
+                    ws = std::max(ws, rp.workspace_bytes);
+                }
+                cp.d = *d;
+                cp.y = yfull;
+                cp.batch_chunk = (int32_t)nc;
+                cp.workspace_bytes = ws;
+                cp.index64 = 1;
+                cp.flops = algorithmic_flops(*d);
+                cp.bytes = (numel(d->x) + numel(d->w) + (d->has_bias ? d->C_out : 0) + numel(yfull)) * es;
+                *p = cp;
+                return CONV_OK;
+            }
+        }
+    }
+
     conv_plan_t plan;
     std::memset(&plan, 0, sizeof(plan));
     plan.d = *d;
@@ -529,6 +579,37 @@ extern "C" int conv_plan_ex(const conv_desc *d, const conv_tensor *y, const conv
     *p = plan;
     return CONV_OK;
 }
+
+namespace miconv {
+
+// The plan of n images of a chunked plan's batch: its chunk plan when n is a
+// whole chunk, otherwise the same kernel planned for n images (the rule's
+// kernel if that one does not take them).
+int plan_batch_part(const conv_plan_t &whole, int64_t n, conv_plan_t *out)
+{
+    if (n == whole.batch_chunk) {
+        *out = whole;
+        out->d.N = n;
+        out->d.x.sizes[0] = n;
+        out->y.sizes[0] = n;
+        out->batch_chunk = 0;
+        return CONV_OK;
+    }
+    conv_desc d = whole.d;
+    conv_tensor y = whole.y;
+    d.N = n;
+    d.x.sizes[0] = n;
+    y.sizes[0] = n;
+    conv_plan_opts o;
+    std::memset(&o, 0, sizeof(o));
+    o.force_kernel = whole.kernel;
+    o.force_variant = -1;
+    if (conv_plan_ex(&d, &y, &o, out) == CONV_OK) return CONV_OK;
+    o.force_kernel = CONV_K_AUTO;
+    return conv_plan_ex(&d, &y, &o, out);
+}
+
+}  // namespace miconv
 
 extern "C" int conv_plan(const conv_desc *d, const conv_tensor *y, int32_t force_kernel, conv_plan_t *p)
 {

@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <mutex>
 
+#include <algorithm>
 #include <cstring>
 
 #include "internal.h"
@@ -52,6 +53,21 @@ extern "C" int conv_run(const conv_plan_t *p, const void *x, const void *w, cons
         if (!aligned(workspace, 16)) return CONV_EALIGN;
     }
     if (!have_device()) return CONV_EDEVICE;
+    if (p->batch_chunk > 0 && p->batch_chunk < d.N) {
+        // x or y spans 2 GiB or more: the batch in chunks of images, each a
+        // plain call on its own slices of x and y.
+        const int64_t xs = d.x.strides[0] * (int64_t)es, ys = p->y.strides[0] * (int64_t)es;
+        for (int64_t n0 = 0; n0 < d.N; n0 += p->batch_chunk) {
+            conv_plan_t sub;
+            int st = plan_batch_part(*p, std::min<int64_t>(p->batch_chunk, d.N - n0), &sub);
+            if (st != CONV_OK) return st;
+            if (sub.workspace_bytes > p->workspace_bytes) return CONV_EINVAL;
+            st = conv_run(&sub, static_cast<const char *>(x) + n0 * xs, w, b, static_cast<char *>(y) + n0 * ys,
+                          workspace, workspace_bytes, stream);
+            if (st != CONV_OK) return st;
+        }
+        return CONV_OK;
+    }
     const bool vec = p->vec_ok && aligned(x, 16) && aligned(y, 16);
     switch (p->kernel) {
     case CONV_K_DW_CL:
@@ -133,4 +149,4 @@ extern "C" const char *conv_status_string(int32_t status)
     }
 }
 
-extern "C" int32_t conv_abi_version(void) { return 2; }
+extern "C" int32_t conv_abi_version(void) { return 3; }

@@ -156,7 +156,10 @@ typedef struct conv_plan_t {
     int32_t block;
     int32_t lds_bytes;
     int32_t flags;                    /* CONV_PLAN_* bits */
-    int32_t reserved1;
+    int32_t batch_chunk;              /* 0: one launch covers the batch; else images per launch (x or y
+                                         spans 2 GiB or more: the kernels take 32-bit buffer offsets, so
+                                         conv_run runs the batch in chunks; d and y stay the whole call,
+                                         tile / grid / variant are those of a chunk) */
     int64_t flops;                    /* algorithmic FLOPs of the call */
     int64_t bytes;                    /* algorithmic bytes: x + w + b read once, y written once */
 } conv_plan_t;

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_names():
     lib = A.lib()
-    assert lib.conv_abi_version() == 2
+    assert lib.conv_abi_version() == 3
     for name, val in A.KERNELS.items():
         assert lib.conv_kernel_name(val).decode() == name
     assert lib.conv_kernel_name(99).decode() == "?"

@@ -476,3 +476,24 @@ def test_untuned_call_plans_by_the_rule():
     p, _ = _cands(synth.dense_bf16_cl())
     t = api.conv_plan_tuned(p.desc, api.tensor_desc(p.sizes, p.strides, torch.bfloat16))
     assert not (t.flags & A.PLAN_TUNED) and bytes(t) == bytes(p.plan)
+
+
+def test_batch_spanning_2gib_runs_in_chunks():
+    """x (or y) spanning 2 GiB or more: the kernels take 32-bit buffer
+    offsets, so the plan covers a chunk of images whose spans stay below
+    2 GiB; d and y stay the whole call (FLOPs and bytes of the whole call),
+    and the workspace also covers the last, smaller chunk."""
+    N, C, H = 600, 32, 256
+    x = torch.empty_strided((N, C, H, H), (C * H * H, 1, H * C, C), dtype=torch.bfloat16)   # NHWC, not touched
+    w = T((C, C, 3, 3))
+    p = prep(x, w, padding_before=1, padding_after=1)
+    nc = int(p.plan.batch_chunk)
+    assert 0 < nc < N and N % nc
+    assert int(p.plan.d.N) == N and int(p.plan.y.sizes[0]) == N and tuple(p.sizes)[0] == N
+    img = C * H * H * 2
+    assert nc * img <= (1 << 31) - 4096 < (nc + 1) * img
+    assert api.kernel_name(p.plan.kernel) == "igemm"
+    assert int(p.plan.flops) == 2 * N * H * H * C * C * 9
+    # A batch that fits is one launch.
+    small = torch.empty_strided((8, C, H, H), (C * H * H, 1, H * C, C), dtype=torch.bfloat16)
+    assert int(prep(small, w, padding_before=1, padding_after=1).plan.batch_chunk) == 0

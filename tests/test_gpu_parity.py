@@ -908,3 +908,41 @@ def test_one_by_one_plain_gemm(wl):
     torch.cuda.synchronize()
     yr, A = oracle.conv(*ref_inputs(x, w, b))
     assert_close(ym, yr, A, EPS[wl.dtype], "1x1 misaligned x")
+
+
+# ------------------------------------------- batches spanning 2 GiB --
+
+@pytest.mark.parametrize("kind", ["dense", "depthwise"])
+def test_batch_spanning_2gib(kind):
+    """x and y of more than 2 GiB (bf16, channels-last): the plan runs the
+    batch in chunks of images, each below the kernels' 32-bit buffer range.
+    Whole images on both sides of the first chunk boundary and the last
+    (smaller) chunk against the reference; the other images' outputs are
+    finite (every chunk ran)."""
+    g = torch.Generator(device="cuda").manual_seed(11)
+    if kind == "dense":
+        N, C, H, k = 600, 32, 256, 3
+        w = (torch.randn((C, C, k, k), device="cuda", generator=g) / (C * k * k) ** 0.5).to(torch.bfloat16)
+        groups = 1
+    else:
+        N, C, H, k = 400, 256, 112, 3
+        w = (torch.randn((C, 1, k, k), device="cuda", generator=g) / k).to(torch.bfloat16)
+        groups = C
+    x = torch.empty_strided((N, C, H, H), (C * H * H, 1, H * C, C), dtype=torch.bfloat16, device="cuda")
+    x.copy_(torch.randn((N, C, H, H), device="cuda", generator=g).to(torch.bfloat16))
+    b = (0.1 * torch.randn((C,), device="cuda", generator=g)).to(torch.bfloat16)
+    kw = dict(stride=(1, 1), padding_before=(1, 1), padding_after=(1, 1), dilation=(1, 1), groups=groups)
+    prep = api.Prepared(x, w, b, api.make_args(**kw))
+    nc = int(prep.plan.batch_chunk)
+    _flush(f"2 GiB batch {kind}: N={N} chunk={nc} kernel={api.kernel_name(prep.plan.kernel)}")
+    assert 0 < nc < N and N % nc
+    y = prep.run(x, w, b, prep.empty_output(x.device), prep.workspace(x.device))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y.float().sum(dim=(1, 2, 3))).all())
+    last = N - N % nc
+    for n in sorted({0, nc - 1, nc, last - 1, last, N - 1}):
+        xr, wr, br = ref_inputs(x[n:n + 1], w, b)
+        yr, A = oracle.conv(xr, wr, br, **kw)
+        assert_close(y[n:n + 1], yr, A, EPS["bf16"], f"{kind} image {n}")
+    del x, y
+    torch.cuda.empty_cache()
