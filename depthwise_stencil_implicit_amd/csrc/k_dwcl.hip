@@ -601,6 +601,98 @@ __global__ __launch_bounds__(256) void dwg_kernel(DwgArgs a)
     }
 }
 
+// The multiplier schedule (16-bit, m = MO in {2, 4}): lane = one word of
+// INPUT channels (c0, c0 + 1) x TO output columns; it computes all 2 MO
+// output channels c0*m .. c0*m + 2m - 1 of its two input channels from one
+// word load per window column (the multiplier fan-out), and stores them as
+// one 8- or 16-byte run per output column.
+template <typename T, int MO, int KB, int S>
+__global__ __launch_bounds__(256) void dwm_kernel(DwgArgs a)
+{
+    constexpr int TO = DWG_TO;
+    constexpr int NX = (TO - 1) * S + KB;
+    constexpr int NO = 2 * MO;                   // output channels per lane
+    const int tid = threadIdx.x, cl = tid & 31, st = tid >> 5;
+    int b = blockIdx.x;
+    const int chb = b % a.ch_blocks;
+    b /= a.ch_blocks;
+    const int cb = b % a.col_blocks;
+    b /= a.col_blocks;
+    const int oh = b % a.OH;
+    const int n = b / a.OH;
+    const int Cin = a.Cout / MO;
+    const int c0 = (chb * 32 + cl) * 2;          // first input channel of the lane
+    const int ow0 = (cb * 8 + st) * TO;
+    if (c0 >= Cin || ow0 >= a.OW) return;        // no barriers below
+    const int co0 = c0 * MO;
+    const bool two = c0 + 1 < Cin;               // both input channels present
+
+    const T *__restrict__ Bp = static_cast<const T *>(a.b);
+    float acc[TO][NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+        const float bv = (a.has_bias && (o < MO || two)) ? to_f32(Bp[co0 + o]) : 0.f;
+#pragma unroll
+        for (int t = 0; t < TO; ++t) acc[t][o] = bv;
+    }
+    const T *__restrict__ X = static_cast<const T *>(a.x) + (int64_t)n * a.xs_n;
+    const T *__restrict__ Wt = static_cast<const T *>(a.w);
+    const int iw0 = ow0 * S - a.PW;
+    const int nx = (min(TO, a.OW - ow0) - 1) * S + a.KW;
+    for (int kh = 0; kh < a.KH; ++kh) {
+        const int ih = oh * a.SH - a.PH + kh;
+        if ((unsigned)ih >= (unsigned)a.H) continue;
+        const T *__restrict__ Xr = X + (int64_t)ih * a.xs_h;
+        float wv[KB][NO];
+#pragma unroll
+        for (int kw = 0; kw < KB; ++kw)
+#pragma unroll
+            for (int o = 0; o < NO; ++o)
+                wv[kw][o] = (kw < a.KW && (o < MO || two))
+                                ? to_f32(Wt[(int64_t)(co0 + o) * a.ws0 + kh * a.ws2 + kw * a.ws3])
+                                : 0.f;
+        float xw[NX][2];
+#pragma unroll
+        for (int j = 0; j < NX; ++j) {
+            const int iw = iw0 + j;
+            const bool ok = j < nx && (unsigned)iw < (unsigned)a.W;
+            const uint32_t u = ok ? *reinterpret_cast<const uint32_t *>(Xr + (int64_t)iw * a.xs_w + c0) : 0u;
+            T lo, hi;
+            lo.u = (uint16_t)u;
+            hi.u = (uint16_t)(u >> 16);
+            xw[j][0] = to_f32(lo);
+            xw[j][1] = to_f32(hi);
+        }
+#pragma unroll
+        for (int t = 0; t < TO; ++t)
+#pragma unroll
+            for (int kw = 0; kw < KB; ++kw)
+#pragma unroll
+                for (int o = 0; o < NO; ++o)
+                    acc[t][o] = __builtin_fmaf(xw[t * S + kw][o / MO], wv[kw][o], acc[t][o]);
+    }
+    T *__restrict__ Y = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h + co0;
+#pragma unroll
+    for (int t = 0; t < TO; ++t) {
+        const int ow = ow0 + t;
+        if (ow >= a.OW) break;
+        T *py = Y + (int64_t)ow * a.ys_w;
+        uint32_t wd[MO];
+#pragma unroll
+        for (int q = 0; q < MO; ++q) wd[q] = pack2<T>(acc[t][2 * q], acc[t][2 * q + 1]);
+        if (two) {
+            if constexpr (MO == 2) {
+                *reinterpret_cast<uint2 *>(py) = uint2{wd[0], wd[1]};
+            } else {
+                *reinterpret_cast<uint4 *>(py) = uint4{wd[0], wd[1], wd[2], wd[3]};
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < MO / 2; ++q) reinterpret_cast<uint32_t *>(py)[q] = wd[q];
+        }
+    }
+}
+
 namespace {
 
 template <typename T, bool WX>
@@ -656,6 +748,35 @@ int launch_dwg(const conv_plan_t &p, const void *x, const void *w, const void *b
     // boundaries of x.
     const bool wx = a.M == 1 && esize(d.dtype) == 2 && (reinterpret_cast<uintptr_t>(x) & 3) == 0 && d.C_in % 2 == 0 &&
                     a.xs_n % 2 == 0 && a.xs_h % 2 == 0 && a.xs_w % 2 == 0;
+    // The multiplier schedule: 16-bit, m = 2 or 4, input channel pairs on
+    // 4-byte boundaries of x and output runs of 2m channels on 4m-byte
+    // boundaries of y.
+    const int64_t ysa = 2 * a.M;
+    const bool mult = esize(d.dtype) == 2 && (a.M == 2 || a.M == 4) && d.C_in % 2 == 0 &&
+                      (reinterpret_cast<uintptr_t>(x) & 3) == 0 && a.xs_n % 2 == 0 && a.xs_h % 2 == 0 &&
+                      a.xs_w % 2 == 0 && (reinterpret_cast<uintptr_t>(y) & (4 * a.M - 1)) == 0 && a.ys_n % ysa == 0 &&
+                      a.ys_h % ysa == 0 && a.ys_w % ysa == 0;
+    if (mult) {
+        DwgArgs m = a;
+        m.ch_blocks = (int32_t)cdiv(d.C_in / 2, 32);
+        const dim3 mgrid((unsigned)(d.N * (int64_t)a.OH * a.col_blocks * m.ch_blocks));
+        const int kb = a.KW <= 3 ? 3 : (a.KW <= 5 ? 5 : 9);
+        hipError_t e = hipErrorInvalidValue;
+#define MICONV_DWM(MO_, KB_, S_)                                                                     \
+    if (a.M == MO_ && kb == KB_ && a.SW == S_) {                                                      \
+        if (d.dtype == CONV_F16)                                                                      \
+            hipLaunchKernelGGL((dwm_kernel<f16_t, MO_, KB_, S_>), mgrid, dim3(256), 0, s, m);         \
+        else                                                                                          \
+            hipLaunchKernelGGL((dwm_kernel<bf16_t, MO_, KB_, S_>), mgrid, dim3(256), 0, s, m);        \
+        e = hipGetLastError();                                                                        \
+    }
+        MICONV_DWM(2, 3, 1) MICONV_DWM(2, 5, 1) MICONV_DWM(2, 9, 1) MICONV_DWM(2, 3, 2) MICONV_DWM(2, 5, 2)
+        MICONV_DWM(2, 9, 2) MICONV_DWM(2, 3, 3) MICONV_DWM(2, 5, 3) MICONV_DWM(2, 9, 3)
+        MICONV_DWM(4, 3, 1) MICONV_DWM(4, 5, 1) MICONV_DWM(4, 9, 1) MICONV_DWM(4, 3, 2) MICONV_DWM(4, 5, 2)
+        MICONV_DWM(4, 9, 2) MICONV_DWM(4, 3, 3) MICONV_DWM(4, 5, 3) MICONV_DWM(4, 9, 3)
+#undef MICONV_DWM
+        return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
+    }
     hipError_t e;
     switch (d.dtype) {
     case CONV_F32: e = dwg_go<float, false>(a, grid, s); break;

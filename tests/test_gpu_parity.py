@@ -688,6 +688,34 @@ def test_dw_cl_generic_schedule(wl):
     check_full(wl, force="dw_cl", variant=2)
 
 
+def _dw_mult_cases():
+    """Multiplier 2 and 4 with even channel counts (the multiplier fan-out:
+    one word load feeds 2m output channels), 16-bit, every compiled kernel
+    width class (3 / 5 / 9) and column stride 1-3, ragged columns."""
+    out = []
+    i = 0
+    for m in (2, 4):
+        for kw, s in ((3, 1), (5, 2), (9, 3), (2, 1), (7, 2), (4, 3)):
+            dtype = ("f16", "bf16")[i % 2]
+            C = (16, 70)[i % 2]
+            kh = (3, 1, 5)[i % 3]
+            out.append(synth.random_case(7600 + i, rank=2, transposed=False, dtype=dtype, channels_last=True,
+                                         N=2, C_in=C, C_out=C * m, groups=C, L=[kh + 6, 9 * s + kw + 13],
+                                         k=[kh, kw], stride=[1 + i % 2, s], padding_before=[kh // 2, kw // 2],
+                                         padding_after=[kh // 2, (kw - 1) // 2], dilation=[1, 1],
+                                         output_padding=[0, 0], has_bias=bool(i % 2)))
+            i += 1
+    return out
+
+
+@pytest.mark.parametrize("wl", _dw_mult_cases(), ids=lambda v: v.name)
+def test_dw_cl_multiplier_fanout(wl):
+    """Whole output of the generic schedule's multiplier fan-out kernels
+    against the reference (the rule routes these calls to dw_cl variant 2)."""
+    _flush(f"dw_cl multiplier: {_desc(wl)}")
+    check_full(wl, force="dw_cl", variant=2)
+
+
 def test_dw_cl_generic_schedule_exact_and_routed():
     """A multiplier-2 call routes to the generic schedule by the rule, and
     with wide integer inputs (outputs beyond 256, one rounding each) its
