@@ -498,7 +498,8 @@ struct DwgArgs {
     const void *x, *w, *b;
     void *y;
     int64_t xs_n, xs_h, xs_w;     // element strides of x (channel stride 1)
-    int64_t ys_n, ys_h, ys_w;     // element strides of y (channel stride 1)
+    int64_t ys_n, ys_h, ys_w;     // element strides of y
+    int64_t ys_c;                 // channel stride of y: 1, or positions contiguous (ys_w == 1)
     int64_t ws0, ws2, ws3;        // weight strides (output channel, kh, kw)
     int32_t H, W, M, Cout, OH, OW, KH, KW, SH, SW, PH, PW;
     int32_t col_blocks, ch_blocks, has_bias;
@@ -583,7 +584,39 @@ __global__ __launch_bounds__(256) void dwg_kernel(DwgArgs a)
 #pragma unroll
                 for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xw[t * S + kw][v], wv[kw][v], acc[t][v]);
     }
-    T *__restrict__ Y = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h + co0;
+    T *__restrict__ Yb = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h;
+    if (a.ys_c != 1) {
+        // Positions contiguous in y (the channel-major output of a 1-D call on
+        // a channels-last input): each output channel's TO results are one
+        // run, stored as 16-byte vectors where the run is whole and aligned,
+        // else element by element.
+        constexpr int NW32 = TO * (int)sizeof(T) / 4;   // 32-bit words of a run
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            if (v >= nv) break;
+            T *py = Yb + (int64_t)(co0 + v) * a.ys_c + ow0;
+            if (ow0 + TO <= a.OW && (reinterpret_cast<uintptr_t>(py) & 15) == 0) {
+                uint32_t wd[NW32];
+#pragma unroll
+                for (int q = 0; q < NW32; ++q) {
+                    if constexpr (sizeof(T) == 2)
+                        wd[q] = pack2<T>(acc[2 * q][v], acc[2 * q + 1][v]);
+                    else
+                        wd[q] = __float_as_uint(acc[q][v]);
+                }
+#pragma unroll
+                for (int q = 0; q < NW32; q += 4)
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<uint32_t *>(py) + q) =
+                        uint4{wd[q], wd[q + 1], wd[q + 2], wd[q + 3]};
+            } else {
+#pragma unroll
+                for (int t = 0; t < TO; ++t)
+                    if (ow0 + t < a.OW) py[t] = from_f32<T>(acc[t][v]);
+            }
+        }
+        return;
+    }
+    T *__restrict__ Y = Yb + co0;
 #pragma unroll
     for (int t = 0; t < TO; ++t) {
         const int ow = ow0 + t;
@@ -724,6 +757,7 @@ int launch_dwg(const conv_plan_t &p, const void *x, const void *w, const void *b
     a.ys_n = p.y.strides[0];
     a.ys_h = two ? p.y.strides[2] : 0;
     a.ys_w = p.y.strides[two ? 3 : 2];
+    a.ys_c = p.y.strides[1];
     a.ws0 = d.w.strides[0];
     a.ws2 = two ? d.w.strides[2] : 0;
     a.ws3 = d.w.strides[two ? 3 : 2];
@@ -752,7 +786,7 @@ int launch_dwg(const conv_plan_t &p, const void *x, const void *w, const void *b
     // 4-byte boundaries of x and output runs of 2m channels on 4m-byte
     // boundaries of y.
     const int64_t ysa = 2 * a.M;
-    const bool mult = esize(d.dtype) == 2 && (a.M == 2 || a.M == 4) && d.C_in % 2 == 0 &&
+    const bool mult = a.ys_c == 1 && esize(d.dtype) == 2 && (a.M == 2 || a.M == 4) && d.C_in % 2 == 0 &&
                       (reinterpret_cast<uintptr_t>(x) & 3) == 0 && a.xs_n % 2 == 0 && a.xs_h % 2 == 0 &&
                       a.xs_w % 2 == 0 && (reinterpret_cast<uintptr_t>(y) & (4 * a.M - 1)) == 0 && a.ys_n % ysa == 0 &&
                       a.ys_h % ysa == 0 && a.ys_w % ysa == 0;

@@ -103,11 +103,16 @@ bool dwcl_generic_ok(const conv_desc &d, const conv_tensor &y)
     if (!stencil_domain(d) || !all_dil1(d)) return false;
     if (cig(d) != 1 || d.groups != d.C_in || d.C_out % d.C_in) return false;
     if (d.stride[d.spatial - 1] > 3) return false;   // compiled column strides 1..3
-    if (d.x.strides[1] != 1 || y.strides[1] != 1) return false;
-    if (esize(d.dtype) == 2)
-        for (int i = 0; i < y.rank; ++i)
-            if (i != 1 && y.sizes[i] > 1 && y.strides[i] % 2) return false;
-    return true;
+    if (d.x.strides[1] != 1) return false;
+    // y channels-last (channel words), or with its positions contiguous (the
+    // channel-major output ATen gives a 1-D call on a channels-last input).
+    if (y.strides[1] == 1) {
+        if (esize(d.dtype) == 2)
+            for (int i = 0; i < y.rank; ++i)
+                if (i != 1 && y.sizes[i] > 1 && y.strides[i] % 2) return false;
+        return true;
+    }
+    return y.strides[y.rank - 1] == 1;
 }
 
 // The ring kernels: multiplier 1, a compiled square (k, s) schedule.

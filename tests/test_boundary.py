@@ -497,3 +497,14 @@ def test_batch_spanning_2gib_runs_in_chunks():
     # A batch that fits is one launch.
     small = torch.empty_strided((8, C, H, H), (C * H * H, 1, H * C, C), dtype=torch.bfloat16)
     assert int(prep(small, w, padding_before=1, padding_after=1).plan.batch_chunk) == 0
+
+
+def test_dw1d_channels_last_input_routes_to_generic_dw_cl():
+    """A 1-D depthwise call on an NLC input has a channel-major (NCL) output by
+    the layout rule; the planner sends it to the generic channels-last
+    schedule, which writes runs of positions per channel."""
+    wl = next(w for w in synth.domain_edge_workloads() if w.name.startswith("edge_dw1d"))
+    x, w, b = wl_tensors(wl)
+    p = prep(x, w, b, **wl_args(wl))
+    assert p.strides[2] == 1 and p.strides[1] == p.sizes[2]
+    assert api.kernel_name(p.plan.kernel) == "dw_cl" and int(p.plan.variant) == 2

@@ -1,7 +1,9 @@
 """GPU parity: the library's kernels against the double-precision reference.
 
-Every comparison is element by element, |y_gpu - y| <= eps * A with
-A = sum|x*w| + |b| (eps = 1e-6 fp32, 2^-11 fp16, 2^-8 bf16); integer-valued
+Every comparison is element by element, |y_gpu - y| <= eps * A + tiny with
+A = sum|x*w| + |b| (eps = 1e-6 fp32, 2^-11 fp16, 2^-8 bf16; tiny = half the
+output dtype's subnormal spacing, the most one rounding can move a result
+below the smallest normal number); integer-valued
 and all-ones inputs must match exactly.  Output shapes and strides must equal
 the reference's layout rule exactly.
 """
@@ -12,7 +14,7 @@ import torch
 import oracle
 from depthwise_stencil_implicit_amd import _abi, api, synth
 
-from gpu_util import EPS, assert_close, check_full, check_points, expand_kw, ref_inputs, run_gpu
+from gpu_util import EPS, TINY, assert_close, check_full, check_points, expand_kw, ref_inputs, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -500,7 +502,7 @@ def test_tail_rows_split_k(transposed):
         pts[: n // 2, 2] = shape[2] - 1 - rng.integers(0, 9000, n // 2)
     yr, A = oracle.conv_points(xr, wr, br, pts, **expand_kw(wl))
     yg = y.detach()[tuple(torch.as_tensor(pts.T, device=y.device))].double().cpu().numpy()
-    bad = ~(np.abs(yg - yr) <= EPS[wl.dtype] * A)
+    bad = ~(np.abs(yg - yr) <= EPS[wl.dtype] * A + TINY[y.dtype])
     assert not bad.any(), f"{int(bad.sum())} outputs outside the bound, e.g. {pts[bad][:3].tolist()}"
 
 
@@ -714,6 +716,40 @@ def test_dw_cl_multiplier_fanout(wl):
     against the reference (the rule routes these calls to dw_cl variant 2)."""
     _flush(f"dw_cl multiplier: {_desc(wl)}")
     check_full(wl, force="dw_cl", variant=2)
+
+
+def _dw1d_ncl_cases():
+    """1-D depthwise calls on a channels-last (NLC) input, whose output is
+    channel-major (NCL): multipliers 1-4, kernels 1-9, strides 1-3,
+    asymmetric padding, output lengths that are and are not multiples of the
+    8-output runs (so runs start on and off 16-byte boundaries), every dtype."""
+    rng = np.random.default_rng(79)
+    out = []
+    for i in range(12):
+        k = int(rng.integers(1, 10))
+        s = int(rng.integers(1, 4))
+        C = int(rng.choice([2, 8, 13, 64, 70]))
+        m = int(rng.choice([1, 1, 2, 4]))
+        dtype = ["f32", "f16", "bf16"][i % 3]
+        if dtype != "f32" and (C * m) % 2:
+            C += 1
+        L = int(rng.integers(k, k + 300))
+        pb, pa = int(rng.integers(0, k)), int(rng.integers(0, k))
+        out.append(synth.random_case(7650 + i, rank=1, transposed=False, dtype=dtype, channels_last=True,
+                                     N=int(rng.integers(1, 3)), C_in=C, C_out=C * m, groups=C, L=[L], k=[k],
+                                     stride=[s], padding_before=[pb], padding_after=[pa], dilation=[1],
+                                     output_padding=[0], has_bias=bool(i % 2)))
+    return out
+
+
+@pytest.mark.parametrize("wl", _dw1d_ncl_cases(), ids=lambda v: v.name)
+def test_dw_cl_generic_1d_channel_major_output(wl):
+    """Whole output of the generic channels-last schedule writing the NCL
+    output of a 1-D call (per output channel, runs of 8 positions) against
+    the reference, with the output strides the layout rule gives."""
+    _flush(f"dw_cl generic, 1-D NCL output: {_desc(wl)}")
+    y = check_full(wl, force="dw_cl", variant=2)
+    assert y.stride(2) == 1 and y.stride(1) == y.shape[2]
 
 
 def test_dw_cl_generic_schedule_exact_and_routed():
