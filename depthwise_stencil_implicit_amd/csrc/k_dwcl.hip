@@ -503,6 +503,7 @@ struct DwgArgs {
     int64_t ws0, ws2, ws3;        // weight strides (output channel, kh, kw)
     int32_t H, W, M, Cout, OH, OW, KH, KW, SH, SW, PH, PW;
     int32_t col_blocks, ch_blocks, has_bias;
+    int32_t x_bytes, w_bytes;     // buffer ranges: x from the image's start, the weights
 };
 
 constexpr int DWG_TO = 8;         // output columns per lane
@@ -543,46 +544,104 @@ __global__ __launch_bounds__(256) void dwg_kernel(DwgArgs a)
 #pragma unroll
         for (int t = 0; t < TO; ++t) acc[t][v] = bv;
     }
-    const T *__restrict__ X = static_cast<const T *>(a.x) + (int64_t)n * a.xs_n;
-    const T *__restrict__ Wt = static_cast<const T *>(a.w);
+    constexpr int ES = (int)sizeof(T);
+    constexpr int INVALID = 0x7fffff00;
     const int iw0 = ow0 * S - a.PW;
     const int nx = (min(TO, a.OW - ow0) - 1) * S + a.KW;   // window columns any output uses
-    for (int kh = 0; kh < a.KH; ++kh) {
-        const int ih = oh * a.SH - a.PH + kh;
-        if ((unsigned)ih >= (unsigned)a.H) continue;   // uniform over the workgroup
-        const T *__restrict__ Xr = X + (int64_t)ih * a.xs_h;
-        float wv[KB][V];
+    const int ih0 = oh * a.SH - a.PH;
+    // Buffer loads from this image of x and from the weights: per-lane byte
+    // offsets of the window columns and the weight taps are the same for
+    // every kernel row (absent columns get an offset the buffer range
+    // drops, which reads zero); the row rides in the scalar offset.
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(static_cast<const T *>(a.x) + (int64_t)n * a.xs_n), (short)0, a.x_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.w), (short)0, a.w_bytes, 0x00020000);
+    int xo[NX][V], wb[V];
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+        const int iw = iw0 + j;
+        const bool ok = j < nx && (unsigned)iw < (unsigned)a.W;
+        xo[j][0] = ok ? (iw * (int)a.xs_w + (WX ? co0 : ci[0])) * ES : INVALID;
+        if constexpr (V == 2) xo[j][1] = ok ? (iw * (int)a.xs_w + ci[1]) * ES : INVALID;
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) wb[v] = v < nv ? (co0 + v) * (int)a.ws0 * ES : INVALID;
+    // Kernel rows are software-pipelined: the next row's window and weights
+    // are loaded (as raw bits, converted only when used) while the current
+    // row is multiplied, so each row does not wait out a load latency of its
+    // own.  Rows outside the input load nothing and multiply nothing.
+    auto val = [](uint32_t u) -> float {
+        if constexpr (sizeof(T) == 2) {
+            T t;
+            t.u = (uint16_t)u;
+            return to_f32(t);
+        } else {
+            return __uint_as_float(u);
+        }
+    };
+    auto ld = [](__amdgpu_buffer_rsrc_t r, int voff, int soff) -> uint32_t {
+        if constexpr (sizeof(T) == 2) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        else return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    };
+    auto fetch = [&](int kh, uint32_t (&px)[NX][V], uint32_t (&pw)[KB][V]) {
+        const int ih = ih0 + kh;
+        if ((unsigned)ih >= (unsigned)a.H) return;   // uniform over the workgroup
+        const int xs = ih * (int)a.xs_h * ES, ws = kh * (int)a.ws2 * ES;
 #pragma unroll
         for (int kw = 0; kw < KB; ++kw)
 #pragma unroll
-            for (int v = 0; v < V; ++v)
-                wv[kw][v] = (kw < a.KW && v < nv) ? to_f32(Wt[(int64_t)(co0 + v) * a.ws0 + kh * a.ws2 + kw * a.ws3])
-                                                  : 0.f;
-        float xw[NX][V];
+            for (int v = 0; v < V; ++v) pw[kw][v] = kw < a.KW ? ld(wr, wb[v], ws + kw * (int)a.ws3 * ES) : 0u;
 #pragma unroll
         for (int j = 0; j < NX; ++j) {
-            const int iw = iw0 + j;
-            const bool ok = j < nx && (unsigned)iw < (unsigned)a.W;
-            const T *px = Xr + (int64_t)(ok ? iw : 0) * a.xs_w;
             if constexpr (WX) {
                 // m = 1, 16-bit: the word of input channels co0, co0 + 1.
-                const uint32_t u = ok ? *reinterpret_cast<const uint32_t *>(px + co0) : 0u;
-                T lo, hi;
-                lo.u = (uint16_t)u;
-                hi.u = (uint16_t)(u >> 16);
-                xw[j][0] = to_f32(lo);
-                xw[j][V - 1] = to_f32(hi);
+                px[j][0] = __builtin_amdgcn_raw_buffer_load_b32(xr, xo[j][0], xs, 0);
             } else {
-                xw[j][0] = ok ? to_f32(px[ci[0]]) : 0.f;
-                if constexpr (V == 2) xw[j][1] = same ? xw[j][0] : (ok ? to_f32(px[ci[1]]) : 0.f);
+                px[j][0] = ld(xr, xo[j][0], xs);
+                if constexpr (V == 2) px[j][1] = same ? px[j][0] : ld(xr, xo[j][1], xs);
             }
         }
-#pragma unroll
-        for (int t = 0; t < TO; ++t)
+    };
+    uint32_t rx[NX][V], rw[KB][V];
+    fetch(0, rx, rw);
+    for (int kh = 0; kh < a.KH; ++kh) {
+        uint32_t qx[NX][V], qw[KB][V];
+        const bool more = kh + 1 < a.KH;
+        if (more) fetch(kh + 1, qx, qw);
+        if ((unsigned)(ih0 + kh) < (unsigned)a.H) {
+            float wv[KB][V], xw[NX][V];
 #pragma unroll
             for (int kw = 0; kw < KB; ++kw)
 #pragma unroll
-                for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xw[t * S + kw][v], wv[kw][v], acc[t][v]);
+                for (int v = 0; v < V; ++v) wv[kw][v] = val(rw[kw][v]);
+#pragma unroll
+            for (int j = 0; j < NX; ++j) {
+                if constexpr (WX) {
+                    xw[j][0] = val(rx[j][0] & 0xffffu);
+                    xw[j][V - 1] = val(rx[j][0] >> 16);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) xw[j][v] = val(rx[j][v]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TO; ++t)
+#pragma unroll
+                for (int kw = 0; kw < KB; ++kw)
+#pragma unroll
+                    for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xw[t * S + kw][v], wv[kw][v], acc[t][v]);
+        }
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < NX; ++j)
+#pragma unroll
+                for (int v = 0; v < V; ++v) rx[j][v] = qx[j][v];
+#pragma unroll
+            for (int kw = 0; kw < KB; ++kw)
+#pragma unroll
+                for (int v = 0; v < V; ++v) rw[kw][v] = qw[kw][v];
+        }
     }
     T *__restrict__ Yb = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h;
     if (a.ys_c != 1) {
@@ -668,41 +727,76 @@ __global__ __launch_bounds__(256) void dwm_kernel(DwgArgs a)
 #pragma unroll
         for (int t = 0; t < TO; ++t) acc[t][o] = bv;
     }
-    const T *__restrict__ X = static_cast<const T *>(a.x) + (int64_t)n * a.xs_n;
-    const T *__restrict__ Wt = static_cast<const T *>(a.w);
+    constexpr int INVALID = 0x7fffff00;
     const int iw0 = ow0 * S - a.PW;
     const int nx = (min(TO, a.OW - ow0) - 1) * S + a.KW;
-    for (int kh = 0; kh < a.KH; ++kh) {
-        const int ih = oh * a.SH - a.PH + kh;
-        if ((unsigned)ih >= (unsigned)a.H) continue;
-        const T *__restrict__ Xr = X + (int64_t)ih * a.xs_h;
-        float wv[KB][NO];
+    const int ih0 = oh * a.SH - a.PH;
+    // Buffer loads with per-lane offsets fixed over the kernel rows and the
+    // next row's words and weights in flight while the current row is
+    // multiplied (as in the generic kernel above).
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(static_cast<const T *>(a.x) + (int64_t)n * a.xs_n), (short)0, a.x_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.w), (short)0, a.w_bytes, 0x00020000);
+    int xo[NX], wb[NO];
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+        const int iw = iw0 + j;
+        xo[j] = (j < nx && (unsigned)iw < (unsigned)a.W) ? (iw * (int)a.xs_w + c0) * 2 : INVALID;
+    }
+#pragma unroll
+    for (int o = 0; o < NO; ++o) wb[o] = (o < MO || two) ? (co0 + o) * (int)a.ws0 * 2 : INVALID;
+    auto fetch = [&](int kh, uint32_t (&px)[NX], uint32_t (&pw)[KB][NO]) {
+        const int ih = ih0 + kh;
+        if ((unsigned)ih >= (unsigned)a.H) return;   // uniform over the workgroup
+        const int xs = ih * (int)a.xs_h * 2, ws = kh * (int)a.ws2 * 2;
 #pragma unroll
         for (int kw = 0; kw < KB; ++kw)
 #pragma unroll
             for (int o = 0; o < NO; ++o)
-                wv[kw][o] = (kw < a.KW && (o < MO || two))
-                                ? to_f32(Wt[(int64_t)(co0 + o) * a.ws0 + kh * a.ws2 + kw * a.ws3])
-                                : 0.f;
-        float xw[NX][2];
+                pw[kw][o] =
+                    kw < a.KW ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, wb[o], ws + kw * (int)a.ws3 * 2, 0) : 0u;
 #pragma unroll
-        for (int j = 0; j < NX; ++j) {
-            const int iw = iw0 + j;
-            const bool ok = j < nx && (unsigned)iw < (unsigned)a.W;
-            const uint32_t u = ok ? *reinterpret_cast<const uint32_t *>(Xr + (int64_t)iw * a.xs_w + c0) : 0u;
-            T lo, hi;
-            lo.u = (uint16_t)u;
-            hi.u = (uint16_t)(u >> 16);
-            xw[j][0] = to_f32(lo);
-            xw[j][1] = to_f32(hi);
-        }
-#pragma unroll
-        for (int t = 0; t < TO; ++t)
+        for (int j = 0; j < NX; ++j) px[j] = __builtin_amdgcn_raw_buffer_load_b32(xr, xo[j], xs, 0);
+    };
+    auto val = [](uint32_t u) -> float {
+        T t;
+        t.u = (uint16_t)u;
+        return to_f32(t);
+    };
+    uint32_t rx[NX], rw[KB][NO];
+    fetch(0, rx, rw);
+    for (int kh = 0; kh < a.KH; ++kh) {
+        uint32_t qx[NX], qw[KB][NO];
+        const bool more = kh + 1 < a.KH;
+        if (more) fetch(kh + 1, qx, qw);
+        if ((unsigned)(ih0 + kh) < (unsigned)a.H) {
+            float wv[KB][NO], xw[NX][2];
 #pragma unroll
             for (int kw = 0; kw < KB; ++kw)
 #pragma unroll
-                for (int o = 0; o < NO; ++o)
-                    acc[t][o] = __builtin_fmaf(xw[t * S + kw][o / MO], wv[kw][o], acc[t][o]);
+                for (int o = 0; o < NO; ++o) wv[kw][o] = val(rw[kw][o]);
+#pragma unroll
+            for (int j = 0; j < NX; ++j) {
+                xw[j][0] = val(rx[j] & 0xffffu);
+                xw[j][1] = val(rx[j] >> 16);
+            }
+#pragma unroll
+            for (int t = 0; t < TO; ++t)
+#pragma unroll
+                for (int kw = 0; kw < KB; ++kw)
+#pragma unroll
+                    for (int o = 0; o < NO; ++o)
+                        acc[t][o] = __builtin_fmaf(xw[t * S + kw][o / MO], wv[kw][o], acc[t][o]);
+        }
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < NX; ++j) rx[j] = qx[j];
+#pragma unroll
+            for (int kw = 0; kw < KB; ++kw)
+#pragma unroll
+                for (int o = 0; o < NO; ++o) rw[kw][o] = qw[kw][o];
+        }
     }
     T *__restrict__ Y = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h + co0;
 #pragma unroll
@@ -776,6 +870,16 @@ int launch_dwg(const conv_plan_t &p, const void *x, const void *w, const void *b
     a.col_blocks = (int32_t)p.tile[DW_COLCHUNKS];
     a.ch_blocks = (int32_t)p.tile[DW_CHCHUNKS];
     a.has_bias = d.has_bias;
+    {
+        // One image of x (every dim but the batch) and the weight, in bytes;
+        // the planner keeps both below 2^31.
+        const int64_t es = esize(d.dtype);
+        int64_t xi = 0, wi = 0;
+        for (int i = 1; i < d.x.rank; ++i) xi += (d.x.sizes[i] - 1) * d.x.strides[i];
+        for (int i = 0; i < d.w.rank; ++i) wi += (d.w.sizes[i] - 1) * d.w.strides[i];
+        a.x_bytes = (int32_t)((xi + 1) * es);
+        a.w_bytes = (int32_t)((wi + 1) * es);
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)p.grid[0]);
     // Word loads of x: multiplier 1 with 16-bit channel pairs on 4-byte

@@ -104,6 +104,18 @@ bool dwcl_generic_ok(const conv_desc &d, const conv_tensor &y)
     if (cig(d) != 1 || d.groups != d.C_in || d.C_out % d.C_in) return false;
     if (d.stride[d.spatial - 1] > 3) return false;   // compiled column strides 1..3
     if (d.x.strides[1] != 1) return false;
+    // Buffer loads: non-negative strides, one image of x and the weight each
+    // below 2^31 bytes.
+    int64_t xi = 0, wi = 0;
+    for (int i = 0; i < d.x.rank; ++i) {
+        if (d.x.strides[i] < 0) return false;
+        if (i > 0) xi += (d.x.sizes[i] - 1) * d.x.strides[i];
+    }
+    for (int i = 0; i < d.w.rank; ++i) {
+        if (d.w.strides[i] < 0) return false;
+        wi += (d.w.sizes[i] - 1) * d.w.strides[i];
+    }
+    if ((xi + 1) * esize(d.dtype) > kI32 - 4096 || (wi + 1) * esize(d.dtype) > kI32 - 4096) return false;
     // y channels-last (channel words), or with its positions contiguous (the
     // channel-major output ATen gives a 1-D call on a channels-last input).
     if (y.strides[1] == 1) {
