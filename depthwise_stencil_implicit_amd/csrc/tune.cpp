@@ -72,7 +72,13 @@ extern "C" int conv_plan_candidates(const conv_desc *d, const conv_tensor *y, co
     if (max > 0) out[0] = probe;
     n = 1;
     for (int32_t k : {CONV_K_DW_CL, CONV_K_PLANE}) add(d, y, k, -1, out, max, n);
-    add(d, y, CONV_K_DW_CL, DWCL_GENERIC, out, max, n);
+    // The generic channels-last schedule only where no ring schedule applies:
+    // it re-reads each input row once per kernel row from L2, which timing
+    // on the caller's (warm) buffers rewards and a cold input does not (3x3
+    // stride 2: 14.7 us on the ring, 20.5 us generic, with the input out of
+    // the caches).
+    const bool ring = probe.kernel == CONV_K_DW_CL && probe.variant != DWCL_GENERIC;
+    if (!ring) add(d, y, CONV_K_DW_CL, DWCL_GENERIC, out, max, n);
     // The one-wave-per-output reduction only where outputs are few.
     if (d->out[0] * d->out[1] * d->out[2] <= 16) add(d, y, CONV_K_REDUCE, -1, out, max, n);
     for (int32_t v : {GRP_SCHED_VALU, GRP_SCHED_MMA}) add(d, y, CONV_K_GRP, v, out, max, n);

@@ -345,7 +345,9 @@ MICONV_API int conv_run_backward(const conv_bwd_plan_t *p, const void *x, const 
  * kernels that have several (the implicit GEMM's tile table, the grouped
  * stencil's schedules, the transposed both-phases kernels), as conv_plan_ex
  * accepts them -- except implicit-GEMM plans that pad each group's input
- * channels more than fourfold, which multiply mostly zeros (executorch PR
+ * channels more than fourfold, which multiply mostly zeros, and the generic
+ * channels-last depthwise schedule where a ring schedule applies, whose
+ * re-reads of input rows from L2 time well only on warm buffers (executorch PR
  * #25085, description: the stencil's schedules
  * are timed when the call is compiled; torch/_inductor/kernel/conv.py,
  * autotune_select_algorithm).  Host only.

@@ -508,3 +508,15 @@ def test_dw1d_channels_last_input_routes_to_generic_dw_cl():
     p = prep(x, w, b, **wl_args(wl))
     assert p.strides[2] == 1 and p.strides[1] == p.sizes[2]
     assert api.kernel_name(p.plan.kernel) == "dw_cl" and int(p.plan.variant) == 2
+
+
+def test_generic_depthwise_candidate_only_without_a_ring_schedule():
+    """Where a ring schedule applies (3x3 stride 2) the candidates leave out
+    the generic channels-last schedule, which times well only on warm
+    buffers; a multiplier-2 call (no ring schedule) keeps it."""
+    _, c = _cands(synth.depthwise_bf16_cl(3, 2))
+    dw = {int(q.variant) for q in c if api.kernel_name(q.kernel) == "dw_cl"}
+    assert 2 not in dw and dw
+    m2 = next(w for w in synth.domain_edge_workloads() if w.name.endswith("_m2"))
+    _, c = _cands(m2)
+    assert 2 in {int(q.variant) for q in c if api.kernel_name(q.kernel) == "dw_cl"}
