@@ -2,7 +2,7 @@
 """Throughput of the canonical convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-    python bench.py --probe-copy MIB | --probe-mfma | --probe-lds
+    python bench.py --probe-copy MIB | --probe-mfma | --probe-valu | --probe-lds | --probe-gemm
 
 A step is one pass over the workload's calls (kernels only: binding, output
 layout and planning run once per call before timing, and their host time is
@@ -52,8 +52,8 @@ METRIC = "HBM GB/s (stencil) and TFLOP/s (implicit GEMM), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6        # dense bf16/fp16 MFMA, 256 CUs x 2048 FMA/clk x 2.4 GHz x 2
 MFMA_F32_PEAK_TFLOPS = 157.3          # dense fp32 MFMA
-VALU_FP32_PEAK_TFLOPS = 78.6          # 256 CUs x 64 lanes x 2 FLOP/FMA x 2.4 GHz (no packed fp32)
-VALU_DOT2_PEAK_TFLOPS = 157.3         # the same lanes issuing v_dot2_f32_{bf16,f16}: two FMAs each
+VALU_FP32_PEAK_TFLOPS = 157.3         # published fp32 vector peak; v_fmac_f32 issues a wave in ~2 clocks (probe)
+VALU_DOT2_PEAK_TFLOPS = 157.3         # v_dot2_f32_{bf16,f16}: two FMAs per lane, a wave in 4 clocks
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -86,6 +86,12 @@ def parse():
     ap.add_argument("--probe-mfma", action="store_true",
                     help="instead of a workload, time a kernel of independent bf16 MFMAs (the "
                          "measured matrix-core ceiling)")
+    ap.add_argument("--probe-valu", action="store_true",
+                    help="instead of a workload, time kernels of independent vector bf16 dot2 and fp32 FMA "
+                         "instructions (the measured vector-ALU ceilings)")
+    ap.add_argument("--probe-gemm", action="store_true",
+                    help="instead of a workload, time torch.mm (the vendor GEMM) on explicit operands of the "
+                         "implicit GEMMs' shapes, and on one large square GEMM")
     ap.add_argument("--probe-lds", action="store_true",
                     help="instead of a workload, time a kernel of conflict-free 16-byte LDS reads")
     return ap.parse_args()
@@ -113,11 +119,42 @@ def copy_probe(mib, steps, warmup):
                       "avg_us": round(us, 2), "GBps": round(moved / us / 1e3, 1)}), flush=True)
 
 
+def gemm_probe(steps, warmup):
+    """The vendor GEMM (torch.mm, bf16) on explicit, contiguous operands with
+    the implicit GEMMs' shapes: the dense 3x3 call's im2col product (M = 64*56*56
+    positions, N = 256 channels, K = 9*256) and one output phase of the 1-D
+    transposed call (M = 16*8192 positions of the phase, N = 512, K = 2 taps x
+    512 channels), plus a large square product for the library's best case."""
+    import torch
+    shapes = [("dense_3x3_im2col", 200704, 256, 2304), ("transposed_phase", 131072, 512, 1024),
+              ("square_16k", 16384, 16384, 8192)]
+    for name, m, n, k in shapes:
+        g = torch.Generator(device="cuda:0").manual_seed(0)
+        a = torch.randn(m, k, device="cuda:0", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(k, n, device="cuda:0", dtype=torch.bfloat16, generator=g).contiguous()
+        c = torch.empty(m, n, device="cuda:0", dtype=torch.bfloat16)
+        reps = max(1, steps if m * n * k < 1 << 36 else steps // 4)
+        for _ in range(warmup):
+            torch.mm(a, b, out=c)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            torch.mm(a, b, out=c)
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / reps
+        rate = 2.0 * m * n * k / us / 1e6
+        print(json.dumps({"probe": "torch.mm " + name, "m": m, "n": n, "k": k, "avg_us": round(us, 1),
+                          "TFLOPs": round(rate, 1), "frac": round(rate / MFMA_BF16_PEAK_TFLOPS, 4)}), flush=True)
+        del a, b, c
+
+
 def unit_probe(kind, steps, warmup):
-    """MFMA issue rate or LDS read bandwidth from the probe library's kernels
-    (8 workgroups of 256 threads per CU, 256 CUs).  The MFMA probe also reads
-    the shader clock against the 100 MHz real-time counter inside its loop,
-    which gives the clock the units ran at."""
+    """MFMA or vector-ALU issue rate, or LDS read bandwidth, from the probe
+    library's kernels (8 workgroups of 256 threads per CU, 256 CUs).  The MFMA
+    and vector probes also read the shader clock against the 100 MHz real-time
+    counter inside their loops, which gives the clock the units ran at."""
     import ctypes
     import torch
     from depthwise_stencil_implicit_amd import build
@@ -155,6 +192,35 @@ def unit_probe(kind, steps, warmup):
                               "TFLOPs": round(rate, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
                               "frac": round(rate / MFMA_BF16_PEAK_TFLOPS, 4), "shader_clock_MHz": round(mhz),
                               "clocks_per_mfma_per_wave": round(cyc, 2)}), flush=True)
+    elif kind == "valu":
+        lib.probe_valu.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+        lib.probe_valu.restype = ctypes.c_int
+        iters = 8192
+        # FLOPs per lane per round: 8 instructions of 2 products (dot2) or 1 (FMA), 2 FLOP each.
+        shapes = [("valu_dot2_f32_bf16", 0, 8 * 2 * 2, VALU_DOT2_PEAK_TFLOPS),
+                  ("valu_fma_f32", 1, 8 * 1 * 2, VALU_FP32_PEAK_TFLOPS)]
+        for name, kind_id, flop_per_round, peak in shapes:
+            fn = lambda: lib.probe_valu(out.data_ptr(), clk.data_ptr(), blocks, iters, kind_id, stream.cuda_stream)
+            for _ in range(warmup):
+                assert fn() == 0
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(steps):
+                assert fn() == 0
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            us = ev0.elapsed_time(ev1) * 1e3 / steps
+            flops = blocks * 256 * iters * flop_per_round
+            rate = flops / us / 1e6
+            c = clk.view(-1, 2).double()
+            mhz = float((c[:, 0] / c[:, 1].clamp(min=1)).median()) * 100.0
+            cyc = float(c[:, 0].median()) / iters / 8
+            print(json.dumps({"probe": name, "flops_per_launch": flops, "avg_us": round(us, 2),
+                              "TFLOPs": round(rate, 1), "peak_TFLOPs": peak, "frac": round(rate / peak, 4),
+                              "shader_clock_MHz": round(mhz), "clocks_per_instr_per_wave": round(cyc, 2)}),
+                  flush=True)
     else:
         lib.probe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         lib.probe_lds.restype = ctypes.c_int
@@ -357,8 +423,11 @@ def main():
     if a.probe_copy:
         copy_probe(a.probe_copy, a.steps, a.warmup)
         return
-    if a.probe_mfma or a.probe_lds:
-        unit_probe("mfma" if a.probe_mfma else "lds", a.steps, a.warmup)
+    if a.probe_gemm:
+        gemm_probe(a.steps, a.warmup)
+        return
+    if a.probe_mfma or a.probe_valu or a.probe_lds:
+        unit_probe("mfma" if a.probe_mfma else ("valu" if a.probe_valu else "lds"), a.steps, a.warmup)
         return
     calls = workload_calls(a.workload)
 

@@ -53,15 +53,26 @@ __global__ __launch_bounds__(256) void plane_kernel(PlArgs a)
     const int ih0 = th * a.TH * a.SH - a.PH;
     const int iw0 = tw * a.TW * a.SW - a.PW;
     const int plane = a.IH * a.IW;
-    for (int i = tid; i < a.Cig * plane; i += blockDim.x) {
-        const int c = i / plane;
-        const int rem = i - c * plane;
-        const int r = rem / a.IW, q = rem - r * a.IW;
-        const int ih = ih0 + r, iw = iw0 + q;
-        float v = 0.f;
-        if ((unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W)
-            v = to_f32(X[(int64_t)c * a.xs_c + (int64_t)ih * a.xs_h + (int64_t)iw * a.xs_w]);
-        sx[i] = v;
+    const int halo = a.Cig * plane;
+    // SL values per thread per pass, all loads issued before the first LDS
+    // write, so their latencies overlap.
+    constexpr int SL = 4;
+    for (int i0 = tid; i0 < halo; i0 += SL * 256) {
+        float v[SL];
+#pragma unroll
+        for (int u = 0; u < SL; ++u) {
+            const int i = i0 + u * 256;
+            const int c = i / plane;
+            const int rem = i - c * plane;
+            const int r = rem / a.IW, q = rem - r * a.IW;
+            const int ih = ih0 + r, iw = iw0 + q;
+            v[u] = 0.f;
+            if (i < halo && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W)
+                v[u] = to_f32(X[(int64_t)c * a.xs_c + (int64_t)ih * a.xs_h + (int64_t)iw * a.xs_w]);
+        }
+#pragma unroll
+        for (int u = 0; u < SL; ++u)
+            if (i0 + u * 256 < halo) sx[i0 + u * 256] = v[u];
     }
     __syncthreads();
 

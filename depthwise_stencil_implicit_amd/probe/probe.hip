@@ -1,6 +1,7 @@
 // Ceiling probes for gfx950 (measurement only; not part of the convolution
-// library): the issue rate of dense bf16 MFMAs and the read bandwidth of
-// LDS, each from a kernel that does nothing else.  The benchmark times them
+// library): the issue rate of dense bf16 MFMAs, of the vector unit's packed
+// bf16 dot2 and fp32 FMA, and the read bandwidth of LDS, each from a kernel
+// that does nothing else.  The benchmark times them
 // with events and prints the achieved rate next to the published peaks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -8,6 +9,7 @@
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // Every wave issues `iters` rounds of 8 independent bf16 MFMAs (eight
 // accumulators, so no MFMA waits on another's result): 16x16x32 when
@@ -65,6 +67,51 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float *out, uint64_t *c
     }
 }
 
+// Every wave issues `iters` rounds of 8 independent vector multiply-adds
+// per lane (eight accumulators, so none waits on another's result):
+// v_dot2_f32_bf16 (two products per lane) when `kind` is 0, v_fma_f32 (one)
+// otherwise.  Outputs as in probe_mfma_kernel.
+__global__ __launch_bounds__(256) void probe_valu_kernel(float *out, uint64_t *clk, int iters, float seed, int kind)
+{
+    const float fa = seed * (float)(threadIdx.x + 1), fb = seed * (float)(blockIdx.x + 3);
+    const bf16x2 a{(__bf16)fa, (__bf16)(fa + 1.f)}, b{(__bf16)fb, (__bf16)(fb + 2.f)};
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    float s0 = 0.f, s1 = 1.f, s2 = 2.f, s3 = 3.f, s4 = 4.f, s5 = 5.f, s6 = 6.f, s7 = 7.f;
+    if (kind == 0) {
+#pragma unroll 4
+        for (int it = 0; it < iters; ++it) {
+            s0 = __builtin_amdgcn_fdot2_f32_bf16(a, b, s0, false);
+            s1 = __builtin_amdgcn_fdot2_f32_bf16(a, b, s1, false);
+            s2 = __builtin_amdgcn_fdot2_f32_bf16(a, b, s2, false);
+            s3 = __builtin_amdgcn_fdot2_f32_bf16(a, b, s3, false);
+            s4 = __builtin_amdgcn_fdot2_f32_bf16(a, b, s4, false);
+            s5 = __builtin_amdgcn_fdot2_f32_bf16(a, b, s5, false);
+            s6 = __builtin_amdgcn_fdot2_f32_bf16(a, b, s6, false);
+            s7 = __builtin_amdgcn_fdot2_f32_bf16(a, b, s7, false);
+        }
+    } else {
+#pragma unroll 4
+        for (int it = 0; it < iters; ++it) {
+            s0 = __builtin_fmaf(fa, fb, s0);
+            s1 = __builtin_fmaf(fa, fb, s1);
+            s2 = __builtin_fmaf(fa, fb, s2);
+            s3 = __builtin_fmaf(fa, fb, s3);
+            s4 = __builtin_fmaf(fa, fb, s4);
+            s5 = __builtin_fmaf(fa, fb, s5);
+            s6 = __builtin_fmaf(fa, fb, s6);
+            s7 = __builtin_fmaf(fa, fb, s7);
+        }
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s0 + s1 + s2 + s3 + s4 + s5 + s6 + s7;
+    if (threadIdx.x == 0) {
+        clk[2 * blockIdx.x] = c1 - c0;
+        clk[2 * blockIdx.x + 1] = r1 - r0;
+    }
+}
+
 // Every lane reads `iters` 16-byte LDS words (ds_read_b128, consecutive
 // lanes on consecutive words, so no bank conflicts) from a 64 KiB buffer it
 // first fills, folds them into a register, and writes one word per lane.
@@ -94,6 +141,14 @@ extern "C" __attribute__((visibility("default"))) int probe_mfma(void *out, void
 {
     hipLaunchKernelGGL(probe_mfma_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (float *)out,
                        (uint64_t *)clk, iters, 1e-3f, big);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+extern "C" __attribute__((visibility("default"))) int probe_valu(void *out, void *clk, int blocks, int iters,
+                                                                  int kind, void *stream)
+{
+    hipLaunchKernelGGL(probe_valu_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (float *)out,
+                       (uint64_t *)clk, iters, 1e-3f, kind);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
