@@ -940,7 +940,7 @@ constexpr IgemmCfg kCfgs[] = {
     {128, 256, 64, 2, 4, 3, 70},   // 8: 8 waves, wave tile 64 x 64
     {256, 256, 32, 2, 4, 4, 93},   // 9: 8 waves, K step 32, 4 stages (deeper prefetch)
     {256, 256, 32, 2, 4, 3, 88},   // 10: 8 waves, K step 32, 3 stages
-    {64, 256, 64, 1, 4, 3, 40},    // 11: 4 waves, wave tile 64 x 64 (rows left after the full rounds)
+    {64, 256, 64, 1, 8, 3, 40},    // 11: 8 waves, wave tile 64 x 32 (rows left after the full rounds)
 };
 
 // Weight repack through an LDS tile, for weights whose packed rows (g, j, t)
