@@ -2,7 +2,7 @@
 """Throughput of the canonical convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-    python bench.py --probe-copy MIB | --probe-mfma | --probe-valu | --probe-lds | --probe-gemm
+    python bench.py --probe-copy MIB | --probe-mfma | --probe-valu | --probe-lds
 
 A step is one pass over the workload's calls (kernels only: binding, output
 layout and planning run once per call before timing, and their host time is
@@ -89,9 +89,6 @@ def parse():
     ap.add_argument("--probe-valu", action="store_true",
                     help="instead of a workload, time kernels of independent vector bf16 dot2 and fp32 FMA "
                          "instructions (the measured vector-ALU ceilings)")
-    ap.add_argument("--probe-gemm", action="store_true",
-                    help="instead of a workload, time torch.mm (the vendor GEMM) on explicit operands of the "
-                         "implicit GEMMs' shapes, and on one large square GEMM")
     ap.add_argument("--probe-lds", action="store_true",
                     help="instead of a workload, time a kernel of conflict-free 16-byte LDS reads")
     return ap.parse_args()
@@ -117,37 +114,6 @@ def copy_probe(mib, steps, warmup):
     moved = 2 * n * 4
     print(json.dumps({"probe": "copy", "bytes_per_launch": moved, "read_bytes": n * 4, "write_bytes": n * 4,
                       "avg_us": round(us, 2), "GBps": round(moved / us / 1e3, 1)}), flush=True)
-
-
-def gemm_probe(steps, warmup):
-    """The vendor GEMM (torch.mm, bf16) on explicit, contiguous operands with
-    the implicit GEMMs' shapes: the dense 3x3 call's im2col product (M = 64*56*56
-    positions, N = 256 channels, K = 9*256) and one output phase of the 1-D
-    transposed call (M = 16*8192 positions of the phase, N = 512, K = 2 taps x
-    512 channels), plus a large square product for the library's best case."""
-    import torch
-    shapes = [("dense_3x3_im2col", 200704, 256, 2304), ("transposed_phase", 131072, 512, 1024),
-              ("square_16k", 16384, 16384, 8192)]
-    for name, m, n, k in shapes:
-        g = torch.Generator(device="cuda:0").manual_seed(0)
-        a = torch.randn(m, k, device="cuda:0", dtype=torch.bfloat16, generator=g)
-        b = torch.randn(k, n, device="cuda:0", dtype=torch.bfloat16, generator=g).contiguous()
-        c = torch.empty(m, n, device="cuda:0", dtype=torch.bfloat16)
-        reps = max(1, steps if m * n * k < 1 << 36 else steps // 4)
-        for _ in range(warmup):
-            torch.mm(a, b, out=c)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for _ in range(reps):
-            torch.mm(a, b, out=c)
-        ev1.record()
-        torch.cuda.synchronize()
-        us = ev0.elapsed_time(ev1) * 1e3 / reps
-        rate = 2.0 * m * n * k / us / 1e6
-        print(json.dumps({"probe": "torch.mm " + name, "m": m, "n": n, "k": k, "avg_us": round(us, 1),
-                          "TFLOPs": round(rate, 1), "frac": round(rate / MFMA_BF16_PEAK_TFLOPS, 4)}), flush=True)
-        del a, b, c
 
 
 def unit_probe(kind, steps, warmup):
@@ -422,9 +388,6 @@ def main():
     dev = torch.device("cuda:0")
     if a.probe_copy:
         copy_probe(a.probe_copy, a.steps, a.warmup)
-        return
-    if a.probe_gemm:
-        gemm_probe(a.steps, a.warmup)
         return
     if a.probe_mfma or a.probe_valu or a.probe_lds:
         unit_probe("mfma" if a.probe_mfma else ("valu" if a.probe_valu else "lds"), a.steps, a.warmup)
