@@ -165,7 +165,11 @@ def unit_probe(kind, steps, warmup):
         iters = 8192
         # FLOPs per lane per round: 8 instructions of 2 products (dot2) or 1 (FMA), 2 FLOP each.
         shapes = [("valu_dot2_f32_bf16", 0, 8 * 2 * 2, VALU_DOT2_PEAK_TFLOPS),
-                  ("valu_fma_f32", 1, 8 * 1 * 2, VALU_FP32_PEAK_TFLOPS)]
+                  ("valu_fma_f32", 1, 8 * 1 * 2, VALU_FP32_PEAK_TFLOPS),
+                  ("valu_dot2c_bf16 operands in one register bank", 2, 8 * 2 * 2, VALU_DOT2_PEAK_TFLOPS),
+                  ("valu_dot2c_bf16 operands in three banks", 3, 8 * 2 * 2, VALU_DOT2_PEAK_TFLOPS),
+                  ("valu_dot2c_bf16 accumulator and second source in one bank", 4, 8 * 2 * 2,
+                   VALU_DOT2_PEAK_TFLOPS)]
         for name, kind_id, flop_per_round, peak in shapes:
             fn = lambda: lib.probe_valu(out.data_ptr(), clk.data_ptr(), blocks, iters, kind_id, stream.cuda_stream)
             for _ in range(warmup):

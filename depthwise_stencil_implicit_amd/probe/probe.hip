@@ -70,7 +70,11 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float *out, uint64_t *c
 // Every wave issues `iters` rounds of 8 independent vector multiply-adds
 // per lane (eight accumulators, so none waits on another's result):
 // v_dot2_f32_bf16 (two products per lane) when `kind` is 0, v_fma_f32 (one)
-// otherwise.  Outputs as in probe_mfma_kernel.
+// when it is 1.  Kinds 2-4 issue the accumulating dot2 form with operands in
+// fixed registers, to see whether register banks (register number mod 4)
+// shared between operands slow the issue: 2 = accumulator and both sources
+// in one bank, 3 = three different banks, 4 = accumulator and second source
+// in one bank.  Outputs as in probe_mfma_kernel.
 __global__ __launch_bounds__(256) void probe_valu_kernel(float *out, uint64_t *clk, int iters, float seed, int kind)
 {
     const float fa = seed * (float)(threadIdx.x + 1), fb = seed * (float)(blockIdx.x + 3);
@@ -103,6 +107,48 @@ __global__ __launch_bounds__(256) void probe_valu_kernel(float *out, uint64_t *c
             s7 = __builtin_fmaf(fa, fb, s7);
         }
     }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s0 + s1 + s2 + s3 + s4 + s5 + s6 + s7;
+    if (threadIdx.x == 0) {
+        clk[2 * blockIdx.x] = c1 - c0;
+        clk[2 * blockIdx.x + 1] = r1 - r0;
+    }
+}
+
+// Kinds 2-4 of probe_valu: the accumulating dot2 form with operands in
+// fixed registers (one kernel per kind, so that no kind's register choices
+// carry over to another's loop as copies).
+template <int KIND>
+__global__ __launch_bounds__(256) void probe_bank_kernel(float *out, uint64_t *clk, int iters, float seed)
+{
+    const float fa = seed * (float)(threadIdx.x + 1), fb = seed * (float)(blockIdx.x + 3);
+    const bf16x2 a{(__bf16)fa, (__bf16)(fa + 1.f)}, b{(__bf16)fb, (__bf16)(fb + 2.f)};
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    float s0 = 0.f, s1 = 1.f, s2 = 2.f, s3 = 3.f, s4 = 4.f, s5 = 5.f, s6 = 6.f, s7 = 7.f;
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+#define PROBE_DOT8(A0, A1, A2, A3, A4, A5, A6, A7, X, Y)                                                          \
+    asm volatile("v_dot2c_f32_bf16 %0, %8, %9\n v_dot2c_f32_bf16 %1, %8, %9\n v_dot2c_f32_bf16 %2, %8, %9\n"        \
+                 " v_dot2c_f32_bf16 %3, %8, %9\n v_dot2c_f32_bf16 %4, %8, %9\n v_dot2c_f32_bf16 %5, %8, %9\n"       \
+                 " v_dot2c_f32_bf16 %6, %8, %9\n v_dot2c_f32_bf16 %7, %8, %9"                                    \
+                 : "+{" A0 "}"(s0), "+{" A1 "}"(s1), "+{" A2 "}"(s2), "+{" A3 "}"(s3), "+{" A4 "}"(s4),           \
+                   "+{" A5 "}"(s5), "+{" A6 "}"(s6), "+{" A7 "}"(s7)                                              \
+                 : "{" X "}"(ua), "{" Y "}"(ub))
+    if constexpr (KIND == 2) {
+#pragma unroll 4
+        for (int it = 0; it < iters; ++it)
+            PROBE_DOT8("v40", "v44", "v48", "v52", "v56", "v60", "v64", "v68", "v72", "v76");
+    } else if constexpr (KIND == 3) {
+#pragma unroll 4
+        for (int it = 0; it < iters; ++it)
+            PROBE_DOT8("v41", "v45", "v49", "v53", "v57", "v61", "v65", "v69", "v74", "v79");
+    } else {
+#pragma unroll 4
+        for (int it = 0; it < iters; ++it)
+            PROBE_DOT8("v40", "v44", "v48", "v52", "v56", "v60", "v64", "v68", "v74", "v76");
+    }
+#undef PROBE_DOT8
     const uint64_t c1 = __builtin_amdgcn_s_memtime();
     const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
     out[blockIdx.x * blockDim.x + threadIdx.x] = s0 + s1 + s2 + s3 + s4 + s5 + s6 + s7;
@@ -147,8 +193,18 @@ extern "C" __attribute__((visibility("default"))) int probe_mfma(void *out, void
 extern "C" __attribute__((visibility("default"))) int probe_valu(void *out, void *clk, int blocks, int iters,
                                                                   int kind, void *stream)
 {
-    hipLaunchKernelGGL(probe_valu_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (float *)out,
-                       (uint64_t *)clk, iters, 1e-3f, kind);
+    if (kind == 2)
+        hipLaunchKernelGGL(probe_bank_kernel<2>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (float *)out,
+                           (uint64_t *)clk, iters, 1e-3f);
+    else if (kind == 3)
+        hipLaunchKernelGGL(probe_bank_kernel<3>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (float *)out,
+                           (uint64_t *)clk, iters, 1e-3f);
+    else if (kind == 4)
+        hipLaunchKernelGGL(probe_bank_kernel<4>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (float *)out,
+                           (uint64_t *)clk, iters, 1e-3f);
+    else
+        hipLaunchKernelGGL(probe_valu_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (float *)out,
+                           (uint64_t *)clk, iters, 1e-3f, kind);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
