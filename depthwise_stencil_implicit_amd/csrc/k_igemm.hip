@@ -382,8 +382,12 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgArgs a)
 // accesses on their side of it); before it each wave waits for its own loads of
 // the stage about to be read, so after it every wave's loads have landed.  A
 // fenced __syncthreads() would instead drain every load in flight.
+// Launch bounds: a configuration whose stages fit in half the LDS (80 KB)
+// runs two workgroups per CU, so its waves are held to the registers of
+// twice as many waves per SIMD.
 template <typename T, int BM, int BN, int WM, int WN, int STAGES, int KC>
-__global__ __launch_bounds__(64 * WM * WN) void igemm_dma_kernel(IgArgs a)
+__global__ __launch_bounds__(64 * WM * WN, (STAGES * (BM + BN) * KC * 16 <= 80 * 1024 ? 2 : 1) * WM * WN / 4) void
+igemm_dma_kernel(IgArgs a)
 {
     // The body uses LDS address-space pointers that only the device pass can
     // instantiate; the host pass needs nothing but the launch stub.
@@ -937,7 +941,7 @@ constexpr IgemmCfg kCfgs[] = {
     {128, 64, 32, 2, 2, 2, 100},   // 5: fp32 (register-staged path only)
     {128, 256, 64, 2, 2, 3, 70},   // 6: 4 waves, wave tile 64 x 128
     {256, 128, 64, 2, 2, 3, 60},   // 7: 4 waves, wave tile 128 x 64
-    {128, 256, 64, 2, 4, 3, 70},   // 8: 8 waves, wave tile 64 x 64
+    {128, 128, 64, 2, 2, 2, 100},  // 8: 4 waves, two stages: two workgroups per CU
     {256, 256, 32, 2, 4, 4, 93},   // 9: 8 waves, K step 32, 4 stages (deeper prefetch)
     {256, 256, 32, 2, 4, 3, 88},   // 10: 8 waves, K step 32, 3 stages
     {64, 256, 64, 1, 8, 3, 40},    // 11: 8 waves, wave tile 64 x 32 (rows left after the full rounds)
