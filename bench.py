@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --probe-copy MIB | --probe-mfma | --probe-valu | --probe-lds
+    python bench.py --backward     gradients (dx, dw, db) of every call of the default run
 
 A step is one pass over the workload's calls (kernels only: binding, output
 layout and planning run once per call before timing, and their host time is
@@ -80,6 +81,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="capture each rotation set's step once in a HIP graph and time graph replays (default: "
                          "eager launches; on the default workload both measure the same step time)")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward step, time conv_run_backward (dx, dw and db) for every call of "
+                         "the default run, one JSON line with a row per call")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="MIB",
                     help="instead of a workload, time a plain device copy of MIB mebibytes (the "
                          "measured bandwidth ceiling, and the reference for HBM byte counters)")
@@ -114,6 +118,57 @@ def copy_probe(mib, steps, warmup):
     moved = 2 * n * 4
     print(json.dumps({"probe": "copy", "bytes_per_launch": moved, "read_bytes": n * 4, "write_bytes": n * 4,
                       "avg_us": round(us, 2), "GBps": round(moved / us / 1e3, 1)}), flush=True)
+
+
+def backward_bench(steps, warmup):
+    """Gradients of every call of the default run: conv_run_backward with dx,
+    dw and db together, averaged over HIP events on the launch stream (warm
+    buffers, no rotation).  A call's time at the roofline is the longer of its
+    algorithmic bytes (the plan's dx + dw + db bytes) at 8 TB/s and its FLOPs
+    (dx and dw each count as many as the forward call) at the matrix-core peak
+    of its dtype (the vector peak for fp32)."""
+    import torch
+    from depthwise_stencil_implicit_amd import api, synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for wname, wl in workload_calls("all"):
+        x, w, b = synth.make_inputs(wl, device="cuda")
+        args = make_args(wl)
+        y = api.Prepared(x, w, b, args).empty_output(dev)
+        g = torch.Generator(device="cuda").manual_seed(wl.seed + 1)
+        gy = torch.randn(y.shape, generator=g, device=dev, dtype=torch.float32).to(y.dtype)
+        gy = torch.empty_strided(y.shape, y.stride(), dtype=y.dtype, device=dev).copy_(gy)
+        try:
+            pb = api.PreparedBackward(x, w, gy, args)
+        except api.ConvError as e:
+            rows.append({"workload": wname, "call": wl.name, "error": str(e)})
+            continue
+        dx, dw, db = pb.outputs(dev)
+        ws = pb.workspace(dev)
+        for _ in range(warmup):
+            pb.run(x, w, gy, dx, dw, db, ws, stream.cuda_stream)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            pb.run(x, w, gy, dx, dw, db, ws, stream.cuda_stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / steps
+        fl, by = int(sum(pb.plan.flops)), int(sum(pb.plan.bytes))
+        peak = VALU_FP32_PEAK_TFLOPS if wl.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+        t_mem, t_cmp = by / (HBM_PEAK_GBS * 1e3), fl / (peak * 1e6)
+        bound = "mfma" if t_cmp > t_mem and wl.dtype != "f32" else ("alu" if t_cmp > t_mem else "hbm")
+        rows.append({"workload": wname, "call": wl.name, "dgrad_kernel": api.kernel_name(pb.plan.dgrad.kernel),
+                     "avg_us": round(us, 2), "gflop": round(fl / 1e9, 3), "mb": round(by / 1e6, 2),
+                     "TFLOPs": round(fl / us / 1e6, 2), "GBps": round(by / us / 1e3, 1), "bound": bound,
+                     "frac": round(max(t_mem, t_cmp) / us, 4)})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del x, w, b, y, gy, dx, dw, db, ws, pb
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "backward", "steps": steps, "warmup": warmup, "data": "synthetic",
+                      "per_call": rows}), flush=True)
 
 
 def unit_probe(kind, steps, warmup):
@@ -392,6 +447,9 @@ def main():
     dev = torch.device("cuda:0")
     if a.probe_copy:
         copy_probe(a.probe_copy, a.steps, a.warmup)
+        return
+    if a.backward:
+        backward_bench(a.steps, a.warmup)
         return
     if a.probe_mfma or a.probe_valu or a.probe_lds:
         unit_probe("mfma" if a.probe_mfma else ("valu" if a.probe_valu else "lds"), a.steps, a.warmup)

@@ -59,7 +59,7 @@ class ConvPlan(ctypes.Structure):
 
 class ConvBwdPlan(ctypes.Structure):
     _fields_ = [("d", ConvDesc), ("gy", ConvTensor), ("dx", ConvTensor), ("dw", ConvTensor), ("db", ConvTensor),
-                ("need_dx", _i32), ("need_dw", _i32), ("need_db", _i32), ("reserved0", _i32),
+                ("need_dx", _i32), ("need_dw", _i32), ("need_db", _i32), ("dgrad_flip", _i32),
                 ("dgrad", ConvPlan), ("wg_tile", _i64 * 8), ("db_splits", _i64), ("workspace_bytes", _i64),
                 ("flops", _i64 * 3), ("bytes", _i64 * 3)]
 

@@ -8,7 +8,15 @@
 // read as [C_in', Cog', k]) with output_padding (L + pb + pa - dil(k-1) - 1)
 // mod s, whose output length is exactly L; a transposed call's dx is the
 // forward call of gy (output length L as long as output_padding < stride).
-// So dx runs on the planner's own kernels, chosen for that call.
+// So dx runs on the planner's own kernels, chosen for that call.  With stride
+// 1 the transposed adjoint is itself a forward call: per dim
+//   dx[i] = sum_t gy[i + pb - t*dil] w[t] = sum_t' gy[i - pb' + t'*dil] w[K-1-t']
+// with pb' = (K-1)*dil - pb, a correlation of gy with the taps reversed and,
+// per group, the two channel dims of the weight exchanged.  Where that forward
+// call has at most 8 input channels per group (depthwise and few-channel
+// grouped calls, whose transposed adjoint the implicit GEMM would pad to its
+// 64-channel K step), the weight is first copied reversed into the workspace
+// and dx runs on the forward stencils.
 //
 // Weight and bias gradients.  The weight gradient is the GEMM over
 // positions described in k_bwd.hip, split over workgroups by ranges of
@@ -111,6 +119,48 @@ bool adjoint_desc(const conv_desc &d, const conv_tensor &gy, conv_desc &a)
     return true;
 }
 
+// The stride-1 input gradient as a forward call of gy with the reversed,
+// channel-exchanged weight (contiguous [C_in][C_out/groups][k...]).
+bool flipped_desc(const conv_desc &d, const conv_tensor &gy, conv_desc &f)
+{
+    if (d.transposed || d.spatial > 2) return false;
+    const int64_t Cog = d.C_out / d.groups;
+    if (Cog > 8) return false;
+    std::memset(&f, 0, sizeof(f));
+    f.spatial = d.spatial;
+    f.dtype = d.dtype;
+    f.N = d.N;
+    f.C_in = d.C_out;
+    f.C_out = d.C_in;
+    f.groups = d.groups;
+    for (int i = 0; i < 3; ++i) {
+        f.in[i] = d.out[i];
+        f.k[i] = d.k[i];
+        f.stride[i] = 1;
+        f.dilation[i] = d.dilation[i];
+        f.out[i] = d.in[i];
+        if (i >= d.spatial) continue;
+        const int64_t reach = (d.k[i] - 1) * d.dilation[i];
+        if (d.stride[i] != 1 || d.padding_before[i] > reach || d.padding_after[i] > reach) return false;
+        f.padding_before[i] = reach - d.padding_before[i];
+        f.padding_after[i] = reach - d.padding_after[i];
+        if (out_len(0, f.in[i], f.k[i], 1, f.padding_before[i], f.padding_after[i], f.dilation[i], 0) != d.in[i])
+            return false;
+    }
+    f.x = gy;
+    f.w.rank = d.spatial + 2;
+    f.w.dtype = d.dtype;
+    f.w.sizes[0] = d.C_in;
+    f.w.sizes[1] = Cog;
+    for (int i = 0; i < d.spatial; ++i) f.w.sizes[2 + i] = d.k[i];
+    int64_t acc = 1;
+    for (int i = f.w.rank - 1; i >= 0; --i) {
+        f.w.strides[i] = acc;
+        acc *= f.w.sizes[i];
+    }
+    return true;
+}
+
 // Dense strides in the dim order of t's strides (its memory format).
 void dense_like(const conv_tensor &t, conv_tensor &o)
 {
@@ -187,9 +237,19 @@ extern "C" int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int
         conv_desc a;
         if (!adjoint_desc(*d, plan.gy, a)) return CONV_EUNSUPPORTED;
         batched_out(a, plan.dx);
-        const int st = conv_plan(&a, &plan.dx, CONV_K_AUTO, &plan.dgrad);
-        if (st != CONV_OK) return st;
-        ws = std::max<int64_t>(ws, round_up(plan.dgrad.workspace_bytes, 256));
+        conv_desc f;
+        conv_plan_t fp;
+        if (flipped_desc(*d, plan.gy, f) && conv_plan(&f, &plan.dx, CONV_K_AUTO, &fp) == CONV_OK &&
+            fp.kernel != CONV_K_IGEMM && fp.kernel != CONV_K_IGEMM_T) {
+            // The reversed weight first, then the stencil's own scratch.
+            plan.dgrad = fp;
+            plan.dgrad_flip = 1;
+            ws = std::max<int64_t>(ws, round_up(numel(f.w) * es, 256) + round_up(fp.workspace_bytes, 256));
+        } else {
+            const int st = conv_plan(&a, &plan.dx, CONV_K_AUTO, &plan.dgrad);
+            if (st != CONV_OK) return st;
+            ws = std::max<int64_t>(ws, round_up(plan.dgrad.workspace_bytes, 256));
+        }
         plan.flops[0] = plan.dgrad.flops;
         plan.bytes[0] = plan.dgrad.bytes;
     }
@@ -279,7 +339,15 @@ extern "C" int conv_run_backward(const conv_bwd_plan_t *p, const void *x, const 
         if (q && (reinterpret_cast<uintptr_t>(q) & (es - 1))) return CONV_EALIGN;
     int st = CONV_OK;
     if (p->need_dx && numel(p->dx) > 0) {
-        st = conv_run(&p->dgrad, gy, w, nullptr, dx, workspace, workspace_bytes, stream);
+        if (p->dgrad_flip) {
+            const size_t off = (size_t)round_up(numel(p->dgrad.d.w) * (int64_t)es, 256);
+            st = launch_flip_weight(*p, w, workspace, stream);
+            if (st != CONV_OK) return st;
+            st = conv_run(&p->dgrad, gy, workspace, nullptr, dx, static_cast<char *>(workspace) + off,
+                          workspace_bytes - off, stream);
+        } else {
+            st = conv_run(&p->dgrad, gy, w, nullptr, dx, workspace, workspace_bytes, stream);
+        }
         if (st != CONV_OK) return st;
     }
     if (p->need_dw && numel(p->dw) > 0) {

@@ -141,6 +141,10 @@ int launch_grp(const conv_plan_t &p, const void *x, const void *w, const void *b
 int launch_wgrad(const conv_bwd_plan_t &p, const void *x, const void *gy, void *dw, void *ws, void *stream);
 int launch_bgrad(const conv_bwd_plan_t &p, const void *gy, void *db, void *ws, void *stream);
 int launch_fill_zero(void *out, const conv_tensor &t, void *stream);
+// The weight reversed along every tap dim with its two channel dims exchanged
+// per group, contiguous [C_in][C_out/groups][k...], into dst (the stride-1
+// input gradient's forward call).
+int launch_flip_weight(const conv_bwd_plan_t &p, const void *w, void *dst, void *stream);
 int launch_reduce(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *stream);
 
 }  // namespace miconv

@@ -475,6 +475,49 @@ int launch_fill_zero(void *out, const conv_tensor &t, void *stream)
     return hipGetLastError() == hipSuccess ? CONV_OK : CONV_EDEVICE;
 }
 
+// The stride-1 input gradient's weight: element (ci, o, t0, t1) of the
+// contiguous [C_in][Cog][K0][K1] copy is w[g*Cog + o][i][K0-1-t0][K1-1-t1]
+// with ci = g*Cig + i (K1 = 1 for 1-D), bits copied unchanged.
+template <typename U>
+__global__ void flip_weight_kernel(const U *__restrict__ w, U *__restrict__ out, int64_t count, int32_t Cig,
+                                   int32_t Cog, int32_t K0, int32_t K1, int64_t ws0, int64_t ws1, int64_t ws2,
+                                   int64_t ws3)
+{
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += (int64_t)gridDim.x * blockDim.x) {
+        int64_t r = e;
+        const int t1 = (int)(r % K1);
+        r /= K1;
+        const int t0 = (int)(r % K0);
+        r /= K0;
+        const int o = (int)(r % Cog);
+        const int64_t ci = r / Cog;
+        const int64_t g = ci / Cig, i = ci % Cig;
+        out[e] = w[(g * Cog + o) * ws0 + i * ws1 + (int64_t)(K0 - 1 - t0) * ws2 + (int64_t)(K1 - 1 - t1) * ws3];
+    }
+}
+
+int launch_flip_weight(const conv_bwd_plan_t &p, const void *w, void *dst, void *stream)
+{
+    const conv_desc &d = p.d;
+    const bool two = d.spatial == 2;
+    const int32_t Cig = (int32_t)(d.C_in / d.groups), Cog = (int32_t)(d.C_out / d.groups);
+    const int32_t K0 = (int32_t)d.k[0], K1 = two ? (int32_t)d.k[1] : 1;
+    const int64_t count = d.C_in * (int64_t)Cog * K0 * K1;
+    if (count == 0) return CONV_OK;
+    const int64_t ws2 = d.w.strides[2], ws3 = two ? d.w.strides[3] : 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(count, 256), 4096);
+    if (esize(d.dtype) == 4)
+        hipLaunchKernelGGL((flip_weight_kernel<uint32_t>), dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint32_t *>(w), static_cast<uint32_t *>(dst), count, Cig, Cog, K0, K1,
+                           d.w.strides[0], d.w.strides[1], ws2, ws3);
+    else
+        hipLaunchKernelGGL((flip_weight_kernel<uint16_t>), dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(w), static_cast<uint16_t *>(dst), count, Cig, Cog, K0, K1,
+                           d.w.strides[0], d.w.strides[1], ws2, ws3);
+    return hipGetLastError() == hipSuccess ? CONV_OK : CONV_EDEVICE;
+}
+
 int launch_wgrad(const conv_bwd_plan_t &p, const void *x, const void *gy, void *dw, void *ws, void *stream)
 {
     const conv_desc &d = p.d;

@@ -274,8 +274,9 @@ typedef struct conv_bwd_plan_t {
     conv_tensor dx;                   /* batched input gradient (layout of conv_backward_layout) */
     conv_tensor dw;                   /* weight gradient: w's sizes, dense in w's memory format */
     conv_tensor db;                   /* [C_out] contiguous, or rank 0 */
-    int32_t need_dx, need_dw, need_db, reserved0;
-    conv_plan_t dgrad;                /* the adjoint call that computes dx */
+    int32_t need_dx, need_dw, need_db;
+    int32_t dgrad_flip;               /* 1: dgrad reads the weight reversed from the workspace (below) */
+    conv_plan_t dgrad;                /* the call that computes dx */
     int64_t wg_tile[8];               /* weight-gradient schedule */
     int64_t db_splits;                /* ranges of positions of the bias gradient */
     int64_t workspace_bytes;          /* device scratch conv_run_backward needs */
@@ -309,7 +310,14 @@ MICONV_API int conv_backward_layout(const conv_desc *d, const conv_tensor *gy, c
  *
  *   dx = the adjoint call of gy: for a forward call the transposed call
  *        with output_padding (L + pb + pa - dil(k-1) - 1) mod s, for a
- *        transposed call the forward call; planned by conv_plan.
+ *        transposed call the forward call; planned by conv_plan.  A forward
+ *        call of stride 1 with at most 8 output channels per group (r <= 2)
+ *        instead gets dgrad = the forward call of gy with padding
+ *        ((k-1)dil - pb, (k-1)dil - pa) on the weight reversed along every
+ *        tap dim with its two channel dims exchanged per group, a contiguous
+ *        [C_in][C_out/groups][k...] copy that conv_run_backward writes at the
+ *        start of the workspace (dgrad_flip = 1), when conv_plan sends that
+ *        call to a stencil kernel.
  *   dw[g*PC + a, b, t] = sum over positions m of P[m, g*PC + a] *
  *        Q[m*s - pb + t*dil, g*QC + b] with (P, Q) = (gy, x) for a forward
  *        call and (x, gy) for a transposed one.

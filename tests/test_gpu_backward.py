@@ -180,3 +180,45 @@ def test_misaligned_operands_use_the_simple_weight_gradient():
     f = lambda t: t.detach().double().cpu().contiguous().numpy()
     _, _, rdw, Adw, _, _ = oracle.conv_backward(f(x), f(w), f(gy), **expand_kw(wl))
     _close(dw, rdw, Adw, EPS["f16"], "misaligned dw")
+
+
+def _flip_cases():
+    """Stride-1 calls whose input gradient runs as the forward call of gy
+    with the reversed, channel-exchanged weight on the stencils: depthwise
+    channels-last 3x3 / 5x5 / 7x7 (asymmetric padding), channel multiplier 2,
+    few-channel grouped NCHW, 1-D NLC and fp32 NCHW."""
+    mk = synth.random_case
+    return [
+        mk(8700, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=64, C_out=64, groups=64,
+           L=[17, 23], k=[5, 5], stride=[1, 1], padding_before=[2, 2], padding_after=[2, 2], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+        mk(8701, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=64, C_out=64, groups=64,
+           L=[16, 19], k=[7, 7], stride=[1, 1], padding_before=[3, 3], padding_after=[3, 3], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+        mk(8702, rank=2, transposed=False, dtype="f16", channels_last=True, N=2, C_in=32, C_out=32, groups=32,
+           L=[13, 11], k=[3, 3], stride=[1, 1], padding_before=[0, 2], padding_after=[2, 1], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+        mk(8703, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=32, C_out=64, groups=32,
+           L=[12, 14], k=[3, 3], stride=[1, 1], padding_before=[1, 1], padding_after=[1, 1], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+        mk(8704, rank=2, transposed=False, dtype="f16", channels_last=False, N=2, C_in=32, C_out=64, groups=8,
+           L=[14, 14], k=[3, 3], stride=[1, 1], padding_before=[1, 1], padding_after=[1, 1], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+        mk(8705, rank=1, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=48, C_out=48, groups=48,
+           L=[40], k=[7], stride=[1], padding_before=[3], padding_after=[3], dilation=[1], output_padding=[0],
+           has_bias=False),
+        mk(8706, rank=2, transposed=False, dtype="f32", channels_last=False, N=1, C_in=16, C_out=16, groups=16,
+           L=[20, 18], k=[3, 3], stride=[1, 1], padding_before=[1, 1], padding_after=[1, 1], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+    ]
+
+
+@pytest.mark.parametrize("wl", _flip_cases(), ids=lambda w: w.name)
+def test_stride1_input_gradient_on_the_stencils(wl):
+    """dx of stride-1 depthwise and few-channel grouped calls: the reversed
+    weight copied into the workspace, then the forward stencil on gy; every
+    element against the reference, and dw / db alongside."""
+    print(f"flipped-weight input gradient: {_desc(wl)}", flush=True)
+    prep, _ = check_backward(wl, seed=6)
+    assert int(prep.plan.dgrad_flip) == 1
+    assert api.kernel_name(prep.plan.dgrad.kernel) in ("dw_cl", "plane", "grp", "reduce")
