@@ -279,11 +279,25 @@ extern "C" int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int
         const bool cm_p = channel_major(P, PC), cm_q = channel_major(Q, QC);
         const bool pm_ok = Elast % 8 == 0;
         bool mfma = d->dtype != CONV_F32 && PC >= 32 && QC >= 32 && (cm_p || pm_ok) && (cm_q || pm_ok);
-        const int64_t mode = mfma ? (1 | (cm_p ? 0 : 2) | (cm_q ? 0 : 4)) : 0;
+        // Depthwise on channels-last 16-bit operands: the stencil over channel
+        // words (every stride of both operands even, so words stay aligned).
+        auto words = [&](const conv_tensor &t) {
+            bool ok = t.strides[1] == 1 && span_bytes(t, es) < kI32 - 4096;
+            for (int i = 0; i < t.rank && ok; ++i) ok = i == 1 || t.strides[i] % 2 == 0;
+            return ok;
+        };
+        const bool dwk = !tr && d->dtype != CONV_F32 && d->spatial <= 2 && PC == 1 && QC == 1 &&
+                         d->groups == d->C_in && d->C_in % 2 == 0 && T <= 88 && words(P) && words(Q);
+        if (dwk) mfma = false;
+        const int64_t mode = dwk ? WB_DW : mfma ? (1 | (cm_p ? 0 : 2) | (cm_q ? 0 : 4)) : 0;
         const int64_t apad = mfma ? round_up(PC, 128) : PC, bpad = mfma ? round_up(QC, 128) : QC;
         const int64_t steps = std::max<int64_t>(1, cdiv(M, 32));
         int64_t splits;
-        if (mfma) {
+        if (dwk) {
+            // Ranges of rows (image, output row), about 1024 workgroups.
+            const int64_t rows = d->N * (d->spatial == 2 ? d->out[0] : 1);
+            splits = std::max<int64_t>(1, std::min<int64_t>(rows, cdiv(1024, cdiv(d->C_in, 64))));
+        } else if (mfma) {
             const int64_t tiles = d->groups * T * (apad / 128) * (bpad / 128);
             splits = std::max<int64_t>(1, std::min<int64_t>(steps / 4 > 0 ? steps / 4 : 1, cdiv(1024, tiles)));
         } else {
@@ -355,10 +369,12 @@ extern "C" int conv_run_backward(const conv_bwd_plan_t *p, const void *x, const 
             // No terms: the gradient is zero.
             st = launch_fill_zero(dw, p->dw, stream);
         } else {
-            // 16-byte loads need aligned operands; otherwise the simple kernel.
+            // 16-byte loads (4-byte words for the depthwise stencil) need
+            // aligned operands; otherwise the simple kernel.
             conv_bwd_plan_t q = *p;
-            if ((q.wg_tile[WB_MFMA] & 6) != 6 && q.wg_tile[WB_MFMA] &&
-                ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(gy)) & 15)) {
+            const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(gy);
+            if ((q.wg_tile[WB_MFMA] == WB_DW && (al & 3)) ||
+                (q.wg_tile[WB_MFMA] != WB_DW && (q.wg_tile[WB_MFMA] & 6) != 6 && q.wg_tile[WB_MFMA] && (al & 15))) {
                 q.wg_tile[WB_MFMA] = 0;
                 q.wg_tile[WB_APAD] = d.transposed ? d.C_in / d.groups : d.C_out / d.groups;
                 q.wg_tile[WB_BPAD] = d.transposed ? d.C_out / d.groups : d.C_in / d.groups;

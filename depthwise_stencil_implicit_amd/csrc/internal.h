@@ -121,10 +121,13 @@ enum { DW_CW = 0, DW_OCOLS = 1, DW_CHCHUNKS = 2, DW_COLCHUNKS = 3, DW_XBYTES = 4
        DW_RPB = 7 };
 
 // Weight-gradient schedule fields (conv_bwd_plan_t.wg_tile[]): WB_MFMA is 0
-// for the simple kernel, else 1 | 2 (P read position-major) | 4 (Q read
+// for the simple kernel, WB_DW for the depthwise stencil (channel words of
+// channels-last operands), else 1 | 2 (P read position-major) | 4 (Q read
 // position-major) for the matrix-core one; padded a / b extents, ranges of
-// positions, and the byte ranges of the two operands for the 16-byte loads.
+// positions (of rows of positions for WB_DW), and the byte ranges of the two
+// operands for the 16-byte loads.
 enum { WB_MFMA = 0, WB_APAD = 1, WB_BPAD = 2, WB_SPLITS = 3, WB_PBYTES = 4, WB_QBYTES = 5 };
+constexpr int64_t WB_DW = 8;
 
 // Launchers (defined in the .hip files).  `vec` selects the 16-byte path.
 int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *ws,

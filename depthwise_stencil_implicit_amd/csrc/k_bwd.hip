@@ -27,6 +27,11 @@
 //                 current one is multiplied.
 //   wgrad_simple  any dtype and layout: one thread per weight element and
 //                 range of m, fp32 sums.
+//   wgrad_dw      depthwise, 16-bit, channels-last x and gy: a workgroup owns
+//                 32 channel words (64 channels) and one range of rows (n,
+//                 output row); thread = one channel word x one of 8 tap groups
+//                 (taps tg, tg + 8, ...), looping over the row's positions:
+//                 one gy word, then one x word per tap, two fp32 FMAs each.
 //   bgrad         per-channel sums of gy over one range of positions.
 //   bwd_reduce    sums the fp32 partial sums of the ranges, rounds once to
 //                 the dtype and stores at the gradient's strides.
@@ -390,6 +395,93 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(RdArgs a)
 
 namespace {
 
+// Depthwise weight gradient, channel words: dw[c, t] = sum over (n, e1, e2)
+// of gy[n, e1, e2, c] * x[n, e1*S1 - PB1 + kh*D1, e2*S2 - PB2 + kw*D2, c] for
+// tap t = (kh, kw), in the slots 1 and 2 of WgArgs (slot 0 has extent 1).
+// Partial sums per range of rows go to part[sp][c][t] (apad = bpad = 1).
+template <typename T, int MT>
+__global__ __launch_bounds__(256) void wgrad_dw_kernel(WgArgs a)
+{
+    const int tid = threadIdx.x;
+    const int wd = tid & 31, tg = tid >> 5;
+    const int cchunks = (a.G + 63) / 64;
+    const int cc = blockIdx.x % cchunks, sp = blockIdx.x / cchunks;
+    const int word = cc * 32 + wd;
+    const bool cok = 2 * word < a.G;
+    const int KW = a.K[2];
+    int dh[MT], dwo[MT];
+    bool tv[MT];
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+        const int t = tg + 8 * j;
+        tv[j] = t < a.T;
+        dh[j] = tv[j] ? (t / KW) * a.D[1] : 0;
+        dwo[j] = tv[j] ? (t % KW) * a.D[2] : 0;
+    }
+    float acc[MT][2];
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[j][0] = acc[j][1] = 0.f;
+    const int64_t rows = (int64_t)a.N * a.E[1];
+    const int64_t r0 = rows * sp / a.splits, r1 = rows * (sp + 1) / a.splits;
+    const uint32_t *P = static_cast<const uint32_t *>(a.P);
+    const uint32_t *Q = static_cast<const uint32_t *>(a.Q);
+    for (int64_t r = r0; r < r1 && cok; ++r) {
+        const int n = (int)(r / a.E[1]), e1 = (int)(r % a.E[1]);
+        const int64_t pbase = ((int64_t)n * a.ps_n + (int64_t)e1 * a.ps_l[1]) / 2 + word;
+        const int ih0 = e1 * a.S[1] - a.PB[1];
+        int64_t qrow[MT];
+        bool hok[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            const int ih = ih0 + dh[j];
+            hok[j] = tv[j] && (unsigned)ih < (unsigned)a.F[1];
+            qrow[j] = hok[j] ? ((int64_t)n * a.qs_n + (int64_t)ih * a.qs_l[1]) / 2 + word : 0;
+        }
+        for (int e2 = 0; e2 < a.E[2]; ++e2) {
+            const uint32_t g = P[pbase + (int64_t)e2 * (a.ps_l[2] / 2)];
+            const float g0 = lo_f32(g, T{}), g1 = hi_f32(g, T{});
+            const int iw0 = e2 * a.S[2] - a.PB[2];
+            uint32_t xv[MT];
+#pragma unroll
+            for (int j = 0; j < MT; ++j) {
+                const int iw = iw0 + dwo[j];
+                const bool ok = hok[j] && (unsigned)iw < (unsigned)a.F[2];
+                xv[j] = ok ? Q[qrow[j] + (int64_t)iw * (a.qs_l[2] / 2)] : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < MT; ++j) {
+                acc[j][0] = __builtin_fmaf(g0, lo_f32(xv[j], T{}), acc[j][0]);
+                acc[j][1] = __builtin_fmaf(g1, hi_f32(xv[j], T{}), acc[j][1]);
+            }
+        }
+    }
+    if (!cok) return;
+    float *part = a.part + (int64_t)sp * a.G * a.T;
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+        if (!tv[j]) continue;
+        const int t = tg + 8 * j;
+        part[(int64_t)(2 * word) * a.T + t] = acc[j][0];
+        part[(int64_t)(2 * word + 1) * a.T + t] = acc[j][1];
+    }
+}
+
+template <typename T>
+hipError_t launch_wgrad_dw(const WgArgs &a, hipStream_t s)
+{
+    if constexpr (Dt<T>::size == 2) {
+        const dim3 blocks((unsigned)(((a.G + 63) / 64) * (int64_t)a.splits));
+        const int mt = (a.T + 7) / 8;
+        if (mt <= 2) hipLaunchKernelGGL((wgrad_dw_kernel<T, 2>), blocks, dim3(256), 0, s, a);
+        else if (mt <= 4) hipLaunchKernelGGL((wgrad_dw_kernel<T, 4>), blocks, dim3(256), 0, s, a);
+        else if (mt <= 7) hipLaunchKernelGGL((wgrad_dw_kernel<T, 7>), blocks, dim3(256), 0, s, a);
+        else if (mt <= 11) hipLaunchKernelGGL((wgrad_dw_kernel<T, 11>), blocks, dim3(256), 0, s, a);
+        else return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
 template <typename T>
 hipError_t launch_wgrad_t(const WgArgs &a, bool mfma, bool pm_p, bool pm_q, hipStream_t s)
 {
@@ -563,13 +655,14 @@ int launch_wgrad(const conv_bwd_plan_t &p, const void *x, const void *gy, void *
     a.M = (int64_t)d.N * a.E[0] * a.E[1] * a.E[2];
     a.p_bytes = (int32_t)p.wg_tile[WB_PBYTES];
     a.q_bytes = (int32_t)p.wg_tile[WB_QBYTES];
-    const bool mfma = p.wg_tile[WB_MFMA] != 0;
+    const bool dwk = p.wg_tile[WB_MFMA] == WB_DW;
+    const bool mfma = p.wg_tile[WB_MFMA] != 0 && !dwk;
     const bool pm_p = (p.wg_tile[WB_MFMA] & 2) != 0, pm_q = (p.wg_tile[WB_MFMA] & 4) != 0;
     hipError_t e;
     switch (d.dtype) {
     case CONV_F32: e = launch_wgrad_t<float>(a, false, false, false, s); break;
-    case CONV_F16: e = launch_wgrad_t<f16_t>(a, mfma, pm_p, pm_q, s); break;
-    default: e = launch_wgrad_t<bf16_t>(a, mfma, pm_p, pm_q, s); break;
+    case CONV_F16: e = dwk ? launch_wgrad_dw<f16_t>(a, s) : launch_wgrad_t<f16_t>(a, mfma, pm_p, pm_q, s); break;
+    default: e = dwk ? launch_wgrad_dw<bf16_t>(a, s) : launch_wgrad_t<bf16_t>(a, mfma, pm_p, pm_q, s); break;
     }
     if (e != hipSuccess) return CONV_EDEVICE;
     RdArgs r;

@@ -381,14 +381,21 @@ def test_gradient_layouts_of_the_workloads():
 def test_gradient_schedules():
     """The dense call's weight gradient runs on the matrix cores with both
     operands channel-major; the transposed 1-D call's with its contiguous gy
-    read position-major; depthwise weight gradients use the simple kernel;
-    the input gradient of a forward call is a transposed call and vice versa."""
+    read position-major; channels-last 16-bit depthwise weight gradients use
+    the depthwise stencil (mode 8) and fp32 NCHW ones the simple kernel; the
+    input gradient of a forward call is a transposed call and vice versa,
+    except stride-1 stencil calls, whose dx is a forward call on the reversed
+    weight."""
     _, _, dense = _bwd(synth.dense_bf16_cl())
     assert dense.plan.wg_tile[0] == 1 and api.kernel_name(dense.plan.dgrad.kernel) == "igemm_t"
     _, _, tr = _bwd(synth.transposed_bf16_nlc())
     assert tr.plan.wg_tile[0] == 1 | 4 and api.kernel_name(tr.plan.dgrad.kernel) == "igemm"
     _, _, dw = _bwd(synth.depthwise_bf16_cl(3, 1))
-    assert dw.plan.wg_tile[0] == 0
+    assert dw.plan.wg_tile[0] == 8 and dw.plan.dgrad_flip == 1 and api.kernel_name(dw.plan.dgrad.kernel) == "dw_cl"
+    _, _, dw2 = _bwd(synth.depthwise_bf16_cl(5, 2))
+    assert dw2.plan.wg_tile[0] == 8 and dw2.plan.dgrad_flip == 0
+    _, _, small = _bwd(synth.depthwise_f32_small())
+    assert small.plan.wg_tile[0] == 0 and small.plan.dgrad_flip == 1
     assert dense.plan.flops[1] == dense.plan.flops[0] == 2 * 200704 * 256 * 2304
     assert dense.plan.workspace_bytes >= dense.plan.wg_tile[3] * 9 * 256 * 256 * 4
 

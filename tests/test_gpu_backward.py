@@ -222,3 +222,34 @@ def test_stride1_input_gradient_on_the_stencils(wl):
     prep, _ = check_backward(wl, seed=6)
     assert int(prep.plan.dgrad_flip) == 1
     assert api.kernel_name(prep.plan.dgrad.kernel) in ("dw_cl", "plane", "grp", "reduce")
+
+
+def _dw_wgrad_cases():
+    """Depthwise weight gradients on the channel-word stencil: channel counts
+    that are not multiples of its 64-channel workgroups, strides 1-2,
+    dilation, asymmetric padding, 1x7 to 9x9 (up to 11 taps per thread)."""
+    mk = synth.random_case
+    return [
+        mk(8800, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=40, C_out=40, groups=40,
+           L=[15, 17], k=[3, 3], stride=[2, 2], padding_before=[0, 1], padding_after=[1, 1], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+        mk(8801, rank=2, transposed=False, dtype="f16", channels_last=True, N=3, C_in=96, C_out=96, groups=96,
+           L=[14, 12], k=[5, 3], stride=[1, 2], padding_before=[2, 1], padding_after=[2, 0], dilation=[2, 1],
+           output_padding=[0, 0], has_bias=False),
+        mk(8802, rank=2, transposed=False, dtype="bf16", channels_last=True, N=1, C_in=130, C_out=130, groups=130,
+           L=[20, 21], k=[9, 9], stride=[1, 1], padding_before=[4, 4], padding_after=[4, 4], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+        mk(8803, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=64, C_out=64, groups=64,
+           L=[6, 50], k=[1, 7], stride=[1, 2], padding_before=[0, 2], padding_after=[0, 3], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+    ]
+
+
+@pytest.mark.parametrize("wl", _dw_wgrad_cases(), ids=lambda w: w.name)
+def test_depthwise_weight_gradient_stencil(wl):
+    """Every element of dw (and db) against the reference, on the depthwise
+    weight-gradient stencil (fp32 partial sums per range of rows, reduced
+    and rounded once)."""
+    print(f"depthwise weight gradient: {_desc(wl)}", flush=True)
+    prep, _ = check_backward(wl, seed=7, need=(False, True, True))
+    assert int(prep.plan.wg_tile[0]) == 8
