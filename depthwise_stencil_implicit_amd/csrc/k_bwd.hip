@@ -335,17 +335,50 @@ __global__ __launch_bounds__(256) void bgrad_kernel(BgArgs a)
     const int sp = blockIdx.x / chunks, ck = blockIdx.x % chunks;
     const int c = ck * 64 + (threadIdx.x & 63), grp = threadIdx.x >> 6;
     const int64_t per = (a.M + a.splits - 1) / a.splits;
-    const int64_t lo = per * sp, hi = std::min<int64_t>(lo + per, a.M);
+    const int64_t lo0 = per * sp, hi0 = std::min<int64_t>(lo0 + per, a.M);
+    // The four wave groups take consecutive quarters of the range, so each
+    // lane walks its positions in order: the position is decomposed once and
+    // then advanced (no division per element); the 64 lanes of a wave read
+    // 64 channels of one position.
+    const int64_t q = (std::max<int64_t>(hi0 - lo0, 0) + 3) / 4;
+    const int64_t lo = std::min<int64_t>(lo0 + q * grp, hi0), hi = std::min<int64_t>(lo + q, hi0);
     const T *__restrict__ G = static_cast<const T *>(a.gy);
     const int64_t O12 = (int64_t)a.O[1] * a.O[2], O012 = O12 * a.O[0];
     float sum = 0.f;
-    if (c < a.C)
-        for (int64_t m = lo + grp; m < hi; m += 4) {
-            const int64_t n = m / O012, r = m - n * O012;
-            const int64_t o0 = r / O12, r2 = r - o0 * O12;
-            const int64_t o1 = r2 / a.O[2], o2 = r2 - o1 * a.O[2];
-            sum += to_f32(G[n * a.gs_n + (int64_t)c * a.gs_c + o0 * a.gs_l[0] + o1 * a.gs_l[1] + o2 * a.gs_l[2]]);
+    if (c < a.C && lo < hi) {
+        const int64_t n = lo / O012, r = lo - n * O012;
+        int o0 = (int)(r / O12);
+        const int64_t r2 = r - (int64_t)o0 * O12;
+        int o1 = (int)(r2 / a.O[2]), o2 = (int)(r2 - (int64_t)o1 * a.O[2]);
+        int64_t off = n * a.gs_n + (int64_t)c * a.gs_c + o0 * a.gs_l[0] + o1 * a.gs_l[1] + o2 * a.gs_l[2];
+        auto advance = [&]() {
+            if (++o2 < a.O[2]) { off += a.gs_l[2]; return; }
+            o2 = 0;
+            off -= (int64_t)(a.O[2] - 1) * a.gs_l[2];
+            if (++o1 < a.O[1]) { off += a.gs_l[1]; return; }
+            o1 = 0;
+            off -= (int64_t)(a.O[1] - 1) * a.gs_l[1];
+            if (++o0 < a.O[0]) { off += a.gs_l[0]; return; }
+            o0 = 0;
+            off += a.gs_n - (int64_t)(a.O[0] - 1) * a.gs_l[0];
+        };
+        int64_t m = lo;
+        for (; m + 4 <= hi; m += 4) {
+            // Four loads in flight before the adds.
+            T v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v[u] = G[off];
+                advance();
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sum += to_f32(v[u]);
         }
+        for (; m < hi; ++m) {
+            sum += to_f32(G[off]);
+            advance();
+        }
+    }
     red[grp][threadIdx.x & 63] = sum;
     __syncthreads();
     if (grp == 0 && c < a.C)

@@ -822,6 +822,108 @@ __global__ __launch_bounds__(256) void dwm_kernel(DwgArgs a)
 
 namespace {
 
+// Transposed depthwise calls (multiplier 1, dilation 1) on the same lane
+// layout: output o reads input (o + pb - t)/s at tap t when the quotient is an
+// exact integer inside the input, per dim (executorch PR #25091 description,
+// second paragraph).  Lane = one word of channels (two 16-bit or one fp32) x
+// DWG_TO consecutive output columns of one output row.  With the column
+// stride S (1 or 2) dividing DWG_TO, every lane's first column is a multiple
+// of S, so the phase (o + pb) mod S of each of its columns is fixed by the
+// launch's PHW = pb mod S: which (column, tap) pairs meet, and at which input
+// column of the lane's window, is decided at compile time.  Rows are
+// uniform over the workgroup: a kernel row whose numerator is not a multiple
+// of the row stride, or that falls outside the input, is skipped.  Element
+// loads and stores (no alignment beyond the element), fp32 accumulation from
+// the bias, one rounding.
+__host__ __device__ constexpr int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+template <typename T, int KB, int S, int PHW>
+__global__ __launch_bounds__(256) void dwt_kernel(DwgArgs a)
+{
+    constexpr int V = Dt<T>::size == 2 ? 2 : 1;
+    constexpr int TO = DWG_TO;
+    static_assert(TO % S == 0, "column phase");
+    constexpr int JMIN = floor_div(PHW - (KB - 1), S), JMAX = floor_div(TO - 1 + PHW, S);
+    constexpr int NX = JMAX - JMIN + 1;          // input columns of the lane's window
+    const int tid = threadIdx.x, cl = tid & 31, st = tid >> 5;
+    int b = blockIdx.x;
+    const int chb = b % a.ch_blocks;
+    b /= a.ch_blocks;
+    const int cb = b % a.col_blocks;
+    b /= a.col_blocks;
+    const int oh = b % a.OH;
+    const int n = b / a.OH;
+    const int co0 = (chb * 32 + cl) * V;
+    const int ow0 = (cb * 8 + st) * TO;
+    if (co0 >= a.Cout || ow0 >= a.OW) return;
+    const int nv = min(V, a.Cout - co0);
+    const T *__restrict__ X = static_cast<const T *>(a.x) + (int64_t)n * a.xs_n + co0;
+    const T *__restrict__ Wt = static_cast<const T *>(a.w);
+    const T *__restrict__ Bp = static_cast<const T *>(a.b);
+    float acc[TO][V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const float bv = (a.has_bias && v < nv) ? to_f32(Bp[co0 + v]) : 0.f;
+#pragma unroll
+        for (int t = 0; t < TO; ++t) acc[t][v] = bv;
+    }
+    const int base = (ow0 + a.PW - PHW) / S + JMIN;   // first input column of the window
+    for (int kh = 0; kh < a.KH; ++kh) {
+        const int num = oh + a.PH - kh;
+        if (num < 0 || num % a.SH) continue;
+        const int ih = num / a.SH;
+        if (ih >= a.H) continue;
+        float wv[KB][V], xw[NX][V];
+#pragma unroll
+        for (int kw = 0; kw < KB; ++kw)
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                wv[kw][v] = (kw < a.KW && v < nv)
+                                ? to_f32(Wt[(int64_t)(co0 + v) * a.ws0 + (int64_t)kh * a.ws2 + (int64_t)kw * a.ws3])
+                                : 0.f;
+        const T *xr = X + (int64_t)ih * a.xs_h;
+#pragma unroll
+        for (int j = 0; j < NX; ++j) {
+            const int iw = base + j;
+            const bool ok = (unsigned)iw < (unsigned)a.W;
+#pragma unroll
+            for (int v = 0; v < V; ++v) xw[j][v] = (ok && v < nv) ? to_f32(xr[(int64_t)iw * a.xs_w + v]) : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < TO; ++t)
+#pragma unroll
+            for (int kw = 0; kw < KB; ++kw) {
+                if (((t + PHW - kw) % S + S) % S != 0) continue;
+                const int j = floor_div(t + PHW - kw, S) - JMIN;
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[t][v] = __builtin_fmaf(xw[j][v], wv[kw][v], acc[t][v]);
+            }
+    }
+    T *__restrict__ Y = static_cast<T *>(a.y) + (int64_t)n * a.ys_n + (int64_t)oh * a.ys_h + (int64_t)co0 * a.ys_c;
+#pragma unroll
+    for (int t = 0; t < TO; ++t) {
+        const int ow = ow0 + t;
+        if (ow >= a.OW) break;
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (v < nv) Y[(int64_t)ow * a.ys_w + (int64_t)v * a.ys_c] = from_f32<T>(acc[t][v]);
+    }
+}
+
+template <typename T>
+hipError_t dwt_go(const DwgArgs &a, dim3 grid, hipStream_t s)
+{
+    const int kb = a.KW <= 3 ? 3 : (a.KW <= 5 ? 5 : (a.KW <= 7 ? 7 : 9));
+    const int ph = a.PW % a.SW;
+#define MICONV_DWT(KB_, S_, P_) \
+    if (kb == KB_ && a.SW == S_ && ph == P_) hipLaunchKernelGGL((dwt_kernel<T, KB_, S_, P_>), grid, dim3(256), 0, s, a); else
+    MICONV_DWT(3, 1, 0) MICONV_DWT(5, 1, 0) MICONV_DWT(7, 1, 0) MICONV_DWT(9, 1, 0)
+    MICONV_DWT(3, 2, 0) MICONV_DWT(5, 2, 0) MICONV_DWT(7, 2, 0) MICONV_DWT(9, 2, 0)
+    MICONV_DWT(3, 2, 1) MICONV_DWT(5, 2, 1) MICONV_DWT(7, 2, 1) MICONV_DWT(9, 2, 1) return hipErrorInvalidValue;
+#undef MICONV_DWT
+    return hipGetLastError();
+}
+
 template <typename T, bool WX>
 hipError_t dwg_go(const DwgArgs &a, dim3 grid, hipStream_t s)
 {
@@ -882,6 +984,15 @@ int launch_dwg(const conv_plan_t &p, const void *x, const void *w, const void *b
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)p.grid[0]);
+    if (d.transposed) {
+        hipError_t e;
+        switch (d.dtype) {
+        case CONV_F32: e = dwt_go<float>(a, grid, s); break;
+        case CONV_F16: e = dwt_go<f16_t>(a, grid, s); break;
+        default: e = dwt_go<bf16_t>(a, grid, s); break;
+        }
+        return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
+    }
     // Word loads of x: multiplier 1 with 16-bit channel pairs on 4-byte
     // boundaries of x.
     const bool wx = a.M == 1 && esize(d.dtype) == 2 && (reinterpret_cast<uintptr_t>(x) & 3) == 0 && d.C_in % 2 == 0 &&

@@ -14,7 +14,9 @@
 // transposed gather.
 //
 // Routing (host only, deterministic):
-//   transposed                                        -> IGEMM_T
+//   transposed depthwise (multiplier 1, dil 1, k <= 9, r <= 2, column
+//     stride <= 2), channel-contiguous x              -> DW_CL (generic)
+//   other transposed                                  -> IGEMM_T
 //   r <= 2, dil 1, k <= 9, groups > 1, Cig <= 8:
 //       few outputs (<= 4 positions, >= 32 taps each) -> REDUCE
 //       depthwise, channel-contiguous x and y          -> DW_CL
@@ -127,6 +129,22 @@ bool dwcl_generic_ok(const conv_desc &d, const conv_tensor &y)
     return y.strides[y.rank - 1] == 1;
 }
 
+// The transposed generic schedule: transposed depthwise calls with
+// multiplier 1, dilation 1, kernels up to 9 wide, column stride 1 or 2 (any
+// row stride), 1-D or 2-D, channel-contiguous x, y at any non-negative
+// strides (element stores).
+bool dwcl_tgeneric_ok(const conv_desc &d, const conv_tensor &y)
+{
+    if (!d.transposed || (d.spatial != 1 && d.spatial != 2) || !all_dil1(d) || !k_le(d, 9)) return false;
+    if (d.groups != d.C_in || d.C_out != d.C_in) return false;
+    if (d.stride[d.spatial - 1] > 2) return false;
+    if (d.x.strides[1] != 1) return false;
+    for (const conv_tensor *t : {&d.x, &d.w, &y})
+        for (int i = 0; i < t->rank; ++i)
+            if (t->strides[i] < 0) return false;
+    return true;
+}
+
 // The ring kernels: multiplier 1, a compiled square (k, s) schedule.
 bool dwcl_ring_ok(const conv_desc &d, const conv_tensor &y)
 {
@@ -143,7 +161,10 @@ bool dwcl_ring_ok(const conv_desc &d, const conv_tensor &y)
     return span_bytes(d.x, esize(d.dtype)) <= kI32 - 4096 && span_bytes(y, esize(d.dtype)) <= kI32 - 4096;
 }
 
-bool supports_dwcl(const conv_desc &d, const conv_tensor &y) { return dwcl_ring_ok(d, y) || dwcl_generic_ok(d, y); }
+bool supports_dwcl(const conv_desc &d, const conv_tensor &y)
+{
+    return dwcl_ring_ok(d, y) || dwcl_generic_ok(d, y) || dwcl_tgeneric_ok(d, y);
+}
 
 bool supports_plane(const conv_desc &d) { return stencil_domain(d); }
 
@@ -161,7 +182,7 @@ bool few_outputs(const conv_desc &d)
 
 int route(const conv_desc &d, const conv_tensor &y)
 {
-    if (d.transposed) return CONV_K_IGEMM_T;
+    if (d.transposed) return dwcl_tgeneric_ok(d, y) ? CONV_K_DW_CL : CONV_K_IGEMM_T;
     if (stencil_domain(d) && all_dil1(d) && d.groups > 1) {
         if (few_outputs(d)) return CONV_K_REDUCE;
         if (supports_dwcl(d, y)) return CONV_K_DW_CL;
@@ -557,7 +578,8 @@ extern "C" int conv_plan_ex(const conv_desc *d, const conv_tensor *y, const conv
     case CONV_K_DW_CL:
         // The ring kernels where they apply; the generic schedule otherwise
         // or when forced (the only selectable dw_cl schedule).
-        if (force_variant >= 0 && (force_variant != DWCL_GENERIC || !dwcl_generic_ok(*d, yb)))
+        if (force_variant >= 0 &&
+            (force_variant != DWCL_GENERIC || !(dwcl_generic_ok(*d, yb) || dwcl_tgeneric_ok(*d, yb))))
             return CONV_EUNSUPPORTED;
         geom_dwcl(*d, plan, force_variant == DWCL_GENERIC || !dwcl_ring_ok(*d, yb));
         break;

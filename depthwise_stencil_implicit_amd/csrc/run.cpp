@@ -72,8 +72,9 @@ extern "C" int conv_run(const conv_plan_t *p, const void *x, const void *w, cons
     switch (p->kernel) {
     case CONV_K_DW_CL:
         // Lanes move 4-byte channel words; a view that is not word-aligned
-        // runs on the layout-generic plane stencil instead.
-        if (!aligned(x, 4) || !aligned(y, 4)) {
+        // runs on the layout-generic plane stencil instead (the transposed
+        // schedule moves single elements).
+        if (!d.transposed && (!aligned(x, 4) || !aligned(y, 4))) {
             conv_tensor yc = p->y;
             if (d.unbatched) {
                 for (int i = 1; i < yc.rank; ++i) {

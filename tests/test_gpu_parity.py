@@ -1010,3 +1010,45 @@ def test_batch_spanning_2gib(kind):
         assert_close(y[n:n + 1], yr, A, EPS["bf16"], f"{kind} image {n}")
     del x, y
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------- transposed depthwise (dw_cl) --
+
+def _dwt_cases(n, seed):
+    """Transposed depthwise calls inside the transposed generic schedule's
+    domain: multiplier 1, dilation 1, kernels 1-9 (square or not), column
+    stride 1 or 2, row stride 1-3, asymmetric padding, output_padding, 1-D
+    and 2-D channels-last, every dtype, odd channel counts."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        i = len(out)
+        r = 1 + int(rng.integers(0, 4) > 0)
+        dtype = ["bf16", "f16", "f32"][i % 3]
+        C = int(rng.choice([3, 16, 37, 64, 130]))
+        k = [int(rng.integers(1, 10)) for _ in range(r)]
+        s = [int(rng.integers(1, 4)) for _ in range(r - 1)] + [int(rng.integers(1, 3))]
+        L = [int(rng.integers(2, 14)) for _ in range(r)]
+        pb = [int(rng.integers(0, ki)) for ki in k]
+        pa = [int(rng.integers(0, ki)) for ki in k]
+        op = [int(rng.integers(0, si)) for si in s]
+        if any((Li - 1) * si + ki + opi - pbi - pai < 1 for Li, si, ki, pbi, pai, opi in zip(L, s, k, pb, pa, op)):
+            continue
+        out.append(synth.random_case(9300 + i + 100 * seed, rank=r, transposed=True, dtype=dtype, channels_last=True,
+                                     N=int(rng.integers(1, 3)), C_in=C, C_out=C, groups=C, L=L, k=k, stride=s,
+                                     padding_before=pb, padding_after=pa, dilation=[1] * r, output_padding=op,
+                                     has_bias=bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("wl", _dwt_cases(16, 1), ids=lambda v: v.name)
+def test_transposed_depthwise_generic(wl):
+    """Transposed depthwise calls on the dw_cl transposed schedule (the
+    router's choice), whole output against the reference."""
+    _flush(f"transposed depthwise: {_desc(wl)}")
+    x, w, b = synth.make_inputs(wl, device="cuda")
+    kw = expand_kw(wl)
+    plan = api.Prepared(x, w, b, api.make_args(**{k: v for k, v in kw.items() if k not in ("groups", "transposed")},
+                                               groups=wl.groups, transposed=wl.transposed)).plan
+    assert api.kernel_name(plan.kernel) == "dw_cl" and int(plan.variant) == 2
+    check_full(wl)
