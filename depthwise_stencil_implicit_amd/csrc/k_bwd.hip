@@ -33,8 +33,9 @@
 //                 (taps tg, tg + 8, ...), looping over the row's positions:
 //                 one gy word, then one x word per tap, two fp32 FMAs each.
 //   bgrad         per-channel sums of gy over one range of positions.
-//   bwd_reduce    sums the fp32 partial sums of the ranges, rounds once to
-//                 the dtype and stores at the gradient's strides.
+//   bwd_reduce    sums the fp32 partial sums of the ranges (64 outputs x 4
+//                 interleaved quarters of the ranges per workgroup), rounds
+//                 once to the dtype and stores at the gradient's strides.
 #include "dev_common.h"
 #include "internal.h"
 
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(256) void bgrad_kernel(BgArgs a)
     // The four wave groups take consecutive quarters of the range, so each
     // lane walks its positions in order: the position is decomposed once and
     // then advanced (no division per element); the 64 lanes of a wave read
-    // 64 channels of one position.
+    // 64 channels of one position, 16 positions in flight.
     const int64_t q = (std::max<int64_t>(hi0 - lo0, 0) + 3) / 4;
     const int64_t lo = std::min<int64_t>(lo0 + q * grp, hi0), hi = std::min<int64_t>(lo + q, hi0);
     const T *__restrict__ G = static_cast<const T *>(a.gy);
@@ -363,16 +364,16 @@ __global__ __launch_bounds__(256) void bgrad_kernel(BgArgs a)
             off += a.gs_n - (int64_t)(a.O[0] - 1) * a.gs_l[0];
         };
         int64_t m = lo;
-        for (; m + 4 <= hi; m += 4) {
-            // Four loads in flight before the adds.
-            T v[4];
+        constexpr int LU = 16;   // loads in flight before the adds
+        for (; m + LU <= hi; m += LU) {
+            T v[LU];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < LU; ++u) {
                 v[u] = G[off];
                 advance();
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) sum += to_f32(v[u]);
+            for (int u = 0; u < LU; ++u) sum += to_f32(v[u]);
         }
         for (; m < hi; ++m) {
             sum += to_f32(G[off]);
@@ -398,12 +399,17 @@ struct RdArgs {
 };
 
 template <typename T>
+// Lane (o, q) of a workgroup: output e = 64 * block + o, summing the ranges
+// k = q, q + 4, ... with four independent partial sums (loads in flight);
+// the four quarter sums meet in LDS and lane q = 0 rounds once and stores.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(RdArgs a)
 {
+    __shared__ float red[4][64];
     T *__restrict__ out = static_cast<T *>(a.out);
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < a.count;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        int64_t src, dst;
+    const int o = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int64_t e = (int64_t)blockIdx.x * 64 + o;
+    int64_t src = 0, dst = 0;
+    if (e < a.count) {
         if (a.is_w) {
             int64_t r = e;
             const int b = (int)(r % a.QC);
@@ -420,10 +426,20 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(RdArgs a)
             src = e;
             dst = e * a.os0;
         }
-        float s = 0.f;
-        for (int k = 0; k < a.splits; ++k) s += a.part[(int64_t)k * a.plane + src];
-        out[dst] = from_f32<T>(s);
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+        const float *p = a.part + src;
+        int k = q;
+        for (; k + 12 < a.splits; k += 16) {
+            s0 += p[(int64_t)k * a.plane];
+            s1 += p[(int64_t)(k + 4) * a.plane];
+            s2 += p[(int64_t)(k + 8) * a.plane];
+            s3 += p[(int64_t)(k + 12) * a.plane];
+        }
+        for (; k < a.splits; k += 4) s0 += p[(int64_t)k * a.plane];
+        red[q][o] = (s0 + s1) + (s2 + s3);
     }
+    __syncthreads();
+    if (q == 0 && e < a.count) out[dst] = from_f32<T>((red[0][o] + red[1][o]) + (red[2][o] + red[3][o]));
 }
 
 namespace {
@@ -470,21 +486,31 @@ __global__ __launch_bounds__(256) void wgrad_dw_kernel(WgArgs a)
             hok[j] = tv[j] && (unsigned)ih < (unsigned)a.F[1];
             qrow[j] = hok[j] ? ((int64_t)n * a.qs_n + (int64_t)ih * a.qs_l[1]) / 2 + word : 0;
         }
-        for (int e2 = 0; e2 < a.E[2]; ++e2) {
-            const uint32_t g = P[pbase + (int64_t)e2 * (a.ps_l[2] / 2)];
-            const float g0 = lo_f32(g, T{}), g1 = hi_f32(g, T{});
-            const int iw0 = e2 * a.S[2] - a.PB[2];
-            uint32_t xv[MT];
+        // PU positions per pass: all their loads in flight before the FMAs.
+        constexpr int PU = MT <= 4 ? 4 : 2;
+        for (int e2b = 0; e2b < a.E[2]; e2b += PU) {
+            uint32_t g[PU], xv[PU][MT];
 #pragma unroll
-            for (int j = 0; j < MT; ++j) {
-                const int iw = iw0 + dwo[j];
-                const bool ok = hok[j] && (unsigned)iw < (unsigned)a.F[2];
-                xv[j] = ok ? Q[qrow[j] + (int64_t)iw * (a.qs_l[2] / 2)] : 0u;
+            for (int u = 0; u < PU; ++u) {
+                const int e2 = e2b + u;
+                const bool pok = e2 < a.E[2];
+                g[u] = pok ? P[pbase + (int64_t)e2 * (a.ps_l[2] / 2)] : 0u;
+                const int iw0 = e2 * a.S[2] - a.PB[2];
+#pragma unroll
+                for (int j = 0; j < MT; ++j) {
+                    const int iw = iw0 + dwo[j];
+                    const bool ok = pok && hok[j] && (unsigned)iw < (unsigned)a.F[2];
+                    xv[u][j] = ok ? Q[qrow[j] + (int64_t)iw * (a.qs_l[2] / 2)] : 0u;
+                }
             }
 #pragma unroll
-            for (int j = 0; j < MT; ++j) {
-                acc[j][0] = __builtin_fmaf(g0, lo_f32(xv[j], T{}), acc[j][0]);
-                acc[j][1] = __builtin_fmaf(g1, hi_f32(xv[j], T{}), acc[j][1]);
+            for (int u = 0; u < PU; ++u) {
+                const float g0 = lo_f32(g[u], T{}), g1 = hi_f32(g[u], T{});
+#pragma unroll
+                for (int j = 0; j < MT; ++j) {
+                    acc[j][0] = __builtin_fmaf(g0, lo_f32(xv[u][j], T{}), acc[j][0]);
+                    acc[j][1] = __builtin_fmaf(g1, hi_f32(xv[u][j], T{}), acc[j][1]);
+                }
             }
         }
     }
@@ -539,7 +565,7 @@ hipError_t launch_wgrad_t(const WgArgs &a, bool mfma, bool pm_p, bool pm_q, hipS
 template <typename T>
 hipError_t launch_reduce_t(const RdArgs &r, hipStream_t s)
 {
-    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(r.count, 256), 16384);
+    const unsigned blocks = (unsigned)cdiv(r.count, 64);
     hipLaunchKernelGGL((bwd_reduce_kernel<T>), dim3(blocks), dim3(256), 0, s, r);
     return hipGetLastError();
 }
