@@ -318,7 +318,9 @@ extern "C" int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int
     // ---- bias gradient ----
     if (plan.need_db) {
         const int64_t chunks = cdiv(d->C_out, 64);
-        plan.db_splits = std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, chunks), cdiv(M_y, 64)));
+        plan.db_splits = bgrad_by_rows(*d, plan.gy)
+                             ? d->N
+                             : std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, chunks), cdiv(M_y, 64)));
         ws = std::max<int64_t>(ws, round_up(plan.db_splits * d->C_out * 4, 256));
         plan.flops[2] = M_y * d->C_out;
         plan.bytes[2] = (numel(plan.gy) + d->C_out) * es;

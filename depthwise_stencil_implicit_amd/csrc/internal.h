@@ -129,6 +129,21 @@ enum { DW_CW = 0, DW_OCOLS = 1, DW_CHCHUNKS = 2, DW_COLCHUNKS = 3, DW_XBYTES = 4
 enum { WB_MFMA = 0, WB_APAD = 1, WB_BPAD = 2, WB_SPLITS = 3, WB_PBYTES = 4, WB_QBYTES = 5 };
 constexpr int64_t WB_DW = 8;
 
+// The bias gradient by rows: gy's channel stride is not 1 and every image's
+// channel plane is one dense run of at least 64 positions (channel-major gy),
+// so a workgroup per (image, channel) reads its run with consecutive lanes;
+// the ranges of the partial sums are then the images.
+inline bool bgrad_by_rows(const conv_desc &d, const conv_tensor &gy)
+{
+    if (gy.strides[1] == 1) return false;
+    int64_t acc = 1;
+    for (int i = d.spatial - 1; i >= 0; --i) {
+        if (d.out[i] > 1 && gy.strides[2 + i] != acc) return false;
+        acc *= d.out[i];
+    }
+    return acc >= 64 && d.N <= 65536;
+}
+
 // Launchers (defined in the .hip files).  `vec` selects the 16-byte path.
 int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *ws,
                  void *stream, bool vec);

@@ -325,9 +325,9 @@ struct BgArgs {
 };
 
 // Block (split, 64-channel chunk): 4 groups of 64 threads, thread = channel;
-// each group walks every 4th position of the split's range.  Channel-fastest
-// lanes read consecutive channels of one position (channels-last gy); the
-// partial sums of the 4 groups are added in LDS.
+// the groups take consecutive quarters of the split's range of positions.
+// Channel-fastest lanes read consecutive channels of one position
+// (channels-last gy); the partial sums of the 4 groups are added in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void bgrad_kernel(BgArgs a)
 {
@@ -570,9 +570,39 @@ hipError_t launch_reduce_t(const RdArgs &r, hipStream_t s)
     return hipGetLastError();
 }
 
+// Position-contiguous gy (channel-major, every image's channel plane one
+// run): block (n, c) sums the run of positions of one plane, lanes on
+// consecutive positions, into part[n][c] (the ranges are the images).
 template <typename T>
-hipError_t launch_bgrad_t(const BgArgs &b, hipStream_t s)
+__global__ __launch_bounds__(256) void bgrad_rows_kernel(BgArgs a)
 {
+    __shared__ float red[256];
+    const int c = blockIdx.x % a.C, n = blockIdx.x / a.C;
+    const int64_t L = (int64_t)a.O[0] * a.O[1] * a.O[2];
+    const T *__restrict__ G = static_cast<const T *>(a.gy) + (int64_t)n * a.gs_n + (int64_t)c * a.gs_c;
+    float s0 = 0.f, s1 = 0.f;
+    int64_t i = threadIdx.x;
+    for (; i + 256 < L; i += 512) {
+        s0 += to_f32(G[i]);
+        s1 += to_f32(G[i + 256]);
+    }
+    if (i < L) s0 += to_f32(G[i]);
+    red[threadIdx.x] = s0 + s1;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) a.part[(int64_t)n * a.C + c] = red[0];
+}
+
+template <typename T>
+hipError_t launch_bgrad_t(const BgArgs &b, bool rows, hipStream_t s)
+{
+    if (rows) {
+        hipLaunchKernelGGL((bgrad_rows_kernel<T>), dim3((unsigned)((int64_t)b.N * b.C)), dim3(256), 0, s, b);
+        return hipGetLastError();
+    }
     const int blocks = b.splits * (int)cdiv(b.C, 64);
     hipLaunchKernelGGL((bgrad_kernel<T>), dim3(blocks), dim3(256), 0, s, b);
     return hipGetLastError();
@@ -767,11 +797,12 @@ int launch_bgrad(const conv_bwd_plan_t &p, const void *gy, void *db, void *ws, v
     b.C = (int32_t)d.C_out;
     b.splits = (int32_t)p.db_splits;
     b.M = (int64_t)d.N * b.O[0] * b.O[1] * b.O[2];
+    const bool rows = bgrad_by_rows(d, p.gy);
     hipError_t e;
     switch (d.dtype) {
-    case CONV_F32: e = launch_bgrad_t<float>(b, s); break;
-    case CONV_F16: e = launch_bgrad_t<f16_t>(b, s); break;
-    default: e = launch_bgrad_t<bf16_t>(b, s); break;
+    case CONV_F32: e = launch_bgrad_t<float>(b, rows, s); break;
+    case CONV_F16: e = launch_bgrad_t<f16_t>(b, rows, s); break;
+    default: e = launch_bgrad_t<bf16_t>(b, rows, s); break;
     }
     if (e != hipSuccess) return CONV_EDEVICE;
     RdArgs r;
