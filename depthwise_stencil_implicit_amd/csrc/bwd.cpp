@@ -289,11 +289,27 @@ extern "C" int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int
         const bool dwk = !tr && d->dtype != CONV_F32 && d->spatial <= 2 && PC == 1 && QC == 1 &&
                          d->groups == d->C_in && d->C_in % 2 == 0 && T <= 88 && words(P) && words(Q);
         if (dwk) mfma = false;
-        const int64_t mode = dwk ? WB_DW : mfma ? (1 | (cm_p ? 0 : 2) | (cm_q ? 0 : 4)) : 0;
+        // Few channels per group on channel-major operands (every (image,
+        // channel) plane dense): the plane-staged schedule, one thread per
+        // (out channel, in channel, tap), the planes within 64 KB of LDS.
+        auto planes = [&](const conv_tensor &t, const int64_t *ext) {
+            int64_t acc = 1;
+            for (int i = d->spatial - 1; i >= 0; --i) {
+                if (ext[i] > 1 && t.strides[2 + i] != acc) return false;
+                acc *= ext[i];
+            }
+            return t.strides[1] != 1 || d->C_in == 1;
+        };
+        const bool plk = !tr && !dwk && !mfma && d->spatial <= 2 && PC * QC * T <= 1024 &&
+                         wgrad_plane_lds(*d) <= 64 * 1024 && planes(P, d->out) && planes(Q, d->in);
+        const int64_t mode = dwk ? WB_DW : plk ? WB_PLANE : mfma ? (1 | (cm_p ? 0 : 2) | (cm_q ? 0 : 4)) : 0;
         const int64_t apad = mfma ? round_up(PC, 128) : PC, bpad = mfma ? round_up(QC, 128) : QC;
         const int64_t steps = std::max<int64_t>(1, cdiv(M, 32));
         int64_t splits;
-        if (dwk) {
+        if (plk) {
+            // Ranges of images, about 1024 workgroups.
+            splits = std::max<int64_t>(1, std::min<int64_t>(d->N, cdiv(1024, d->groups)));
+        } else if (dwk) {
             // Ranges of rows (image, output row), about 1024 workgroups.
             const int64_t rows = d->N * (d->spatial == 2 ? d->out[0] : 1);
             splits = std::max<int64_t>(1, std::min<int64_t>(rows, cdiv(1024, cdiv(d->C_in, 64))));
@@ -375,8 +391,9 @@ extern "C" int conv_run_backward(const conv_bwd_plan_t *p, const void *x, const 
             // aligned operands; otherwise the simple kernel.
             conv_bwd_plan_t q = *p;
             const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(gy);
-            if ((q.wg_tile[WB_MFMA] == WB_DW && (al & 3)) ||
-                (q.wg_tile[WB_MFMA] != WB_DW && (q.wg_tile[WB_MFMA] & 6) != 6 && q.wg_tile[WB_MFMA] && (al & 15))) {
+            const int64_t md = q.wg_tile[WB_MFMA];
+            if ((md == WB_DW && (al & 3)) ||
+                (md != WB_DW && md != WB_PLANE && (md & 6) != 6 && md && (al & 15))) {
                 q.wg_tile[WB_MFMA] = 0;
                 q.wg_tile[WB_APAD] = d.transposed ? d.C_in / d.groups : d.C_out / d.groups;
                 q.wg_tile[WB_BPAD] = d.transposed ? d.C_out / d.groups : d.C_in / d.groups;

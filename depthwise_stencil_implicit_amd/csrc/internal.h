@@ -128,6 +128,23 @@ enum { DW_CW = 0, DW_OCOLS = 1, DW_CHCHUNKS = 2, DW_COLCHUNKS = 3, DW_XBYTES = 4
 // operands for the 16-byte loads.
 enum { WB_MFMA = 0, WB_APAD = 1, WB_BPAD = 2, WB_SPLITS = 3, WB_PBYTES = 4, WB_QBYTES = 5 };
 constexpr int64_t WB_DW = 8;
+// WB_PLANE: forward calls on channel-major operands (each (image, channel)
+// plane of x and gy dense), few channels per group: a workgroup per (group,
+// range of images) stages each image's planes in LDS as fp32 and a thread per
+// (output channel, input channel, tap) walks the positions.
+constexpr int64_t WB_PLANE = 16;
+// LDS of that schedule: the group's gy planes plus its x planes with the
+// padding as a zero halo, fp32.
+inline int64_t wgrad_plane_lds(const conv_desc &d)
+{
+    const int64_t Cig = d.C_in / d.groups, Cog = d.C_out / d.groups;
+    int64_t pos = 1, halo = 1;
+    for (int i = 0; i < d.spatial; ++i) {
+        pos *= d.out[i];
+        halo *= d.in[i] + d.padding_before[i] + d.padding_after[i];
+    }
+    return (Cog * pos + Cig * halo) * 4;
+}
 
 // The bias gradient by rows: gy's channel stride is not 1 and every image's
 // channel plane is one dense run of at least 64 positions (channel-major gy),

@@ -27,6 +27,9 @@
 //                 current one is multiplied.
 //   wgrad_simple  any dtype and layout: one thread per weight element and
 //                 range of m, fp32 sums.
+//   wgrad_plane   few channels per group, channel-major x and gy: a workgroup
+//                 per (group, range of images) stages each image's planes in
+//                 LDS; a thread per (out channel, in channel, tap) walks them.
 //   wgrad_dw      depthwise, 16-bit, channels-last x and gy: a workgroup owns
 //                 32 channel words (64 channels) and one range of rows (n,
 //                 output row); thread = one channel word x one of 8 tap groups
@@ -54,6 +57,7 @@ struct WgArgs {
     int32_t E[3];                // P's spatial extents (positions m)
     int32_t F[3];                // Q's spatial extents
     int32_t K[3], S[3], PB[3], D[3];
+    int32_t PH2, PW2;            // padding after in slots 1 and 2 (the plane schedule's halo)
     int32_t splits;              // ranges of m
     int64_t M;                   // N * E0 * E1 * E2
     int32_t p_bytes, q_bytes;    // buffer ranges (16-byte path)
@@ -525,6 +529,77 @@ __global__ __launch_bounds__(256) void wgrad_dw_kernel(WgArgs a)
     }
 }
 
+// Few-channel grouped weight gradient on channel-major operands (forward
+// calls, rank <= 2 in slots 1 and 2 of WgArgs): workgroup = (group g, range of
+// images).  Per image, the group's QC x planes land in LDS as fp32 inside a
+// zero halo of the padding, and its PC gy planes beside them; thread j walks
+// the (a, b, t) = (output channel, input channel, tap) elements j, j + 256,
+// ... and, per element, every position:
+//   dw[g*PC + a, b, t] += gy[a, e1, e2] * xh[b, e1*S1 + kh*D1, e2*S2 + kw*D2].
+// fp32 partial sums per range of images go to part[sp][g][t][a][b].
+template <typename T>
+__global__ __launch_bounds__(256) void wgrad_plane_kernel(WgArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) float wl[];
+    const int g = blockIdx.x % a.G, sp = blockIdx.x / a.G;
+    const int E1 = a.E[1], E2 = a.E[2];
+    const int HH = a.F[1] + a.PB[1] + a.PH2, WW = a.F[2] + a.PB[2] + a.PW2;   // haloed x plane
+    float *gyl = wl;                                  // [PC][E1][E2]
+    float *xl = wl + a.PC * E1 * E2;                  // [QC][HH][WW]
+    const int EL = a.PC * a.QC * a.T;                 // elements of the group's gradient
+    const int n0 = (int)((int64_t)a.N * sp / a.splits), n1 = (int)((int64_t)a.N * (sp + 1) / a.splits);
+    const T *__restrict__ P = static_cast<const T *>(a.P);
+    const T *__restrict__ Q = static_cast<const T *>(a.Q);
+    const int KW = a.K[2];
+    float acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = 0.f;
+    for (int n = n0; n < n1; ++n) {
+        __syncthreads();   // the previous image's planes are no longer read
+        for (int i = threadIdx.x; i < a.PC * E1 * E2; i += 256) {
+            const int c = i / (E1 * E2), pos = i - c * (E1 * E2);
+            const int e1 = pos / E2, e2 = pos - e1 * E2;
+            gyl[i] = to_f32(P[(int64_t)n * a.ps_n + (int64_t)(g * a.PC + c) * a.ps_c + (int64_t)e1 * a.ps_l[1] +
+                              (int64_t)e2 * a.ps_l[2]]);
+        }
+        for (int i = threadIdx.x; i < a.QC * HH * WW; i += 256) {
+            const int c = i / (HH * WW), pos = i - c * (HH * WW);
+            const int h = pos / WW - a.PB[1], w = pos % WW - a.PB[2];
+            float v = 0.f;
+            if ((unsigned)h < (unsigned)a.F[1] && (unsigned)w < (unsigned)a.F[2])
+                v = to_f32(Q[(int64_t)n * a.qs_n + (int64_t)(g * a.QC + c) * a.qs_c + (int64_t)h * a.qs_l[1] +
+                             (int64_t)w * a.qs_l[2]]);
+            xl[i] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int el = threadIdx.x + r * 256;
+            if (el >= EL) break;
+            const int t = el % a.T, ab = el / a.T;
+            const int bi = ab % a.QC, ai = ab / a.QC;
+            const int kh = t / KW, kw = t % KW;
+            const float *gp = gyl + ai * E1 * E2;
+            const float *xp = xl + bi * HH * WW + kh * a.D[1] * WW + kw * a.D[2];
+            float s = 0.f;
+            for (int e1 = 0; e1 < E1; ++e1) {
+                const float *gr = gp + e1 * E2;
+                const float *xr = xp + e1 * a.S[1] * WW;
+                for (int e2 = 0; e2 < E2; ++e2) s = __builtin_fmaf(gr[e2], xr[e2 * a.S[2]], s);
+            }
+            acc[r] += s;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int el = threadIdx.x + r * 256;
+        if (el >= EL) break;
+        const int t = el % a.T, ab = el / a.T;
+        const int bi = ab % a.QC, ai = ab / a.QC;
+        a.part[(((int64_t)sp * a.G + g) * a.T + t) * a.apad * a.bpad + (int64_t)ai * a.bpad + bi] = acc[r];
+    }
+}
+
 template <typename T>
 hipError_t launch_wgrad_dw(const WgArgs &a, hipStream_t s)
 {
@@ -744,14 +819,28 @@ int launch_wgrad(const conv_bwd_plan_t &p, const void *x, const void *gy, void *
     a.M = (int64_t)d.N * a.E[0] * a.E[1] * a.E[2];
     a.p_bytes = (int32_t)p.wg_tile[WB_PBYTES];
     a.q_bytes = (int32_t)p.wg_tile[WB_QBYTES];
+    a.PH2 = d.spatial == 2 ? (int32_t)d.padding_after[0] : 0;
+    a.PW2 = (int32_t)d.padding_after[d.spatial - 1];
+    if (p.wg_tile[WB_MFMA] == WB_PLANE) {
+        const size_t lds = (size_t)wgrad_plane_lds(d);
+        const dim3 blocks((unsigned)((int64_t)a.G * a.splits));
+        switch (d.dtype) {
+        case CONV_F32: hipLaunchKernelGGL((wgrad_plane_kernel<float>), blocks, dim3(256), lds, s, a); break;
+        case CONV_F16: hipLaunchKernelGGL((wgrad_plane_kernel<f16_t>), blocks, dim3(256), lds, s, a); break;
+        default: hipLaunchKernelGGL((wgrad_plane_kernel<bf16_t>), blocks, dim3(256), lds, s, a); break;
+        }
+        if (hipGetLastError() != hipSuccess) return CONV_EDEVICE;
+    }
     const bool dwk = p.wg_tile[WB_MFMA] == WB_DW;
-    const bool mfma = p.wg_tile[WB_MFMA] != 0 && !dwk;
+    const bool mfma = p.wg_tile[WB_MFMA] != 0 && !dwk && p.wg_tile[WB_MFMA] != WB_PLANE;
     const bool pm_p = (p.wg_tile[WB_MFMA] & 2) != 0, pm_q = (p.wg_tile[WB_MFMA] & 4) != 0;
-    hipError_t e;
-    switch (d.dtype) {
-    case CONV_F32: e = launch_wgrad_t<float>(a, false, false, false, s); break;
-    case CONV_F16: e = dwk ? launch_wgrad_dw<f16_t>(a, s) : launch_wgrad_t<f16_t>(a, mfma, pm_p, pm_q, s); break;
-    default: e = dwk ? launch_wgrad_dw<bf16_t>(a, s) : launch_wgrad_t<bf16_t>(a, mfma, pm_p, pm_q, s); break;
+    hipError_t e = hipSuccess;
+    if (p.wg_tile[WB_MFMA] != WB_PLANE) {
+        switch (d.dtype) {
+        case CONV_F32: e = launch_wgrad_t<float>(a, false, false, false, s); break;
+        case CONV_F16: e = dwk ? launch_wgrad_dw<f16_t>(a, s) : launch_wgrad_t<f16_t>(a, mfma, pm_p, pm_q, s); break;
+        default: e = dwk ? launch_wgrad_dw<bf16_t>(a, s) : launch_wgrad_t<bf16_t>(a, mfma, pm_p, pm_q, s); break;
+        }
     }
     if (e != hipSuccess) return CONV_EDEVICE;
     RdArgs r;

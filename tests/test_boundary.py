@@ -382,7 +382,8 @@ def test_gradient_schedules():
     """The dense call's weight gradient runs on the matrix cores with both
     operands channel-major; the transposed 1-D call's with its contiguous gy
     read position-major; channels-last 16-bit depthwise weight gradients use
-    the depthwise stencil (mode 8) and fp32 NCHW ones the simple kernel; the
+    the depthwise stencil (mode 8), channel-major few-channel ones (fp32
+    depthwise NCHW, the grouped workload) the plane-staged schedule (16); the
     input gradient of a forward call is a transposed call and vice versa,
     except stride-1 stencil calls, whose dx is a forward call on the reversed
     weight."""
@@ -395,7 +396,9 @@ def test_gradient_schedules():
     _, _, dw2 = _bwd(synth.depthwise_bf16_cl(5, 2))
     assert dw2.plan.wg_tile[0] == 8 and dw2.plan.dgrad_flip == 0
     _, _, small = _bwd(synth.depthwise_f32_small())
-    assert small.plan.wg_tile[0] == 0 and small.plan.dgrad_flip == 1
+    assert small.plan.wg_tile[0] == 16 and small.plan.dgrad_flip == 1
+    _, _, gp = _bwd(synth.grouped_f16())
+    assert gp.plan.wg_tile[0] == 16 and gp.plan.dgrad_flip == 1 and api.kernel_name(gp.plan.dgrad.kernel) == "grp"
     assert dense.plan.flops[1] == dense.plan.flops[0] == 2 * 200704 * 256 * 2304
     assert dense.plan.workspace_bytes >= dense.plan.wg_tile[3] * 9 * 256 * 256 * 4
 
