@@ -832,12 +832,13 @@ namespace {
 // launch's PHW = pb mod S: which (column, tap) pairs meet, and at which input
 // column of the lane's window, is decided at compile time.  Rows are
 // uniform over the workgroup: a kernel row whose numerator is not a multiple
-// of the row stride, or that falls outside the input, is skipped.  Element
-// loads and stores (no alignment beyond the element), fp32 accumulation from
-// the bias, one rounding.
+// of the row stride, or that falls outside the input, is skipped.  x is read
+// as channel words where it is word-aligned with an even channel count (WX),
+// else element by element; element stores at y's strides; fp32 accumulation
+// from the bias, one rounding.
 __host__ __device__ constexpr int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
-template <typename T, int KB, int S, int PHW>
+template <typename T, int KB, int S, int PHW, bool WX>
 __global__ __launch_bounds__(256) void dwt_kernel(DwgArgs a)
 {
     constexpr int V = Dt<T>::size == 2 ? 2 : 1;
@@ -886,8 +887,16 @@ __global__ __launch_bounds__(256) void dwt_kernel(DwgArgs a)
         for (int j = 0; j < NX; ++j) {
             const int iw = base + j;
             const bool ok = (unsigned)iw < (unsigned)a.W;
+            if constexpr (WX) {
+                // Both channels of the word in one 4-byte load (even C,
+                // word-aligned x).
+                const uint32_t u = ok ? *reinterpret_cast<const uint32_t *>(xr + (int64_t)iw * a.xs_w) : 0u;
+                xw[j][0] = lo_f32(u, T{});
+                xw[j][V - 1] = hi_f32(u, T{});
+            } else {
 #pragma unroll
-            for (int v = 0; v < V; ++v) xw[j][v] = (ok && v < nv) ? to_f32(xr[(int64_t)iw * a.xs_w + v]) : 0.f;
+                for (int v = 0; v < V; ++v) xw[j][v] = (ok && v < nv) ? to_f32(xr[(int64_t)iw * a.xs_w + v]) : 0.f;
+            }
         }
 #pragma unroll
         for (int t = 0; t < TO; ++t)
@@ -910,13 +919,13 @@ __global__ __launch_bounds__(256) void dwt_kernel(DwgArgs a)
     }
 }
 
-template <typename T>
+template <typename T, bool WX>
 hipError_t dwt_go(const DwgArgs &a, dim3 grid, hipStream_t s)
 {
     const int kb = a.KW <= 3 ? 3 : (a.KW <= 5 ? 5 : (a.KW <= 7 ? 7 : 9));
     const int ph = a.PW % a.SW;
 #define MICONV_DWT(KB_, S_, P_) \
-    if (kb == KB_ && a.SW == S_ && ph == P_) hipLaunchKernelGGL((dwt_kernel<T, KB_, S_, P_>), grid, dim3(256), 0, s, a); else
+    if (kb == KB_ && a.SW == S_ && ph == P_) hipLaunchKernelGGL((dwt_kernel<T, KB_, S_, P_, WX>), grid, dim3(256), 0, s, a); else
     MICONV_DWT(3, 1, 0) MICONV_DWT(5, 1, 0) MICONV_DWT(7, 1, 0) MICONV_DWT(9, 1, 0)
     MICONV_DWT(3, 2, 0) MICONV_DWT(5, 2, 0) MICONV_DWT(7, 2, 0) MICONV_DWT(9, 2, 0)
     MICONV_DWT(3, 2, 1) MICONV_DWT(5, 2, 1) MICONV_DWT(7, 2, 1) MICONV_DWT(9, 2, 1) return hipErrorInvalidValue;
@@ -985,11 +994,14 @@ int launch_dwg(const conv_plan_t &p, const void *x, const void *w, const void *b
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)p.grid[0]);
     if (d.transposed) {
+        // Word loads of x: 16-bit, even channel count, x word-aligned.
+        const bool twx = esize(d.dtype) == 2 && d.C_in % 2 == 0 && (reinterpret_cast<uintptr_t>(x) & 3) == 0 &&
+                         a.xs_n % 2 == 0 && a.xs_h % 2 == 0 && a.xs_w % 2 == 0;
         hipError_t e;
         switch (d.dtype) {
-        case CONV_F32: e = dwt_go<float>(a, grid, s); break;
-        case CONV_F16: e = dwt_go<f16_t>(a, grid, s); break;
-        default: e = dwt_go<bf16_t>(a, grid, s); break;
+        case CONV_F32: e = dwt_go<float, false>(a, grid, s); break;
+        case CONV_F16: e = twx ? dwt_go<f16_t, true>(a, grid, s) : dwt_go<f16_t, false>(a, grid, s); break;
+        default: e = twx ? dwt_go<bf16_t, true>(a, grid, s) : dwt_go<bf16_t, false>(a, grid, s); break;
         }
         return e == hipSuccess ? CONV_OK : CONV_EDEVICE;
     }
