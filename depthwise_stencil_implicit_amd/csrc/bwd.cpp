@@ -312,7 +312,8 @@ extern "C" int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int
         } else if (dwk) {
             // Ranges of rows (image, output row), about 1024 workgroups.
             const int64_t rows = d->N * (d->spatial == 2 ? d->out[0] : 1);
-            splits = std::max<int64_t>(1, std::min<int64_t>(rows, cdiv(1024, cdiv(d->C_in, 64))));
+            const int64_t per_wg = 2 * 256 / wgrad_dw_tg(T);   // channels of a workgroup
+            splits = std::max<int64_t>(1, std::min<int64_t>(rows, cdiv(1024, cdiv(d->C_in, per_wg))));
         } else if (mfma) {
             const int64_t tiles = d->groups * T * (apad / 128) * (bpad / 128);
             splits = std::max<int64_t>(1, std::min<int64_t>(steps / 4 > 0 ? steps / 4 : 1, cdiv(1024, tiles)));

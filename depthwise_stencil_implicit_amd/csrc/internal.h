@@ -128,6 +128,10 @@ enum { DW_CW = 0, DW_OCOLS = 1, DW_CHCHUNKS = 2, DW_COLCHUNKS = 3, DW_XBYTES = 4
 // operands for the 16-byte loads.
 enum { WB_MFMA = 0, WB_APAD = 1, WB_BPAD = 2, WB_SPLITS = 3, WB_PBYTES = 4, WB_QBYTES = 5 };
 constexpr int64_t WB_DW = 8;
+// Tap groups of the depthwise weight-gradient stencil: a workgroup holds
+// 256 / TG channel words x TG groups of taps, fewer groups for small kernels
+// so that one gy word feeds more taps.
+inline int wgrad_dw_tg(int64_t taps) { return taps <= 16 ? 2 : (taps <= 28 ? 4 : 8); }
 // WB_PLANE: forward calls on channel-major operands (each (image, channel)
 // plane of x and gy dense), few channels per group: a workgroup per (group,
 // range of images) stages each image's planes in LDS as fp32 and a thread per

@@ -31,10 +31,11 @@
 //                 per (group, range of images) stages each image's planes in
 //                 LDS; a thread per (out channel, in channel, tap) walks them.
 //   wgrad_dw      depthwise, 16-bit, channels-last x and gy: a workgroup owns
-//                 32 channel words (64 channels) and one range of rows (n,
-//                 output row); thread = one channel word x one of 8 tap groups
-//                 (taps tg, tg + 8, ...), looping over the row's positions:
-//                 one gy word, then one x word per tap, two fp32 FMAs each.
+//                 256/TG channel words and one range of rows (n, output
+//                 row); thread = one channel word x one of TG tap groups (taps
+//                 tg, tg + TG, ...; TG = 2, 4 or 8 by kernel size), looping over
+//                 the row's positions: one gy word, then one x word per tap,
+//                 two fp32 FMAs each.
 //   bgrad         per-channel sums of gy over one range of positions.
 //   bwd_reduce    sums the fp32 partial sums of the ranges (64 outputs x 4
 //                 interleaved quarters of the ranges per workgroup), rounds
@@ -452,21 +453,22 @@ namespace {
 // of gy[n, e1, e2, c] * x[n, e1*S1 - PB1 + kh*D1, e2*S2 - PB2 + kw*D2, c] for
 // tap t = (kh, kw), in the slots 1 and 2 of WgArgs (slot 0 has extent 1).
 // Partial sums per range of rows go to part[sp][c][t] (apad = bpad = 1).
-template <typename T, int MT>
+template <typename T, int MT, int TG>
 __global__ __launch_bounds__(256) void wgrad_dw_kernel(WgArgs a)
 {
+    constexpr int WPG = 256 / TG;                // channel words of the workgroup
     const int tid = threadIdx.x;
-    const int wd = tid & 31, tg = tid >> 5;
-    const int cchunks = (a.G + 63) / 64;
+    const int wd = tid % WPG, tg = tid / WPG;
+    const int cchunks = (a.G + 2 * WPG - 1) / (2 * WPG);
     const int cc = blockIdx.x % cchunks, sp = blockIdx.x / cchunks;
-    const int word = cc * 32 + wd;
+    const int word = cc * WPG + wd;
     const bool cok = 2 * word < a.G;
     const int KW = a.K[2];
     int dh[MT], dwo[MT];
     bool tv[MT];
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-        const int t = tg + 8 * j;
+        const int t = tg + TG * j;
         tv[j] = t < a.T;
         dh[j] = tv[j] ? (t / KW) * a.D[1] : 0;
         dwo[j] = tv[j] ? (t % KW) * a.D[2] : 0;
@@ -523,7 +525,7 @@ __global__ __launch_bounds__(256) void wgrad_dw_kernel(WgArgs a)
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
         if (!tv[j]) continue;
-        const int t = tg + 8 * j;
+        const int t = tg + TG * j;
         part[(int64_t)(2 * word) * a.T + t] = acc[j][0];
         part[(int64_t)(2 * word + 1) * a.T + t] = acc[j][1];
     }
@@ -604,12 +606,14 @@ template <typename T>
 hipError_t launch_wgrad_dw(const WgArgs &a, hipStream_t s)
 {
     if constexpr (Dt<T>::size == 2) {
-        const dim3 blocks((unsigned)(((a.G + 63) / 64) * (int64_t)a.splits));
-        const int mt = (a.T + 7) / 8;
-        if (mt <= 2) hipLaunchKernelGGL((wgrad_dw_kernel<T, 2>), blocks, dim3(256), 0, s, a);
-        else if (mt <= 4) hipLaunchKernelGGL((wgrad_dw_kernel<T, 4>), blocks, dim3(256), 0, s, a);
-        else if (mt <= 7) hipLaunchKernelGGL((wgrad_dw_kernel<T, 7>), blocks, dim3(256), 0, s, a);
-        else if (mt <= 11) hipLaunchKernelGGL((wgrad_dw_kernel<T, 11>), blocks, dim3(256), 0, s, a);
+        const int tg = wgrad_dw_tg(a.T);
+        const dim3 blocks((unsigned)(((a.G + 2 * (256 / tg) - 1) / (2 * (256 / tg))) * (int64_t)a.splits));
+        const int mt = (a.T + tg - 1) / tg;
+        if (tg == 2 && mt <= 5) hipLaunchKernelGGL((wgrad_dw_kernel<T, 5, 2>), blocks, dim3(256), 0, s, a);
+        else if (tg == 2 && mt <= 8) hipLaunchKernelGGL((wgrad_dw_kernel<T, 8, 2>), blocks, dim3(256), 0, s, a);
+        else if (tg == 4 && mt <= 7) hipLaunchKernelGGL((wgrad_dw_kernel<T, 7, 4>), blocks, dim3(256), 0, s, a);
+        else if (tg == 8 && mt <= 7) hipLaunchKernelGGL((wgrad_dw_kernel<T, 7, 8>), blocks, dim3(256), 0, s, a);
+        else if (tg == 8 && mt <= 11) hipLaunchKernelGGL((wgrad_dw_kernel<T, 11, 8>), blocks, dim3(256), 0, s, a);
         else return hipErrorInvalidValue;
         return hipGetLastError();
     }
