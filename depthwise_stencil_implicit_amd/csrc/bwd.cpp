@@ -161,6 +161,23 @@ bool flipped_desc(const conv_desc &d, const conv_tensor &gy, conv_desc &f)
     return true;
 }
 
+// A channel-major 16-bit gy of 16 MiB or more beside channels-last x is
+// first copied channels-last (one transpose pass), so the input and weight
+// gradients read both operands in 16-byte channel chunks (and dx takes x's
+// channels-last layout).  Returns the bytes of the copy (0: gy is read as
+// given) and the layout the gradients read in G.
+int64_t gy_stage(const conv_desc &d, const conv_tensor &gyb, conv_tensor &G)
+{
+    G = gyb;
+    const int64_t bytes = numel(gyb) * esize(d.dtype);
+    if (d.dtype == CONV_F32 || d.x.strides[1] != 1 || d.N > 65535 || d.C_out < 64 || d.C_out % 8 != 0 ||
+        !bgrad_by_rows(d, gyb) || bytes < (16 << 20) || bytes >= kI32 - 4096 ||
+        cdiv(numel(gyb) / (d.N * d.C_out), 64) > 65535)
+        return 0;
+    channels_last_of(gyb, G);
+    return round_up(bytes, 256);
+}
+
 // Dense strides in the dim order of t's strides (its memory format).
 void dense_like(const conv_tensor &t, conv_tensor &o)
 {
@@ -190,7 +207,9 @@ extern "C" int conv_backward_layout(const conv_desc *d, const conv_tensor *gy, c
     if (!batched_like_y(*d, *gy, gyb)) return CONV_ELAYOUT;
     if (dx) {
         conv_desc a;
-        if (!adjoint_desc(*d, gyb, a)) return CONV_EUNSUPPORTED;
+        conv_tensor G;
+        gy_stage(*d, gyb, G);
+        if (!adjoint_desc(*d, G, a)) return CONV_EUNSUPPORTED;
         conv_tensor xb;
         batched_out(a, xb);
         if (!d->unbatched) {
@@ -231,15 +250,19 @@ extern "C" int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int
     const int64_t es = esize(d->dtype);
     int64_t ws = 0;
     const int64_t M_y = d->N * d->out[0] * d->out[1] * d->out[2];
+    // G: the gy layout the gradient kernels read (a channels-last copy of a
+    // large channel-major gy, when staged).
+    conv_tensor G;
+    const int64_t stage = (need_dx || need_dw) ? gy_stage(*d, plan.gy, G) : (G = plan.gy, 0);
 
     // ---- input gradient: the adjoint call on the planner's kernels ----
     if (plan.need_dx) {
         conv_desc a;
-        if (!adjoint_desc(*d, plan.gy, a)) return CONV_EUNSUPPORTED;
+        if (!adjoint_desc(*d, G, a)) return CONV_EUNSUPPORTED;
         batched_out(a, plan.dx);
         conv_desc f;
         conv_plan_t fp;
-        if (flipped_desc(*d, plan.gy, f) && conv_plan(&f, &plan.dx, CONV_K_AUTO, &fp) == CONV_OK &&
+        if (flipped_desc(*d, G, f) && conv_plan(&f, &plan.dx, CONV_K_AUTO, &fp) == CONV_OK &&
             fp.kernel != CONV_K_IGEMM && fp.kernel != CONV_K_IGEMM_T) {
             // The reversed weight first, then the stencil's own scratch.
             plan.dgrad = fp;
@@ -258,8 +281,8 @@ extern "C" int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int
     conv_backward_layout(d, gy, nullptr, &plan.dw, nullptr);
     if (plan.need_dw) {
         const bool tr = d->transposed != 0;
-        const conv_tensor &P = tr ? d->x : plan.gy;
-        const conv_tensor &Q = tr ? plan.gy : d->x;
+        const conv_tensor &P = tr ? d->x : G;
+        const conv_tensor &Q = tr ? G : d->x;
         const int64_t Cig = d->C_in / d->groups, Cog = d->C_out / d->groups;
         const int64_t PC = tr ? Cig : Cog, QC = tr ? Cog : Cig;
         const int64_t T = d->k[0] * d->k[1] * d->k[2];
@@ -346,7 +369,8 @@ extern "C" int conv_plan_backward(const conv_desc *d, const conv_tensor *gy, int
         plan.db.sizes[0] = d->C_out;
         plan.db.strides[0] = 1;
     }
-    plan.workspace_bytes = ws;
+    plan.wg_tile[WB_GYCL] = stage;
+    plan.workspace_bytes = stage + ws;
     *p = plan;
     return CONV_OK;
 }
@@ -371,6 +395,22 @@ extern "C" int conv_run_backward(const conv_bwd_plan_t *p, const void *x, const 
     for (const void *q : {(const void *)x, (const void *)w, gy, (const void *)dx, (const void *)dw, (const void *)db})
         if (q && (reinterpret_cast<uintptr_t>(q) & (es - 1))) return CONV_EALIGN;
     int st = CONV_OK;
+    // A staged gy: the channels-last copy first, then the input and weight
+    // gradients read it, with the rest of the workspace after it.
+    conv_bwd_plan_t staged;
+    const conv_bwd_plan_t *const p0 = p;
+    const void *const gy0 = gy;
+    const int64_t stage = p->wg_tile[WB_GYCL];
+    if (stage > 0 && have_pos) {
+        st = launch_gy_to_cl(*p, gy, workspace, stream);
+        if (st != CONV_OK) return st;
+        staged = *p;
+        channels_last_of(p->gy, staged.gy);
+        gy = workspace;
+        workspace = static_cast<char *>(workspace) + stage;
+        workspace_bytes -= (size_t)stage;
+        p = &staged;
+    }
     if (p->need_dx && numel(p->dx) > 0) {
         if (p->dgrad_flip) {
             const size_t off = (size_t)round_up(numel(p->dgrad.d.w) * (int64_t)es, 256);
@@ -404,6 +444,7 @@ extern "C" int conv_run_backward(const conv_bwd_plan_t *p, const void *x, const 
         if (st != CONV_OK) return st;
     }
     if (p->need_db && d.C_out > 0)
-        st = have_pos ? launch_bgrad(*p, gy, db, workspace, stream) : launch_fill_zero(db, p->db, stream);
+        // The bias gradient reads gy as given (a channel-major gy by rows).
+        st = have_pos ? launch_bgrad(*p0, gy0, db, workspace, stream) : launch_fill_zero(db, p->db, stream);
     return st;
 }

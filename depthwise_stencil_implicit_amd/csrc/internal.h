@@ -126,7 +126,22 @@ enum { DW_CW = 0, DW_OCOLS = 1, DW_CHCHUNKS = 2, DW_COLCHUNKS = 3, DW_XBYTES = 4
 // position-major) for the matrix-core one; padded a / b extents, ranges of
 // positions (of rows of positions for WB_DW), and the byte ranges of the two
 // operands for the 16-byte loads.
-enum { WB_MFMA = 0, WB_APAD = 1, WB_BPAD = 2, WB_SPLITS = 3, WB_PBYTES = 4, WB_QBYTES = 5 };
+enum { WB_MFMA = 0, WB_APAD = 1, WB_BPAD = 2, WB_SPLITS = 3, WB_PBYTES = 4, WB_QBYTES = 5, WB_GYCL = 6 };
+// WB_GYCL (conv_bwd_plan_t.wg_tile[6]): bytes of a channels-last copy of a
+// channel-major gy at the start of the workspace (0: gy is read as given).
+// The gradients of a call with channels-last x then read gy channels-last
+// too: the 16-byte implicit-GEMM and matrix-core weight-gradient paths.
+inline void channels_last_of(const conv_tensor &t, conv_tensor &o)
+{
+    o = t;
+    int64_t acc = t.sizes[1];
+    o.strides[1] = 1;
+    for (int i = t.rank - 1; i >= 2; --i) {
+        o.strides[i] = acc;
+        acc *= t.sizes[i];
+    }
+    o.strides[0] = acc;
+}
 constexpr int64_t WB_DW = 8;
 // Tap groups of the depthwise weight-gradient stencil: a workgroup holds
 // 256 / TG channel words x TG groups of taps, fewer groups for small kernels
@@ -164,6 +179,10 @@ inline bool bgrad_by_rows(const conv_desc &d, const conv_tensor &gy)
     }
     return acc >= 64 && d.N <= 65536;
 }
+
+// The channels-last copy of a channel-major gy (each (image, channel) plane
+// one dense run of L positions), into dst.
+int launch_gy_to_cl(const conv_bwd_plan_t &p, const void *gy, void *dst, void *stream);
 
 // Launchers (defined in the .hip files).  `vec` selects the 16-byte path.
 int launch_igemm(const conv_plan_t &p, const void *x, const void *w, const void *b, void *y, void *ws,

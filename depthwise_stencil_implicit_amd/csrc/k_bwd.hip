@@ -37,6 +37,9 @@
 //                 the row's positions: one gy word, then one x word per tap,
 //                 two fp32 FMAs each.
 //   bgrad         per-channel sums of gy over one range of positions.
+//   gy_to_cl      a channel-major 16-bit gy copied channels-last through LDS
+//                 tiles, so the gradients of a channels-last call read both
+//                 operands in 16-byte channel chunks.
 //   bwd_reduce    sums the fp32 partial sums of the ranges (64 outputs x 4
 //                 interleaved quarters of the ranges per workgroup), rounds
 //                 once to the dtype and stores at the gradient's strides.
@@ -775,6 +778,55 @@ int launch_flip_weight(const conv_bwd_plan_t &p, const void *w, void *dst, void 
         hipLaunchKernelGGL((flip_weight_kernel<uint16_t>), dim3(blocks), dim3(256), 0, s,
                            static_cast<const uint16_t *>(w), static_cast<uint16_t *>(dst), count, Cig, Cog, K0, K1,
                            d.w.strides[0], d.w.strides[1], ws2, ws3);
+    return hipGetLastError() == hipSuccess ? CONV_OK : CONV_EDEVICE;
+}
+
+// A channel-major 16-bit gy (image stride gs0, channel stride gs1, each
+// (image, channel) plane a dense run of L positions) copied to the dense
+// channels-last [N][L][C]: a workgroup moves a 128-channel x 64-position
+// tile of one image through LDS, reading runs of 64 positions (128 bytes per
+// wave row) and writing runs of 128 channels as channel pairs (256 bytes per
+// wave row).  Channel tiles are the fastest grid dimension, so neighbouring
+// workgroups complete the same output rows.  Rows of 66 elements (33 words)
+// keep the column reads on distinct banks.  C is even.
+__global__ __launch_bounds__(256) void gy_to_cl_kernel(const uint16_t *__restrict__ gy, uint16_t *__restrict__ out,
+                                                        int64_t L, int32_t C, int64_t gs0, int64_t gs1)
+{
+    __shared__ uint16_t t[128][66];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c0 = blockIdx.x * 128;
+    const int64_t l0 = (int64_t)blockIdx.y * 64;
+    const int64_t n = blockIdx.z;
+    const uint16_t *src = gy + n * gs0;
+    const int64_t l = l0 + lane;
+#pragma unroll 8
+    for (int r = wv; r < 128; r += 4) {
+        const int c = c0 + r;
+        t[r][lane] = (c < C && l < L) ? src[(int64_t)c * gs1 + l] : (uint16_t)0;
+    }
+    __syncthreads();
+    uint32_t *dst = reinterpret_cast<uint32_t *>(out + n * L * C);
+    const int c = c0 + 2 * lane;
+#pragma unroll 4
+    for (int r = wv; r < 64; r += 4) {
+        const int64_t lr = l0 + r;
+        if (lr < L && c < C)
+            dst[(lr * C + c) >> 1] = (uint32_t)t[2 * lane][r] | ((uint32_t)t[2 * lane + 1][r] << 16);
+    }
+}
+
+int launch_gy_to_cl(const conv_bwd_plan_t &p, const void *gy, void *dst, void *stream)
+{
+    const conv_desc &d = p.d;
+    if (esize(d.dtype) != 2 || p.gy.strides[1] == 1) return CONV_EINVAL;
+    int64_t L = 1;
+    for (int i = 0; i < d.spatial; ++i) L *= d.out[i];
+    if (d.N == 0 || L == 0 || d.C_out == 0) return CONV_OK;
+    if (d.N > 65535 || cdiv(L, 64) > 65535) return CONV_EUNSUPPORTED;
+    if (d.C_out % 2 != 0) return CONV_EINVAL;
+    hipLaunchKernelGGL(gy_to_cl_kernel, dim3((unsigned)cdiv(d.C_out, 128), (unsigned)cdiv(L, 64), (unsigned)d.N),
+                       dim3(256), 0, static_cast<hipStream_t>(stream), static_cast<const uint16_t *>(gy),
+                       static_cast<uint16_t *>(dst), L, (int32_t)d.C_out, p.gy.strides[0], p.gy.strides[1]);
     return hipGetLastError() == hipSuccess ? CONV_OK : CONV_EDEVICE;
 }
 

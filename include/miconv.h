@@ -294,7 +294,12 @@ typedef struct conv_bwd_plan_t {
  *       for an unbatched call), any non-negative strides.
  *   dx  receives the input gradient's layout: the output layout of the
  *       adjoint call (forward and transposed exchanged, gy as its input, the
- *       same weight tensor), which has x's sizes.  May be NULL.
+ *       same weight tensor), which has x's sizes.  A 16-bit channel-major gy
+ *       of 16 MiB or more (each (image, channel) plane dense, C_out >= 64 and
+ *       a multiple of 8) beside channels-last x is read through a
+ *       channels-last copy (conv_bwd_plan_t.wg_tile[6] bytes at the start of
+ *       the workspace), and dx is then the adjoint call's output on that
+ *       copy (channels-last for 2-D and 3-D calls).  May be NULL.
  *   dw  receives w's sizes, dense in w's memory format.  May be NULL.
  *   db  receives [C_out], stride 1.  May be NULL.
  *

@@ -380,8 +380,9 @@ def test_gradient_layouts_of_the_workloads():
 
 def test_gradient_schedules():
     """The dense call's weight gradient runs on the matrix cores with both
-    operands channel-major; the transposed 1-D call's with its contiguous gy
-    read position-major; channels-last 16-bit depthwise weight gradients use
+    operands channel-major; the transposed 1-D call's contiguous gy is first
+    copied channels-last (wg_tile[6] bytes), so both of its gradients read
+    channel-major operands too; channels-last 16-bit depthwise weight gradients use
     the depthwise stencil (mode 8), channel-major few-channel ones (fp32
     depthwise NCHW, the grouped workload) the plane-staged schedule (16); the
     input gradient of a forward call is a transposed call and vice versa,
@@ -390,7 +391,8 @@ def test_gradient_schedules():
     _, _, dense = _bwd(synth.dense_bf16_cl())
     assert dense.plan.wg_tile[0] == 1 and api.kernel_name(dense.plan.dgrad.kernel) == "igemm_t"
     _, _, tr = _bwd(synth.transposed_bf16_nlc())
-    assert tr.plan.wg_tile[0] == 1 | 4 and api.kernel_name(tr.plan.dgrad.kernel) == "igemm"
+    assert tr.plan.wg_tile[0] == 1 and api.kernel_name(tr.plan.dgrad.kernel) == "igemm"
+    assert tr.plan.wg_tile[6] == 16 * 512 * 16383 * 2 and tr.plan.workspace_bytes > tr.plan.wg_tile[6]
     _, _, dw = _bwd(synth.depthwise_bf16_cl(3, 1))
     assert dw.plan.wg_tile[0] == 8 and dw.plan.dgrad_flip == 1 and api.kernel_name(dw.plan.dgrad.kernel) == "dw_cl"
     _, _, dw2 = _bwd(synth.depthwise_bf16_cl(5, 2))

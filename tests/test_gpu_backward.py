@@ -253,3 +253,46 @@ def test_depthwise_weight_gradient_stencil(wl):
     print(f"depthwise weight gradient: {_desc(wl)}", flush=True)
     prep, _ = check_backward(wl, seed=7, need=(False, True, True))
     assert int(prep.plan.wg_tile[0]) == 8
+
+
+def _staged_cases():
+    """Channels-last x with a channel-major gy of at least 16 MiB: depthwise
+    3x3, a transposed 1-D call with 72 output channels (a ragged 64-channel
+    tile) and a dense f16 3x3 with 80 output channels."""
+    mk = synth.random_case
+    return [
+        mk(8960, rank=2, transposed=False, dtype="bf16", channels_last=True, N=2, C_in=64, C_out=64, groups=64,
+           L=[256, 258], k=[3, 3], stride=[1, 1], padding_before=[1, 1], padding_after=[1, 1], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+        mk(8961, rank=1, transposed=True, dtype="bf16", channels_last=True, N=2, C_in=64, C_out=72, groups=1,
+           L=[30001], k=[4], stride=[2], padding_before=[1], padding_after=[1], dilation=[1], output_padding=[0],
+           has_bias=False),
+        mk(8962, rank=2, transposed=False, dtype="f16", channels_last=True, N=2, C_in=32, C_out=80, groups=1,
+           L=[210, 250], k=[3, 3], stride=[1, 1], padding_before=[1, 1], padding_after=[1, 1], dilation=[1, 1],
+           output_padding=[0, 0], has_bias=False),
+    ]
+
+
+@pytest.mark.parametrize("wl", _staged_cases(), ids=lambda w: w.name)
+def test_channel_major_gy_copied_channels_last(wl):
+    """A channel-major gy beside channels-last x is first copied
+    channels-last into the workspace (a 2-D call's dx then channels-last like
+    x, a 1-D call's dx contiguous as before); every
+    element of dx, dw and db read from the copy against the reference."""
+    print(f"staged gy: {_desc(wl)}", flush=True)
+    x, w, _ = synth.make_inputs(wl, device="cuda")
+    prep = api.Prepared(x, w, None, _args(wl))
+    g = torch.Generator().manual_seed(9)
+    gy = torch.randn(prep.sizes, generator=g).to(x.dtype).to("cuda").contiguous()
+    pb = api.PreparedBackward(x, w, gy, _args(wl))
+    assert int(pb.plan.wg_tile[6]) >= gy.numel() * gy.element_size()
+    dx, dw, db = pb.outputs(gy.device)
+    assert dx.stride(1) == 1 or x.dim() == 3, "a 2-D call's dx takes x's channels-last layout"
+    pb.run(x, w, gy, dx, dw, db, pb.workspace(gy.device))
+    torch.cuda.synchronize()
+    f = lambda t: t.detach().double().cpu().contiguous().numpy()
+    rdx, Adx, rdw, Adw, rdb, Adb = oracle.conv_backward(f(x), f(w), f(gy), **expand_kw(wl))
+    eps = EPS[wl.dtype]
+    _close(dx, rdx, Adx, eps, f"{wl.name} dx")
+    _close(dw, rdw, Adw, eps, f"{wl.name} dw")
+    _close(db, rdb, Adb, eps, f"{wl.name} db")
