@@ -799,15 +799,19 @@ __global__ __launch_bounds__(256) void gy_to_cl_kernel(const uint16_t *__restric
     const int64_t n = blockIdx.z;
     const uint16_t *src = gy + n * gs0;
     const int64_t l = l0 + lane;
-#pragma unroll 8
-    for (int r = wv; r < 128; r += 4) {
-        const int c = c0 + r;
-        t[r][lane] = (c < C && l < L) ? src[(int64_t)c * gs1 + l] : (uint16_t)0;
+    // All 32 reads of a thread in flight before the first LDS write.
+    uint16_t v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+        const int c = c0 + wv + 4 * u;
+        v[u] = (c < C && l < L) ? src[(int64_t)c * gs1 + l] : (uint16_t)0;
     }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) t[wv + 4 * u][lane] = v[u];
     __syncthreads();
     uint32_t *dst = reinterpret_cast<uint32_t *>(out + n * L * C);
     const int c = c0 + 2 * lane;
-#pragma unroll 4
+#pragma unroll
     for (int r = wv; r < 64; r += 4) {
         const int64_t lr = l0 + r;
         if (lr < L && c < C)
