@@ -32,8 +32,8 @@
 // instruction, fp32 accumulation); an odd kernel's last column pairs with a
 // zero half.  fp32 uses one FMA per tap.  Stores are issued by every step that
 // follows a finished output row (dropped out of range for an absent row or
-// column), so the number of VMEM instructions issued after each ring row is a
-// compile-time constant and the wait before reading it is exact.
+// column).  The wait before reading a ring row allows only the younger ring
+// loads to be pending, so the stores issued since are waited for too.
 //
 // Row blocks of one image alternate direction: odd blocks stream their rows
 // bottom to top (the same recurrence with the kernel flipped vertically), so
@@ -104,16 +104,16 @@ template <int K, int S> __device__ constexpr bool dw_stores(int v, bool first)
     return (!first || v >= 1) && dw_finishes<K, S>(v - 1);
 }
 // VMEM instructions that may still be pending when step u (position in the
-// unrolled block) waits for its ring row: the loads (LPW per row) of the D-2
-// rows issued after it and the stores (NS each) of the D-1 steps before it --
-// of this block's stream only when the unrolled block is the first (earlier
-// rows came from the prologue, which stores nothing).
-template <int K, int S, int LPW, int NS, int D> __device__ constexpr int dw_pending_at(int u, bool first)
+// unrolled block) waits for its ring row: only the loads (LPW per row) of the
+// D-2 rows issued after it.  Loads retire in order among themselves, so a
+// count at or below that bound means the row's own loads have landed.  The
+// output stores issued in between are not counted: they may retire before
+// older loads (measured: with input written by the kernel just before, a
+// bound that also allowed the pending stores let a step read a ring row that
+// had not landed yet), so they are waited for as well.
+template <int K, int S, int LPW, int NS, int D> __device__ constexpr int dw_pending_at(int, bool)
 {
-    int n = (D - 2) * LPW;
-    for (int d = 1; d < D; ++d)
-        if ((!first || u - d >= 0) && dw_stores<K, S>(u - d, first)) n += NS;
-    return n;
+    return (D - 2) * LPW;
 }
 template <int N> __device__ __forceinline__ void wait_vmcnt()
 {
